@@ -1,0 +1,231 @@
+"""Benchmark of the PlaneZip hot path on one MI355X.
+
+One step = compress and then decompress every tensor of the workload (the
+GPT-2-XL activations at batch 8, sequence 1024: MLP GELU output 8x1024x6400,
+causal softmax 8x25x1024x1024, residual 8x1024x1600, all BF16, ~0.55 GB),
+with inputs already resident in HBM. Prints one JSON line.
+
+value = raw bytes of the workload / time of one step (each raw byte is both
+compressed and decompressed in a step). The roofline object reports the
+dominant kernel call's algorithmic HBM traffic (read raw + write compressed
+for compression, the reverse for decompression) against MI355X's 8 TB/s.
+The CPU baseline is the oracle (oracle/pzref.c) on a bounded sample of the
+same tensors, on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--config", type=int, default=5)
+    p.add_argument("--cpu-sample-mb", type=float, default=24.0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-verify", action="store_true")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): the codec has no "
+              "cross-GPU path in this build; see DESIGN.md for how it would shard.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import lossless_bit_plane_amd as pz
+    import pzinputs
+
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    tensors = pzinputs.config(args.config)
+    log(f"generated config {args.config} in {time.time() - t0:.1f}s: "
+        + ", ".join(f"{t.name} {t.nbytes / 1e6:.1f} MB" for t in tensors))
+
+    # Device buffers, allocated once.
+    items = []
+    for t in tensors:
+        src = torch.from_numpy(t.data).to(dev)
+        cap = pz.max_compressed_bytes(t.nbytes)
+        items.append(dict(
+            t=t, src=src,
+            stream=torch.empty(cap, dtype=torch.uint8, device=dev),
+            nbytes=torch.zeros(1, dtype=torch.int64, device=dev),
+            out=torch.empty(t.nbytes, dtype=torch.uint8, device=dev),
+            status=torch.zeros(1, dtype=torch.int32, device=dev),
+        ))
+    torch.cuda.synchronize()
+
+    # Compressed sizes (device-side, read once before timing).
+    for it in items:
+        pz.pz_compress(it["src"], it["t"].dtype, it["t"].elem_bits, it["stream"], it["nbytes"])
+    torch.cuda.synchronize()
+    for it in items:
+        it["comp"] = int(it["nbytes"].item())
+
+    cur = torch.cuda.current_stream()
+
+    def step(events=None):
+        for i, it in enumerate(items):
+            t = it["t"]
+            if events is not None:
+                events[i][0].record(cur)
+            pz.pz_compress(it["src"], t.dtype, t.elem_bits, it["stream"], it["nbytes"])
+            if events is not None:
+                events[i][1].record(cur)
+        for i, it in enumerate(items):
+            t = it["t"]
+            if events is not None:
+                events[i][2].record(cur)
+            pz.pz_decompress(it["stream"], it["comp"], t.nbytes, t.dtype, t.elem_bits,
+                             it["out"], it["status"])
+            if events is not None:
+                events[i][3].record(cur)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    if not args.no_verify:
+        for it in items:
+            assert int(it["status"].item()) == 0, "decompress reported a corrupt stream"
+            assert torch.equal(it["out"], it["src"]), f"round trip mismatch on {it['t'].name}"
+        log("round trip verified on the device")
+
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in items]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    start = time.perf_counter()
+    for k in range(args.steps):
+        step(ev[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - start
+
+    raw_total = sum(it["t"].nbytes for it in items)
+    comp_total = sum(it["comp"] for it in items)
+    t_comp = np.zeros(len(items))
+    t_dec = np.zeros(len(items))
+    for k in range(args.steps):
+        for i in range(len(items)):
+            t_comp[i] += ev[k][i][0].elapsed_time(ev[k][i][1]) / 1e3
+            t_dec[i] += ev[k][i][2].elapsed_time(ev[k][i][3]) / 1e3
+    t_comp /= args.steps
+    t_dec /= args.steps
+    ms_per_step = wall / args.steps * 1e3
+    value = raw_total / (wall / args.steps) / 1e9
+
+    comp_s, dec_s = t_comp.sum(), t_dec.sum()
+    algo = raw_total + comp_total  # algorithmic HBM bytes per direction
+    comp_gbps = algo / comp_s / 1e9
+    dec_gbps = algo / dec_s / 1e9
+    dominant = "compress" if comp_s >= dec_s else "decompress"
+    achieved = comp_gbps if dominant == "compress" else dec_gbps
+    roofline = {
+        "bound": "hbm",
+        "kernel": "compress_kernel (pz_compress call)" if dominant == "compress"
+        else "locate_kernel + decode_kernel (pz_decompress call)",
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBPS, 4),
+        "traffic": None,
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(tensors, args.cpu_sample_mb)
+
+    per_tensor = {it["t"].name: {
+        "raw_bytes": it["t"].nbytes, "compressed_bytes": it["comp"],
+        "ratio": round(it["t"].nbytes / it["comp"], 4),
+        "compress_raw_gbps": round(it["t"].nbytes / t_comp[i] / 1e9, 1),
+        "decompress_raw_gbps": round(it["t"].nbytes / t_dec[i] / 1e9, 1),
+    } for i, it in enumerate(items)}
+
+    out = {
+        "metric": "compress & decompress GB/s (raw bytes), % of HBM roofline; ratio = oracle",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u16 symbols (bf16 bit patterns), integer codec",
+        "data": "synthetic (seeded generators in pzinputs, stand-ins for captured activations)",
+        "config": {
+            "workload": "GPT-2-XL BF16 saved activations, batch 8, seq 1024: MLP GELU 8x1024x6400, "
+                        "causal softmax 8x25x1024x1024, residual 8x1024x1600",
+            "raw_bytes": raw_total,
+            "compressed_bytes": comp_total,
+            "ratio": round(raw_total / comp_total, 4),
+            "parallelism": "single GPU",
+        },
+        "compress_raw_gbps": round(raw_total / comp_s / 1e9, 1),
+        "decompress_raw_gbps": round(raw_total / dec_s / 1e9, 1),
+        "compress_hbm_frac": round(comp_gbps / HBM_PEAK_GBPS, 4),
+        "decompress_hbm_frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "tensors": per_tensor,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(tensors, sample_mb):
+    """The oracle, as it stands, on a bounded sample: the same fraction of
+    whole chunks from the start of every tensor, compress then decompress."""
+    import oracle
+
+    total = sum(t.nbytes for t in tensors)
+    frac = min(1.0, sample_mb * 1e6 / total)
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    raw = 0
+    t_c = t_d = 0.0
+    for t in tensors:
+        n = max(4096, int(t.nbytes * frac) // 4096 * 4096)
+        part = t.data[:n]
+        a = time.perf_counter()
+        s = oracle.compress(part, t.elem_bits, threads=threads)
+        b = time.perf_counter()
+        back = oracle.decompress(s, n, t.elem_bits, threads=threads)
+        c = time.perf_counter()
+        assert np.array_equal(back, part)
+        raw += n
+        t_c += b - a
+        t_d += c - b
+    log(f"cpu baseline: {raw / 1e6:.1f} MB sample, {threads} threads, compress {t_c:.2f}s decompress {t_d:.2f}s")
+    return {
+        "value": round(raw / (t_c + t_d) / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"first {frac * 100:.1f}% (whole chunks) of each tensor, {raw / 1e6:.1f} MB; "
+                  f"compress {raw / t_c / 1e6:.1f} MB/s, decompress {raw / t_d / 1e6:.1f} MB/s",
+    }
+
+
+if __name__ == "__main__":
+    main()

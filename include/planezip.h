@@ -1,0 +1,110 @@
+/*
+ * planezip.h — C ABI of the MI355X (gfx950) PlaneZip block codec.
+ *
+ * The codec is the one of "PlaneZip: Lossless Bit-Plane Compression of
+ * Training Activations Offloaded over PCIe" (arXiv:2610.25033), §III-A
+ * "Codec" and its "Stream format" paragraph, and Fig. 2: every 128-byte block
+ * of a tensor is read as N symbols of w bits, sized under four encodings
+ * (ZVC, DBX, BX, ZBX) and as a raw block, and the smallest is kept under a
+ * 3-bit tag; 32 blocks form a 4 KB chunk with a 16-bit size header, and a
+ * chunk that would grow is stored raw. The exact bit layout (which the paper
+ * leaves partly open) is the repository's FORMAT.md, version 1.
+ *
+ * Conventions for every entry point:
+ *   - All data pointers are device pointers (hipMalloc'd memory or a torch
+ *     CUDA/HIP tensor's data_ptr()), owned by the caller, and must be 16-byte
+ *     aligned. The library allocates temporary device scratch per call with
+ *     hipMallocAsync on the given stream and frees it the same way.
+ *   - `stream` is a hipStream_t (NULL means the null stream). Every call only
+ *     enqueues work and returns; results written to device memory are valid
+ *     once the stream has been synchronized.
+ *   - Errors that the host can see (bad arguments, a launch failure) are
+ *     returned synchronously and nothing is enqueued. Errors that depend on the
+ *     data (a corrupt stream) are written to device memory.
+ *   - Calls on different streams are independent; the library keeps no state
+ *     between calls.
+ */
+#ifndef PLANEZIP_H
+#define PLANEZIP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of the tensor, as carried in the paper's copy descriptor
+ * (§III-A: "The runtime passes the element type in the copy descriptor"). */
+typedef enum {
+    PZ_DTYPE_BF16 = 0,
+    PZ_DTYPE_FP32 = 1,
+    PZ_DTYPE_OTHER = 2
+} pz_dtype_t;
+
+typedef enum {
+    PZ_SUCCESS = 0,
+    PZ_ERROR_INVALID_VALUE = 1,      /* bad pointer, size, dtype/width pair or alignment */
+    PZ_ERROR_INSUFFICIENT_BUFFER = 2, /* destination capacity below the worst case */
+    PZ_ERROR_CORRUPT_STREAM = 3,     /* stream fails the decoder's checks */
+    PZ_ERROR_HIP = 4                 /* a HIP runtime call or launch failed */
+} pz_status_t;
+
+#define PZ_BLOCK_BYTES 128
+#define PZ_CHUNK_BYTES 4096
+#define PZ_NUM_CHUNKS(n) (((n) + 4095) / 4096)
+/* Worst case stream size: every chunk stored raw, plus its 2-byte header. */
+#define PZ_MAX_COMPRESSED_BYTES(n) (2 * PZ_NUM_CHUNKS(n) + (n))
+
+/* Allowed (dtype, elem_bits) pairs; elem_bits is the symbol width w:
+ *   BF16 with 16 (the paper's w for BF16) or 32 (BPC's original width, the
+ *   §V-A ablation); FP32 with 32; OTHER with 32 ("other types use w = 32").
+ * Any other pair returns PZ_ERROR_INVALID_VALUE. */
+
+/* Exact size in bytes of the stream pz_compress would write for the same
+ * input, computed without writing a stream — the paper's profiling-iteration
+ * measurement (§III-B: the engine "compresses them into a scratch buffer and
+ * discards the output"; the reported size is the sum of the chunk headers).
+ *   d_src        raw tensor bytes, raw_bytes long (any length, including 0)
+ *   d_out_bytes  one uint64: 2*chunks + sum of chunk payload lengths
+ *   d_chunk_lens nullable; PZ_NUM_CHUNKS(raw_bytes) uint16 header values */
+pz_status_t pz_compressed_size(const void *d_src, size_t raw_bytes, int dtype,
+                               int elem_bits, uint64_t *d_out_bytes,
+                               uint16_t *d_chunk_lens, void *stream);
+
+/* Compress raw_bytes bytes of d_src into d_dst (FORMAT.md §5: the uint16
+ * header table H[0..C-1], then the chunk payloads). dst_capacity must be at
+ * least PZ_MAX_COMPRESSED_BYTES(raw_bytes); d_out_bytes receives the stream
+ * length. The stream is a pure function of (bytes, dtype, elem_bits). */
+pz_status_t pz_compress(const void *d_src, size_t raw_bytes, int dtype,
+                        int elem_bits, void *d_dst, size_t dst_capacity,
+                        uint64_t *d_out_bytes, void *stream);
+
+/* Decompress a stream of comp_bytes bytes into raw_bytes bytes at d_dst.
+ * raw_bytes, dtype and elem_bits must be those given to pz_compress; they are
+ * not stored in the stream. d_status (nullable, one int32) receives
+ * PZ_SUCCESS or PZ_ERROR_CORRUPT_STREAM (FORMAT.md §6); on a corrupt stream
+ * the contents of d_dst are unspecified but nothing outside
+ * [d_dst, d_dst + raw_bytes) is written and nothing outside
+ * [d_src, d_src + comp_bytes) is read. A comp_bytes below 2*chunks is
+ * reported synchronously as PZ_ERROR_CORRUPT_STREAM. */
+pz_status_t pz_decompress(const void *d_src, size_t comp_bytes, int dtype,
+                          int elem_bits, void *d_dst, size_t raw_bytes,
+                          int32_t *d_status, void *stream);
+
+/* Diagnostics of the size pass, per 128-byte block (nblocks =
+ * ceil(raw_bytes/128)): d_sizes (nullable) receives the five candidate sizes
+ * in bits (ZVC, DBX, BX, ZBX, RAW; payload only, no tag) as 5*nblocks
+ * uint16; d_tags (nullable) receives the chosen tag per block. */
+pz_status_t pz_block_sizes(const void *d_src, size_t raw_bytes, int dtype,
+                           int elem_bits, uint16_t *d_sizes, uint8_t *d_tags,
+                           void *stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *pz_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PLANEZIP_H */

@@ -1,0 +1,51 @@
+"""ctypes binding of ``libplanezip.so`` (the C ABI in include/planezip.h).
+
+Argument marshalling only: every step of the codec runs in the HIP kernels.
+There is no CPU fallback; importing fails loudly if the library is missing.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libplanezip.so")
+
+PZ_SUCCESS = 0
+PZ_ERROR_INVALID_VALUE = 1
+PZ_ERROR_INSUFFICIENT_BUFFER = 2
+PZ_ERROR_CORRUPT_STREAM = 3
+PZ_ERROR_HIP = 4
+
+EXPORTS = ("pz_compressed_size", "pz_compress", "pz_decompress", "pz_block_sizes", "pz_status_string")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python lossless_bit_plane_amd/build.py` "
+            "(hipcc, gfx950). There is no fallback implementation.")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz, i = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    lib.pz_compressed_size.argtypes = [vp, sz, i, i, vp, vp, vp]
+    lib.pz_compress.argtypes = [vp, sz, i, i, vp, sz, vp, vp]
+    lib.pz_decompress.argtypes = [vp, sz, i, i, vp, sz, vp, vp]
+    lib.pz_block_sizes.argtypes = [vp, sz, i, i, vp, vp, vp]
+    for name in ("pz_compressed_size", "pz_compress", "pz_decompress", "pz_block_sizes"):
+        getattr(lib, name).restype = ctypes.c_int
+    lib.pz_status_string.argtypes = [ctypes.c_int]
+    lib.pz_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+class PlaneZipError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        msg = lib.pz_status_string(status).decode()
+        super().__init__(f"{call} failed: {msg} ({status})")
+        self.status = status
+
+
+def check(status: int, call: str) -> None:
+    if status != PZ_SUCCESS:
+        raise PlaneZipError(status, call)

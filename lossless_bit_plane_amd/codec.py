@@ -1,0 +1,119 @@
+"""Python entry points with the names of the C ABI (argument marshalling only).
+
+Tensors must be contiguous device tensors; the stream defaults to the current
+torch stream. Every call only enqueues work, like the C functions.
+"""
+from __future__ import annotations
+
+import torch
+
+from ._lib import PZ_ERROR_CORRUPT_STREAM, PlaneZipError, check, lib
+
+BF16, FP32, OTHER = 0, 1, 2
+_TORCH_DTYPE = {torch.bfloat16: (BF16, 16), torch.float32: (FP32, 32)}
+
+
+def num_chunks(raw_bytes: int) -> int:
+    return (raw_bytes + 4095) // 4096
+
+
+def max_compressed_bytes(raw_bytes: int) -> int:
+    return 2 * num_chunks(raw_bytes) + raw_bytes
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _ptr(t):
+    return t.data_ptr() if t is not None else None
+
+
+def _byte_view(t: torch.Tensor) -> torch.Tensor:
+    if not t.is_cuda:
+        raise ValueError("PlaneZip works on device tensors only")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.reshape(-1).view(torch.uint8)
+
+
+def _kind(t: torch.Tensor, dtype, elem_bits):
+    if dtype is None:
+        dtype, bits = _TORCH_DTYPE.get(t.dtype, (OTHER, 32))
+        elem_bits = bits if elem_bits is None else elem_bits
+    return dtype, (32 if elem_bits is None else elem_bits)
+
+
+def pz_compressed_size(src: torch.Tensor, dtype=None, elem_bits=None, chunk_lens: bool = False,
+                       stream=None):
+    """Device int64 tensor (1,) with the exact stream size, and optionally the
+    int16 (bit pattern of uint16) chunk header values."""
+    dtype, elem_bits = _kind(src, dtype, elem_bits)
+    b = _byte_view(src)
+    out = torch.empty(1, dtype=torch.int64, device=b.device)
+    lens = torch.empty(num_chunks(b.numel()), dtype=torch.int16, device=b.device) if chunk_lens else None
+    check(lib.pz_compressed_size(_ptr(b), b.numel(), dtype, elem_bits, _ptr(out), _ptr(lens),
+                                 _stream(stream)), "pz_compressed_size")
+    return out, lens
+
+
+def pz_block_sizes(src: torch.Tensor, dtype=None, elem_bits=None, stream=None):
+    """Per-block candidate sizes (int16 view of uint16, shape (nblocks, 5))
+    and chosen tags (uint8, nblocks)."""
+    dtype, elem_bits = _kind(src, dtype, elem_bits)
+    b = _byte_view(src)
+    nb = (b.numel() + 127) // 128
+    sizes = torch.empty((max(nb, 1), 5), dtype=torch.int16, device=b.device)
+    tags = torch.empty(max(nb, 1), dtype=torch.uint8, device=b.device)
+    check(lib.pz_block_sizes(_ptr(b), b.numel(), dtype, elem_bits, _ptr(sizes), _ptr(tags),
+                             _stream(stream)), "pz_block_sizes")
+    return sizes[:nb], tags[:nb]
+
+
+def pz_compress(src: torch.Tensor, dtype=None, elem_bits=None, dst: torch.Tensor | None = None,
+                out_bytes: torch.Tensor | None = None, stream=None):
+    """Compress into ``dst`` (uint8, capacity >= max_compressed_bytes).
+    Returns (dst, out_bytes) where out_bytes is a device int64 tensor (1,)."""
+    dtype, elem_bits = _kind(src, dtype, elem_bits)
+    b = _byte_view(src)
+    cap = max_compressed_bytes(b.numel())
+    if dst is None:
+        dst = torch.empty(max(cap, 16), dtype=torch.uint8, device=b.device)
+    if out_bytes is None:
+        out_bytes = torch.empty(1, dtype=torch.int64, device=b.device)
+    check(lib.pz_compress(_ptr(b), b.numel(), dtype, elem_bits, _ptr(dst), dst.numel(),
+                          _ptr(out_bytes), _stream(stream)), "pz_compress")
+    return dst, out_bytes
+
+
+def pz_decompress(src: torch.Tensor, comp_bytes: int, raw_bytes: int, dtype: int, elem_bits: int,
+                  dst: torch.Tensor | None = None, status: torch.Tensor | None = None, stream=None):
+    """Decompress ``comp_bytes`` of ``src`` into ``dst`` (uint8, raw_bytes).
+    Returns (dst, status) where status is a device int32 tensor (1,)."""
+    b = _byte_view(src)
+    if dst is None:
+        dst = torch.empty(max(raw_bytes, 16), dtype=torch.uint8, device=b.device)
+    if status is None:
+        status = torch.empty(1, dtype=torch.int32, device=b.device)
+    check(lib.pz_decompress(_ptr(b), comp_bytes, dtype, elem_bits, _ptr(dst), raw_bytes,
+                            _ptr(status), _stream(stream)), "pz_decompress")
+    return dst, status
+
+
+def compress(t: torch.Tensor, dtype=None, elem_bits=None):
+    """Compress and synchronize: returns the stream as a uint8 device tensor
+    of its exact length."""
+    dst, nbytes = pz_compress(t, dtype, elem_bits)
+    n = int(nbytes.item())
+    return dst[:n]
+
+
+def decompress(stream_bytes: torch.Tensor, raw_bytes: int, dtype: int, elem_bits: int):
+    """Decompress and synchronize; raises on a corrupt stream. Returns uint8."""
+    dst, status = pz_decompress(stream_bytes, stream_bytes.numel(), raw_bytes, dtype, elem_bits)
+    st = int(status.item())
+    if st != 0:
+        raise PlaneZipError(PZ_ERROR_CORRUPT_STREAM if st == PZ_ERROR_CORRUPT_STREAM else st,
+                            "pz_decompress (device status)")
+    return dst[:raw_bytes]

@@ -1,0 +1,250 @@
+// Device helpers shared by the PlaneZip compress and decompress kernels
+// (gfx950, wave64).
+//
+// Codec: PlaneZip paper, §III-A and Fig. 2 (128-byte blocks of N w-bit
+// symbols; ZVC, DBX, BX, ZBX and raw candidates; BPC's plane prefix code;
+// 4 KB chunks with 16-bit headers). Bit layout: FORMAT.md version 1.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define PZ_DEV __device__ __forceinline__
+
+namespace pz {
+
+constexpr int kBlockBytes = 128;
+constexpr int kChunkBytes = 4096;
+constexpr int kBlocksPerChunk = 32;
+constexpr int kWave = 64;
+constexpr int kWavesPerGroup = 4;
+constexpr int kGroupThreads = kWave * kWavesPerGroup;
+
+// Candidate tags (Fig. 2 order).
+constexpr int kZVC = 0, kDBX = 1, kBX = 2, kZBX = 3, kRAW = 4;
+
+// Per-wave LDS: two chunk buffers of kChunkBufDwords, or 64 per-lane regions
+// of kLaneStride dwords (stride 33 keeps lane-strided reads conflict free).
+constexpr int kChunkBufDwords = 1032;
+constexpr int kLaneStride = 33;
+constexpr int kWaveLdsDwords = 2 * kChunkBufDwords > kWave * kLaneStride
+                                   ? 2 * kChunkBufDwords
+                                   : kWave * kLaneStride;
+
+// Look-back status words: flag in the top two bits, value below.
+constexpr uint64_t kFlagAggregate = 1ull << 62;
+constexpr uint64_t kFlagPrefix = 2ull << 62;
+constexpr uint64_t kValueMask = kFlagAggregate - 1;
+
+constexpr uint64_t kBadChunk = ~0ull;
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+PZ_DEV uint32_t pk_sub_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, a) - __builtin_bit_cast(u16x2, b));
+}
+PZ_DEV uint32_t pk_add_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, a) + __builtin_bit_cast(u16x2, b));
+}
+PZ_DEV uint32_t pk_min_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(
+      uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, a), __builtin_bit_cast(u16x2, b)));
+}
+
+PZ_DEV uint32_t funnel(uint32_t hi, uint32_t lo, uint32_t shift) {
+  // Low 32 bits of ((hi:lo) >> shift), shift in [0, 31].
+  return __builtin_amdgcn_alignbit(hi, lo, shift);
+}
+
+PZ_DEV int popc64(uint64_t x) { return __popcll(x); }
+PZ_DEV int popc32(uint32_t x) { return __popc(x); }
+
+PZ_DEV uint32_t lane_id() { return __lane_id(); }
+
+PZ_DEV uint64_t all_ones64(int L) { return L >= 64 ? ~0ull : ((1ull << L) - 1ull); }
+
+// ceil(log2 L) for L >= 2, else 0: width of the position field.
+PZ_DEV int position_bits(int L) { return L >= 2 ? 32 - __clz(L - 1) : 0; }
+
+// ---------------------------------------------------------------------------
+// 32x32 bit-matrix transpose in registers: afterwards a[c] bit r equals the
+// old a[r] bit c. Five butterfly stages; the 16- and 8-bit stages move whole
+// bytes and compile to byte permutes.
+// ---------------------------------------------------------------------------
+template <int J>
+PZ_DEV void transpose_stage(uint32_t (&a)[32], uint32_t m) {
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    if (k & J) continue;
+    const uint32_t x = a[k], y = a[k + J];
+    a[k] = (x & m) | ((y << J) & ~m);
+    a[k + J] = ((x >> J) & m) | (y & ~m);
+  }
+}
+
+PZ_DEV void transpose32(uint32_t (&a)[32]) {
+  transpose_stage<16>(a, 0x0000FFFFu);
+  transpose_stage<8>(a, 0x00FF00FFu);
+  transpose_stage<4>(a, 0x0F0F0F0Fu);
+  transpose_stage<2>(a, 0x33333333u);
+  transpose_stage<1>(a, 0x55555555u);
+}
+
+// ---------------------------------------------------------------------------
+// Wave-wide helpers.
+// ---------------------------------------------------------------------------
+PZ_DEV uint64_t wave_sum_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Inclusive scan of a 32-bit value within each 32-lane half of the wave.
+PZ_DEV uint32_t half_inclusive_scan(uint32_t v) {
+  const uint32_t l = lane_id() & 31;
+#pragma unroll
+  for (int off = 1; off < 32; off <<= 1) {
+    uint32_t t = __shfl_up(v, off, 32);
+    if (l >= (uint32_t)off) v += t;
+  }
+  return v;
+}
+
+PZ_DEV uint64_t wave_inclusive_scan_u64(uint64_t v) {
+  const uint32_t l = lane_id();
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    uint64_t t = __shfl_up(v, off, 64);
+    if (l >= (uint32_t)off) v += t;
+  }
+  return v;
+}
+
+PZ_DEV uint64_t atomic_load_agent(const uint64_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+PZ_DEV void atomic_store_agent(uint64_t *p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Next tile index for this wave, from a device-wide counter, so that every
+// tile a wave waits on in the look-back belongs to a wave that is already
+// running (tiles are handed out in the order waves start).
+PZ_DEV uint32_t acquire_tile(uint32_t *counter) {
+  uint32_t t = 0;
+  if (lane_id() == 0) t = atomicAdd(counter, 1u);
+  return __shfl(t, 0, 64);
+}
+
+// Decoupled look-back (Merrill & Garland, "Single-pass Parallel Prefix Scan
+// with Decoupled Look-back"): publishes this tile's aggregate, then walks back
+// over predecessors 64 at a time until it meets an inclusive prefix, and
+// publishes its own inclusive prefix. Returns the exclusive prefix of `agg`.
+PZ_DEV uint64_t lookback(uint64_t *status, uint32_t tile, uint64_t agg) {
+  const uint32_t lane = lane_id();
+  if (tile == 0) {
+    if (lane == 0) atomic_store_agent(&status[0], kFlagPrefix | agg);
+    return 0;
+  }
+  if (lane == 0) atomic_store_agent(&status[tile], kFlagAggregate | agg);
+  uint64_t excl = 0;
+  int64_t base = (int64_t)tile - 1;
+  while (true) {
+    const int64_t idx = base - (int64_t)lane;
+    const uint64_t st = idx >= 0 ? atomic_load_agent(&status[idx]) : kFlagPrefix;
+    const uint64_t flag = st >> 62;
+    const uint64_t not_ready = __ballot(flag == 0);
+    const uint64_t prefix = __ballot(flag == 2);
+    const uint64_t first = prefix & (~prefix + 1);         // nearest inclusive prefix
+    const uint64_t need = prefix ? (first << 1) - 1 : ~0ull;  // lanes up to it
+    if (not_ready & need) {
+      __builtin_amdgcn_s_sleep(1);
+      continue;
+    }
+    const uint64_t mine = ((need >> lane) & 1ull) ? (st & kValueMask) : 0;
+    excl += wave_sum_u64(mine);
+    if (prefix) break;
+    base -= 64;
+  }
+  if (lane == 0) atomic_store_agent(&status[tile], kFlagPrefix | (excl + agg));
+  return excl;
+}
+
+// Orders this wave's LDS accesses before and after (all lanes of a wave run
+// the same instruction stream; this keeps the compiler from moving LDS
+// accesses across phases that hand data between lanes).
+PZ_DEV void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// ---------------------------------------------------------------------------
+// Bit writer into LDS: stream bit t is bit (t % 32) of dword (t / 32), which
+// for a little-endian machine is bit (t % 8) of byte (t / 8). Fields are
+// written least-significant bit first. Dwords are OR-ed in, so adjacent
+// writers that share a boundary dword do not clobber each other.
+// ---------------------------------------------------------------------------
+struct LdsBitWriter {
+  uint32_t *buf;
+  uint64_t acc;   // pending bits, aligned so that bit 0 is dword bit 0
+  uint32_t nacc;  // number of meaningful bits in acc (including the lead-in)
+  uint32_t wpos;  // dword index of acc's first dword
+
+  PZ_DEV void init(uint32_t *b, uint32_t bit_offset) {
+    buf = b;
+    acc = 0;
+    nacc = bit_offset & 31;
+    wpos = bit_offset >> 5;
+  }
+  // Append n <= 32 bits of v (v < 2^n).
+  PZ_DEV void put(uint32_t v, uint32_t n) {
+    acc |= (uint64_t)v << nacc;
+    nacc += n;
+    if (nacc >= 32) {
+      atomicOr(&buf[wpos], (uint32_t)acc);
+      acc >>= 32;
+      nacc -= 32;
+      ++wpos;
+    }
+  }
+  // Append n <= 64 bits of v.
+  PZ_DEV void put64(uint64_t v, uint32_t n) {
+    if (n > 32) {
+      put((uint32_t)v, 32);
+      put((uint32_t)(v >> 32), n - 32);
+    } else {
+      put((uint32_t)v, n);
+    }
+  }
+  PZ_DEV void flush() {
+    if (nacc) atomicOr(&buf[wpos], (uint32_t)acc);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Plane-code size from per-plane class masks (bit j describes plane j):
+// nz: XORed plane non-zero; ones: XORed plane all ones; pz: plane before the
+// XOR is zero; pair: exactly two adjacent ones; single: exactly one one.
+// Codes of §III-A: a lone zero plane 3 bits, a run of zero planes 2+R bits,
+// all-ones and pre-XOR-zero planes 5 bits, pair and single 5 + PW bits, any
+// other plane 1 + L bits; the first matching class wins, in that order.
+// ---------------------------------------------------------------------------
+PZ_DEV int plane_code_bits(uint64_t nz, uint64_t ones, uint64_t pz, uint64_t pair,
+                           uint64_t single, int K, int L, int R) {
+  const uint64_t kmask = (K >= 64) ? ~0ull : ((1ull << K) - 1ull);
+  nz &= kmask;
+  const uint64_t a = nz & ones;
+  const uint64_t b = nz & ~a & pz;
+  const uint64_t rest = nz & ~a & ~b;
+  const uint64_t cd = rest & (pair | single);
+  const uint64_t e = rest & ~cd;
+  const uint64_t z = ~nz & kmask;
+  const uint64_t starts = z & ~(z >> 1);
+  const uint64_t lone = starts & ~(z << 1);
+  const int runs = popc64(starts), lones = popc64(lone);
+  const int pw = position_bits(L);
+  return 5 * popc64(a | b) + (5 + pw) * popc64(cd) + (1 + L) * popc64(e) + 3 * lones +
+         (2 + R) * (runs - lones);
+}
+
+}  // namespace pz

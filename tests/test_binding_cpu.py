@@ -1,0 +1,58 @@
+"""Host-side checks of the C-ABI library that need no GPU: it loads, exports
+every function declared in include/planezip.h, and rejects bad arguments
+synchronously before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            names += re.findall(r"^\s*(?:pz_status_t|const char \*)\s*(pz_\w+)\s*\(", text, re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    path = os.path.join(ROOT, "lossless_bit_plane_amd", "libplanezip.so")
+    if not os.path.exists(path):
+        pytest.fail("libplanezip.so is not built (run __graft_entry__.build())")
+    from lossless_bit_plane_amd import _lib
+
+    return _lib.lib
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared()
+    assert set(declared) >= {"pz_compress", "pz_decompress", "pz_compressed_size"}
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_rejects_bad_arguments_on_host(lib):
+    from lossless_bit_plane_amd import _lib
+
+    vp = ctypes.c_void_p
+    fake = 256  # aligned, never dereferenced: every call below fails its checks first
+    # Unsupported (dtype, elem_bits) pairs.
+    assert lib.pz_compress(fake, 100, 0, 8, fake, 1000, fake, None) == _lib.PZ_ERROR_INVALID_VALUE
+    assert lib.pz_compress(fake, 100, 1, 16, fake, 1000, fake, None) == _lib.PZ_ERROR_INVALID_VALUE
+    assert lib.pz_compress(fake, 100, 3, 32, fake, 1000, fake, None) == _lib.PZ_ERROR_INVALID_VALUE
+    # Null pointers with data.
+    assert lib.pz_compress(None, 100, 0, 16, fake, 1000, fake, None) == _lib.PZ_ERROR_INVALID_VALUE
+    assert lib.pz_compress(fake, 100, 0, 16, fake, 1000, None, None) == _lib.PZ_ERROR_INVALID_VALUE
+    # Misaligned source.
+    assert lib.pz_compress(fake + 4, 100, 0, 16, fake, 1000, fake, None) == _lib.PZ_ERROR_INVALID_VALUE
+    # Capacity below the worst case 2*chunks + raw.
+    assert lib.pz_compress(fake, 4097, 0, 16, fake, 4100, fake, None) == _lib.PZ_ERROR_INSUFFICIENT_BUFFER
+    # A stream shorter than its header table.
+    assert lib.pz_decompress(fake, 3, 0, 16, fake, 8193, None, None) == _lib.PZ_ERROR_CORRUPT_STREAM
+    assert lib.pz_compressed_size(fake, 10, 2, 16, fake, None, None) == _lib.PZ_ERROR_INVALID_VALUE
+    assert lib.pz_status_string(3) == b"corrupt stream"
