@@ -41,6 +41,8 @@ def parse():
     p.add_argument("--cpu-sample-mb", type=float, default=24.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-verify", action="store_true")
+    p.add_argument("--calibrate-copy-mib", type=int, default=0,
+                   help="run one plain device copy of this many MiB first (HBM counter calibration)")
     return p.parse_args()
 
 
@@ -57,6 +59,15 @@ def main():
     import pzinputs
 
     dev = torch.device("cuda:0")
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {n} bytes read, {n} bytes written")
+        del a, b
     t0 = time.time()
     tensors = pzinputs.config(args.config)
     log(f"generated config {args.config} in {time.time() - t0:.1f}s: "

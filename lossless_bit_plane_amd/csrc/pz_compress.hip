@@ -13,9 +13,10 @@
 // count reductions over the block's symbols, evaluated bit-parallel on all
 // planes at once (two BF16 symbols per 32-bit register). Only the chosen
 // encoding is transposed (a 32x32 bit-matrix butterfly in registers) and
-// emitted, bit by bit-field, into a per-chunk LDS buffer. Chunk offsets come
-// from a single-pass decoupled look-back over per-wave chunk-length sums, so
-// the input is read once and the stream written once.
+// emitted: every code is OR-ed into a per-chunk LDS buffer at its bit offset,
+// with no branches on the bit position. Chunk offsets come from a single-pass
+// decoupled look-back over per-wave chunk-length sums, so the input is read
+// once and the stream written once.
 #include <type_traits>
 
 #include "pz_device.h"
@@ -39,35 +40,39 @@ PZ_DEV void load_block(const uint8_t *__restrict__ src, uint64_t raw_bytes, uint
       d[4 * q + 3] = v.w;
     }
   } else {
+    // The tensor's last block: whole dwords, then the 1..3 trailing bytes.
+    const uint64_t n = off < raw_bytes ? raw_bytes - off : 0;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) d[i] = 0;
-    if (off < raw_bytes) {
-      const uint32_t n = (uint32_t)(raw_bytes - off);
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        uint32_t v = 0;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const uint32_t k = 4 * i + b;
-          if (k < n) v |= (uint32_t)src[off + k] << (8 * b);
-        }
-        d[i] = v;
+    for (int i = 0; i < 32; ++i) {
+      const uint64_t b = 4 * (uint64_t)i;
+      uint32_t v = 0;
+      if (b + 4 <= n) {
+        v = *reinterpret_cast<const uint32_t *>(src + off + b);
+      } else if (b < n) {
+        for (uint64_t k = b; k < n; ++k) v |= (uint32_t)src[off + k] << (8 * (k - b));
       }
+      d[i] = v;
     }
   }
 }
 
-// ---------------------------------------------------------------------------
-// Candidate sizes, w = 16. d[i] holds symbols 2i (low half) and 2i+1 (high).
-// ---------------------------------------------------------------------------
-struct Sizes {
-  int sz[5];
-  int n;          // non-zero symbols
-  uint64_t bm;    // DBX top plane: borrow bits of the deltas
-};
+// Makes the compiler treat the block's registers as new values, so that
+// expressions of one phase are recomputed in the next instead of being kept
+// alive across it (which would double the register footprint).
+PZ_DEV void launder_regs(uint32_t (&d)[32]) {
+#pragma unroll
+  for (int i = 0; i < 32; ++i) asm volatile("" : "+v"(d[i]));
+}
 
 PZ_DEV uint32_t lo16(uint32_t x) { return x & 0xFFFFu; }
 PZ_DEV uint32_t hi16(uint32_t x) { return x >> 16; }
+
+struct Sizes {
+  int sz[5];
+  int n;         // non-zero symbols
+  uint32_t b0;   // DBX borrow bits (layout: candidate_sizes16 / 32)
+  uint32_t b1;
+};
 
 // Merges per-half saturating counters (>=1, >=2, >=3 ones) of the two halves.
 PZ_DEV void fold_counts16(uint32_t t1, uint32_t t2, uint32_t t3, uint32_t &c1, uint32_t &c2,
@@ -77,12 +82,13 @@ PZ_DEV void fold_counts16(uint32_t t1, uint32_t t2, uint32_t t3, uint32_t &c1, u
   c3 = lo16(t3) | hi16(t3) | (lo16(t2) & hi16(t1)) | (lo16(t1) & hi16(t2));
 }
 
-PZ_DEV void candidate_sizes16(const uint32_t (&d)[32], Sizes &out) {
-  uint32_t bx_or_s = 0, bx_or = 0, bx_and = ~0u, bx_t1 = 0, bx_t2 = 0, bx_t3 = 0, bx_adj = 0;
-  uint32_t db_or_s = 0, db_or = 0, db_and = ~0u, db_t1 = 0, db_t2 = 0, db_t3 = 0, db_adj = 0;
-  uint32_t zb_and = ~0u, zb_adj = 0, zb_prev = 0;
-  uint32_t cnt = 0, gh_prev = 0, dgh_prev = 0;
-  uint64_t bm = 0;
+// ---------------------------------------------------------------------------
+// Candidate sizes, w = 16. d[i] holds symbols 2i (low half) and 2i+1 (high).
+// ---------------------------------------------------------------------------
+PZ_DEV void candidate_sizes16(uint32_t (&d)[32], Sizes &out) {
+  uint32_t bx_or_s = 0, bx_or = 0, bx_and = ~0u, bx_t2 = 0, bx_t3 = 0, bx_adj = 0, gh_prev = 0;
+  uint32_t db_or_s = 0, db_or = 0, db_and = ~0u, db_t2 = 0, db_t3 = 0, db_adj = 0, dgh_prev = 0;
+  uint32_t cnt = 0, b0 = 0, b1 = 0;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
     const uint32_t s = d[i];
@@ -90,33 +96,21 @@ PZ_DEV void candidate_sizes16(const uint32_t (&d)[32], Sizes &out) {
     const uint32_t g = s ^ ((s >> 1) & 0x7FFF7FFFu);
     const uint32_t gh = g >> 16;
     bx_or_s |= s;
+    bx_t3 |= bx_t2 & g;
+    bx_t2 |= bx_or & g;
     bx_or |= g;
     bx_and &= g;
-    bx_t3 |= bx_t2 & g;
-    bx_t2 |= bx_t1 & g;
-    bx_t1 |= g;
-    bx_adj |= g & (gh | gh_prev);  // pairs (2i, 2i+1) and (2i-1, 2i), in the low half
+    bx_adj |= g & (gh | gh_prev);  // pairs (2i, 2i+1) and (2i-1, 2i), low half
     gh_prev = gh;
-
-    // Zero symbols: zfill is 0xFFFF in a half whose symbol is zero.
-    const uint32_t nzh = pk_min_u16(s, 0x00010001u);
-    const uint32_t zfill = pk_sub_u16(nzh, 0x00010001u);
-    cnt = pk_add_u16(cnt, nzh);
-
-    // ZBX: AND over the non-zero symbols only; adjacency in compacted order
-    // (zb_prev is the last non-zero symbol's g, in the low half).
-    zb_and &= g | zfill;
-    const uint32_t q = g | (zb_prev & zfill);
-    zb_adj |= (zb_prev & g) | (q & gh);
-    zb_prev = gh | (q & (zfill >> 16));
+    cnt = pk_add_u16(cnt, pk_min_u16(s, 0x00010001u));
 
     // DBX: deltas s[k] - s[k-1] as 17-bit two's complement; the low 16 bits
-    // come from a packed subtract, bit 16 is the borrow. The XORed planes are
-    // the bits of D ^ (D >> 1), whose bit 15 mixes in the borrow.
+    // come from a packed subtract, bit 16 is the borrow (bits 15 and 31 of
+    // bo). The XORed planes are the bits of D ^ (D >> 1).
     const uint32_t prevp = i == 0 ? (s << 16) : funnel(s, d[i - 1], 16);
     uint32_t ld = pk_sub_u16(s, prevp);
-    uint32_t bo = ((~s & prevp) | (~(s ^ prevp) & ld)) & 0x80008000u;
-    uint32_t gd = ld ^ (((ld >> 1) & 0x7FFF7FFFu) | bo);
+    uint32_t bo = (~s & prevp) | (~(s ^ prevp) & ld);
+    uint32_t gd = ld ^ (((ld >> 1) & 0x7FFF7FFFu) | (bo & 0x80008000u));
     if (i == 0) {  // symbol 0 is the base, not a delta
       ld &= 0xFFFF0000u;
       gd &= 0xFFFF0000u;
@@ -124,106 +118,139 @@ PZ_DEV void candidate_sizes16(const uint32_t (&d)[32], Sizes &out) {
     }
     const uint32_t dgh = gd >> 16;
     db_or_s |= ld;
+    db_t3 |= db_t2 & gd;
+    db_t2 |= db_or & gd;
     db_or |= gd;
     db_and &= (i == 0) ? (gd | 0xFFFFu) : gd;
-    db_t3 |= db_t2 & gd;
-    db_t2 |= db_t1 & gd;
-    db_t1 |= gd;
     db_adj |= gd & (dgh | dgh_prev);
     dgh_prev = dgh;
-    // Delta 2i (low half) is plane element 2i-1; delta 2i+1 is element 2i.
-    if (i > 0) bm |= (uint64_t)((bo >> 15) & 1u) << (2 * i - 1);
-    bm |= (uint64_t)(bo >> 31) << (2 * i);
+    // Borrow bits, shifted in from the top: b0 bit i = borrow of delta 2i,
+    // bit 16+i = borrow of delta 2i+1 (i < 16); b1 likewise for deltas 32+.
+    if (i < 16)
+      b0 = (b0 >> 1) | (bo & 0x80008000u);
+    else
+      b1 = (b1 >> 1) | (bo & 0x80008000u);
   }
 
   const int n = (int)(lo16(cnt) + hi16(cnt));
   uint32_t c1, c2, c3;
 
   // BX: 16 planes of 64 bits.
-  fold_counts16(bx_t1, bx_t2, bx_t3, c1, c2, c3);
-  const uint32_t nz = lo16(bx_or) | hi16(bx_or);
+  fold_counts16(bx_or, bx_t2, bx_t3, c1, c2, c3);
+  const uint32_t nz = c1;
   const uint32_t pz = ~(lo16(bx_or_s) | hi16(bx_or_s)) & 0xFFFFu;
   const uint32_t single = c1 & ~c2;
-  const uint32_t adj = lo16(bx_adj);
-  out.sz[kBX] = plane_code_bits(nz, lo16(bx_and) & hi16(bx_and), pz, c2 & ~c3 & adj, single, 16, 64, 4);
-
-  // ZBX: mask, then 16 planes of n bits (same zero, count and pre-XOR masks).
-  const uint32_t zadj = lo16(zb_adj);
-  out.sz[kZBX] = 64 + plane_code_bits(nz, lo16(zb_and) & hi16(zb_and), pz, c2 & ~c3 & zadj, single,
-                                      16, n, 4);
+  const uint32_t exactly2 = c2 & ~c3;
+  out.sz[kBX] = plane_code_bits(nz, lo16(bx_and) & hi16(bx_and), pz, exactly2 & lo16(bx_adj), single,
+                                16, 64, 4);
 
   // DBX: base, then 17 planes of 63 bits; plane 16 is the borrow plane.
-  fold_counts16(db_t1, db_t2, db_t3, c1, c2, c3);
-  uint64_t dnz = lo16(db_or) | hi16(db_or);
+  fold_counts16(db_or, db_t2, db_t3, c1, c2, c3);
+  uint64_t dnz = c1;
   uint64_t dones = lo16(db_and) & hi16(db_and);
   const uint64_t dpz = ~(lo16(db_or_s) | hi16(db_or_s)) & 0xFFFFu;
   uint64_t dsingle = c1 & ~c2;
   uint64_t dpair = c2 & ~c3 & lo16(db_adj);
-  const int bc = popc64(bm);
-  dnz |= (uint64_t)(bm != 0) << 16;
-  dones |= (uint64_t)(bm == 0x7FFFFFFFFFFFFFFFull) << 16;
+  const int bc = popc32(b0) + popc32(b1);
+  // Adjacent borrows: deltas (2i, 2i+1), (2i+1, 2i+2), and (31, 32).
+  const uint32_t badj = ((b0 & (b0 >> 16)) & 0xFFFFu) | (((b0 >> 16) & (b0 >> 1)) & 0x7FFFu) |
+                        ((b1 & (b1 >> 16)) & 0xFFFFu) | (((b1 >> 16) & (b1 >> 1)) & 0x7FFFu) |
+                        ((b0 >> 31) & b1 & 1u);
+  dnz |= (uint64_t)(bc != 0) << 16;
+  dones |= (uint64_t)(bc == 63) << 16;
   dsingle |= (uint64_t)(bc == 1) << 16;
-  dpair |= (uint64_t)(bc == 2 && (bm & (bm >> 1)) != 0) << 16;
+  dpair |= (uint64_t)(bc == 2 && badj != 0) << 16;
   out.sz[kDBX] = 16 + plane_code_bits(dnz, dones, dpz, dpair, dsingle, 17, 63, 4);
+
+  // ZBX: the zero, count and pre-XOR masks are those of BX (zero symbols add
+  // nothing); "all ones" and adjacency run over the non-zero symbols only.
+  // (Computed for every wave: a wave-uniform skip of this loop costs more in
+  // register pressure than it saves in instructions.)
+  launder_regs(d);
+  uint32_t zb_and = ~0u, zb_adj = 0, zprev = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const uint32_t s = d[i];
+    const uint32_t g = s ^ ((s >> 1) & 0x7FFF7FFFu);
+    const uint32_t gh = g >> 16;
+    const uint32_t zfill = pk_sub_u16(pk_min_u16(s, 0x00010001u), 0x00010001u);  // 0xFFFF if zero
+    zb_and &= g | zfill;
+    const uint32_t q = g | (zprev & zfill);  // low half: last non-zero g up to symbol 2i
+    zb_adj |= (zprev & g) | (q & gh);
+    zprev = gh | (q & (zfill >> 16));
+  }
+  out.sz[kZBX] = 64 + plane_code_bits(nz, lo16(zb_and) & hi16(zb_and), pz, exactly2 & lo16(zb_adj),
+                                      single, 16, n, 4);
 
   out.sz[kZVC] = 64 + 16 * n;
   out.sz[kRAW] = 1024;
   out.n = n;
-  out.bm = bm;
+  out.b0 = b0;
+  out.b1 = b1;
 }
 
 // ---------------------------------------------------------------------------
 // Candidate sizes, w = 32. d[i] is symbol i.
 // ---------------------------------------------------------------------------
-PZ_DEV void candidate_sizes32(const uint32_t (&d)[32], Sizes &out) {
-  uint32_t bx_or_s = 0, bx_or = 0, bx_and = ~0u, t1 = 0, t2 = 0, t3 = 0, adj = 0, gprev = 0;
-  uint32_t db_or_s = 0, db_or = 0, db_and = ~0u, u1 = 0, u2 = 0, u3 = 0, dadj = 0, dgprev = 0;
-  uint32_t zand = ~0u, zadj = 0, zprev = 0, bm = 0;
+PZ_DEV void candidate_sizes32(uint32_t (&d)[32], Sizes &out) {
+  uint32_t bx_or_s = 0, bx_or = 0, bx_and = ~0u, t2 = 0, t3 = 0, adj = 0, gprev = 0;
+  uint32_t db_or_s = 0, db_or = 0, db_and = ~0u, u2 = 0, u3 = 0, dadj = 0, dgprev = 0;
+  uint32_t bacc = 0;
   int n = 0;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
     const uint32_t s = d[i];
     const uint32_t g = s ^ (s >> 1);
     bx_or_s |= s;
+    t3 |= t2 & g;
+    t2 |= bx_or & g;
     bx_or |= g;
     bx_and &= g;
-    t3 |= t2 & g;
-    t2 |= t1 & g;
-    t1 |= g;
     adj |= g & gprev;
     gprev = g;
-
-    const bool nzs = s != 0;
-    n += nzs ? 1 : 0;
-    zand &= nzs ? g : ~0u;
-    zadj |= zprev & g;
-    zprev = nzs ? g : zprev;
-
+    n += s != 0 ? 1 : 0;
     if (i > 0) {
       const uint32_t p = d[i - 1];
       const uint32_t ld = s - p;
-      const uint32_t bo = ((~s & p) | (~(s ^ p) & ld)) & 0x80000000u;
-      const uint32_t gd = ld ^ ((ld >> 1) | bo);
+      const uint32_t bo = (~s & p) | (~(s ^ p) & ld);  // borrow in bit 31
+      const uint32_t gd = ld ^ ((ld >> 1) | (bo & 0x80000000u));
       db_or_s |= ld;
+      u3 |= u2 & gd;
+      u2 |= db_or & gd;
       db_or |= gd;
       db_and &= gd;
-      u3 |= u2 & gd;
-      u2 |= u1 & gd;
-      u1 |= gd;
       dadj |= gd & dgprev;
       dgprev = gd;
-      bm |= (bo >> 31) << (i - 1);
+      bacc = (bacc >> 1) | (bo & 0x80000000u);  // ends with delta i's borrow at bit i
     }
   }
-  const uint32_t single = t1 & ~t2;
-  out.sz[kBX] = plane_code_bits(bx_or, bx_and, ~bx_or_s, t2 & ~t3 & adj, single, 32, 32, 5);
-  out.sz[kZBX] = 32 + plane_code_bits(bx_or, zand, ~bx_or_s, t2 & ~t3 & zadj, single, 32, n, 5);
+  const uint32_t bm = bacc >> 1;  // plane element k = borrow of delta k+1
+  const uint32_t single = bx_or & ~t2;
+  const uint32_t exactly2 = t2 & ~t3;
+  out.sz[kBX] = plane_code_bits(bx_or, bx_and, ~bx_or_s, exactly2 & adj, single, 32, 32, 5);
+
+  uint32_t zand = bx_and, zadj = adj;
+  if (__ballot(n > 0 && n < 32)) {
+    launder_regs(d);
+    uint32_t za = ~0u, zj = 0, zprev = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const uint32_t s = d[i];
+      const uint32_t g = s ^ (s >> 1);
+      za &= s != 0 ? g : ~0u;
+      zj |= zprev & g;
+      zprev = s != 0 ? g : zprev;
+    }
+    zand = za;
+    zadj = zj;
+  }
+  out.sz[kZBX] = 32 + plane_code_bits(bx_or, zand, ~bx_or_s, exactly2 & zadj, single, 32, n, 5);
 
   const int bc = popc32(bm);
   const uint64_t dnz = (uint64_t)db_or | ((uint64_t)(bm != 0) << 32);
   const uint64_t dones = (uint64_t)db_and | ((uint64_t)(bm == 0x7FFFFFFFu) << 32);
   const uint64_t dpz = (uint64_t)(~db_or_s);
-  const uint64_t dsingle = (uint64_t)(u1 & ~u2) | ((uint64_t)(bc == 1) << 32);
+  const uint64_t dsingle = (uint64_t)(db_or & ~u2) | ((uint64_t)(bc == 1) << 32);
   const uint64_t dpair =
       (uint64_t)(u2 & ~u3 & dadj) | ((uint64_t)(bc == 2 && (bm & (bm >> 1)) != 0) << 32);
   out.sz[kDBX] = 32 + plane_code_bits(dnz, dones, dpz, dpair, dsingle, 33, 31, 5);
@@ -231,19 +258,21 @@ PZ_DEV void candidate_sizes32(const uint32_t (&d)[32], Sizes &out) {
   out.sz[kZVC] = 32 + 32 * n;
   out.sz[kRAW] = 1024;
   out.n = n;
-  out.bm = bm;
+  out.b0 = bm;
+  out.b1 = 0;
 }
 
 template <int W>
-PZ_DEV void candidate_sizes(const uint32_t (&d)[32], Sizes &out) {
+PZ_DEV void candidate_sizes(uint32_t (&d)[32], Sizes &out) {
   if constexpr (W == 16)
     candidate_sizes16(d, out);
   else
     candidate_sizes32(d, out);
 }
 
-// Smallest candidate; equal sizes go to the lowest tag.
-PZ_DEV int select_tag(const Sizes &s) {
+// Smallest candidate; equal sizes go to the lowest tag. Returns the tag and
+// its size (no indexing of the size array by a lane-varying tag).
+PZ_DEV int select_tag(const Sizes &s, int &best_size) {
   int best = 0, bsz = s.sz[0];
 #pragma unroll
   for (int t = 1; t < 5; ++t) {
@@ -252,6 +281,7 @@ PZ_DEV int select_tag(const Sizes &s) {
       bsz = s.sz[t];
     }
   }
+  best_size = bsz;
   return best;
 }
 
@@ -259,7 +289,7 @@ PZ_DEV int select_tag(const Sizes &s) {
 // Size pass: chunk lengths (pz_compressed_size) and per-block diagnostics.
 // ---------------------------------------------------------------------------
 template <int W>
-__global__ __launch_bounds__(kGroupThreads) void size_kernel(
+__global__ __launch_bounds__(kGroupThreads, 4) void size_kernel(
     const uint8_t *__restrict__ src, uint64_t raw_bytes, uint64_t nchunks,
     uint64_t *__restrict__ out_bytes, uint16_t *__restrict__ chunk_lens,
     uint16_t *__restrict__ block_sizes, uint8_t *__restrict__ block_tags) {
@@ -273,8 +303,9 @@ __global__ __launch_bounds__(kGroupThreads) void size_kernel(
   load_block(src, raw_bytes, off, d);
   Sizes s;
   candidate_sizes<W>(d, s);
-  const int tag = select_tag(s);
-  const uint32_t cost = valid ? 3u + (uint32_t)s.sz[tag] : 0u;
+  int best_size;
+  const int tag = select_tag(s, best_size);
+  const uint32_t cost = valid ? 3u + (uint32_t)best_size : 0u;
   if (valid && block_sizes) {
 #pragma unroll
     for (int t = 0; t < 5; ++t) block_sizes[block * 5 + t] = (uint16_t)s.sz[t];
@@ -297,103 +328,103 @@ __global__ __launch_bounds__(kGroupThreads) void size_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Plane construction for the chosen encoding.
+// Emission helpers: fields are OR-ed into the zeroed LDS chunk buffer at an
+// explicit bit offset (stream bit t = bit t%32 of dword t/32).
 // ---------------------------------------------------------------------------
+struct BitSink {
+  uint32_t *buf;
+  uint32_t off;  // next bit
 
-// w = 16: from packed symbols (d[i] = sym 2i | sym 2i+1 << 16) to 16 planes of
-// 64 bits (bit k of plane j = bit j of symbol k). Symbols k and k+32 are
-// paired in one dword first, so that one 32x32 transpose yields the low and
-// high halves of every plane.
-PZ_DEV void planes_from_symbols16(const uint32_t (&d)[32], uint64_t (&P)[17]) {
-  uint32_t e[32];
-#pragma unroll
-  for (int r = 0; r < 32; ++r) {
-    const uint32_t a = d[r >> 1], b = d[16 + (r >> 1)];
-    const uint32_t lo = (r & 1) ? (a >> 16) : (a & 0xFFFFu);
-    const uint32_t hi = (r & 1) ? (b & 0xFFFF0000u) : (b << 16);
-    e[r] = lo | hi;
+  // n <= 32 bits of v (v < 2^n).
+  PZ_DEV void put(uint32_t v, uint32_t n) {
+    const uint32_t q = off >> 5, sh = off & 31u;
+    atomicOr(&buf[q], v << sh);
+    atomicOr(&buf[q + 1], (v >> 1) >> (31u - sh));  // v >> (32 - sh); 0 when sh == 0
+    off += n;
   }
-  transpose32(e);
-#pragma unroll
-  for (int j = 0; j < 16; ++j) P[j] = (uint64_t)e[j] | ((uint64_t)e[j + 16] << 32);
+  // n <= 64 bits of v (v < 2^n).
+  PZ_DEV void put64(uint64_t v, uint32_t n) {
+    const uint32_t q = off >> 5, sh = off & 31u;
+    const uint64_t lowpart = v << sh;
+    atomicOr(&buf[q], (uint32_t)lowpart);
+    atomicOr(&buf[q + 1], (uint32_t)(lowpart >> 32));
+    atomicOr(&buf[q + 2], ((uint32_t)(v >> 32) >> 1) >> (31u - sh));
+    off += n;
+  }
+};
+
+// Morton spread: bit i of the low 16 bits goes to bit 2i.
+PZ_DEV uint32_t spread16(uint32_t v) {
+  v &= 0xFFFFu;
+  v = (v | (v << 8)) & 0x00FF00FFu;
+  v = (v | (v << 4)) & 0x0F0F0F0Fu;
+  v = (v | (v << 2)) & 0x33333333u;
+  v = (v | (v << 1)) & 0x55555555u;
+  return v;
 }
 
-// Emits the plane code of P[0..K-1] (K <= KMAX, P[K] treated as zero), top
-// plane first: zero runs, all-ones, pre-XOR-zero, pair, single, verbatim.
-template <typename PT, int KMAX>
-PZ_DEV void emit_plane_code(LdsBitWriter &bw, const PT (&P)[KMAX], int K, int L, int R,
-                            bool active) {
-  const uint32_t pw = (uint32_t)position_bits(L);
-  const PT ones = (PT)all_ones64(L);
-  uint32_t run = 0;
-  PT above = 0;
-#pragma unroll
-  for (int j = KMAX - 1; j >= 0; --j) {
-    const bool live = active && j < K;
-    const PT p = live ? P[j] : (PT)0;
-    const PT x = p ^ above;
-    above = p;
-    if (!live) continue;
-    if (x == 0) {
-      ++run;
-      continue;
-    }
-    // Pending zero run first, then this plane's code, in one field.
-    uint32_t field = 0, flen = 0;
-    if (run) {
-      if (run == 1) {
-        field = 4u;
-        flen = 3;
-      } else {
-        field = 2u | ((run - 2u) << 2);
-        flen = 2 + (uint32_t)R;
-      }
-      run = 0;
-    }
-    uint32_t code, clen;
-    bool verbatim = false;
-    const int cnt = sizeof(PT) == 8 ? popc64((uint64_t)x) : popc32((uint32_t)x);
-    const uint32_t low = sizeof(PT) == 8 ? (uint32_t)__builtin_ctzll((uint64_t)x)
-                                         : (uint32_t)__builtin_ctz((uint32_t)x);
-    if (x == ones) {
-      code = 0u;
-      clen = 5;
-    } else if (p == 0) {
-      code = 16u;
-      clen = 5;
-    } else if (cnt == 2 && (x >> low) == (PT)3) {
-      code = 8u | (low << 5);
-      clen = 5 + pw;
-    } else if (cnt == 1) {
-      code = 24u | (low << 5);
-      clen = 5 + pw;
-    } else {
-      code = 1u;
-      clen = 1;
-      verbatim = true;
-    }
-    bw.put(field | (code << flen), flen + clen);
-    if (verbatim) bw.put64((uint64_t)x, (uint32_t)L);
+// One plane's code: the pending zero run (if any) and this plane's code in one
+// field, then the verbatim payload. x is the XORed plane, p the plane itself.
+template <typename PT>
+PZ_DEV void emit_plane(BitSink &bs, PT x, PT p, PT ones, uint32_t L, uint32_t pw, uint32_t R,
+                       uint32_t &run) {
+  if (x == 0) {
+    ++run;
+    return;
   }
-  if (active && run) {
-    if (run == 1)
-      bw.put(4u, 3);
+  uint32_t rcode = 0, rlen = 0;
+  if (run) {
+    rlen = run == 1 ? 3u : 2u + R;
+    rcode = run == 1 ? 4u : (2u | ((run - 2u) << 2));
+  }
+  run = 0;
+  int cnt;
+  uint32_t low;
+  if constexpr (sizeof(PT) == 8) {
+    cnt = popc64((uint64_t)x);
+    low = (uint32_t)__builtin_ctzll((uint64_t)x);
+  } else {
+    cnt = popc32((uint32_t)x);
+    low = (uint32_t)__builtin_ctz((uint32_t)x);
+  }
+  const bool is_ones = x == ones;
+  const bool is_pz = p == 0;
+  const bool is_pair = cnt == 2 && (x >> low) == (PT)3;
+  const bool is_single = cnt == 1;
+  uint32_t code, clen;
+  if (is_ones || is_pz) {
+    code = is_ones ? 0u : 16u;
+    clen = 5;
+  } else if (is_pair || is_single) {
+    code = (is_pair ? 8u : 24u) | (low << 5);
+    clen = 5 + pw;
+  } else {
+    code = 1u;
+    clen = 1;
+  }
+  bs.put(rcode | (code << rlen), rlen + clen);
+  if (!(is_ones || is_pz || is_pair || is_single)) {
+    if constexpr (sizeof(PT) == 8)
+      bs.put64((uint64_t)x, L);
     else
-      bw.put(2u | ((run - 2u) << 2), 2 + (uint32_t)R);
+      bs.put((uint32_t)x, L);
   }
+}
+
+PZ_DEV void emit_run(BitSink &bs, uint32_t run, uint32_t R) {
+  if (run) bs.put(run == 1 ? 4u : (2u | ((run - 2u) << 2)), run == 1 ? 3u : 2u + R);
 }
 
 // ---------------------------------------------------------------------------
 // Single-pass compression.
 // ---------------------------------------------------------------------------
 template <int W>
-__global__ __launch_bounds__(kGroupThreads) void compress_kernel(
+__global__ __launch_bounds__(kGroupThreads, 4) void compress_kernel(
     const uint8_t *__restrict__ src, uint64_t raw_bytes, uint64_t nchunks, uint64_t ntiles,
     uint8_t *__restrict__ dst, uint64_t *__restrict__ out_bytes, uint64_t *status,
     uint32_t *tile_counter) {
   constexpr int N = 1024 / W;
-  constexpr int R = W == 16 ? 4 : 5;
-  constexpr int KMAX = W + 1;
+  constexpr uint32_t R = W == 16 ? 4 : 5;
   using PT = typename std::conditional<W == 16, uint64_t, uint32_t>::type;
   __shared__ __attribute__((aligned(16))) uint32_t lds_all[kWavesPerGroup * kWaveLdsDwords];
   uint32_t *lds = lds_all + (threadIdx.x >> 6) * kWaveLdsDwords;
@@ -412,8 +443,10 @@ __global__ __launch_bounds__(kGroupThreads) void compress_kernel(
   load_block(src, raw_bytes, off, d);
   Sizes s;
   candidate_sizes<W>(d, s);
-  const int tag = select_tag(s);
-  const uint32_t cost = valid ? 3u + (uint32_t)s.sz[tag] : 0u;
+  launder_regs(d);
+  int best_size;
+  const int tag = select_tag(s, best_size);
+  const uint32_t cost = valid ? 3u + (uint32_t)best_size : 0u;
 
   // Chunk assembly: bit offsets of the blocks, chunk length, raw decision.
   const uint32_t incl = half_inclusive_scan(cost);
@@ -434,12 +467,31 @@ __global__ __launch_bounds__(kGroupThreads) void compress_kernel(
   if ((lane & 31) == 0 && chunk < nchunks) reinterpret_cast<uint16_t *>(dst)[chunk] = (uint16_t)len;
   if (tile == ntiles - 1 && lane == 0) *out_bytes = 2 * nchunks + before + len0 + len1;
 
-  // --- ZBX: move the non-zero symbols to the front (through LDS). ---
   const bool coded = valid && !raw_chunk;
-  const bool want_planes = coded && (tag == kDBX || tag == kBX || tag == kZBX);
+  const bool want_raw = valid && (raw_chunk || tag == kRAW);
+  const bool want_zvc = coded && tag == kZVC;
+  const bool want_dbx = coded && tag == kDBX;
   const bool want_zbx = coded && tag == kZBX;
-  uint32_t cd[32];
-  if (__ballot(want_zbx)) {
+  const bool want_planes = coded && (tag == kDBX || tag == kBX || tag == kZBX);
+
+  // Non-zero mask (ZVC and ZBX prefix), bit i = symbol i non-zero.
+  uint64_t nzmask = 0;
+  if (__ballot(want_zvc || want_zbx)) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if constexpr (W == 16) {
+        nzmask |= (uint64_t)((d[i] & 0xFFFFu) != 0) << (2 * i);
+        nzmask |= (uint64_t)((d[i] >> 16) != 0) << (2 * i + 1);
+      } else {
+        nzmask |= (uint64_t)(d[i] != 0) << i;
+      }
+    }
+  }
+  const uint32_t base = W == 16 ? (d[0] & 0xFFFFu) : d[0];
+
+  // --- ZBX: move the non-zero symbols to the front (through LDS). ---
+  const bool any_zbx = __ballot(want_zbx) != 0;
+  if (any_zbx) {
     uint32_t *region = lds + lane * kLaneStride;
     if (want_zbx) {
 #pragma unroll
@@ -463,13 +515,32 @@ __global__ __launch_bounds__(kGroupThreads) void compress_kernel(
       }
     }
     wave_lds_fence();
-#pragma unroll
-    for (int i = 0; i < 32; ++i) cd[i] = want_zbx ? region[i] : 0u;
-    wave_lds_fence();
-  } else {
-#pragma unroll
-    for (int i = 0; i < 32; ++i) cd[i] = 0;
   }
+
+  // Transpose input (and raw/ZVC payload source): the symbols, the deltas
+  // (DBX, arranged so that plane element k is delta k+1) or the compacted
+  // symbols (ZBX).
+  uint32_t e[32];
+  {
+    const uint32_t *region = lds + lane * kLaneStride;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      uint32_t v = d[i];
+      if (want_dbx) {
+        if constexpr (W == 16) {
+          // dword i = (delta 2i+1, delta 2i+2); the last slot is empty.
+          const uint32_t cur = funnel(i < 31 ? d[i + 1] : 0u, d[i], 16);  // (s 2i+1, s 2i+2)
+          v = pk_sub_u16(cur, d[i]);
+          if (i == 31) v &= 0xFFFFu;
+        } else {
+          v = i < 31 ? d[i + 1] - d[i] : 0u;
+        }
+      }
+      if (any_zbx && want_zbx) v = region[i];
+      e[i] = v;
+    }
+  }
+  if (any_zbx) wave_lds_fence();
 
   // --- Zero the two chunk buffers. ---
   {
@@ -479,91 +550,99 @@ __global__ __launch_bounds__(kGroupThreads) void compress_kernel(
   wave_lds_fence();
 
   // --- Emit this lane's block into its chunk buffer. ---
-  uint32_t *cbuf = lds + half * kChunkBufDwords;
-  const uint32_t lead = 8u * (uint32_t)(pay_off & 3);
-  LdsBitWriter bw;
-  bw.init(cbuf, lead + (raw_chunk ? 1024u * (lane & 31) : excl));
-  if (coded) bw.put((uint32_t)tag, 3);
+  BitSink bs;
+  bs.buf = lds + half * kChunkBufDwords;
+  bs.off = 8u * (uint32_t)(pay_off & 3) + (raw_chunk ? 1024u * (lane & 31) : excl);
+  if (coded) bs.put((uint32_t)tag, 3);
 
-  const bool want_raw = valid && (raw_chunk || tag == kRAW);
   if (__ballot(want_raw)) {
     if (want_raw) {
+      // 1024 bits: the first and last dwords are shared with neighbours
+      // (OR), the 31 between belong to this block alone.
+      const uint32_t q = bs.off >> 5, sh = bs.off & 31u;
+      atomicOr(&bs.buf[q], e[0] << sh);
 #pragma unroll
-      for (int i = 0; i < 32; ++i) bw.put(d[i], 32);
+      for (int i = 1; i < 32; ++i) bs.buf[q + i] = (e[i] << sh) | ((e[i - 1] >> 1) >> (31u - sh));
+      atomicOr(&bs.buf[q + 32], (e[31] >> 1) >> (31u - sh));
+      bs.off += 1024;
     }
   }
 
-  // Non-zero mask (ZVC and ZBX prefix), bit i = symbol i non-zero.
-  const bool want_zvc = coded && tag == kZVC;
-  uint64_t nzmask = 0;
-  if (__ballot(want_zvc || want_zbx)) {
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      if constexpr (W == 16) {
-        nzmask |= (uint64_t)((d[i] & 0xFFFFu) != 0) << (2 * i);
-        nzmask |= (uint64_t)((d[i] >> 16) != 0) << (2 * i + 1);
-      } else {
-        nzmask |= (uint64_t)(d[i] != 0) << i;
-      }
-    }
-  }
   if (__ballot(want_zvc)) {
     if (want_zvc) {
-      bw.put64(nzmask, N);
+      bs.put64(nzmask, N);
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
         if constexpr (W == 16) {
-          const uint32_t a = d[i] & 0xFFFFu, b = d[i] >> 16;
-          if (a) bw.put(a, 16);
-          if (b) bw.put(b, 16);
+          const uint32_t a = e[i] & 0xFFFFu, b = e[i] >> 16;
+          if (a) bs.put(a, 16);
+          if (b) bs.put(b, 16);
         } else {
-          if (d[i]) bw.put(d[i], 32);
+          if (e[i]) bs.put(e[i], 32);
         }
       }
     }
   }
 
   if (__ballot(want_planes)) {
-    // Prefix fields.
-    if (want_planes && tag == kDBX) bw.put(W == 16 ? (d[0] & 0xFFFFu) : d[0], W);
-    if (want_zbx) bw.put64(nzmask, N);
-    // Transpose input: symbols (BX), compacted symbols (ZBX) or deltas (DBX).
-    uint32_t e[32];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      uint32_t delta;
+    if (want_dbx) bs.put(base, W);
+    if (want_zbx) bs.put64(nzmask, N);
+    const uint32_t L = want_dbx ? (uint32_t)(N - 1) : (want_zbx ? (uint32_t)s.n : (uint32_t)N);
+    const uint32_t pw = (uint32_t)position_bits((int)L);
+    const PT ones = (PT)all_ones64((int)L);
+    uint32_t run = 0;
+    PT above = 0;
+    // DBX's top plane: the borrow bits of the deltas.
+    if (__ballot(want_dbx)) {
+      PT bm;
       if constexpr (W == 16) {
-        const uint32_t prevp = i == 0 ? (d[0] << 16) : funnel(d[i], d[i - 1], 16);
-        delta = pk_sub_u16(d[i], prevp);
-        if (i == 0) delta &= 0xFFFF0000u;
+        const uint32_t m0 = spread16(s.b0) | (spread16(s.b0 >> 16) << 1);  // bit m: delta m
+        const uint32_t m1 = spread16(s.b1) | (spread16(s.b1 >> 16) << 1);  // bit m: delta 32+m
+        bm = (((uint64_t)m1 << 32) | m0) >> 1;
       } else {
-        delta = i == 0 ? 0u : d[i] - d[i - 1];
+        bm = s.b0;
       }
-      e[i] = tag == kDBX ? delta : (tag == kZBX ? cd[i] : d[i]);
+      if (want_dbx) {
+        emit_plane<PT>(bs, bm, bm, ones, L, pw, R, run);
+        above = bm;
+      }
     }
-    PT P[KMAX];
     if constexpr (W == 16) {
-      planes_from_symbols16(e, P);
+      uint64_t P[16];
+      {
+        // Symbols k and k+32 share a dword, so one 32x32 transpose yields the
+        // low and high halves of every 64-bit plane.
+        uint32_t t[32];
+#pragma unroll
+        for (int r = 0; r < 32; ++r) {
+          const uint32_t a = e[r >> 1], b = e[16 + (r >> 1)];
+          t[r] = ((r & 1) ? (a >> 16) : (a & 0xFFFFu)) | ((r & 1) ? (b & 0xFFFF0000u) : (b << 16));
+        }
+        transpose32(t);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) P[j] = (uint64_t)t[j] | ((uint64_t)t[j + 16] << 32);
+      }
+#pragma unroll
+      for (int j = 15; j >= 0; --j) {
+        if (want_planes) {
+          const uint64_t p = P[j];
+          emit_plane<uint64_t>(bs, p ^ above, p, ones, L, pw, R, run);
+          above = p;
+        }
+      }
     } else {
       transpose32(e);
 #pragma unroll
-      for (int j = 0; j < 32; ++j) P[j] = e[j];
+      for (int j = 31; j >= 0; --j) {
+        if (want_planes) {
+          const uint32_t p = e[j];
+          emit_plane<uint32_t>(bs, p ^ above, p, ones, L, pw, R, run);
+          above = p;
+        }
+      }
     }
-    int K = W, L = N;
-    if (tag == kDBX) {
-      // Delta k sits at bit k; plane element k-1 is delta k.
-#pragma unroll
-      for (int j = 0; j < W; ++j) P[j] >>= 1;
-      P[W] = (PT)s.bm;
-      K = W + 1;
-      L = N - 1;
-    } else {
-      P[W] = 0;
-      if (tag == kZBX) L = s.n;
-    }
-    emit_plane_code<PT, KMAX>(bw, P, K, L, R, want_planes);
+    if (want_planes) emit_run(bs, run, R);
   }
-  if (valid) bw.flush();
   wave_lds_fence();
 
   // --- Store both payloads: LDS byte i goes to dst byte (pay_off & ~3) + i. ---

@@ -48,29 +48,102 @@ struct GlobalBits {
   }
 };
 
-// Walks the codes of one coded chunk, recording each block's bit offset.
-// Returns false when the chunk fails a decoder check (FORMAT.md §6).
+// Per-lane LDS region of the locate kernel: a 32-dword ring of the chunk's
+// stream (plus one mirror dword so that slot 31's successor is slot 32) and
+// the chunk's 32 block offsets (16-bit).
+constexpr int kRingDwords = 32;
+constexpr int kRingRegion = kRingDwords + 1 + 16;  // 49: odd, spreads lanes over banks
+
+// A chunk's stream, read sequentially by one lane: 16-byte prefetches land in
+// registers, move into the LDS ring one refill later, and codes are peeked
+// from the ring. The lane never waits on a load it issued for the current
+// code, and every global load is a 16-byte aligned vector load.
+struct RingReader {
+  uint32_t *ring;
+  const uint8_t *src;
+  uint64_t limit;   // comp_bytes: nothing at or past it is read
+  uint64_t q0;      // absolute dword index of ring dword 0 (16-byte aligned)
+  uint32_t lead;    // bit offset of the chunk payload within ring dword 0
+  uint32_t fill;    // next relative dword to move from pend into the ring
+  uint4 pend0, pend1;
+
+  PZ_DEV uint4 load4(uint32_t r) const {
+    const uint64_t b = (q0 + r) * 4;
+    if (b + 16 <= limit) return *reinterpret_cast<const uint4 *>(src + b);
+    uint32_t v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t x = 0;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        if (b + 4 * k + t < limit) x |= (uint32_t)src[b + 4 * k + t] << (8 * t);
+      v[k] = x;
+    }
+    return make_uint4(v[0], v[1], v[2], v[3]);
+  }
+  PZ_DEV void put4(uint32_t slot, uint4 v) {
+    ring[slot] = v.x;
+    ring[slot + 1] = v.y;
+    ring[slot + 2] = v.z;
+    ring[slot + 3] = v.w;
+  }
+  PZ_DEV void init(uint32_t *r, const uint8_t *s, uint64_t lim, uint64_t payload_off) {
+    ring = r;
+    src = s;
+    limit = lim;
+    q0 = (payload_off >> 2) & ~3ull;
+    lead = (uint32_t)(8 * (payload_off - 4 * q0));
+#pragma unroll
+    for (uint32_t k = 0; k < 24; k += 4) put4(k, load4(k));
+    ring[kRingDwords] = ring[0];
+    pend0 = load4(24);
+    pend1 = load4(28);
+    fill = 24;
+  }
+  // Keeps at least 16 dwords ahead of payload bit `pos` in the ring.
+  PZ_DEV void refill(uint32_t pos) {
+    if (((lead + pos) >> 5) + 16 >= fill) {
+      const uint32_t slot = fill & (kRingDwords - 1);
+      put4(slot, pend0);
+      put4(slot + 4, pend1);
+      if (slot == 0) ring[kRingDwords] = pend0.x;
+      fill += 8;
+      pend0 = load4(fill);
+      pend1 = load4(fill + 4);
+    }
+  }
+  PZ_DEV uint32_t peek(uint32_t pos) const {
+    const uint32_t a = lead + pos;
+    const uint32_t slot = (a >> 5) & (kRingDwords - 1);
+    return funnel(ring[slot + 1], ring[slot], a & 31u);
+  }
+};
+
+// Walks the codes of one coded chunk, recording each block's bit offset in
+// boff (LDS). Returns false when the chunk fails a decoder check (FORMAT.md
+// §6). Code classes come from the trailing-zero count of the next 32 bits.
 template <int W>
-PZ_DEV bool parse_chunk(const GlobalBits &in, uint32_t H, uint32_t raw_len, uint16_t *boff) {
+PZ_DEV bool parse_chunk(RingReader &in, uint32_t H, uint32_t raw_len, uint16_t *boff) {
   constexpr int N = 1024 / W;
-  constexpr int R = W == 16 ? 4 : 5;
+  constexpr uint32_t R = W == 16 ? 4 : 5;
   const uint32_t end = H * 8;
   const int nb = (int)((raw_len + kBlockBytes - 1) / kBlockBytes);
   uint32_t pos = 0;
-  for (int b = 0; b < nb; ++b) {
+  bool ok = true;
+  for (int b = 0; b < nb && ok; ++b) {
     boff[b] = (uint16_t)pos;
+    in.refill(pos);
     const uint32_t tag = in.peek(pos) & 7u;
     pos += 3;
-    if (tag > 4) return false;
-    int K = 0, L = 0;
+    uint32_t K = 0, L = 0;
     if (tag == kRAW) {
       pos += 1024;
     } else if (tag == kZVC || tag == kZBX) {
-      int n = popc32(in.peek(pos));
-      if (W == 16) n += popc32(in.peek(pos + 32));
+      uint32_t n = (uint32_t)popc32(in.peek(pos));
+      if (W == 16) n += (uint32_t)popc32(in.peek(pos + 32));
       pos += N;
       if (tag == kZVC) {
-        pos += (uint32_t)(W * n);
+        pos += W * n;
       } else {
         K = W;
         L = n;
@@ -79,45 +152,36 @@ PZ_DEV bool parse_chunk(const GlobalBits &in, uint32_t H, uint32_t raw_len, uint
       pos += W;
       K = W + 1;
       L = N - 1;
-    } else {
+    } else if (tag == kBX) {
       K = W;
       L = N;
+    } else {
+      ok = false;
     }
-    if (K) {
-      const uint32_t pw = (uint32_t)position_bits(L);
-      int left = K;
-      while (left > 0) {
-        const uint32_t win = in.peek(pos);
-        const uint32_t tz = win ? (uint32_t)__builtin_ctz(win) : 32u;
-        if (tz == 0) {
-          pos += 1 + (uint32_t)L;
-          --left;
-        } else if (tz == 1) {
-          const int k = (int)((win >> 2) & ((1u << R) - 1u)) + 2;
-          if (k > left) return false;
-          pos += 2 + R;
-          left -= k;
-        } else if (tz == 2) {
-          pos += 3;
-          --left;
-        } else if (tz == 3) {
-          const int p = (int)((win >> 5) & ((1u << pw) - 1u));
-          const bool single = (win >> 4) & 1u;
-          if (p > L - (single ? 1 : 2)) return false;
-          pos += 5 + pw;
-          --left;
-        } else {
-          pos += 5;
-          --left;
-        }
+    const uint32_t pw = (uint32_t)position_bits((int)L);
+    uint32_t left = K;
+    while (left > 0) {
+      in.refill(pos);
+      const uint32_t win = in.peek(pos);
+      const uint32_t tz = win ? (uint32_t)__builtin_ctz(win) : 32u;
+      const uint32_t k = tz == 1 ? ((win >> 2) & ((1u << R) - 1u)) + 2u : 1u;
+      const uint32_t p = (win >> 5) & ((1u << pw) - 1u);
+      const uint32_t pmax = L - (((win >> 4) & 1u) ? 1u : 2u);  // single: L-1, pair: L-2
+      const uint32_t len = tz == 0 ? 1 + L : tz == 1 ? 2 + R : tz == 2 ? 3u : tz == 3 ? 5 + pw : 5u;
+      if ((tz == 1 && k > left) || (tz == 3 && (int)p > (int)pmax)) {
+        ok = false;
+        left = 0;
+      } else {
+        left -= k;
       }
+      pos += len;
     }
-    if (pos > end) return false;
+    if (pos > end) ok = false;
   }
-  if ((pos + 7) / 8 != H) return false;
+  if (!ok || (pos + 7) / 8 != H) return false;
   if (pos & 7u) {
-    const uint32_t rest = in.peek(pos) & ((1u << (8 - (pos & 7u))) - 1u);
-    if (rest) return false;
+    in.refill(pos);
+    if (in.peek(pos) & ((1u << (8 - (pos & 7u))) - 1u)) return false;
   }
   return true;
 }
@@ -127,7 +191,9 @@ __global__ __launch_bounds__(kGroupThreads) void locate_kernel(
     const uint8_t *__restrict__ src, uint64_t comp_bytes, uint64_t raw_bytes, uint64_t nchunks,
     uint64_t ntiles, uint64_t *__restrict__ chunk_off, uint16_t *__restrict__ block_off,
     int32_t *status_out, uint64_t *lb_status, uint32_t *tile_counter) {
+  __shared__ uint32_t lds_all[kGroupThreads * kRingRegion];
   const uint32_t lane = lane_id();
+  uint32_t *region = lds_all + threadIdx.x * kRingRegion;
   const uint32_t tile = acquire_tile(tile_counter);
   if (tile >= ntiles) return;
   const uint64_t c = (uint64_t)tile * kWave + lane;
@@ -141,9 +207,18 @@ __global__ __launch_bounds__(kGroupThreads) void locate_kernel(
   if (c < nchunks) {
     const uint32_t raw_len = (uint32_t)min<uint64_t>(kChunkBytes, raw_bytes - c * kChunkBytes);
     bool chunk_bad = H > raw_len || off + H > comp_bytes;
-    if (!chunk_bad && H < raw_len) {
-      GlobalBits in{src, comp_bytes, off * 8};
-      chunk_bad = !parse_chunk<W>(in, H, raw_len, block_off + c * kBlocksPerChunk);
+    const bool coded = !chunk_bad && H < raw_len;
+    uint16_t *boff = reinterpret_cast<uint16_t *>(region + kRingDwords + 1);
+    if (coded) {
+      RingReader in;
+      in.init(region, src, comp_bytes, off);
+      chunk_bad = !parse_chunk<W>(in, H, raw_len, boff);
+      // One 64-byte store of the chunk's block offsets.
+      const uint32_t *b32 = region + kRingDwords + 1;
+      uint4 *outp = reinterpret_cast<uint4 *>(block_off + c * kBlocksPerChunk);
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        outp[k] = make_uint4(b32[4 * k], b32[4 * k + 1], b32[4 * k + 2], b32[4 * k + 3]);
     }
     chunk_off[c] = chunk_bad ? kBadChunk : off;
     bad |= chunk_bad;
@@ -168,53 +243,72 @@ struct LdsBits {
   }
 };
 
-// Reads the plane code of K <= KMAX planes (top plane first) into P[0..K-1];
-// planes at or above K are zero.
-template <typename PT, int KMAX>
-PZ_DEV void read_plane_code(const LdsBits &in, uint32_t &pos, PT (&P)[KMAX], int K, int L, int R,
-                            bool active) {
-  const uint32_t pw = (uint32_t)position_bits(L);
-  const PT ones = (PT)all_ones64(L);
-  const uint32_t rmask = (1u << R) - 1u;
+// Reads the plane code of K planes (top plane first) and leaves the planes in
+// the transpose layout: w = 16: plane j = t[j] | t[j+16] << 32; w = 32: plane
+// j = t[j]. DBX planes are stored shifted up by one (delta k at bit k, delta
+// 0 := 0); DBX's top plane (the borrow plane) only feeds the XOR chain. Every
+// plane is decoded with selects rather than branches: the class comes from the
+// trailing-zero count of the next 32 bits, and a pending zero run yields X = 0.
+template <int W>
+PZ_DEV void read_planes(const LdsBits &in, uint32_t &pos, uint32_t (&t)[32], int K, uint32_t L,
+                        bool dbx, bool active) {
+  using PT = typename std::conditional<W == 16, uint64_t, uint32_t>::type;
+  constexpr uint32_t R = W == 16 ? 4 : 5;
+  const uint32_t pw = (uint32_t)position_bits((int)L);
+  const uint32_t pmask = (1u << pw) - 1u;
+  const PT ones = (PT)all_ones64((int)L);
   PT above = 0;
   uint32_t run = 0;
 #pragma unroll
-  for (int j = KMAX - 1; j >= 0; --j) {
+  for (int j = W; j >= 0; --j) {
     const bool live = active && j < K;
-    PT x = 0;
-    if (live) {
-      if (run) {
-        --run;
+    const bool fresh = live && run == 0;
+    const uint32_t win = in.peek(pos);
+    const uint32_t tz = win ? (uint32_t)__builtin_ctz(win) : 32u;
+    PT verb;
+    if constexpr (W == 16)
+      verb = (PT)in.peek64(pos + 1) & ones;
+    else
+      verb = (PT)in.peek(pos + 1) & ones;
+    const PT one_or_pair = (((win >> 4) & 1u) ? (PT)1 : (PT)3) << ((win >> 5) & pmask);
+    PT x = tz >= 5 ? ones : (PT)0;
+    x = tz == 0 ? verb : x;
+    x = tz == 3 ? one_or_pair : x;
+    x = tz == 4 ? above : x;  // the plane before the XOR is zero
+    x = fresh ? x : (PT)0;
+    const uint32_t len = tz == 0 ? 1 + L : tz == 1 ? 2 + R : tz == 2 ? 3u : tz == 3 ? 5 + pw : 5u;
+    const uint32_t newrun = tz == 1 ? ((win >> 2) & ((1u << R) - 1u)) + 1u : 0u;
+    pos += fresh ? len : 0u;
+    run = fresh ? newrun : (live ? run - 1u : run);
+    const PT p = live ? (x ^ above) : (PT)0;
+    above = live ? p : above;
+    if (j < W) {
+      const PT ps = dbx ? (PT)(p << 1) : p;
+      if constexpr (W == 16) {
+        t[j] = (uint32_t)ps;
+        t[j + 16] = (uint32_t)((uint64_t)ps >> 32);
       } else {
-        const uint32_t win = in.peek(pos);
-        const uint32_t tz = win ? (uint32_t)__builtin_ctz(win) : 32u;
-        if (tz == 0) {
-          if constexpr (sizeof(PT) == 8)
-            x = (PT)in.peek64(pos + 1) & ones;
-          else
-            x = (PT)in.peek(pos + 1) & ones;
-          pos += 1 + (uint32_t)L;
-        } else if (tz == 1) {
-          run = ((win >> 2) & rmask) + 1u;
-          pos += 2 + (uint32_t)R;
-        } else if (tz == 2) {
-          pos += 3;
-        } else if (tz == 3) {
-          const uint32_t p = (win >> 5) & ((1u << pw) - 1u);
-          x = (((win >> 4) & 1u) ? (PT)1 : (PT)3) << p;
-          pos += 5 + pw;
-        } else if (tz == 4) {
-          x = above;  // the plane before the XOR is zero
-          pos += 5;
-        } else {
-          x = ones;
-          pos += 5;
-        }
+        t[j] = (uint32_t)ps;
       }
     }
-    const PT p = x ^ above;
-    P[j] = live ? p : (PT)0;
-    if (live) above = p;
+  }
+}
+
+// Stores a decoded block; the tensor's last block only up to raw_bytes.
+PZ_DEV void store_block(uint8_t *__restrict__ dst, uint64_t off, uint64_t raw_bytes,
+                        const uint32_t (&d)[32]) {
+  if (off + kBlockBytes <= raw_bytes) {
+    uint4 *p = reinterpret_cast<uint4 *>(dst + off);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) p[q] = make_uint4(d[4 * q], d[4 * q + 1], d[4 * q + 2], d[4 * q + 3]);
+  } else {
+    const uint64_t n = raw_bytes - off;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        if (4 * (uint64_t)i + b < n) dst[off + 4 * i + b] = (uint8_t)(d[i] >> (8 * b));
+    }
   }
 }
 
@@ -278,19 +372,38 @@ __global__ __launch_bounds__(kGroupThreads) void decode_kernel(
       my_raw = c < nchunks ? (uint32_t)min<uint64_t>(kChunkBytes, raw_bytes - c * kChunkBytes) : 0u;
     }
     if (coff == kBadChunk) continue;
-    const uint32_t sh = (uint32_t)(coff & 3);
-    const uint64_t q0 = coff >> 2;
-    const uint32_t ndw = (sh + H + 3) / 4;
-    uint32_t *buf = lds + h * kChunkBufDwords;
-    GlobalBits g{src, comp_bytes, 0};
-    for (uint32_t i = lane; i < (uint32_t)kChunkBufDwords; i += kWave) buf[i] = i < ndw ? g.dword(q0 + i) : 0u;
+    // Dword-aligned copy starting at a 16-byte boundary of the stream.
+    const uint64_t q0 = (coff >> 2) & ~3ull;
+    const uint32_t lead_bytes = (uint32_t)(coff - 4 * q0);
+    const uint32_t nq = (lead_bytes + H + 15) / 16;  // 16-byte groups, at most 258
+    uint4 *buf4 = reinterpret_cast<uint4 *>(lds + h * kChunkBufDwords);
+    const uint8_t *g = src + 4 * q0;
+    for (uint32_t i = lane; i < nq; i += kWave) {
+      const uint64_t b = 4 * q0 + 16ull * i;
+      uint4 v;
+      if (b + 16 <= comp_bytes) {
+        v = reinterpret_cast<const uint4 *>(g)[i];
+      } else {
+        uint32_t t[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          uint32_t x = 0;
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (b + 4 * k + u < comp_bytes) x |= (uint32_t)src[b + 4 * k + u] << (8 * u);
+          t[k] = x;
+        }
+        v = make_uint4(t[0], t[1], t[2], t[3]);
+      }
+      buf4[i] = v;
+    }
   }
   wave_lds_fence();
 
   const bool ok = valid && my_off != kBadChunk;
   const bool raw_chunk = ok && my_H == my_raw;
   const bool coded = ok && !raw_chunk;
-  LdsBits in{lds + half * kChunkBufDwords, 8u * (uint32_t)(my_off & 3)};
+  LdsBits in{lds + half * kChunkBufDwords, 8u * (uint32_t)(my_off - 4 * ((my_off >> 2) & ~3ull))};
 
   uint32_t pos = 0;
   uint32_t tag = 0;
@@ -301,19 +414,18 @@ __global__ __launch_bounds__(kGroupThreads) void decode_kernel(
     pos += 3;
   }
 
-  uint32_t d[32];
-#pragma unroll
-  for (int i = 0; i < 32; ++i) d[i] = 0;
-
+  // Raw chunks and RAW blocks: 1024 bits verbatim.
   const bool want_raw = raw_chunk || (coded && tag == kRAW);
   if (__ballot(want_raw)) {
     if (want_raw) {
+      uint32_t d[32];
 #pragma unroll
       for (int i = 0; i < 32; ++i) d[i] = in.peek(pos + 32 * i);
+      store_block(dst, off, raw_bytes, d);
     }
   }
 
-  // Zero mask of ZVC and ZBX.
+  // Zero mask of ZVC and ZBX (bit i = symbol i non-zero).
   const bool want_zvc = coded && tag == kZVC;
   const bool want_zbx = coded && tag == kZBX;
   uint64_t nzmask = 0;
@@ -323,6 +435,9 @@ __global__ __launch_bounds__(kGroupThreads) void decode_kernel(
   }
   if (__ballot(want_zvc)) {
     if (want_zvc) {
+      uint32_t d[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) d[i] = 0;
 #pragma unroll
       for (int k = 0; k < N; ++k) {
         if ((nzmask >> k) & 1u) {
@@ -334,6 +449,7 @@ __global__ __launch_bounds__(kGroupThreads) void decode_kernel(
             d[k] = v;
         }
       }
+      store_block(dst, off, raw_bytes, d);
     }
   }
 
@@ -345,60 +461,59 @@ __global__ __launch_bounds__(kGroupThreads) void decode_kernel(
       base = in.peek(pos) & WMASK;
       pos += W;
     }
-    int K = W, L = N;
+    int K = W;
+    uint32_t L = N;
     if (want_dbx) {
       K = W + 1;
       L = N - 1;
     } else if (want_zbx) {
-      L = popc64(nzmask);
+      L = (uint32_t)popc64(nzmask);
     }
-    PT P[KMAX];
-    read_plane_code<PT, KMAX>(in, pos, P, K, L, R, want_planes);
-    if (want_dbx) {
-      // Plane element k-1 is delta k: move delta k to bit k (delta 0 := 0).
-#pragma unroll
-      for (int j = 0; j < W; ++j) P[j] <<= 1;
-    }
-    uint32_t e[32];
+    uint32_t t[32];
+    read_planes<W>(in, pos, t, K, L, want_dbx, want_planes);
+    transpose32(t);
+    uint32_t d[32];
     if constexpr (W == 16) {
-      symbols_from_planes16(P, e);
+      // t[r] = symbol r | symbol r+32 << 16 -> d[i] = symbol 2i | symbol 2i+1 << 16.
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        if (i < 16)
+          d[i] = (t[2 * i] & 0xFFFFu) | (t[2 * i + 1] << 16);
+        else
+          d[i] = (t[2 * i - 32] >> 16) | (t[2 * i - 31] & 0xFFFF0000u);
+      }
     } else {
 #pragma unroll
-      for (int j = 0; j < 32; ++j) e[j] = P[j];
-      transpose32(e);
+      for (int i = 0; i < 32; ++i) d[i] = t[i];
     }
     // DBX: running sum of the deltas from the base symbol, modulo 2^w.
-    if (want_dbx) {
+    if (__ballot(want_dbx)) {
       if constexpr (W == 16) {
         uint32_t carry = base;
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
-          const uint32_t v = e[i];
+          const uint32_t v = d[i];
           const uint32_t pair = v + (v << 16);  // (lo, lo + hi)
           const uint32_t outv = pk_add_u16(pair, carry | (carry << 16));
-          e[i] = outv;
+          d[i] = want_dbx ? outv : v;
           carry = outv >> 16;
         }
       } else {
         uint32_t acc = base;
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
-          acc += e[i];
-          e[i] = acc;
+          acc += d[i];
+          d[i] = want_dbx ? acc : d[i];
         }
       }
     }
-    if (want_planes && !want_zbx) {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) d[i] = e[i];
-    }
     // ZBX: the compacted symbols go back to the non-zero positions.
     if (__ballot(want_zbx)) {
-      wave_lds_fence();  // all lanes are done reading the staged payloads
+      wave_lds_fence();  // every lane is done reading the staged payloads
       uint32_t *region = lds + lane * kLaneStride;
       if (want_zbx) {
 #pragma unroll
-        for (int i = 0; i < 32; ++i) region[i] = e[i];
+        for (int i = 0; i < 32; ++i) region[i] = d[i];
       }
       wave_lds_fence();
       if (want_zbx) {
@@ -406,42 +521,23 @@ __global__ __launch_bounds__(kGroupThreads) void decode_kernel(
         if constexpr (W == 16) {
           const uint16_t *r16 = reinterpret_cast<const uint16_t *>(region);
 #pragma unroll
-          for (int k = 0; k < 64; ++k) {
-            if ((nzmask >> k) & 1u) {
-              d[k >> 1] |= (uint32_t)r16[rank] << (16 * (k & 1));
-              ++rank;
-            }
+          for (int i = 0; i < 32; ++i) {
+            uint32_t v = 0;
+            if ((nzmask >> (2 * i)) & 1u) v = r16[rank++];
+            if ((nzmask >> (2 * i + 1)) & 1u) v |= (uint32_t)r16[rank++] << 16;
+            d[i] = v;
           }
         } else {
 #pragma unroll
           for (int k = 0; k < 32; ++k) {
-            if ((nzmask >> k) & 1u) {
-              d[k] = region[rank];
-              ++rank;
-            }
+            uint32_t v = 0;
+            if ((nzmask >> k) & 1u) v = region[rank++];
+            d[k] = v;
           }
         }
       }
     }
-  }
-
-  // Store the block (the tail block only up to raw_bytes).
-  if (ok) {
-    if (off + kBlockBytes <= raw_bytes) {
-      uint4 *p = reinterpret_cast<uint4 *>(dst + off);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) p[q] = make_uint4(d[4 * q], d[4 * q + 1], d[4 * q + 2], d[4 * q + 3]);
-    } else {
-      const uint32_t n = (uint32_t)(raw_bytes - off);
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const uint32_t k = 4 * i + b;
-          if (k < n) dst[off + k] = (uint8_t)(d[i] >> (8 * b));
-        }
-      }
-    }
+    if (want_planes) store_block(dst, off, raw_bytes, d);
   }
 }
 
@@ -464,7 +560,7 @@ hipError_t launch_decompress(int w, const uint8_t *src, uint64_t comp_bytes, uin
   const uint64_t ntiles_a = (nchunks + kWave - 1) / kWave;
   // Scratch (8-byte words): chunk offsets, block offsets, look-back status,
   // tile counter, and a status word when the caller passes none.
-  const uint64_t w_off = nchunks;
+  const uint64_t w_off = (nchunks + 1) & ~1ull;  // keeps the block offsets 16-byte aligned
   const uint64_t w_boff = (nchunks * kBlocksPerChunk * 2 + 7) / 8;
   const uint64_t w_lb = ntiles_a;
   const size_t words = (size_t)(w_off + w_boff + w_lb + 2);
