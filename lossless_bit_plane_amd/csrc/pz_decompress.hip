@@ -48,24 +48,27 @@ struct GlobalBits {
   }
 };
 
-// Per-lane LDS region of the locate kernel: a 32-dword ring of the chunk's
-// stream (plus one mirror dword so that slot 31's successor is slot 32) and
+// Per-lane LDS region of the locate kernel: a 64-dword ring of the chunk's
+// stream (plus one mirror dword so that slot 63's successor is slot 64) and
 // the chunk's 32 block offsets (16-bit).
-constexpr int kRingDwords = 32;
-constexpr int kRingRegion = kRingDwords + 1 + 16;  // 49: odd, spreads lanes over banks
+constexpr int kRingDwords = 64;
+constexpr int kRingRegion = kRingDwords + 1 + 16;  // 81: odd, spreads lanes over banks
+constexpr int kLocateThreads = 64;                 // one wave per workgroup
 
-// A chunk's stream, read sequentially by one lane: 16-byte prefetches land in
-// registers, move into the LDS ring one refill later, and codes are peeked
-// from the ring. The lane never waits on a load it issued for the current
-// code, and every global load is a 16-byte aligned vector load.
+// A chunk's stream, read sequentially by one lane through the LDS ring. Two
+// 16-dword groups are always in flight in registers; a refill moves the older
+// one into the ring and issues the next, so the data a refill stores was
+// requested two refills earlier. Refills happen only at block starts (a
+// wave-uniform point), keeping at least 38 dwords (one worst-case block and
+// its look-ahead) in the ring.
 struct RingReader {
   uint32_t *ring;
   const uint8_t *src;
   uint64_t limit;   // comp_bytes: nothing at or past it is read
-  uint64_t q0;      // absolute dword index of ring dword 0 (16-byte aligned)
-  uint32_t lead;    // bit offset of the chunk payload within ring dword 0
-  uint32_t fill;    // next relative dword to move from pend into the ring
-  uint4 pend0, pend1;
+  uint64_t q0;      // absolute dword index of relative dword 0 (16-byte aligned)
+  uint32_t lead;    // bit offset of the chunk payload within relative dword 0
+  uint32_t fill;    // relative dwords [fill - 64, fill) are in the ring
+  uint4 ga[4], gb[4];  // relative dwords [fill, fill + 16) and [fill + 16, fill + 32)
 
   PZ_DEV uint4 load4(uint32_t r) const {
     const uint64_t b = (q0 + r) * 4;
@@ -81,36 +84,39 @@ struct RingReader {
     }
     return make_uint4(v[0], v[1], v[2], v[3]);
   }
-  PZ_DEV void put4(uint32_t slot, uint4 v) {
-    ring[slot] = v.x;
-    ring[slot + 1] = v.y;
-    ring[slot + 2] = v.z;
-    ring[slot + 3] = v.w;
-  }
-  PZ_DEV void init(uint32_t *r, const uint8_t *s, uint64_t lim, uint64_t payload_off) {
+  PZ_DEV void start(uint32_t *r, const uint8_t *s, uint64_t lim, uint64_t payload_off) {
     ring = r;
     src = s;
     limit = lim;
     q0 = (payload_off >> 2) & ~3ull;
     lead = (uint32_t)(8 * (payload_off - 4 * q0));
+    fill = 0;
 #pragma unroll
-    for (uint32_t k = 0; k < 24; k += 4) put4(k, load4(k));
-    ring[kRingDwords] = ring[0];
-    pend0 = load4(24);
-    pend1 = load4(28);
-    fill = 24;
-  }
-  // Keeps at least 16 dwords ahead of payload bit `pos` in the ring.
-  PZ_DEV void refill(uint32_t pos) {
-    if (((lead + pos) >> 5) + 16 >= fill) {
-      const uint32_t slot = fill & (kRingDwords - 1);
-      put4(slot, pend0);
-      put4(slot + 4, pend1);
-      if (slot == 0) ring[kRingDwords] = pend0.x;
-      fill += 8;
-      pend0 = load4(fill);
-      pend1 = load4(fill + 4);
+    for (int k = 0; k < 4; ++k) {
+      ga[k] = load4(4 * k);
+      gb[k] = load4(16 + 4 * k);
     }
+  }
+  PZ_DEV void refill_step() {
+    const uint32_t slot = fill & (kRingDwords - 1);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      ring[slot + 4 * k + 0] = ga[k].x;
+      ring[slot + 4 * k + 1] = ga[k].y;
+      ring[slot + 4 * k + 2] = ga[k].z;
+      ring[slot + 4 * k + 3] = ga[k].w;
+    }
+    if (slot == 0) ring[kRingDwords] = ga[0].x;  // mirror of slot 0
+    fill += 16;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      ga[k] = gb[k];
+      gb[k] = load4(fill + 16 + 4 * k);
+    }
+  }
+  // Makes relative dwords [dword of pos, +38) available.
+  PZ_DEV void ensure(uint32_t pos) {
+    while (((lead + pos) >> 5) + 38 > fill) refill_step();
   }
   PZ_DEV uint32_t peek(uint32_t pos) const {
     const uint32_t a = lead + pos;
@@ -119,79 +125,71 @@ struct RingReader {
   }
 };
 
-// Walks the codes of one coded chunk, recording each block's bit offset in
-// boff (LDS). Returns false when the chunk fails a decoder check (FORMAT.md
-// §6). Code classes come from the trailing-zero count of the next 32 bits.
+// Walks the codes of every lane's coded chunk, recording each block's bit
+// offset in boff (LDS). Returns false for a chunk that fails a decoder check
+// (FORMAT.md §6). Blocks are taken in wave-uniform steps: all lanes read a
+// block header together (tag, then the base or the zero mask), then run a
+// per-lane loop over that block's plane codes, whose class is the
+// trailing-zero count of the next bits and whose length comes from a
+// per-block table.
 template <int W>
-PZ_DEV bool parse_chunk(RingReader &in, uint32_t H, uint32_t raw_len, uint16_t *boff) {
-  constexpr int N = 1024 / W;
+PZ_DEV bool parse_chunk(RingReader &in, bool coded, uint32_t H, uint32_t raw_len, uint16_t *boff) {
+  constexpr uint32_t N = 1024 / W;
   constexpr uint32_t R = W == 16 ? 4 : 5;
   const uint32_t end = H * 8;
-  const int nb = (int)((raw_len + kBlockBytes - 1) / kBlockBytes);
+  const uint32_t nb = (raw_len + kBlockBytes - 1) / kBlockBytes;
   uint32_t pos = 0;
-  bool ok = true;
-  for (int b = 0; b < nb && ok; ++b) {
-    boff[b] = (uint16_t)pos;
-    in.refill(pos);
-    const uint32_t tag = in.peek(pos) & 7u;
-    pos += 3;
-    uint32_t K = 0, L = 0;
-    if (tag == kRAW) {
-      pos += 1024;
-    } else if (tag == kZVC || tag == kZBX) {
-      uint32_t n = (uint32_t)popc32(in.peek(pos));
-      if (W == 16) n += (uint32_t)popc32(in.peek(pos + 32));
-      pos += N;
-      if (tag == kZVC) {
-        pos += W * n;
-      } else {
-        K = W;
-        L = n;
-      }
-    } else if (tag == kDBX) {
-      pos += W;
-      K = W + 1;
-      L = N - 1;
-    } else if (tag == kBX) {
-      K = W;
-      L = N;
-    } else {
-      ok = false;
+  bool bad = false;
+  for (uint32_t b = 0; b < (uint32_t)kBlocksPerChunk; ++b) {
+    const bool live = coded && !bad && b < nb;
+    if (!__ballot(live)) break;
+    int left = 0;
+    uint32_t L = N, pmask = 0;
+    uint64_t lut = 0;
+    if (live) {
+      in.ensure(pos);
+      boff[b] = (uint16_t)pos;
+      const uint32_t tag = in.peek(pos) & 7u;
+      uint32_t n = (uint32_t)popc32(in.peek(pos + 3));
+      if (W == 16) n += (uint32_t)popc32(in.peek(pos + 35));
+      const bool masked = tag == kZVC || tag == kZBX;
+      pos += 3 + (tag == kDBX ? W : 0u) + (masked ? N : 0u) + (tag == kZVC ? W * n : 0u) +
+             (tag == kRAW ? 1024u : 0u);
+      bad |= tag > 4;
+      L = tag == kDBX ? N - 1 : (tag == kZBX ? n : N);
+      left = (tag == kBX || tag == kZBX) ? (int)W : (tag == kDBX ? (int)W + 1 : 0);
+      // Code length by class (trailing zeros of the next bits, capped at 4):
+      // verbatim 1+L, run 2+R, lone zero 3, pair/single 5+PW, other 5.
+      const uint32_t pw = (uint32_t)position_bits((int)L);
+      pmask = (1u << pw) - 1u;
+      lut = (uint64_t)(1 + L) | ((uint64_t)(2 + R) << 8) | (3ull << 16) |
+            ((uint64_t)(5 + pw) << 24) | (5ull << 32);
     }
-    const uint32_t pw = (uint32_t)position_bits((int)L);
-    uint32_t left = K;
     while (left > 0) {
-      in.refill(pos);
       const uint32_t win = in.peek(pos);
-      const uint32_t tz = win ? (uint32_t)__builtin_ctz(win) : 32u;
-      const uint32_t k = tz == 1 ? ((win >> 2) & ((1u << R) - 1u)) + 2u : 1u;
-      const uint32_t p = (win >> 5) & ((1u << pw) - 1u);
-      const uint32_t pmax = L - (((win >> 4) & 1u) ? 1u : 2u);  // single: L-1, pair: L-2
-      const uint32_t len = tz == 0 ? 1 + L : tz == 1 ? 2 + R : tz == 2 ? 3u : tz == 3 ? 5 + pw : 5u;
-      if ((tz == 1 && k > left) || (tz == 3 && (int)p > (int)pmax)) {
-        ok = false;
-        left = 0;
-      } else {
-        left -= k;
-      }
-      pos += len;
+      const uint32_t tz = min((uint32_t)(__ffs(win) - 1), 4u);  // no set bit: 4
+      pos += (uint32_t)(lut >> (8 * tz)) & 0xFFu;
+      left -= tz == 1 ? (int)((win >> 2) & ((1u << R) - 1u)) + 2 : 1;  // a run past the end: left < 0
+      // A position must lie inside the plane: p <= L-1 (single), L-2 (pair).
+      bad |= tz == 3 && ((win >> 5) & pmask) + 2 > L + ((win >> 4) & 1u);
     }
-    if (pos > end) ok = false;
+    if (live) bad |= left < 0 || pos > end;
   }
-  if (!ok || (pos + 7) / 8 != H) return false;
-  if (pos & 7u) {
-    in.refill(pos);
-    if (in.peek(pos) & ((1u << (8 - (pos & 7u))) - 1u)) return false;
+  if (coded && !bad) {
+    // The last block must end in the payload's last byte, padded with zeros.
+    bad |= (pos + 7) / 8 != H;
+    in.ensure(pos);
+    if ((pos & 7u) && (in.peek(pos) & ((1u << (8 - (pos & 7u))) - 1u))) bad = true;
   }
-  return true;
+  return !bad;
 }
 
 template <int W>
-__global__ __launch_bounds__(kGroupThreads) void locate_kernel(
+__global__ __launch_bounds__(kLocateThreads) void locate_kernel(
     const uint8_t *__restrict__ src, uint64_t comp_bytes, uint64_t raw_bytes, uint64_t nchunks,
     uint64_t ntiles, uint64_t *__restrict__ chunk_off, uint16_t *__restrict__ block_off,
     int32_t *status_out, uint64_t *lb_status, uint32_t *tile_counter) {
-  __shared__ uint32_t lds_all[kGroupThreads * kRingRegion];
+  __shared__ uint32_t lds_all[kLocateThreads * kRingRegion];
   const uint32_t lane = lane_id();
   uint32_t *region = lds_all + threadIdx.x * kRingRegion;
   const uint32_t tile = acquire_tile(tile_counter);
@@ -204,22 +202,24 @@ __global__ __launch_bounds__(kGroupThreads) void locate_kernel(
   const uint64_t off = 2 * nchunks + before + excl;
   bool bad = false;
   if (tile == ntiles - 1 && lane == 0 && 2 * nchunks + before + agg != comp_bytes) bad = true;
-  if (c < nchunks) {
-    const uint32_t raw_len = (uint32_t)min<uint64_t>(kChunkBytes, raw_bytes - c * kChunkBytes);
-    bool chunk_bad = H > raw_len || off + H > comp_bytes;
-    const bool coded = !chunk_bad && H < raw_len;
-    uint16_t *boff = reinterpret_cast<uint16_t *>(region + kRingDwords + 1);
-    if (coded) {
-      RingReader in;
-      in.init(region, src, comp_bytes, off);
-      chunk_bad = !parse_chunk<W>(in, H, raw_len, boff);
-      // One 64-byte store of the chunk's block offsets.
-      const uint32_t *b32 = region + kRingDwords + 1;
-      uint4 *outp = reinterpret_cast<uint4 *>(block_off + c * kBlocksPerChunk);
+  const uint32_t raw_len =
+      c < nchunks ? (uint32_t)min<uint64_t>(kChunkBytes, raw_bytes - c * kChunkBytes) : 0u;
+  const bool header_bad = c < nchunks && (H > raw_len || off + H > comp_bytes);
+  const bool coded = c < nchunks && !header_bad && H < raw_len;
+  uint16_t *boff = reinterpret_cast<uint16_t *>(region + kRingDwords + 1);
+  RingReader in;
+  in.start(region, src, comp_bytes, coded ? off : 0);
+  const bool parsed = parse_chunk<W>(in, coded, H, raw_len, boff);  // whole wave
+  if (coded) {
+    // One 64-byte store of the chunk's block offsets.
+    const uint32_t *b32 = region + kRingDwords + 1;
+    uint4 *outp = reinterpret_cast<uint4 *>(block_off + c * kBlocksPerChunk);
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        outp[k] = make_uint4(b32[4 * k], b32[4 * k + 1], b32[4 * k + 2], b32[4 * k + 3]);
-    }
+    for (int k = 0; k < 4; ++k)
+      outp[k] = make_uint4(b32[4 * k], b32[4 * k + 1], b32[4 * k + 2], b32[4 * k + 3]);
+  }
+  if (c < nchunks) {
+    const bool chunk_bad = header_bad || (coded && !parsed);
     chunk_off[c] = chunk_bad ? kBadChunk : off;
     bad |= chunk_bad;
   }
@@ -257,6 +257,9 @@ PZ_DEV void read_planes(const LdsBits &in, uint32_t &pos, uint32_t (&t)[32], int
   const uint32_t pw = (uint32_t)position_bits((int)L);
   const uint32_t pmask = (1u << pw) - 1u;
   const PT ones = (PT)all_ones64((int)L);
+  // Code length by class: verbatim, run, lone zero, pair/single, pre-zero, ones.
+  const uint64_t lut = (uint64_t)(1 + L) | ((uint64_t)(2 + R) << 8) | (3ull << 16) |
+                       ((uint64_t)(5 + pw) << 24) | (5ull << 32) | (5ull << 40);
   PT above = 0;
   uint32_t run = 0;
 #pragma unroll
@@ -264,7 +267,7 @@ PZ_DEV void read_planes(const LdsBits &in, uint32_t &pos, uint32_t (&t)[32], int
     const bool live = active && j < K;
     const bool fresh = live && run == 0;
     const uint32_t win = in.peek(pos);
-    const uint32_t tz = win ? (uint32_t)__builtin_ctz(win) : 32u;
+    const uint32_t tz = min((uint32_t)(__ffs(win) - 1), 5u);  // 5: five or more zeros
     PT verb;
     if constexpr (W == 16)
       verb = (PT)in.peek64(pos + 1) & ones;
@@ -276,7 +279,7 @@ PZ_DEV void read_planes(const LdsBits &in, uint32_t &pos, uint32_t (&t)[32], int
     x = tz == 3 ? one_or_pair : x;
     x = tz == 4 ? above : x;  // the plane before the XOR is zero
     x = fresh ? x : (PT)0;
-    const uint32_t len = tz == 0 ? 1 + L : tz == 1 ? 2 + R : tz == 2 ? 3u : tz == 3 ? 5 + pw : 5u;
+    const uint32_t len = (uint32_t)(lut >> (8 * tz)) & 0xFFu;
     const uint32_t newrun = tz == 1 ? ((win >> 2) & ((1u << R) - 1u)) + 1u : 0u;
     pos += fresh ? len : 0u;
     run = fresh ? newrun : (live ? run - 1u : run);
@@ -579,13 +582,13 @@ hipError_t launch_decompress(int w, const uint8_t *src, uint64_t comp_bytes, uin
   if (e == hipSuccess && nchunks == 0) {
     if (comp_bytes != 0) e = fill_u32(reinterpret_cast<uint32_t *>(st), 1, (uint32_t)kStatusCorrupt, stream);
   } else if (e == hipSuccess) {
-    const uint64_t groups_a = (ntiles_a + kWavesPerGroup - 1) / kWavesPerGroup;
+    const uint64_t groups_a = ntiles_a;  // one wave per group
     if (w == 16)
-      hipLaunchKernelGGL(locate_kernel<16>, dim3((unsigned)groups_a), dim3(kGroupThreads), 0, stream,
+      hipLaunchKernelGGL(locate_kernel<16>, dim3((unsigned)groups_a), dim3(kLocateThreads), 0, stream,
                          src, comp_bytes, raw_bytes, nchunks, ntiles_a, chunk_off, block_off, st,
                          lb_status, counter);
     else
-      hipLaunchKernelGGL(locate_kernel<32>, dim3((unsigned)groups_a), dim3(kGroupThreads), 0, stream,
+      hipLaunchKernelGGL(locate_kernel<32>, dim3((unsigned)groups_a), dim3(kLocateThreads), 0, stream,
                          src, comp_bytes, raw_bytes, nchunks, ntiles_a, chunk_off, block_off, st,
                          lb_status, counter);
     e = hipGetLastError();
