@@ -416,8 +416,32 @@ PZ_DEV void emit_run(BitSink &bs, uint32_t run, uint32_t R) {
 }
 
 // ---------------------------------------------------------------------------
-// Single-pass compression.
+// Single-pass compression, one workgroup per tile of 8 chunks (256 blocks).
+//
+// Softmax-like activations hold many all-zero blocks, and a wave runs the
+// candidate statistics and the emission for all its lanes at the cost of
+// the slowest. So the group first loads its 256 blocks one per thread,
+// gives every all-zero block its fixed code (below), and packs the non-zero
+// blocks through LDS into the lowest slots: only ceil(nnz / 64) waves then
+// run the statistics and the emission. Chunk offsets come from one decoupled
+// look-back per group.
 // ---------------------------------------------------------------------------
+constexpr int kGroupChunks = kGroupThreads / kBlocksPerChunk;
+constexpr int kStageDwords = kGroupThreads * kLaneStride;
+constexpr int kGroupBufDwords = kGroupChunks * kChunkBufDwords;
+constexpr int kGroupLdsDwords = kStageDwords > kGroupBufDwords ? kStageDwords : kGroupBufDwords;
+
+// An all-zero block codes smallest as BX: every XORed plane is zero, so the
+// planes are one zero run (a 2+R-bit code), which is shorter than the ZVC
+// mask (N bits) and than the DBX and ZBX prefixes.
+template <int W>
+struct ZeroBlock {
+  static constexpr uint32_t R = W == 16 ? 4 : 5;
+  static_assert(W - 2 < (1 << R), "a run of all W planes fits the run field");
+  static constexpr uint32_t code = (uint32_t)kBX | ((2u | ((uint32_t)(W - 2) << 2)) << 3);
+  static constexpr uint32_t bits = 3 + 2 + R;
+};
+
 template <int W>
 __global__ __launch_bounds__(kGroupThreads, 4) void compress_kernel(
     const uint8_t *__restrict__ src, uint64_t raw_bytes, uint64_t nchunks, uint64_t ntiles,
@@ -426,103 +450,128 @@ __global__ __launch_bounds__(kGroupThreads, 4) void compress_kernel(
   constexpr int N = 1024 / W;
   constexpr uint32_t R = W == 16 ? 4 : 5;
   using PT = typename std::conditional<W == 16, uint64_t, uint32_t>::type;
-  __shared__ __attribute__((aligned(16))) uint32_t lds_all[kWavesPerGroup * kWaveLdsDwords];
-  uint32_t *lds = lds_all + (threadIdx.x >> 6) * kWaveLdsDwords;
+  // Staging slots / ZBX compaction regions (stride kLaneStride), later the
+  // eight chunk buffers.
+  __shared__ __attribute__((aligned(16))) uint32_t lds[kGroupLdsDwords];
+  __shared__ uint16_t blk_bits[kGroupThreads];  // per block: its cost, then its bit offset
+  __shared__ uint8_t slot_block[kGroupThreads];  // compacted slot -> block of the group
+  __shared__ uint32_t wave_nz[kWavesPerGroup];
+  __shared__ uint32_t chunk_len[kGroupChunks];
+  __shared__ uint64_t chunk_pay[kGroupChunks];
+  __shared__ uint32_t group_tile;
 
-  const uint32_t lane = lane_id();
-  const uint32_t tile = acquire_tile(tile_counter);
+  const uint32_t t = threadIdx.x, lane = lane_id();
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform: a scalar
+  if (t == 0) group_tile = atomicAdd(tile_counter, 1u);
+  __syncthreads();
+  const uint32_t tile = group_tile;
   if (tile >= ntiles) return;
 
-  const uint32_t half = lane >> 5;
-  const uint64_t block = (uint64_t)tile * kWave + lane;
+  // --- 1. Load block t; find the all-zero blocks. ---
+  const uint64_t block = (uint64_t)tile * kGroupThreads + t;
   const uint64_t chunk = block >> 5;
-  const uint64_t off = block * kBlockBytes;
-  const bool valid = off < raw_bytes;
-
+  const bool valid = block * kBlockBytes < raw_bytes;
   uint32_t d[32];
-  load_block(src, raw_bytes, off, d);
+  load_block(src, raw_bytes, block * kBlockBytes, d);
+  uint32_t any = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) any |= d[i];
+  const bool nonzero = any != 0;  // blocks past the end load as zeros
+  const uint64_t wave_mask = __ballot(nonzero);
+  if (lane == 0) wave_nz[wave] = (uint32_t)popc64(wave_mask);
+  if (!nonzero) blk_bits[t] = (uint16_t)(valid ? ZeroBlock<W>::bits : 0u);
+  __syncthreads();
+
+  // --- 2. Pack the non-zero blocks into slots 0..nnz-1. ---
+  uint32_t nnz = 0, first = 0;
+#pragma unroll
+  for (int k = 0; k < kWavesPerGroup; ++k) {
+    const uint32_t c = wave_nz[k];
+    first += (uint32_t)k < wave ? c : 0u;
+    nnz += c;
+  }
+  if (nonzero) {
+    const uint32_t idx = first + lanes_below(wave_mask);
+    uint32_t *slot = lds + idx * kLaneStride;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) slot[i] = d[i];
+    slot_block[idx] = (uint8_t)t;
+  }
+  __syncthreads();
+
+  // Waves take the slots in an order rotated per tile, so that the busy
+  // waves of successive groups fall on different SIMDs.
+  const uint32_t slot = (t + kGroupThreads - 64u * (tile & 3u)) & (kGroupThreads - 1);
+  const bool active = slot < nnz;
+  const bool wave_active = __ballot(active) != 0;
+
+  // --- 3. Sizes, selection and the transform input of the packed blocks. ---
   Sizes s;
-  candidate_sizes<W>(d, s);
-  launder_regs(d);
-  int best_size;
-  const int tag = select_tag(s, best_size);
-  const uint32_t cost = valid ? 3u + (uint32_t)best_size : 0u;
-
-  // Chunk assembly: bit offsets of the blocks, chunk length, raw decision.
-  const uint32_t incl = half_inclusive_scan(cost);
-  const uint32_t excl = incl - cost;
-  const uint32_t bits = __shfl(incl, (int)((lane & 32) | 31), 64);
-  uint32_t raw_len = 0, len = 0;
-  if (chunk < nchunks) {
-    raw_len = (uint32_t)min<uint64_t>(kChunkBytes, raw_bytes - chunk * kChunkBytes);
-    len = (bits + 7) / 8;
-    if (len >= raw_len) len = raw_len;
-  }
-  const bool raw_chunk = len == raw_len;
-  const uint32_t len0 = __shfl(len, 0, 64), len1 = __shfl(len, 32, 64);
-
-  // Device-wide offsets of this wave's two payloads.
-  const uint64_t before = lookback(status, tile, (uint64_t)len0 + len1);
-  const uint64_t pay_off = 2 * nchunks + before + (half ? len0 : 0);
-  if ((lane & 31) == 0 && chunk < nchunks) reinterpret_cast<uint16_t *>(dst)[chunk] = (uint16_t)len;
-  if (tile == ntiles - 1 && lane == 0) *out_bytes = 2 * nchunks + before + len0 + len1;
-
-  const bool coded = valid && !raw_chunk;
-  const bool want_raw = valid && (raw_chunk || tag == kRAW);
-  const bool want_zvc = coded && tag == kZVC;
-  const bool want_dbx = coded && tag == kDBX;
-  const bool want_zbx = coded && tag == kZBX;
-  const bool want_planes = coded && (tag == kDBX || tag == kBX || tag == kZBX);
-
-  // Non-zero mask (ZVC and ZBX prefix), bit i = symbol i non-zero.
+  s.n = 0;
+  s.b0 = s.b1 = 0;
+  int tag = kRAW;
   uint64_t nzmask = 0;
-  if (__ballot(want_zvc || want_zbx)) {
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      if constexpr (W == 16) {
-        nzmask |= (uint64_t)((d[i] & 0xFFFFu) != 0) << (2 * i);
-        nzmask |= (uint64_t)((d[i] >> 16) != 0) << (2 * i + 1);
-      } else {
-        nzmask |= (uint64_t)(d[i] != 0) << i;
-      }
-    }
-  }
-  const uint32_t base = W == 16 ? (d[0] & 0xFFFFu) : d[0];
-
-  // --- ZBX: move the non-zero symbols to the front (through LDS). ---
-  const bool any_zbx = __ballot(want_zbx) != 0;
-  if (any_zbx) {
-    uint32_t *region = lds + lane * kLaneStride;
-    if (want_zbx) {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) region[i] = 0;
-    }
-    wave_lds_fence();
-    if (want_zbx) {
-      uint32_t k = 0;
-      if constexpr (W == 16) {
-        uint16_t *r16 = reinterpret_cast<uint16_t *>(region);
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          const uint32_t a = d[i] & 0xFFFFu, b = d[i] >> 16;
-          if (a) r16[k++] = (uint16_t)a;
-          if (b) r16[k++] = (uint16_t)b;
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 32; ++i)
-          if (d[i]) region[k++] = d[i];
-      }
-    }
-    wave_lds_fence();
-  }
-
-  // Transpose input (and raw/ZVC payload source): the symbols, the deltas
-  // (DBX, arranged so that plane element k is delta k+1) or the compacted
-  // symbols (ZBX).
+  uint32_t base = 0;
   uint32_t e[32];
-  {
-    const uint32_t *region = lds + lane * kLaneStride;
+  if (wave_active) {
+    uint32_t *region = lds + slot * kLaneStride;
+    if (active) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) d[i] = region[i];
+    }
+    candidate_sizes<W>(d, s);
+    launder_regs(d);
+    int best_size;
+    tag = select_tag(s, best_size);
+    if (active) blk_bits[slot_block[slot]] = (uint16_t)(3 + best_size);
+
+    const bool want_zvc = active && tag == kZVC;
+    const bool want_dbx = active && tag == kDBX;
+    const bool want_zbx = active && tag == kZBX;
+    // Non-zero mask (ZVC and ZBX prefix), bit i = symbol i non-zero.
+    if (__ballot(want_zvc || want_zbx)) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        if constexpr (W == 16) {
+          nzmask |= (uint64_t)((d[i] & 0xFFFFu) != 0) << (2 * i);
+          nzmask |= (uint64_t)((d[i] >> 16) != 0) << (2 * i + 1);
+        } else {
+          nzmask |= (uint64_t)(d[i] != 0) << i;
+        }
+      }
+    }
+    base = W == 16 ? (d[0] & 0xFFFFu) : d[0];
+
+    // ZBX: move the non-zero symbols to the front of this slot's region
+    // (the slot was read above; no other thread touches it).
+    const bool any_zbx = __ballot(want_zbx) != 0;
+    if (any_zbx) {
+      if (want_zbx) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) region[i] = 0;
+      }
+      wave_lds_fence();
+      if (want_zbx) {
+        uint32_t k = 0;
+        if constexpr (W == 16) {
+          uint16_t *r16 = reinterpret_cast<uint16_t *>(region);
+#pragma unroll
+          for (int i = 0; i < 32; ++i) {
+            const uint32_t a = d[i] & 0xFFFFu, b = d[i] >> 16;
+            if (a) r16[k++] = (uint16_t)a;
+            if (b) r16[k++] = (uint16_t)b;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 32; ++i)
+            if (d[i]) region[k++] = d[i];
+        }
+      }
+      wave_lds_fence();
+    }
+
+    // Transform input: the symbols, the deltas (DBX, arranged so that plane
+    // element k is delta k+1) or the compacted symbols (ZBX).
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       uint32_t v = d[i];
@@ -540,122 +589,187 @@ __global__ __launch_bounds__(kGroupThreads, 4) void compress_kernel(
       e[i] = v;
     }
   }
-  if (any_zbx) wave_lds_fence();
+  __syncthreads();  // costs complete; staging and regions free
 
-  // --- Zero the two chunk buffers. ---
+  // --- 4. Chunk assembly in block order: bit offsets, lengths, headers. ---
+  const uint32_t cost = blk_bits[t];
+  const uint32_t incl = half_inclusive_scan(cost);
+  const uint32_t excl = incl - cost;
+  const uint32_t bits = __shfl(incl, (int)((lane & 32) | 31), 64);
+  uint32_t raw_len = 0, len = 0;
+  if (chunk < nchunks) {
+    raw_len = (uint32_t)min<uint64_t>(kChunkBytes, raw_bytes - chunk * kChunkBytes);
+    len = (bits + 7) / 8;
+    if (len >= raw_len) len = raw_len;
+  }
+  const bool raw_chunk = len == raw_len;
+  blk_bits[t] = (uint16_t)excl;
+  if ((lane & 31) == 0) {
+    chunk_len[t >> 5] = len;
+    if (chunk < nchunks) reinterpret_cast<uint16_t *>(dst)[chunk] = (uint16_t)len;
+  }
   {
     uint4 *z = reinterpret_cast<uint4 *>(lds);
-    for (int i = (int)lane; i < (2 * kChunkBufDwords) / 4; i += kWave) z[i] = make_uint4(0, 0, 0, 0);
+    for (uint32_t i = t; i < (uint32_t)kGroupBufDwords / 4; i += kGroupThreads)
+      z[i] = make_uint4(0, 0, 0, 0);
   }
-  wave_lds_fence();
+  __syncthreads();
 
-  // --- Emit this lane's block into its chunk buffer. ---
-  BitSink bs;
-  bs.buf = lds + half * kChunkBufDwords;
-  bs.off = 8u * (uint32_t)(pay_off & 3) + (raw_chunk ? 1024u * (lane & 31) : excl);
-  if (coded) bs.put((uint32_t)tag, 3);
-
-  if (__ballot(want_raw)) {
-    if (want_raw) {
-      // 1024 bits: the first and last dwords are shared with neighbours
-      // (OR), the 31 between belong to this block alone.
-      const uint32_t q = bs.off >> 5, sh = bs.off & 31u;
-      atomicOr(&bs.buf[q], e[0] << sh);
+  // Device-wide payload offsets of the group's chunks.
+  if (wave == 0) {
+    const uint32_t l = lane < (uint32_t)kGroupChunks ? chunk_len[lane] : 0u;
+    uint32_t inc = l;
 #pragma unroll
-      for (int i = 1; i < 32; ++i) bs.buf[q + i] = (e[i] << sh) | ((e[i - 1] >> 1) >> (31u - sh));
-      atomicOr(&bs.buf[q + 32], (e[31] >> 1) >> (31u - sh));
-      bs.off += 1024;
+    for (int o = 1; o < kGroupChunks; o <<= 1) {
+      const uint32_t v = __shfl_up(inc, o, 64);
+      if (lane >= (uint32_t)o) inc += v;
     }
+    const uint32_t agg = __shfl(inc, kGroupChunks - 1, 64);
+    const uint64_t before = lookback(status, tile, agg);
+    if (lane < (uint32_t)kGroupChunks) chunk_pay[lane] = 2 * nchunks + before + (inc - l);
+    if (tile == ntiles - 1 && lane == 0) *out_bytes = 2 * nchunks + before + agg;
+  }
+  __syncthreads();
+
+  // --- 5. Emission into the chunk buffers. ---
+  // All-zero blocks of coded chunks: their one code. (In a raw chunk their
+  // bytes are zeros, which the cleared buffer already holds.)
+  if (valid && !nonzero && !raw_chunk) {
+    BitSink z;
+    z.buf = lds + (t >> 5) * kChunkBufDwords;
+    z.off = 8u * (uint32_t)(chunk_pay[t >> 5] & 3) + excl;
+    z.put(ZeroBlock<W>::code, ZeroBlock<W>::bits);
   }
 
-  if (__ballot(want_zvc)) {
-    if (want_zvc) {
-      bs.put64(nzmask, N);
+  if (wave_active) {
+    const uint32_t sb = active ? (uint32_t)slot_block[slot] : 0u;  // the slot's block in the group
+    const uint32_t ch = sb >> 5;
+    const uint64_t pay = chunk_pay[ch];
+    const uint64_t cchunk = (uint64_t)tile * kGroupChunks + ch;
+    const uint32_t craw_len =
+        cchunk < nchunks ? (uint32_t)min<uint64_t>(kChunkBytes, raw_bytes - cchunk * kChunkBytes) : 0u;
+    const bool craw = chunk_len[ch] == craw_len;
+    const bool coded = active && !craw;
+    const bool want_raw = active && (craw || tag == kRAW);
+    const bool want_zvc = coded && tag == kZVC;
+    const bool want_dbx = coded && tag == kDBX;
+    const bool want_zbx = coded && tag == kZBX;
+    const bool want_planes = coded && (tag == kDBX || tag == kBX || tag == kZBX);
+
+    BitSink bs;
+    bs.buf = lds + ch * kChunkBufDwords;
+    bs.off = 8u * (uint32_t)(pay & 3) + (craw ? 1024u * (sb & 31) : (uint32_t)blk_bits[sb]);
+    if (coded) bs.put((uint32_t)tag, 3);
+
+    if (__ballot(want_raw)) {
+      // A raw chunk needs the symbols themselves back where e holds a transform.
+      const bool reload = want_raw && (tag == kDBX || tag == kZBX);
+      if (__ballot(reload)) {
+        if (reload) load_block(src, raw_bytes, ((uint64_t)tile * kGroupThreads + sb) * kBlockBytes, e);
+      }
+      if (want_raw) {
+        // 1024 bits: the first and last dwords are shared with neighbours
+        // (OR), the 31 between belong to this block alone.
+        const uint32_t q = bs.off >> 5, sh = bs.off & 31u;
+        atomicOr(&bs.buf[q], e[0] << sh);
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
+        for (int i = 1; i < 32; ++i) bs.buf[q + i] = (e[i] << sh) | ((e[i - 1] >> 1) >> (31u - sh));
+        atomicOr(&bs.buf[q + 32], (e[31] >> 1) >> (31u - sh));
+        bs.off += 1024;
+      }
+    }
+
+    if (__ballot(want_zvc)) {
+      if (want_zvc) {
+        bs.put64(nzmask, N);
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          if constexpr (W == 16) {
+            const uint32_t a = e[i] & 0xFFFFu, b = e[i] >> 16;
+            if (a) bs.put(a, 16);
+            if (b) bs.put(b, 16);
+          } else {
+            if (e[i]) bs.put(e[i], 32);
+          }
+        }
+      }
+    }
+
+    if (__ballot(want_planes)) {
+      if (want_dbx) bs.put(base, W);
+      if (want_zbx) bs.put64(nzmask, N);
+      const uint32_t L = want_dbx ? (uint32_t)(N - 1) : (want_zbx ? (uint32_t)s.n : (uint32_t)N);
+      const uint32_t pw = (uint32_t)position_bits((int)L);
+      const PT ones = (PT)all_ones64((int)L);
+      uint32_t run = 0;
+      PT above = 0;
+      // DBX's top plane: the borrow bits of the deltas.
+      if (__ballot(want_dbx)) {
+        PT bm;
         if constexpr (W == 16) {
-          const uint32_t a = e[i] & 0xFFFFu, b = e[i] >> 16;
-          if (a) bs.put(a, 16);
-          if (b) bs.put(b, 16);
+          const uint32_t m0 = spread16(s.b0) | (spread16(s.b0 >> 16) << 1);  // bit m: delta m
+          const uint32_t m1 = spread16(s.b1) | (spread16(s.b1 >> 16) << 1);  // bit m: delta 32+m
+          bm = (((uint64_t)m1 << 32) | m0) >> 1;
         } else {
-          if (e[i]) bs.put(e[i], 32);
+          bm = s.b0;
+        }
+        if (want_dbx) {
+          emit_plane<PT>(bs, bm, bm, ones, L, pw, R, run);
+          above = bm;
         }
       }
-    }
-  }
-
-  if (__ballot(want_planes)) {
-    if (want_dbx) bs.put(base, W);
-    if (want_zbx) bs.put64(nzmask, N);
-    const uint32_t L = want_dbx ? (uint32_t)(N - 1) : (want_zbx ? (uint32_t)s.n : (uint32_t)N);
-    const uint32_t pw = (uint32_t)position_bits((int)L);
-    const PT ones = (PT)all_ones64((int)L);
-    uint32_t run = 0;
-    PT above = 0;
-    // DBX's top plane: the borrow bits of the deltas.
-    if (__ballot(want_dbx)) {
-      PT bm;
       if constexpr (W == 16) {
-        const uint32_t m0 = spread16(s.b0) | (spread16(s.b0 >> 16) << 1);  // bit m: delta m
-        const uint32_t m1 = spread16(s.b1) | (spread16(s.b1 >> 16) << 1);  // bit m: delta 32+m
-        bm = (((uint64_t)m1 << 32) | m0) >> 1;
+        uint64_t P[16];
+        {
+          // Symbols k and k+32 share a dword, so one 32x32 transpose yields
+          // the low and high halves of every 64-bit plane.
+          uint32_t tr[32];
+#pragma unroll
+          for (int r = 0; r < 32; ++r) {
+            const uint32_t a = e[r >> 1], b = e[16 + (r >> 1)];
+            tr[r] = ((r & 1) ? (a >> 16) : (a & 0xFFFFu)) | ((r & 1) ? (b & 0xFFFF0000u) : (b << 16));
+          }
+          transpose32(tr);
+#pragma unroll
+          for (int j = 0; j < 16; ++j) P[j] = (uint64_t)tr[j] | ((uint64_t)tr[j + 16] << 32);
+        }
+#pragma unroll
+        for (int j = 15; j >= 0; --j) {
+          if (want_planes) {
+            const uint64_t p = P[j];
+            emit_plane<uint64_t>(bs, p ^ above, p, ones, L, pw, R, run);
+            above = p;
+          }
+        }
       } else {
-        bm = s.b0;
+        transpose32(e);
+#pragma unroll
+        for (int j = 31; j >= 0; --j) {
+          if (want_planes) {
+            const uint32_t p = e[j];
+            emit_plane<uint32_t>(bs, p ^ above, p, ones, L, pw, R, run);
+            above = p;
+          }
+        }
       }
-      if (want_dbx) {
-        emit_plane<PT>(bs, bm, bm, ones, L, pw, R, run);
-        above = bm;
-      }
+      if (want_planes) emit_run(bs, run, R);
     }
-    if constexpr (W == 16) {
-      uint64_t P[16];
-      {
-        // Symbols k and k+32 share a dword, so one 32x32 transpose yields the
-        // low and high halves of every 64-bit plane.
-        uint32_t t[32];
-#pragma unroll
-        for (int r = 0; r < 32; ++r) {
-          const uint32_t a = e[r >> 1], b = e[16 + (r >> 1)];
-          t[r] = ((r & 1) ? (a >> 16) : (a & 0xFFFFu)) | ((r & 1) ? (b & 0xFFFF0000u) : (b << 16));
-        }
-        transpose32(t);
-#pragma unroll
-        for (int j = 0; j < 16; ++j) P[j] = (uint64_t)t[j] | ((uint64_t)t[j + 16] << 32);
-      }
-#pragma unroll
-      for (int j = 15; j >= 0; --j) {
-        if (want_planes) {
-          const uint64_t p = P[j];
-          emit_plane<uint64_t>(bs, p ^ above, p, ones, L, pw, R, run);
-          above = p;
-        }
-      }
-    } else {
-      transpose32(e);
-#pragma unroll
-      for (int j = 31; j >= 0; --j) {
-        if (want_planes) {
-          const uint32_t p = e[j];
-          emit_plane<uint32_t>(bs, p ^ above, p, ones, L, pw, R, run);
-          above = p;
-        }
-      }
-    }
-    if (want_planes) emit_run(bs, run, R);
   }
-  wave_lds_fence();
+  __syncthreads();
 
-  // --- Store both payloads: LDS byte i goes to dst byte (pay_off & ~3) + i. ---
+  // --- 6. Store: wave w writes chunks 2w and 2w+1; LDS byte i of a chunk
+  // buffer goes to dst byte (payload offset & ~3) + i. ---
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const uint64_t poff = __shfl(pay_off, h * 32, 64);
-    const uint32_t plen = h ? len1 : len0;
+    const uint32_t c = 2 * wave + (uint32_t)h;
+    const uint32_t plen = chunk_len[c];
     if (plen == 0) continue;
+    const uint64_t poff = chunk_pay[c];
     const uint32_t sh = (uint32_t)(poff & 3);
     const uint64_t gbase = poff - sh;
     const uint32_t total = sh + plen;
     const uint32_t ndw = (total + 3) / 4;
-    const uint32_t *buf = lds + h * kChunkBufDwords;
+    const uint32_t *buf = lds + c * kChunkBufDwords;
     for (uint32_t i = lane; i < ndw; i += kWave) {
       const uint32_t v = buf[i];
       const uint32_t b0 = 4 * i, b1 = 4 * i + 4;
@@ -709,8 +823,8 @@ hipError_t launch_compress(int w, const uint8_t *src, uint64_t raw_bytes, uint8_
                            uint64_t *out_bytes, hipStream_t stream) {
   const uint64_t nchunks = (raw_bytes + kChunkBytes - 1) / kChunkBytes;
   if (nchunks == 0) return fill_u64(out_bytes, 1, 0, stream);
-  const uint64_t ntiles = (nchunks + 1) / 2;
-  const uint64_t groups = (ntiles + kWavesPerGroup - 1) / kWavesPerGroup;
+  const uint64_t ntiles = (nchunks + kGroupChunks - 1) / kGroupChunks;
+  const uint64_t groups = ntiles;
   // Scratch: one look-back status word per tile, then the tile counter.
   const size_t words = (size_t)ntiles + 1;
   uint64_t *scratch = nullptr;

@@ -61,6 +61,11 @@ PZ_DEV int popc32(uint32_t x) { return __popc(x); }
 
 PZ_DEV uint32_t lane_id() { return __lane_id(); }
 
+// Number of set bits of a wave mask below this lane.
+PZ_DEV uint32_t lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
 PZ_DEV uint64_t all_ones64(int L) { return L >= 64 ? ~0ull : ((1ull << L) - 1ull); }
 
 // ceil(log2 L) for L >= 2, else 0: width of the position field.
