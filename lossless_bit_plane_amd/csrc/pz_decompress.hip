@@ -7,9 +7,11 @@
 //
 // A chunk's blocks carry no offsets, so the blocks of one chunk must be
 // parsed in order. The work is split in two kernels:
-//   locate: one lane per chunk. Scans the headers (decoupled look-back across
-//           waves), validates them, and walks each chunk's codes without
-//           decoding them to record the bit offset of every block.
+//   locate: one quad of lanes per chunk, 64 chunks per workgroup. Scans the
+//           headers (decoupled look-back across workgroups), validates them,
+//           and walks each chunk's codes without decoding them to record the
+//           bit offset of every block; the quad settles up to 16 verbatim
+//           plane codes per step by speculation.
 //   decode: one lane per block. The wave stages its two chunks' payloads in
 //           LDS with coalesced loads, then every lane decodes its block from
 //           its known bit offset: codes -> XORed planes -> planes -> inverse
@@ -48,75 +50,140 @@ struct GlobalBits {
   }
 };
 
-// Per-lane LDS region of the locate kernel: a 64-dword ring of the chunk's
-// stream (plus one mirror dword so that slot 63's successor is slot 64) and
-// the chunk's 32 block offsets (16-bit).
-constexpr int kRingDwords = 64;
-constexpr int kRingRegion = kRingDwords + 1 + 16;  // 81: odd, spreads lanes over banks
-constexpr int kLocateThreads = 64;                 // one wave per workgroup
+// ---------------------------------------------------------------------------
+// Locate. A workgroup takes a tile of 64 chunks; each chunk is walked by a
+// quad of 4 lanes. Walking is sequential by nature (a block starts where the
+// previous one ends), and a lone wave's time is its instruction count, so the
+// quad shortens the walk by speculation: lane q of the quad reads the windows
+// at pos + (4q + s)(1+L), s = 0..3, i.e. where codes 4q+s would start if all
+// codes before them were verbatim (their length 1+L is fixed within a block).
+// One step thus settles a run of up to 16 verbatim planes, then decodes up to
+// two short codes from the window at the first non-verbatim code.
+// ---------------------------------------------------------------------------
+constexpr int kQuad = 4;                                    // lanes per chunk
+constexpr int kLocateThreads = kGroupThreads;               // four waves
+constexpr int kLocateChunks = kLocateThreads / kQuad;       // 64 chunks per tile
+constexpr int kLocateWaveChunks = kWave / kQuad;            // 16 chunks per wave
+constexpr int kSpec = kQuad * 4;                            // codes tried per step
+// Per-chunk LDS region: a 128-dword ring of the chunk's stream, one mirror
+// dword (slot 128 = slot 0, so a peek at slot 127 reads two dwords), then the
+// chunk's 32 block offsets (16-bit). 145 dwords: odd, spreads chunks over banks.
+constexpr int kRingDwords = 128;
+constexpr int kRingRegion = kRingDwords + 1 + 16;
+constexpr uint32_t kBlockAhead = 38;  // dwords one block (and its look-ahead) can touch
+constexpr uint32_t kGroupDwords = 32;  // refill unit: 8 dwords per quad lane
 
-// A chunk's stream, read sequentially by one lane through the LDS ring. Two
-// 16-dword groups are always in flight in registers; a refill moves the older
-// one into the ring and issues the next, so the data a refill stores was
-// requested two refills earlier. Refills happen only at block starts (a
-// wave-uniform point), keeping at least 38 dwords (one worst-case block and
-// its look-ahead) in the ring.
-struct RingReader {
+// One of four values by the two low bits of k, as bit-tested selects (an
+// equality chain would be turned into branches).
+PZ_DEV uint32_t select4(uint32_t k, uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3) {
+  const bool odd = (k & 1u) != 0;
+  const uint32_t lo = odd ? a1 : a0, hi = odd ? a3 : a2;
+  return (k & 2u) ? hi : lo;
+}
+
+// Value of `v` in lane k (0..3) of this lane's quad (DPP quad broadcast).
+PZ_DEV uint32_t quad_lane(uint32_t v, uint32_t k) {
+  const uint32_t b0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x00, 0xF, 0xF, true);
+  const uint32_t b1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x55, 0xF, 0xF, true);
+  const uint32_t b2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xAA, 0xF, 0xF, true);
+  const uint32_t b3 = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xFF, 0xF, 0xF, true);
+  return select4(k, b0, b1, b2, b3);
+}
+
+// OR of `v` over this lane's quad.
+PZ_DEV uint32_t quad_or(uint32_t v) {
+  v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);  // lanes 1,0,3,2
+  v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);  // lanes 2,3,0,1
+  return v;
+}
+
+// A chunk's stream, read by the chunk's quad through the LDS ring. The ring
+// is topped up only at block starts: the 32 dwords requested at the previous
+// block start are stored, and the next 32 are requested if the ring will have
+// room for them; only if fewer than one block's worth of dwords is then
+// buffered does the quad wait for a load on the spot. Every quad lane holds
+// and stores its own 8 of the 32 dwords.
+struct QuadRing {
   uint32_t *ring;
   const uint8_t *src;
   uint64_t limit;   // comp_bytes: nothing at or past it is read
   uint64_t q0;      // absolute dword index of relative dword 0 (16-byte aligned)
   uint32_t lead;    // bit offset of the chunk payload within relative dword 0
-  uint32_t fill;    // relative dwords [fill - 64, fill) are in the ring
-  uint4 ga[4], gb[4];  // relative dwords [fill, fill + 16) and [fill + 16, fill + 32)
+  uint32_t ql;      // lane within the quad
+  uint32_t fill;    // relative dwords below fill have been stored (the last 128 are kept)
+  bool pending;     // g holds relative dwords [fill + 8 ql, +8)
+  uint4 g[2];
 
   PZ_DEV uint4 load4(uint32_t r) const {
     const uint64_t b = (q0 + r) * 4;
     if (b + 16 <= limit) return *reinterpret_cast<const uint4 *>(src + b);
-    uint32_t v[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      uint32_t x = 0;
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        if (b + 4 * k + t < limit) x |= (uint32_t)src[b + 4 * k + t] << (8 * t);
-      v[k] = x;
+    return load4_tail(b);
+  }
+  // The stream's last bytes: byte loads below limit, zeros above (a plain
+  // loop: it runs at most once per chunk near the end of the stream).
+  PZ_DEV uint4 load4_tail(uint64_t b) const {
+    uint32_t v[4] = {0, 0, 0, 0};
+#pragma unroll 1
+    for (uint32_t k = 0; k < 16 && b + k < limit; ++k) {
+      const uint32_t x = (uint32_t)src[b + k] << (8 * (k & 3));
+      if (k < 4) v[0] |= x; else if (k < 8) v[1] |= x; else if (k < 12) v[2] |= x; else v[3] |= x;
     }
     return make_uint4(v[0], v[1], v[2], v[3]);
   }
-  PZ_DEV void start(uint32_t *r, const uint8_t *s, uint64_t lim, uint64_t payload_off) {
+  PZ_DEV void issue() {
+    g[0] = load4(fill + 8 * ql);
+    g[1] = load4(fill + 8 * ql + 4);
+    pending = true;
+  }
+  // Stores the in-flight group at fill (slots fill % 128 .. +31: never wraps).
+  PZ_DEV void commit() {
+    uint32_t *r = ring + (fill & (kRingDwords - 1)) + 8 * ql;
+    r[0] = g[0].x;
+    r[1] = g[0].y;
+    r[2] = g[0].z;
+    r[3] = g[0].w;
+    r[4] = g[1].x;
+    r[5] = g[1].y;
+    r[6] = g[1].z;
+    r[7] = g[1].w;
+    if ((fill & (kRingDwords - 1)) == 0 && ql == 0) ring[kRingDwords] = g[0].x;  // mirror
+    fill += kGroupDwords;
+    pending = false;
+  }
+  PZ_DEV void start(uint32_t *r, const uint8_t *s, uint64_t lim, uint64_t payload_off, uint32_t lane_in_quad) {
     ring = r;
     src = s;
     limit = lim;
+    ql = lane_in_quad;
     q0 = (payload_off >> 2) & ~3ull;
     lead = (uint32_t)(8 * (payload_off - 4 * q0));
-    fill = 0;
+    // The first 64 dwords in one round trip (16 per lane), then one group in flight.
+    uint4 a[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) a[k] = load4(16 * ql + 4 * k);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      ga[k] = load4(4 * k);
-      gb[k] = load4(16 + 4 * k);
+      ring[16 * ql + 4 * k + 0] = a[k].x;
+      ring[16 * ql + 4 * k + 1] = a[k].y;
+      ring[16 * ql + 4 * k + 2] = a[k].z;
+      ring[16 * ql + 4 * k + 3] = a[k].w;
     }
+    if (ql == 0) ring[kRingDwords] = a[0].x;
+    fill = 64;
+    issue();
   }
-  PZ_DEV void refill_step() {
-    const uint32_t slot = fill & (kRingDwords - 1);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      ring[slot + 4 * k + 0] = ga[k].x;
-      ring[slot + 4 * k + 1] = ga[k].y;
-      ring[slot + 4 * k + 2] = ga[k].z;
-      ring[slot + 4 * k + 3] = ga[k].w;
+  // At a block start whose first bit is pos (quad-uniform): makes relative
+  // dwords [dword of pos, +kBlockAhead) available and requests the next group.
+  PZ_DEV void step(uint32_t pos) {
+    const uint32_t cur = (lead + pos) >> 5;
+    if (pending) commit();
+    while (fill < cur + kBlockAhead) {
+      issue();
+      commit();
     }
-    if (slot == 0) ring[kRingDwords] = ga[0].x;  // mirror of slot 0
-    fill += 16;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      ga[k] = gb[k];
-      gb[k] = load4(fill + 16 + 4 * k);
-    }
-  }
-  // Makes relative dwords [dword of pos, +38) available.
-  PZ_DEV void ensure(uint32_t pos) {
-    while (((lead + pos) >> 5) + 38 > fill) refill_step();
+    // Stored dwords at or above cur stay in the ring until the quad passes them.
+    if (fill + kGroupDwords <= cur + kRingDwords) issue();
+    wave_lds_fence();  // the quad's stores before its reads
   }
   PZ_DEV uint32_t peek(uint32_t pos) const {
     const uint32_t a = lead + pos;
@@ -125,19 +192,20 @@ struct RingReader {
   }
 };
 
-// Walks the codes of every lane's coded chunk, recording each block's bit
-// offset in boff (LDS). Returns false for a chunk that fails a decoder check
-// (FORMAT.md §6). Blocks are taken in wave-uniform steps: all lanes read a
-// block header together (tag, then the base or the zero mask), then run a
-// per-lane loop over that block's plane codes, whose class is the
-// trailing-zero count of the next bits and whose length comes from a
-// per-block table.
+// Walks the codes of a coded chunk (quad-uniform: all four lanes compute the
+// same positions), recording each block's bit offset in boff (LDS, written by
+// quad lane 0). Returns false for a chunk that fails a decoder check
+// (FORMAT.md §6). Blocks are taken in wave-uniform steps: all quads read a
+// block header together (tag, then the base or the zero mask), then the
+// block's plane codes, whose class is the trailing-zero count of the next
+// bits and whose length comes from a per-block table.
 template <int W>
-PZ_DEV bool parse_chunk(RingReader &in, bool coded, uint32_t H, uint32_t raw_len, uint16_t *boff) {
+PZ_DEV bool parse_chunk(QuadRing &in, bool coded, uint32_t H, uint32_t raw_len, uint16_t *boff) {
   constexpr uint32_t N = 1024 / W;
   constexpr uint32_t R = W == 16 ? 4 : 5;
   const uint32_t end = H * 8;
   const uint32_t nb = (raw_len + kBlockBytes - 1) / kBlockBytes;
+  const uint32_t ql = in.ql;
   uint32_t pos = 0;
   bool bad = false;
   for (uint32_t b = 0; b < (uint32_t)kBlocksPerChunk; ++b) {
@@ -147,8 +215,8 @@ PZ_DEV bool parse_chunk(RingReader &in, bool coded, uint32_t H, uint32_t raw_len
     uint32_t L = N, pmask = 0;
     uint64_t lut = 0;
     if (live) {
-      in.ensure(pos);
-      boff[b] = (uint16_t)pos;
+      in.step(pos);
+      if (ql == 0) boff[b] = (uint16_t)pos;
       const uint32_t tag = in.peek(pos) & 7u;
       uint32_t n = (uint32_t)popc32(in.peek(pos + 3));
       if (W == 16) n += (uint32_t)popc32(in.peek(pos + 35));
@@ -165,20 +233,44 @@ PZ_DEV bool parse_chunk(RingReader &in, bool coded, uint32_t H, uint32_t raw_len
       lut = (uint64_t)(1 + L) | ((uint64_t)(2 + R) << 8) | (3ull << 16) |
             ((uint64_t)(5 + pw) << 24) | (5ull << 32);
     }
+    const uint32_t V = (uint32_t)(lut & 0xFFu);
+    const uint32_t spec = 4 * ql * V;  // this lane tries codes 4 ql .. 4 ql + 3
+    const uint32_t runf = (1u << R) - 1u;
+    // Straight-line steps (selects, no branches): a lone wave pays for every
+    // instruction, and exec-mask branches cost more than the selects.
     while (left > 0) {
-      const uint32_t win = in.peek(pos);
-      const uint32_t tz = min((uint32_t)(__ffs(win) - 1), 4u);  // no set bit: 4
-      pos += (uint32_t)(lut >> (8 * tz)) & 0xFFu;
-      left -= tz == 1 ? (int)((win >> 2) & ((1u << R) - 1u)) + 2 : 1;  // a run past the end: left < 0
-      // A position must lie inside the plane: p <= L-1 (single), L-2 (pair).
-      bad |= tz == 3 && ((win >> 5) & pmask) + 2 > L + ((win >> 4) & 1u);
+      const uint32_t a = pos + spec;
+      const uint32_t w0 = in.peek(a), w1 = in.peek(a + V), w2 = in.peek(a + 2 * V),
+                     w3 = in.peek(a + 3 * V);
+      const uint32_t mine = (w0 & 1u) | ((w1 & 1u) << 1) | ((w2 & 1u) << 2) | ((w3 & 1u) << 3);
+      const uint32_t vmask = quad_or(mine << (4 * ql));  // bit k: code k would be verbatim
+      // Leading verbatim codes (~vmask has bit 16 set, so the count is <= 16).
+      const uint32_t j = min((uint32_t)__builtin_ctz(~vmask), (uint32_t)left);
+      pos += j * V;
+      left -= (int)j;
+      // The window of code j: lane j/4 of the quad read it as its w[j%4].
+      uint32_t win = quad_lane(select4(j, w0, w1, w2, w3), j >> 2);
+      bool take = j < (uint32_t)kSpec;
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        take = take && left > 0 && (win & 1u) == 0u;  // a short code (at most 11 bits)
+        const uint32_t tz = (uint32_t)__builtin_ctz(win | 16u);  // trailing zeros, capped at 4
+        const uint32_t len = (uint32_t)(lut >> (8 * tz)) & 0xFFu;
+        const int planes = tz == 1 ? (int)((win >> 2) & runf) + 2 : 1;  // a run past the end: left < 0
+        // A position must lie inside the plane: p <= L-1 (single), L-2 (pair).
+        const bool badpos = tz == 3 && ((win >> 5) & pmask) + 2 > L + ((win >> 4) & 1u);
+        pos += take ? len : 0u;
+        left -= take ? planes : 0;
+        bad |= take && badpos;
+        win >>= len;
+      }
     }
     if (live) bad |= left < 0 || pos > end;
   }
   if (coded && !bad) {
     // The last block must end in the payload's last byte, padded with zeros.
     bad |= (pos + 7) / 8 != H;
-    in.ensure(pos);
+    in.step(pos);
     if ((pos & 7u) && (in.peek(pos) & ((1u << (8 - (pos & 7u))) - 1u))) bad = true;
   }
   return !bad;
@@ -189,41 +281,61 @@ __global__ __launch_bounds__(kLocateThreads) void locate_kernel(
     const uint8_t *__restrict__ src, uint64_t comp_bytes, uint64_t raw_bytes, uint64_t nchunks,
     uint64_t ntiles, uint64_t *__restrict__ chunk_off, uint16_t *__restrict__ block_off,
     int32_t *status_out, uint64_t *lb_status, uint32_t *tile_counter) {
-  __shared__ uint32_t lds_all[kLocateThreads * kRingRegion];
-  const uint32_t lane = lane_id();
-  uint32_t *region = lds_all + threadIdx.x * kRingRegion;
-  const uint32_t tile = acquire_tile(tile_counter);
+  __shared__ uint32_t lds[kLocateChunks * kRingRegion];
+  __shared__ uint64_t wave_sum[kWavesPerGroup];
+  __shared__ uint64_t tile_before;
+  __shared__ uint32_t group_tile;
+  const uint32_t t = threadIdx.x, lane = lane_id(), ql = t & (kQuad - 1);
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  if (t == 0) group_tile = atomicAdd(tile_counter, 1u);
+  __syncthreads();
+  const uint32_t tile = group_tile;
   if (tile >= ntiles) return;
-  const uint64_t c = (uint64_t)tile * kWave + lane;
+
+  // Chunk offsets: a scan of the 16-bit headers over the tile, and one
+  // look-back per tile for the headers before it.
+  const uint32_t ci = t / kQuad;  // chunk within the tile
+  const uint64_t c = (uint64_t)tile * kLocateChunks + ci;
   const uint32_t H = c < nchunks ? reinterpret_cast<const uint16_t *>(src)[c] : 0u;
-  const uint64_t agg = wave_sum_u64(H);
-  const uint64_t before = lookback(lb_status, tile, agg);
-  const uint64_t excl = wave_inclusive_scan_u64(H) - H;
-  const uint64_t off = 2 * nchunks + before + excl;
-  bool bad = false;
-  if (tile == ntiles - 1 && lane == 0 && 2 * nchunks + before + agg != comp_bytes) bad = true;
+  const uint64_t incl = wave_inclusive_scan_u64(ql == 0 ? H : 0u);  // equal over the quad
+  if (lane == kWave - 1) wave_sum[wave] = incl;
+  __syncthreads();
+  if (wave == 0) {
+    uint64_t agg = 0;
+#pragma unroll
+    for (int k = 0; k < kWavesPerGroup; ++k) agg += wave_sum[k];
+    const uint64_t before = lookback(lb_status, tile, agg);
+    if (lane == 0) {
+      tile_before = before;
+      if (tile == ntiles - 1 && 2 * nchunks + before + agg != comp_bytes) *status_out = kStatusCorrupt;
+    }
+  }
+  __syncthreads();
+  uint64_t wave_before = tile_before;
+  for (uint32_t k = 0; k < wave; ++k) wave_before += wave_sum[k];
+  const uint64_t off = 2 * nchunks + wave_before + incl - H;
+
   const uint32_t raw_len =
       c < nchunks ? (uint32_t)min<uint64_t>(kChunkBytes, raw_bytes - c * kChunkBytes) : 0u;
   const bool header_bad = c < nchunks && (H > raw_len || off + H > comp_bytes);
   const bool coded = c < nchunks && !header_bad && H < raw_len;
+  uint32_t *region = lds + ci * kRingRegion;
   uint16_t *boff = reinterpret_cast<uint16_t *>(region + kRingDwords + 1);
-  RingReader in;
-  in.start(region, src, comp_bytes, coded ? off : 0);
+  QuadRing in;
+  in.start(region, src, comp_bytes, coded ? off : 0, ql);
   const bool parsed = parse_chunk<W>(in, coded, H, raw_len, boff);  // whole wave
+  wave_lds_fence();
   if (coded) {
-    // One 64-byte store of the chunk's block offsets.
-    const uint32_t *b32 = region + kRingDwords + 1;
-    uint4 *outp = reinterpret_cast<uint4 *>(block_off + c * kBlocksPerChunk);
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      outp[k] = make_uint4(b32[4 * k], b32[4 * k + 1], b32[4 * k + 2], b32[4 * k + 3]);
+    // The chunk's block offsets: 64 bytes, 16 per quad lane.
+    const uint32_t *b32 = region + kRingDwords + 1 + 4 * ql;
+    *reinterpret_cast<uint4 *>(block_off + c * kBlocksPerChunk + 8 * ql) =
+        make_uint4(b32[0], b32[1], b32[2], b32[3]);
   }
-  if (c < nchunks) {
+  if (c < nchunks && ql == 0) {
     const bool chunk_bad = header_bad || (coded && !parsed);
     chunk_off[c] = chunk_bad ? kBadChunk : off;
-    bad |= chunk_bad;
+    if (chunk_bad) *status_out = kStatusCorrupt;
   }
-  if (bad) *status_out = kStatusCorrupt;
 }
 
 // Bits of a chunk payload staged in LDS; bit `pos` of the payload is bit
@@ -560,7 +672,7 @@ hipError_t fill_u32(uint32_t *p, uint64_t n, uint32_t value, hipStream_t stream)
 hipError_t launch_decompress(int w, const uint8_t *src, uint64_t comp_bytes, uint8_t *dst,
                              uint64_t raw_bytes, int32_t *status, hipStream_t stream) {
   const uint64_t nchunks = (raw_bytes + kChunkBytes - 1) / kChunkBytes;
-  const uint64_t ntiles_a = (nchunks + kWave - 1) / kWave;
+  const uint64_t ntiles_a = (nchunks + kLocateChunks - 1) / kLocateChunks;
   // Scratch (8-byte words): chunk offsets, block offsets, look-back status,
   // tile counter, and a status word when the caller passes none.
   const uint64_t w_off = (nchunks + 1) & ~1ull;  // keeps the block offsets 16-byte aligned
@@ -582,7 +694,7 @@ hipError_t launch_decompress(int w, const uint8_t *src, uint64_t comp_bytes, uin
   if (e == hipSuccess && nchunks == 0) {
     if (comp_bytes != 0) e = fill_u32(reinterpret_cast<uint32_t *>(st), 1, (uint32_t)kStatusCorrupt, stream);
   } else if (e == hipSuccess) {
-    const uint64_t groups_a = ntiles_a;  // one wave per group
+    const uint64_t groups_a = ntiles_a;
     if (w == 16)
       hipLaunchKernelGGL(locate_kernel<16>, dim3((unsigned)groups_a), dim3(kLocateThreads), 0, stream,
                          src, comp_bytes, raw_bytes, nchunks, ntiles_a, chunk_off, block_off, st,
