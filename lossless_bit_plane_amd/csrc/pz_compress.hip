@@ -615,36 +615,35 @@ __global__ __launch_bounds__(kGroupThreads, 4) void compress_kernel(
   }
   __syncthreads();
 
-  // Device-wide payload offsets of the group's chunks.
+  // The group's aggregate goes out now; the device-wide offsets are resolved
+  // after the emission (which works at byte alignment 0), so that waiting on
+  // the predecessors overlaps with it.
+  uint32_t l = 0, inc = 0, agg = 0;
   if (wave == 0) {
-    const uint32_t l = lane < (uint32_t)kGroupChunks ? chunk_len[lane] : 0u;
-    uint32_t inc = l;
+    l = lane < (uint32_t)kGroupChunks ? chunk_len[lane] : 0u;
+    inc = l;
 #pragma unroll
     for (int o = 1; o < kGroupChunks; o <<= 1) {
       const uint32_t v = __shfl_up(inc, o, 64);
       if (lane >= (uint32_t)o) inc += v;
     }
-    const uint32_t agg = __shfl(inc, kGroupChunks - 1, 64);
-    const uint64_t before = lookback(status, tile, agg);
-    if (lane < (uint32_t)kGroupChunks) chunk_pay[lane] = 2 * nchunks + before + (inc - l);
-    if (tile == ntiles - 1 && lane == 0) *out_bytes = 2 * nchunks + before + agg;
+    agg = __shfl(inc, kGroupChunks - 1, 64);
+    lookback_publish(status, tile, agg);
   }
-  __syncthreads();
 
-  // --- 5. Emission into the chunk buffers. ---
+  // --- 5. Emission into the chunk buffers (payload bit i at buffer bit i). ---
   // All-zero blocks of coded chunks: their one code. (In a raw chunk their
   // bytes are zeros, which the cleared buffer already holds.)
   if (valid && !nonzero && !raw_chunk) {
     BitSink z;
     z.buf = lds + (t >> 5) * kChunkBufDwords;
-    z.off = 8u * (uint32_t)(chunk_pay[t >> 5] & 3) + excl;
+    z.off = excl;
     z.put(ZeroBlock<W>::code, ZeroBlock<W>::bits);
   }
 
   if (wave_active) {
     const uint32_t sb = active ? (uint32_t)slot_block[slot] : 0u;  // the slot's block in the group
     const uint32_t ch = sb >> 5;
-    const uint64_t pay = chunk_pay[ch];
     const uint64_t cchunk = (uint64_t)tile * kGroupChunks + ch;
     const uint32_t craw_len =
         cchunk < nchunks ? (uint32_t)min<uint64_t>(kChunkBytes, raw_bytes - cchunk * kChunkBytes) : 0u;
@@ -658,7 +657,7 @@ __global__ __launch_bounds__(kGroupThreads, 4) void compress_kernel(
 
     BitSink bs;
     bs.buf = lds + ch * kChunkBufDwords;
-    bs.off = 8u * (uint32_t)(pay & 3) + (craw ? 1024u * (sb & 31) : (uint32_t)blk_bits[sb]);
+    bs.off = craw ? 1024u * (sb & 31) : (uint32_t)blk_bits[sb];
     if (coded) bs.put((uint32_t)tag, 3);
 
     if (__ballot(want_raw)) {
@@ -755,10 +754,18 @@ __global__ __launch_bounds__(kGroupThreads, 4) void compress_kernel(
       if (want_planes) emit_run(bs, run, R);
     }
   }
+
+  // Device-wide payload offsets of the group's chunks.
+  if (wave == 0) {
+    const uint64_t before = lookback_resolve(status, tile, agg);
+    if (lane < (uint32_t)kGroupChunks) chunk_pay[lane] = 2 * nchunks + before + (inc - l);
+    if (tile == ntiles - 1 && lane == 0) *out_bytes = 2 * nchunks + before + agg;
+  }
   __syncthreads();
 
-  // --- 6. Store: wave w writes chunks 2w and 2w+1; LDS byte i of a chunk
-  // buffer goes to dst byte (payload offset & ~3) + i. ---
+  // --- 6. Store: wave w writes chunks 2w and 2w+1. Payload byte i goes to
+  // dst byte poff + i: with sh = poff & 3, dst dword i of the aligned span
+  // holds buffer bytes 4i - sh .. 4i - sh + 3. ---
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const uint32_t c = 2 * wave + (uint32_t)h;
@@ -771,7 +778,8 @@ __global__ __launch_bounds__(kGroupThreads, 4) void compress_kernel(
     const uint32_t ndw = (total + 3) / 4;
     const uint32_t *buf = lds + c * kChunkBufDwords;
     for (uint32_t i = lane; i < ndw; i += kWave) {
-      const uint32_t v = buf[i];
+      const uint32_t lo = i > 0 ? buf[i - 1] : 0u;
+      const uint32_t v = sh ? funnel(buf[i], lo, 32u - 8u * sh) : buf[i];
       const uint32_t b0 = 4 * i, b1 = 4 * i + 4;
       if (b0 >= sh && b1 <= total) {
         *reinterpret_cast<uint32_t *>(dst + gbase + b0) = v;

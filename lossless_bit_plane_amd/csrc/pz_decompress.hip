@@ -12,11 +12,13 @@
 //           and walks each chunk's codes without decoding them to record the
 //           bit offset of every block; the quad settles up to 16 verbatim
 //           plane codes per step by speculation.
-//   decode: one lane per block. The wave stages its two chunks' payloads in
-//           LDS with coalesced loads, then every lane decodes its block from
-//           its known bit offset: codes -> XORed planes -> planes -> inverse
-//           32x32 bit transpose -> symbols (delta prefix sum for DBX, scatter
-//           by the zero mask for ZVC/ZBX), and stores 128 bytes.
+//   decode: 8 chunks per workgroup. The payloads are staged in LDS with
+//           coalesced loads; all-zero blocks are recognised by their code and
+//           the other blocks packed onto the fewest waves, where a lane decodes
+//           a block from its known bit offset: codes -> XORed planes -> planes
+//           -> inverse 32x32 bit transpose -> symbols (delta prefix sum for
+//           DBX, scatter by the zero mask for ZVC/ZBX). The decoded blocks
+//           are gathered in LDS and leave in coalesced stores.
 #include <type_traits>
 
 #include "pz_device.h"
@@ -446,52 +448,65 @@ PZ_DEV void symbols_from_planes16(const uint64_t (&P)[17], uint32_t (&d)[32]) {
   }
 }
 
+// Decode: one workgroup per tile of 8 chunks (256 blocks). The chunk
+// payloads are staged in LDS; every block's own thread recognises an
+// all-zero block (coded as one zero run over all planes) and the rest are
+// packed into the lowest slots, so that only ceil(n / 64) waves run the
+// decoders. Decoded blocks are gathered in LDS rows (stride 33 dwords, which
+// keeps lane-strided row access conflict free) over the dead payloads, and
+// the group's 32 KB of output leaves in coalesced 16-byte stores.
+constexpr int kDecodeChunks = kGroupThreads / kBlocksPerChunk;  // 8
+constexpr int kDecodeBufDwords = kDecodeChunks * kChunkBufDwords;
+constexpr int kDecodeRowDwords = kGroupThreads * kLaneStride;
+constexpr int kDecodeLdsDwords =
+    kDecodeBufDwords > kDecodeRowDwords ? kDecodeBufDwords : kDecodeRowDwords;
+
+// The code of an all-zero block (the tag of BX, then one run of all W
+// planes), as it appears in the stream's low bits at the block start.
+template <int W>
+struct ZeroCode {
+  static constexpr uint32_t R = W == 16 ? 4 : 5;
+  static constexpr uint32_t code = (uint32_t)kBX | ((2u | ((uint32_t)(W - 2) << 2)) << 3);
+  static constexpr uint32_t mask = (1u << (3 + 2 + R)) - 1u;
+};
+
 template <int W>
 __global__ __launch_bounds__(kGroupThreads) void decode_kernel(
     const uint8_t *__restrict__ src, uint64_t comp_bytes, uint64_t raw_bytes, uint64_t nchunks,
     const uint64_t *__restrict__ chunk_off, const uint16_t *__restrict__ block_off,
     uint8_t *__restrict__ dst) {
   constexpr int N = 1024 / W;
-  constexpr int R = W == 16 ? 4 : 5;
-  constexpr int KMAX = W + 1;
   constexpr uint32_t WMASK = W == 16 ? 0xFFFFu : 0xFFFFFFFFu;
-  using PT = typename std::conditional<W == 16, uint64_t, uint32_t>::type;
-  __shared__ __attribute__((aligned(16))) uint32_t lds_all[kWavesPerGroup * kWaveLdsDwords];
-  uint32_t *lds = lds_all + (threadIdx.x >> 6) * kWaveLdsDwords;
+  __shared__ __attribute__((aligned(16))) uint32_t lds[kDecodeLdsDwords];
+  __shared__ uint32_t blk_info[kGroupThreads];    // per packed block: bit position | tag << 16 | raw << 19
+  __shared__ uint8_t slot_block[kGroupThreads];   // packed slot -> block of the group
+  __shared__ uint32_t chunk_lead[kDecodeChunks];  // bit offset of each payload in its buffer
+  __shared__ uint32_t wave_busy[kWavesPerGroup];
 
-  const uint32_t lane = lane_id();
-  const uint64_t tile = (uint64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
-  if (tile * 2 >= nchunks) return;
-  const uint32_t half = lane >> 5;
-  const uint64_t block = tile * kWave + lane;
-  const uint64_t chunk = block >> 5;
-  const uint64_t off = block * kBlockBytes;
-  const bool valid = off < raw_bytes;
+  const uint32_t t = threadIdx.x, lane = lane_id();
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const uint64_t gtile = blockIdx.x;
+  if (gtile * kDecodeChunks >= nchunks) return;
+  const uint64_t gblock0 = gtile * kGroupThreads;  // first block of the group
 
-  // Stage both chunk payloads (dword-aligned copies) in LDS.
+  // --- 1. Stage the 8 payloads (dword-aligned copies); wave w takes 2w, 2w+1. ---
   const uint16_t *hdr = reinterpret_cast<const uint16_t *>(src);
-  uint64_t my_off = kBadChunk;
-  uint32_t my_H = 0, my_raw = 0;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const uint64_t c = tile * 2 + h;
+    const uint32_t ci = 2 * wave + (uint32_t)h;
+    const uint64_t c = gtile * kDecodeChunks + ci;
     uint64_t coff = kBadChunk;
     uint32_t H = 0;
     if (c < nchunks) {
       coff = chunk_off[c];
       H = hdr[c];
     }
-    if (half == (uint32_t)h) {
-      my_off = coff;
-      my_H = H;
-      my_raw = c < nchunks ? (uint32_t)min<uint64_t>(kChunkBytes, raw_bytes - c * kChunkBytes) : 0u;
-    }
-    if (coff == kBadChunk) continue;
-    // Dword-aligned copy starting at a 16-byte boundary of the stream.
     const uint64_t q0 = (coff >> 2) & ~3ull;
+    if (lane == 0) chunk_lead[ci] = coff == kBadChunk ? 0u : (uint32_t)(8 * (coff - 4 * q0));
+    if (coff == kBadChunk) continue;
     const uint32_t lead_bytes = (uint32_t)(coff - 4 * q0);
     const uint32_t nq = (lead_bytes + H + 15) / 16;  // 16-byte groups, at most 258
-    uint4 *buf4 = reinterpret_cast<uint4 *>(lds + h * kChunkBufDwords);
+    uint4 *buf4 = reinterpret_cast<uint4 *>(lds + ci * kChunkBufDwords);
     const uint8_t *g = src + 4 * q0;
     for (uint32_t i = lane; i < nq; i += kWave) {
       const uint64_t b = 4 * q0 + 16ull * i;
@@ -499,142 +514,196 @@ __global__ __launch_bounds__(kGroupThreads) void decode_kernel(
       if (b + 16 <= comp_bytes) {
         v = reinterpret_cast<const uint4 *>(g)[i];
       } else {
-        uint32_t t[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          uint32_t x = 0;
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            if (b + 4 * k + u < comp_bytes) x |= (uint32_t)src[b + 4 * k + u] << (8 * u);
-          t[k] = x;
+        uint32_t tv[4] = {0, 0, 0, 0};
+#pragma unroll 1
+        for (uint32_t k = 0; k < 16 && b + k < comp_bytes; ++k) {
+          const uint32_t x = (uint32_t)src[b + k] << (8 * (k & 3));
+          if (k < 4) tv[0] |= x; else if (k < 8) tv[1] |= x; else if (k < 12) tv[2] |= x; else tv[3] |= x;
         }
-        v = make_uint4(t[0], t[1], t[2], t[3]);
+        v = make_uint4(tv[0], tv[1], tv[2], tv[3]);
       }
       buf4[i] = v;
     }
   }
-  wave_lds_fence();
+  __syncthreads();
 
-  const bool ok = valid && my_off != kBadChunk;
-  const bool raw_chunk = ok && my_H == my_raw;
-  const bool coded = ok && !raw_chunk;
-  LdsBits in{lds + half * kChunkBufDwords, 8u * (uint32_t)(my_off - 4 * ((my_off >> 2) & ~3ull))};
-
-  uint32_t pos = 0;
-  uint32_t tag = 0;
-  if (raw_chunk) pos = 1024u * (lane & 31);
-  if (coded) {
-    pos = block_off[block];
-    tag = in.peek(pos) & 7u;
-    pos += 3;
-  }
-
-  // Raw chunks and RAW blocks: 1024 bits verbatim.
-  const bool want_raw = raw_chunk || (coded && tag == kRAW);
-  if (__ballot(want_raw)) {
-    if (want_raw) {
-      uint32_t d[32];
-#pragma unroll
-      for (int i = 0; i < 32; ++i) d[i] = in.peek(pos + 32 * i);
-      store_block(dst, off, raw_bytes, d);
+  // --- 2. Block t: all-zero blocks stay here, the rest go to the slot list. ---
+  const uint64_t block = gblock0 + t;
+  const uint64_t chunk = block >> 5;
+  bool busy = false;
+  {
+    const uint32_t ci = t >> 5;
+    uint64_t coff = kBadChunk;
+    uint32_t H = 0, raw_len = 0;
+    if (chunk < nchunks) {
+      coff = chunk_off[chunk];
+      H = hdr[chunk];
+      raw_len = (uint32_t)min<uint64_t>(kChunkBytes, raw_bytes - chunk * kChunkBytes);
     }
+    const bool ok = block * kBlockBytes < raw_bytes && coff != kBadChunk;
+    const bool raw_chunk = ok && H == raw_len;
+    const bool coded = ok && !raw_chunk;
+    uint32_t pos = 1024u * (t & 31), head = 0;
+    if (coded) {
+      const LdsBits in{lds + ci * kChunkBufDwords, chunk_lead[ci]};
+      pos = block_off[block];
+      head = in.peek(pos);
+      pos += 3;
+    }
+    const bool zero = coded && (head & ZeroCode<W>::mask) == ZeroCode<W>::code;
+    busy = raw_chunk || (coded && !zero);
+    if (busy) blk_info[t] = pos | ((head & 7u) << 16) | ((uint32_t)raw_chunk << 19);
   }
+  const uint64_t bmask = __ballot(busy);
+  if (lane == 0) wave_busy[wave] = (uint32_t)popc64(bmask);
+  __syncthreads();
+  uint32_t nbusy = 0, first = 0;
+#pragma unroll
+  for (int k = 0; k < kWavesPerGroup; ++k) {
+    const uint32_t c = wave_busy[k];
+    first += (uint32_t)k < wave ? c : 0u;
+    nbusy += c;
+  }
+  if (busy) slot_block[first + lanes_below(bmask)] = (uint8_t)t;
+  __syncthreads();
 
-  // Zero mask of ZVC and ZBX (bit i = symbol i non-zero).
-  const bool want_zvc = coded && tag == kZVC;
-  const bool want_zbx = coded && tag == kZBX;
+  // --- 3. Packed slots: raw copy, ZVC or plane decoding into d. Waves take the
+  // slots in an order rotated per tile, so that the busy waves of successive
+  // groups fall on different SIMDs. ---
+  const uint32_t slot = (t + kGroupThreads - 64u * (uint32_t)(gtile & 3)) & (kGroupThreads - 1);
+  const bool active = slot < nbusy;
+  const bool wave_active = __ballot(active) != 0;
+  uint32_t sb = 0;
   uint64_t nzmask = 0;
-  if (want_zvc || want_zbx) {
-    nzmask = W == 16 ? in.peek64(pos) : (uint64_t)in.peek(pos);
-    pos += N;
-  }
-  if (__ballot(want_zvc)) {
-    if (want_zvc) {
-      uint32_t d[32];
-#pragma unroll
-      for (int i = 0; i < 32; ++i) d[i] = 0;
-#pragma unroll
-      for (int k = 0; k < N; ++k) {
-        if ((nzmask >> k) & 1u) {
-          const uint32_t v = in.peek(pos) & WMASK;
-          pos += W;
-          if constexpr (W == 16)
-            d[k >> 1] |= v << (16 * (k & 1));
-          else
-            d[k] = v;
-        }
-      }
-      store_block(dst, off, raw_bytes, d);
+  bool want_zbx = false;
+  uint32_t d[32];
+  if (wave_active) {
+    uint32_t pos = 0, tag = kBX;
+    bool raw_chunk = false;
+    if (active) {
+      sb = slot_block[slot];
+      const uint32_t info = blk_info[sb];
+      pos = info & 0xFFFFu;
+      tag = (info >> 16) & 7u;
+      raw_chunk = (info >> 19) & 1u;
     }
-  }
+    const LdsBits in{lds + (sb >> 5) * kChunkBufDwords, chunk_lead[sb >> 5]};
 
-  const bool want_dbx = coded && tag == kDBX;
-  const bool want_planes = coded && (tag == kDBX || tag == kBX || tag == kZBX);
-  if (__ballot(want_planes)) {
-    uint32_t base = 0;
-    if (want_dbx) {
-      base = in.peek(pos) & WMASK;
-      pos += W;
+    const bool coded = active && !raw_chunk;
+    const bool want_raw = active && (raw_chunk || tag == kRAW);
+    const bool want_zvc = coded && tag == kZVC;
+    const bool want_dbx = coded && tag == kDBX;
+    const bool want_planes = coded && (tag == kDBX || tag == kBX || tag == kZBX);
+    want_zbx = coded && tag == kZBX;
+    // Zero mask of ZVC and ZBX (bit i = symbol i non-zero).
+    if (want_zvc || want_zbx) {
+      nzmask = W == 16 ? in.peek64(pos) : (uint64_t)in.peek(pos);
+      pos += N;
     }
-    int K = W;
-    uint32_t L = N;
-    if (want_dbx) {
-      K = W + 1;
-      L = N - 1;
-    } else if (want_zbx) {
-      L = (uint32_t)popc64(nzmask);
-    }
-    uint32_t t[32];
-    read_planes<W>(in, pos, t, K, L, want_dbx, want_planes);
-    transpose32(t);
-    uint32_t d[32];
-    if constexpr (W == 16) {
-      // t[r] = symbol r | symbol r+32 << 16 -> d[i] = symbol 2i | symbol 2i+1 << 16.
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        if (i < 16)
-          d[i] = (t[2 * i] & 0xFFFFu) | (t[2 * i + 1] << 16);
-        else
-          d[i] = (t[2 * i - 32] >> 16) | (t[2 * i - 31] & 0xFFFF0000u);
+
+    // Plane decoding first (it needs the most registers, and d is not yet
+    // holding anything), then the raw and ZVC blocks fill d.
+    if (__ballot(want_planes)) {
+      uint32_t base = 0;
+      if (want_dbx) {
+        base = in.peek(pos) & WMASK;
+        pos += W;
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) d[i] = t[i];
-    }
-    // DBX: running sum of the deltas from the base symbol, modulo 2^w.
-    if (__ballot(want_dbx)) {
+      int K = W;
+      uint32_t L = N;
+      if (want_dbx) {
+        K = W + 1;
+        L = N - 1;
+      } else if (want_zbx) {
+        L = (uint32_t)popc64(nzmask);
+      }
+      uint32_t tp[32];
+      read_planes<W>(in, pos, tp, K, L, want_dbx, want_planes);
+      transpose32(tp);
       if constexpr (W == 16) {
-        uint32_t carry = base;
+        // tp[r] = symbol r | symbol r+32 << 16 -> d[i] = symbol 2i | symbol 2i+1 << 16.
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
-          const uint32_t v = d[i];
-          const uint32_t pair = v + (v << 16);  // (lo, lo + hi)
-          const uint32_t outv = pk_add_u16(pair, carry | (carry << 16));
-          d[i] = want_dbx ? outv : v;
-          carry = outv >> 16;
+          if (i < 16)
+            d[i] = (tp[2 * i] & 0xFFFFu) | (tp[2 * i + 1] << 16);
+          else
+            d[i] = (tp[2 * i - 32] >> 16) | (tp[2 * i - 31] & 0xFFFF0000u);
         }
       } else {
-        uint32_t acc = base;
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          acc += d[i];
-          d[i] = want_dbx ? acc : d[i];
+        for (int i = 0; i < 32; ++i) d[i] = tp[i];
+      }
+      // DBX: running sum of the deltas from the base symbol, modulo 2^w.
+      if (__ballot(want_dbx)) {
+        if constexpr (W == 16) {
+          uint32_t carry = base;
+#pragma unroll
+          for (int i = 0; i < 32; ++i) {
+            const uint32_t v = d[i];
+            const uint32_t pair = v + (v << 16);  // (lo, lo + hi)
+            const uint32_t outv = pk_add_u16(pair, carry | (carry << 16));
+            d[i] = want_dbx ? outv : v;
+            carry = outv >> 16;
+          }
+        } else {
+          uint32_t acc = base;
+#pragma unroll
+          for (int i = 0; i < 32; ++i) {
+            acc += d[i];
+            d[i] = want_dbx ? acc : d[i];
+          }
         }
       }
     }
-    // ZBX: the compacted symbols go back to the non-zero positions.
-    if (__ballot(want_zbx)) {
-      wave_lds_fence();  // every lane is done reading the staged payloads
-      uint32_t *region = lds + lane * kLaneStride;
-      if (want_zbx) {
+
+    // Raw chunks and RAW blocks: 1024 bits verbatim.
+    if (__ballot(want_raw)) {
 #pragma unroll
-        for (int i = 0; i < 32; ++i) region[i] = d[i];
+      for (int i = 0; i < 32; ++i) {
+        const uint32_t v = in.peek(pos + 32 * i);
+        d[i] = want_raw ? v : d[i];
       }
+    }
+    if (__ballot(want_zvc)) {
+      if (want_zvc) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) d[i] = 0;
+#pragma unroll
+        for (int k = 0; k < N; ++k) {
+          if ((nzmask >> k) & 1u) {
+            const uint32_t v = in.peek(pos) & WMASK;
+            pos += W;
+            if constexpr (W == 16)
+              d[k >> 1] |= v << (16 * (k & 1));
+            else
+              d[k] = v;
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();  // payloads dead: LDS becomes the output rows
+
+  // --- 4. Output rows. All-zero (and unusable) blocks: zeros. Packed blocks:
+  // their symbols; ZBX spreads the compacted symbols to the non-zero
+  // positions in place. ---
+  if (!busy) {
+    uint32_t *row = lds + t * kLaneStride;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) row[i] = 0;
+  }
+  if (wave_active) {
+    uint32_t *row = lds + sb * kLaneStride;
+    if (active) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) row[i] = d[i];
+    }
+    if (__ballot(want_zbx)) {
       wave_lds_fence();
       if (want_zbx) {
         uint32_t rank = 0;
         if constexpr (W == 16) {
-          const uint16_t *r16 = reinterpret_cast<const uint16_t *>(region);
+          const uint16_t *r16 = reinterpret_cast<const uint16_t *>(row);
 #pragma unroll
           for (int i = 0; i < 32; ++i) {
             uint32_t v = 0;
@@ -646,13 +715,39 @@ __global__ __launch_bounds__(kGroupThreads) void decode_kernel(
 #pragma unroll
           for (int k = 0; k < 32; ++k) {
             uint32_t v = 0;
-            if ((nzmask >> k) & 1u) v = region[rank++];
+            if ((nzmask >> k) & 1u) v = row[rank++];
             d[k] = v;
           }
         }
       }
+      wave_lds_fence();
+      if (want_zbx) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) row[i] = d[i];
+      }
     }
-    if (want_planes) store_block(dst, off, raw_bytes, d);
+  }
+  __syncthreads();
+
+  // --- 5. Coalesced store of the group's output span (bytes past raw_bytes
+  // are not written). ---
+  const uint64_t span0 = gblock0 * kBlockBytes;
+  const uint64_t span_end = min<uint64_t>(raw_bytes, span0 + (uint64_t)kGroupThreads * kBlockBytes);
+  const uint32_t span = (uint32_t)(span_end - span0);
+#pragma unroll
+  for (int k = 0; k < kBlocksPerChunk / 4; ++k) {
+    const uint32_t u = t + (uint32_t)k * kGroupThreads;  // 16-byte unit of the span
+    const uint32_t b0 = 16 * u;
+    if (b0 >= span) continue;
+    const uint32_t *row = lds + (u >> 3) * kLaneStride + 4 * (u & 7);
+    const uint4 v = make_uint4(row[0], row[1], row[2], row[3]);
+    if (b0 + 16 <= span) {
+      *reinterpret_cast<uint4 *>(dst + span0 + b0) = v;
+    } else {
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+      for (uint32_t bb = b0; bb < span; ++bb)
+        dst[span0 + bb] = (uint8_t)(w4[(bb - b0) >> 2] >> (8 * ((bb - b0) & 3)));
+    }
   }
 }
 
@@ -705,8 +800,7 @@ hipError_t launch_decompress(int w, const uint8_t *src, uint64_t comp_bytes, uin
                          lb_status, counter);
     e = hipGetLastError();
     if (e == hipSuccess) {
-      const uint64_t ntiles_b = (nchunks + 1) / 2;
-      const uint64_t groups_b = (ntiles_b + kWavesPerGroup - 1) / kWavesPerGroup;
+      const uint64_t groups_b = (nchunks + kDecodeChunks - 1) / kDecodeChunks;
       if (w == 16)
         hipLaunchKernelGGL(decode_kernel<16>, dim3((unsigned)groups_b), dim3(kGroupThreads), 0,
                            stream, src, comp_bytes, raw_bytes, nchunks, chunk_off, block_off, dst);

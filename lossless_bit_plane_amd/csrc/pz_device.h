@@ -142,16 +142,18 @@ PZ_DEV uint32_t acquire_tile(uint32_t *counter) {
 }
 
 // Decoupled look-back (Merrill & Garland, "Single-pass Parallel Prefix Scan
-// with Decoupled Look-back"): publishes this tile's aggregate, then walks back
-// over predecessors 64 at a time until it meets an inclusive prefix, and
-// publishes its own inclusive prefix. Returns the exclusive prefix of `agg`.
-PZ_DEV uint64_t lookback(uint64_t *status, uint32_t tile, uint64_t agg) {
+// with Decoupled Look-back"), in two halves so that a tile can do other work
+// between them. lookback_publish makes this tile's aggregate visible (tile 0
+// publishes its inclusive prefix); lookback_resolve walks back over the
+// predecessors 64 at a time until it meets an inclusive prefix, publishes this
+// tile's inclusive prefix and returns the exclusive prefix of `agg`.
+PZ_DEV void lookback_publish(uint64_t *status, uint32_t tile, uint64_t agg) {
+  if (lane_id() == 0) atomic_store_agent(&status[tile], (tile == 0 ? kFlagPrefix : kFlagAggregate) | agg);
+}
+
+PZ_DEV uint64_t lookback_resolve(uint64_t *status, uint32_t tile, uint64_t agg) {
+  if (tile == 0) return 0;
   const uint32_t lane = lane_id();
-  if (tile == 0) {
-    if (lane == 0) atomic_store_agent(&status[0], kFlagPrefix | agg);
-    return 0;
-  }
-  if (lane == 0) atomic_store_agent(&status[tile], kFlagAggregate | agg);
   uint64_t excl = 0;
   int64_t base = (int64_t)tile - 1;
   while (true) {
@@ -175,6 +177,11 @@ PZ_DEV uint64_t lookback(uint64_t *status, uint32_t tile, uint64_t agg) {
   return excl;
 }
 
+PZ_DEV uint64_t lookback(uint64_t *status, uint32_t tile, uint64_t agg) {
+  lookback_publish(status, tile, agg);
+  return lookback_resolve(status, tile, agg);
+}
+
 // Orders this wave's LDS accesses before and after (all lanes of a wave run
 // the same instruction stream; this keeps the compiler from moving LDS
 // accesses across phases that hand data between lanes).
@@ -182,49 +189,6 @@ PZ_DEV void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
 }
-
-// ---------------------------------------------------------------------------
-// Bit writer into LDS: stream bit t is bit (t % 32) of dword (t / 32), which
-// for a little-endian machine is bit (t % 8) of byte (t / 8). Fields are
-// written least-significant bit first. Dwords are OR-ed in, so adjacent
-// writers that share a boundary dword do not clobber each other.
-// ---------------------------------------------------------------------------
-struct LdsBitWriter {
-  uint32_t *buf;
-  uint64_t acc;   // pending bits, aligned so that bit 0 is dword bit 0
-  uint32_t nacc;  // number of meaningful bits in acc (including the lead-in)
-  uint32_t wpos;  // dword index of acc's first dword
-
-  PZ_DEV void init(uint32_t *b, uint32_t bit_offset) {
-    buf = b;
-    acc = 0;
-    nacc = bit_offset & 31;
-    wpos = bit_offset >> 5;
-  }
-  // Append n <= 32 bits of v (v < 2^n).
-  PZ_DEV void put(uint32_t v, uint32_t n) {
-    acc |= (uint64_t)v << nacc;
-    nacc += n;
-    if (nacc >= 32) {
-      atomicOr(&buf[wpos], (uint32_t)acc);
-      acc >>= 32;
-      nacc -= 32;
-      ++wpos;
-    }
-  }
-  // Append n <= 64 bits of v.
-  PZ_DEV void put64(uint64_t v, uint32_t n) {
-    if (n > 32) {
-      put((uint32_t)v, 32);
-      put((uint32_t)(v >> 32), n - 32);
-    } else {
-      put((uint32_t)v, n);
-    }
-  }
-  PZ_DEV void flush() {
-    if (nacc) atomicOr(&buf[wpos], (uint32_t)acc);
-  }
-};
 
 // ---------------------------------------------------------------------------
 // Plane-code size from per-plane class masks (bit j describes plane j):
