@@ -575,7 +575,7 @@ __global__ __launch_bounds__(kGroupThreads) void decode_kernel(
   const bool wave_active = __ballot(active) != 0;
   uint32_t sb = 0;
   uint64_t nzmask = 0;
-  bool want_zbx = false;
+  bool want_spread = false;  // ZVC or ZBX: symbols in order of the non-zero positions
   uint32_t d[32];
   if (wave_active) {
     uint32_t pos = 0, tag = kBX;
@@ -594,7 +594,7 @@ __global__ __launch_bounds__(kGroupThreads) void decode_kernel(
     const bool want_zvc = coded && tag == kZVC;
     const bool want_dbx = coded && tag == kDBX;
     const bool want_planes = coded && (tag == kDBX || tag == kBX || tag == kZBX);
-    want_zbx = coded && tag == kZBX;
+    const bool want_zbx = coded && tag == kZBX;
     // Zero mask of ZVC and ZBX (bit i = symbol i non-zero).
     if (want_zvc || want_zbx) {
       nzmask = W == 16 ? in.peek64(pos) : (uint64_t)in.peek(pos);
@@ -656,36 +656,23 @@ __global__ __launch_bounds__(kGroupThreads) void decode_kernel(
       }
     }
 
-    // Raw chunks and RAW blocks: 1024 bits verbatim.
-    if (__ballot(want_raw)) {
+    // Raw chunks and RAW blocks: 1024 bits verbatim. ZVC: its payload, the
+    // non-zero symbols in order (the same layout as ZBX's compacted
+    // symbols), spread to their positions below.
+    const bool want_copy = want_raw || want_zvc;
+    if (__ballot(want_copy)) {
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
         const uint32_t v = in.peek(pos + 32 * i);
-        d[i] = want_raw ? v : d[i];
+        d[i] = want_copy ? v : d[i];
       }
     }
-    if (__ballot(want_zvc)) {
-      if (want_zvc) {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) d[i] = 0;
-#pragma unroll
-        for (int k = 0; k < N; ++k) {
-          if ((nzmask >> k) & 1u) {
-            const uint32_t v = in.peek(pos) & WMASK;
-            pos += W;
-            if constexpr (W == 16)
-              d[k >> 1] |= v << (16 * (k & 1));
-            else
-              d[k] = v;
-          }
-        }
-      }
-    }
+    want_spread = want_zvc || want_zbx;
   }
   __syncthreads();  // payloads dead: LDS becomes the output rows
 
   // --- 4. Output rows. All-zero (and unusable) blocks: zeros. Packed blocks:
-  // their symbols; ZBX spreads the compacted symbols to the non-zero
+  // their symbols; ZVC and ZBX spread the non-zero symbols to their
   // positions in place. ---
   if (!busy) {
     uint32_t *row = lds + t * kLaneStride;
@@ -698,30 +685,37 @@ __global__ __launch_bounds__(kGroupThreads) void decode_kernel(
 #pragma unroll
       for (int i = 0; i < 32; ++i) row[i] = d[i];
     }
-    if (__ballot(want_zbx)) {
+    if (__ballot(want_spread)) {
       wave_lds_fence();
-      if (want_zbx) {
+      if (want_spread) {
+        // Symbol i takes compacted symbol rank(i) = number of non-zero symbols
+        // before it. Every read is issued (rank <= N stays inside the padded
+        // row) and the zero positions are selected away, so the reads need no
+        // branches and no wait between them.
         uint32_t rank = 0;
         if constexpr (W == 16) {
           const uint16_t *r16 = reinterpret_cast<const uint16_t *>(row);
 #pragma unroll
           for (int i = 0; i < 32; ++i) {
-            uint32_t v = 0;
-            if ((nzmask >> (2 * i)) & 1u) v = r16[rank++];
-            if ((nzmask >> (2 * i + 1)) & 1u) v |= (uint32_t)r16[rank++] << 16;
-            d[i] = v;
+            const bool n0 = (nzmask >> (2 * i)) & 1u, n1 = (nzmask >> (2 * i + 1)) & 1u;
+            const uint32_t a = r16[rank];
+            rank += n0 ? 1u : 0u;
+            const uint32_t b = r16[rank];
+            rank += n1 ? 1u : 0u;
+            d[i] = (n0 ? a : 0u) | ((n1 ? b : 0u) << 16);
           }
         } else {
 #pragma unroll
           for (int k = 0; k < 32; ++k) {
-            uint32_t v = 0;
-            if ((nzmask >> k) & 1u) v = row[rank++];
-            d[k] = v;
+            const bool n0 = (nzmask >> k) & 1u;
+            const uint32_t a = row[rank];
+            rank += n0 ? 1u : 0u;
+            d[k] = n0 ? a : 0u;
           }
         }
       }
       wave_lds_fence();
-      if (want_zbx) {
+      if (want_spread) {
 #pragma unroll
         for (int i = 0; i < 32; ++i) row[i] = d[i];
       }
@@ -751,17 +745,12 @@ __global__ __launch_bounds__(kGroupThreads) void decode_kernel(
   }
 }
 
-__global__ void fill_u32_kernel(uint32_t *p, uint64_t n, uint32_t value) {
-  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (uint64_t)gridDim.x * blockDim.x)
-    p[i] = value;
-}
-
-hipError_t fill_u32(uint32_t *p, uint64_t n, uint32_t value, hipStream_t stream) {
-  if (n == 0) return hipSuccess;
-  const uint64_t groups = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
-  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)groups), dim3(256), 0, stream, p, n, value);
-  return hipGetLastError();
+// Clears the look-back words and the tile counter, and sets the status word,
+// in one launch.
+__global__ void clear_scratch_kernel(uint64_t *words, uint64_t n, int32_t *status, int32_t value) {
+  const uint64_t i0 = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (uint64_t i = i0; i < n; i += (uint64_t)gridDim.x * blockDim.x) words[i] = 0;
+  if (i0 == 0) *status = value;
 }
 
 hipError_t launch_decompress(int w, const uint8_t *src, uint64_t comp_bytes, uint8_t *dst,
@@ -784,11 +773,15 @@ hipError_t launch_decompress(int w, const uint8_t *src, uint64_t comp_bytes, uin
   int32_t *own_status = reinterpret_cast<int32_t *>(lb_status + w_lb + 1);
   int32_t *st = status ? status : own_status;
 
-  e = fill_u64(lb_status, w_lb + 1, 0, stream);
-  if (e == hipSuccess) e = fill_u32(reinterpret_cast<uint32_t *>(st), 1, 0u, stream);
-  if (e == hipSuccess && nchunks == 0) {
-    if (comp_bytes != 0) e = fill_u32(reinterpret_cast<uint32_t *>(st), 1, (uint32_t)kStatusCorrupt, stream);
-  } else if (e == hipSuccess) {
+  {
+    const int32_t first_status = (nchunks == 0 && comp_bytes != 0) ? kStatusCorrupt : 0;
+    const uint64_t n = w_lb + 1;
+    const uint64_t groups = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
+    hipLaunchKernelGGL(clear_scratch_kernel, dim3((unsigned)groups), dim3(256), 0, stream, lb_status, n,
+                       st, first_status);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess && nchunks != 0) {
     const uint64_t groups_a = ntiles_a;
     if (w == 16)
       hipLaunchKernelGGL(locate_kernel<16>, dim3((unsigned)groups_a), dim3(kLocateThreads), 0, stream,

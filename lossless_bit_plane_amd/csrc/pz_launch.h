@@ -7,7 +7,6 @@
 namespace pz {
 
 hipError_t fill_u64(uint64_t *p, uint64_t n, uint64_t value, hipStream_t stream);
-hipError_t fill_u32(uint32_t *p, uint64_t n, uint32_t value, hipStream_t stream);
 
 hipError_t launch_size(int w, const uint8_t *src, uint64_t raw_bytes, uint64_t *out_bytes,
                        uint16_t *chunk_lens, uint16_t *block_sizes, uint8_t *block_tags,
