@@ -52,28 +52,39 @@ struct GlobalBits {
   }
 };
 
+// The code of an all-zero block (the tag of BX, then one run of all W
+// planes), as it appears in the stream's low bits at the block start.
+template <int W>
+struct ZeroCode {
+  static constexpr uint32_t R = W == 16 ? 4 : 5;
+  static constexpr uint32_t code = (uint32_t)kBX | ((2u | ((uint32_t)(W - 2) << 2)) << 3);
+  static constexpr uint32_t bits = 3 + 2 + R;
+  static constexpr uint32_t mask = (1u << bits) - 1u;
+};
+
 // ---------------------------------------------------------------------------
 // Locate. A workgroup takes a tile of 64 chunks; each chunk is walked by a
-// quad of 4 lanes. Walking is sequential by nature (a block starts where the
-// previous one ends), and a lone wave's time is its instruction count, so the
-// quad shortens the walk by speculation: lane q of the quad reads the windows
-// at pos + (4q + s)(1+L), s = 0..3, i.e. where codes 4q+s would start if all
-// codes before them were verbatim (their length 1+L is fixed within a block).
-// One step thus settles a run of up to 16 verbatim planes, then decodes up to
-// two short codes from the window at the first non-verbatim code.
+// group of G = 4 lanes. Walking is sequential by nature (a block starts where
+// the previous one ends), and a wave's time is mostly the length of its
+// dependent instruction chain, so each step speculates: lane q of the group
+// reads the windows at pos + (4q + s)(1+L), s = 0..3, i.e. where codes 4q+s
+// would start if all codes before them were verbatim (their length 1+L is
+// fixed within a block). One step thus settles a run of up to 16 verbatim
+// planes, then decodes up to two short codes from the window at the first
+// non-verbatim code. (One lane per chunk does a quarter of the instructions
+// but walks four times as many steps per wave; it measured slower on every
+// tensor of the bench workload.)
 // ---------------------------------------------------------------------------
-constexpr int kQuad = 4;                                    // lanes per chunk
-constexpr int kLocateThreads = kGroupThreads;               // four waves
-constexpr int kLocateChunks = kLocateThreads / kQuad;       // 64 chunks per tile
-constexpr int kLocateWaveChunks = kWave / kQuad;            // 16 chunks per wave
-constexpr int kSpec = kQuad * 4;                            // codes tried per step
+constexpr int kLocateChunks = 64;  // chunks per tile (per workgroup)
+constexpr int kLocateLanes = 4;    // lanes per chunk
+constexpr int kLocateThreads = kLocateChunks * kLocateLanes;
 // Per-chunk LDS region: a 128-dword ring of the chunk's stream, one mirror
 // dword (slot 128 = slot 0, so a peek at slot 127 reads two dwords), then the
 // chunk's 32 block offsets (16-bit). 145 dwords: odd, spreads chunks over banks.
 constexpr int kRingDwords = 128;
 constexpr int kRingRegion = kRingDwords + 1 + 16;
-constexpr uint32_t kBlockAhead = 38;  // dwords one block (and its look-ahead) can touch
-constexpr uint32_t kGroupDwords = 32;  // refill unit: 8 dwords per quad lane
+constexpr uint32_t kBlockAhead = 38;   // dwords one block (and its look-ahead) can touch
+constexpr uint32_t kGroupDwords = 32;  // refill unit, split over the G lanes
 
 // One of four values by the two low bits of k, as bit-tested selects (an
 // equality chain would be turned into branches).
@@ -83,8 +94,11 @@ PZ_DEV uint32_t select4(uint32_t k, uint32_t a0, uint32_t a1, uint32_t a2, uint3
   return (k & 2u) ? hi : lo;
 }
 
-// Value of `v` in lane k (0..3) of this lane's quad (DPP quad broadcast).
-PZ_DEV uint32_t quad_lane(uint32_t v, uint32_t k) {
+// Value of `v` in lane k (0..3) of this lane's group of four (DPP quad
+// broadcast).
+template <int G>
+PZ_DEV uint32_t group_lane(uint32_t v, uint32_t k) {
+  static_assert(G == 4, "groups are quads");
   const uint32_t b0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x00, 0xF, 0xF, true);
   const uint32_t b1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x55, 0xF, 0xF, true);
   const uint32_t b2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xAA, 0xF, 0xF, true);
@@ -92,29 +106,33 @@ PZ_DEV uint32_t quad_lane(uint32_t v, uint32_t k) {
   return select4(k, b0, b1, b2, b3);
 }
 
-// OR of `v` over this lane's quad.
-PZ_DEV uint32_t quad_or(uint32_t v) {
+// OR of `v` over this lane's group of four.
+template <int G>
+PZ_DEV uint32_t group_or(uint32_t v) {
+  static_assert(G == 4, "groups are quads");
   v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);  // lanes 1,0,3,2
   v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);  // lanes 2,3,0,1
   return v;
 }
 
-// A chunk's stream, read by the chunk's quad through the LDS ring. The ring
+// A chunk's stream, read by the chunk's group through the LDS ring. The ring
 // is topped up only at block starts: the 32 dwords requested at the previous
 // block start are stored, and the next 32 are requested if the ring will have
 // room for them; only if fewer than one block's worth of dwords is then
-// buffered does the quad wait for a load on the spot. Every quad lane holds
-// and stores its own 8 of the 32 dwords.
-struct QuadRing {
+// buffered does the group wait for a load on the spot. Each of the G lanes
+// holds and stores 32/G of the 32 dwords.
+template <int G>
+struct ChunkRing {
+  static constexpr int kPart = kGroupDwords / G;  // dwords per lane per refill
   uint32_t *ring;
   const uint8_t *src;
   uint64_t limit;   // comp_bytes: nothing at or past it is read
   uint64_t q0;      // absolute dword index of relative dword 0 (16-byte aligned)
   uint32_t lead;    // bit offset of the chunk payload within relative dword 0
-  uint32_t ql;      // lane within the quad
+  uint32_t ql;      // lane within the group
   uint32_t fill;    // relative dwords below fill have been stored (the last 128 are kept)
-  bool pending;     // g holds relative dwords [fill + 8 ql, +8)
-  uint4 g[2];
+  bool pending;     // g holds relative dwords [fill + kPart ql, +kPart)
+  uint4 g[kPart / 4];
 
   PZ_DEV uint4 load4(uint32_t r) const {
     const uint64_t b = (q0 + r) * 4;
@@ -133,48 +151,50 @@ struct QuadRing {
     return make_uint4(v[0], v[1], v[2], v[3]);
   }
   PZ_DEV void issue() {
-    g[0] = load4(fill + 8 * ql);
-    g[1] = load4(fill + 8 * ql + 4);
+#pragma unroll
+    for (int k = 0; k < kPart / 4; ++k) g[k] = load4(fill + kPart * ql + 4 * k);
     pending = true;
   }
   // Stores the in-flight group at fill (slots fill % 128 .. +31: never wraps).
   PZ_DEV void commit() {
-    uint32_t *r = ring + (fill & (kRingDwords - 1)) + 8 * ql;
-    r[0] = g[0].x;
-    r[1] = g[0].y;
-    r[2] = g[0].z;
-    r[3] = g[0].w;
-    r[4] = g[1].x;
-    r[5] = g[1].y;
-    r[6] = g[1].z;
-    r[7] = g[1].w;
+    uint32_t *r = ring + (fill & (kRingDwords - 1)) + kPart * ql;
+#pragma unroll
+    for (int k = 0; k < kPart / 4; ++k) {
+      r[4 * k + 0] = g[k].x;
+      r[4 * k + 1] = g[k].y;
+      r[4 * k + 2] = g[k].z;
+      r[4 * k + 3] = g[k].w;
+    }
     if ((fill & (kRingDwords - 1)) == 0 && ql == 0) ring[kRingDwords] = g[0].x;  // mirror
     fill += kGroupDwords;
     pending = false;
   }
-  PZ_DEV void start(uint32_t *r, const uint8_t *s, uint64_t lim, uint64_t payload_off, uint32_t lane_in_quad) {
+  PZ_DEV void start(uint32_t *r, const uint8_t *s, uint64_t lim, uint64_t payload_off, uint32_t lane_in_group) {
     ring = r;
     src = s;
     limit = lim;
-    ql = lane_in_quad;
+    ql = lane_in_group;
     q0 = (payload_off >> 2) & ~3ull;
     lead = (uint32_t)(8 * (payload_off - 4 * q0));
-    // The first 64 dwords in one round trip (16 per lane), then one group in flight.
-    uint4 a[4];
+    // The first two groups in one round trip, then the third requested.
+    uint4 first[kPart / 4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) a[k] = load4(16 * ql + 4 * k);
+    for (int k = 0; k < kPart / 4; ++k) first[k] = load4(kPart * ql + 4 * k);
+    fill = kGroupDwords;
+    issue();
+    uint32_t *w = ring + kPart * ql;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      ring[16 * ql + 4 * k + 0] = a[k].x;
-      ring[16 * ql + 4 * k + 1] = a[k].y;
-      ring[16 * ql + 4 * k + 2] = a[k].z;
-      ring[16 * ql + 4 * k + 3] = a[k].w;
+    for (int k = 0; k < kPart / 4; ++k) {
+      w[4 * k + 0] = first[k].x;
+      w[4 * k + 1] = first[k].y;
+      w[4 * k + 2] = first[k].z;
+      w[4 * k + 3] = first[k].w;
     }
-    if (ql == 0) ring[kRingDwords] = a[0].x;
-    fill = 64;
+    if (ql == 0) ring[kRingDwords] = first[0].x;  // mirror of slot 0
+    commit();
     issue();
   }
-  // At a block start whose first bit is pos (quad-uniform): makes relative
+  // At a block start whose first bit is pos (group-uniform): makes relative
   // dwords [dword of pos, +kBlockAhead) available and requests the next group.
   PZ_DEV void step(uint32_t pos) {
     const uint32_t cur = (lead + pos) >> 5;
@@ -183,9 +203,9 @@ struct QuadRing {
       issue();
       commit();
     }
-    // Stored dwords at or above cur stay in the ring until the quad passes them.
+    // Stored dwords at or above cur stay in the ring until the group passes them.
     if (fill + kGroupDwords <= cur + kRingDwords) issue();
-    wave_lds_fence();  // the quad's stores before its reads
+    wave_lds_fence();  // the group's stores before its reads
   }
   PZ_DEV uint32_t peek(uint32_t pos) const {
     const uint32_t a = lead + pos;
@@ -194,17 +214,18 @@ struct QuadRing {
   }
 };
 
-// Walks the codes of a coded chunk (quad-uniform: all four lanes compute the
+// Walks the codes of a coded chunk (group-uniform: the G lanes compute the
 // same positions), recording each block's bit offset in boff (LDS, written by
-// quad lane 0). Returns false for a chunk that fails a decoder check
-// (FORMAT.md §6). Blocks are taken in wave-uniform steps: all quads read a
+// group lane 0). Returns false for a chunk that fails a decoder check
+// (FORMAT.md §6). Blocks are taken in wave-uniform steps: all groups read a
 // block header together (tag, then the base or the zero mask), then the
 // block's plane codes, whose class is the trailing-zero count of the next
 // bits and whose length comes from a per-block table.
-template <int W>
-PZ_DEV bool parse_chunk(QuadRing &in, bool coded, uint32_t H, uint32_t raw_len, uint16_t *boff) {
+template <int W, int G>
+PZ_DEV bool parse_chunk(ChunkRing<G> &in, bool coded, uint32_t H, uint32_t raw_len, uint16_t *boff) {
   constexpr uint32_t N = 1024 / W;
   constexpr uint32_t R = W == 16 ? 4 : 5;
+  constexpr uint32_t kSpec = 4 * G;  // codes tried per step
   const uint32_t end = H * 8;
   const uint32_t nb = (raw_len + kBlockBytes - 1) / kBlockBytes;
   const uint32_t ql = in.ql;
@@ -219,21 +240,26 @@ PZ_DEV bool parse_chunk(QuadRing &in, bool coded, uint32_t H, uint32_t raw_len, 
     if (live) {
       in.step(pos);
       if (ql == 0) boff[b] = (uint16_t)pos;
-      const uint32_t tag = in.peek(pos) & 7u;
-      uint32_t n = (uint32_t)popc32(in.peek(pos + 3));
-      if (W == 16) n += (uint32_t)popc32(in.peek(pos + 35));
-      const bool masked = tag == kZVC || tag == kZBX;
-      pos += 3 + (tag == kDBX ? W : 0u) + (masked ? N : 0u) + (tag == kZVC ? W * n : 0u) +
-             (tag == kRAW ? 1024u : 0u);
-      bad |= tag > 4;
-      L = tag == kDBX ? N - 1 : (tag == kZBX ? n : N);
-      left = (tag == kBX || tag == kZBX) ? (int)W : (tag == kDBX ? (int)W + 1 : 0);
-      // Code length by class (trailing zeros of the next bits, capped at 4):
-      // verbatim 1+L, run 2+R, lone zero 3, pair/single 5+PW, other 5.
-      const uint32_t pw = (uint32_t)position_bits((int)L);
-      pmask = (1u << pw) - 1u;
-      lut = (uint64_t)(1 + L) | ((uint64_t)(2 + R) << 8) | (3ull << 16) |
-            ((uint64_t)(5 + pw) << 24) | (5ull << 32);
+      const uint32_t head = in.peek(pos);
+      const uint32_t tag = head & 7u;
+      if ((head & ZeroCode<W>::mask) == ZeroCode<W>::code) {
+        pos += ZeroCode<W>::bits;  // an all-zero block: one run over all planes
+      } else {
+        uint32_t n = (uint32_t)popc32(in.peek(pos + 3));
+        if (W == 16) n += (uint32_t)popc32(in.peek(pos + 35));
+        const bool masked = tag == kZVC || tag == kZBX;
+        pos += 3 + (tag == kDBX ? W : 0u) + (masked ? N : 0u) + (tag == kZVC ? W * n : 0u) +
+               (tag == kRAW ? 1024u : 0u);
+        bad |= tag > 4;
+        L = tag == kDBX ? N - 1 : (tag == kZBX ? n : N);
+        left = (tag == kBX || tag == kZBX) ? (int)W : (tag == kDBX ? (int)W + 1 : 0);
+        // Code length by class (trailing zeros of the next bits, capped at 4):
+        // verbatim 1+L, run 2+R, lone zero 3, pair/single 5+PW, other 5.
+        const uint32_t pw = (uint32_t)position_bits((int)L);
+        pmask = (1u << pw) - 1u;
+        lut = (uint64_t)(1 + L) | ((uint64_t)(2 + R) << 8) | (3ull << 16) |
+              ((uint64_t)(5 + pw) << 24) | (5ull << 32);
+      }
     }
     const uint32_t V = (uint32_t)(lut & 0xFFu);
     const uint32_t spec = 4 * ql * V;  // this lane tries codes 4 ql .. 4 ql + 3
@@ -245,14 +271,14 @@ PZ_DEV bool parse_chunk(QuadRing &in, bool coded, uint32_t H, uint32_t raw_len, 
       const uint32_t w0 = in.peek(a), w1 = in.peek(a + V), w2 = in.peek(a + 2 * V),
                      w3 = in.peek(a + 3 * V);
       const uint32_t mine = (w0 & 1u) | ((w1 & 1u) << 1) | ((w2 & 1u) << 2) | ((w3 & 1u) << 3);
-      const uint32_t vmask = quad_or(mine << (4 * ql));  // bit k: code k would be verbatim
-      // Leading verbatim codes (~vmask has bit 16 set, so the count is <= 16).
+      const uint32_t vmask = group_or<G>(mine << (4 * ql));  // bit k: code k would be verbatim
+      // Leading verbatim codes (~vmask has bit 4G set, so the count is <= 4G).
       const uint32_t j = min((uint32_t)__builtin_ctz(~vmask), (uint32_t)left);
       pos += j * V;
       left -= (int)j;
-      // The window of code j: lane j/4 of the quad read it as its w[j%4].
-      uint32_t win = quad_lane(select4(j, w0, w1, w2, w3), j >> 2);
-      bool take = j < (uint32_t)kSpec;
+      // The window of code j: lane j/4 of the group read it as its w[j%4].
+      uint32_t win = group_lane<G>(select4(j, w0, w1, w2, w3), j >> 2);
+      bool take = j < kSpec;
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         take = take && left > 0 && (win & 1u) == 0u;  // a short code (at most 11 bits)
@@ -278,16 +304,17 @@ PZ_DEV bool parse_chunk(QuadRing &in, bool coded, uint32_t H, uint32_t raw_len, 
   return !bad;
 }
 
-template <int W>
-__global__ __launch_bounds__(kLocateThreads) void locate_kernel(
+template <int W, int G>
+__global__ __launch_bounds__(kLocateChunks * G) void locate_kernel(
     const uint8_t *__restrict__ src, uint64_t comp_bytes, uint64_t raw_bytes, uint64_t nchunks,
     uint64_t ntiles, uint64_t *__restrict__ chunk_off, uint16_t *__restrict__ block_off,
     int32_t *status_out, uint64_t *lb_status, uint32_t *tile_counter) {
+  constexpr int kWaves = G;  // 64 chunks x G lanes
   __shared__ uint32_t lds[kLocateChunks * kRingRegion];
-  __shared__ uint64_t wave_sum[kWavesPerGroup];
+  __shared__ uint64_t wave_sum[kWaves];
   __shared__ uint64_t tile_before;
   __shared__ uint32_t group_tile;
-  const uint32_t t = threadIdx.x, lane = lane_id(), ql = t & (kQuad - 1);
+  const uint32_t t = threadIdx.x, lane = lane_id(), ql = t & (G - 1);
   const uint32_t wave = __builtin_amdgcn_readfirstlane(t >> 6);
   if (t == 0) group_tile = atomicAdd(tile_counter, 1u);
   __syncthreads();
@@ -296,16 +323,16 @@ __global__ __launch_bounds__(kLocateThreads) void locate_kernel(
 
   // Chunk offsets: a scan of the 16-bit headers over the tile, and one
   // look-back per tile for the headers before it.
-  const uint32_t ci = t / kQuad;  // chunk within the tile
+  const uint32_t ci = t / G;  // chunk within the tile
   const uint64_t c = (uint64_t)tile * kLocateChunks + ci;
   const uint32_t H = c < nchunks ? reinterpret_cast<const uint16_t *>(src)[c] : 0u;
-  const uint64_t incl = wave_inclusive_scan_u64(ql == 0 ? H : 0u);  // equal over the quad
+  const uint64_t incl = wave_inclusive_scan_u64(ql == 0 ? H : 0u);  // equal over the group
   if (lane == kWave - 1) wave_sum[wave] = incl;
   __syncthreads();
   if (wave == 0) {
     uint64_t agg = 0;
 #pragma unroll
-    for (int k = 0; k < kWavesPerGroup; ++k) agg += wave_sum[k];
+    for (int k = 0; k < kWaves; ++k) agg += wave_sum[k];
     const uint64_t before = lookback(lb_status, tile, agg);
     if (lane == 0) {
       tile_before = before;
@@ -323,15 +350,17 @@ __global__ __launch_bounds__(kLocateThreads) void locate_kernel(
   const bool coded = c < nchunks && !header_bad && H < raw_len;
   uint32_t *region = lds + ci * kRingRegion;
   uint16_t *boff = reinterpret_cast<uint16_t *>(region + kRingDwords + 1);
-  QuadRing in;
+  ChunkRing<G> in;
   in.start(region, src, comp_bytes, coded ? off : 0, ql);
-  const bool parsed = parse_chunk<W>(in, coded, H, raw_len, boff);  // whole wave
+  const bool parsed = parse_chunk<W, G>(in, coded, H, raw_len, boff);  // whole wave
   wave_lds_fence();
   if (coded) {
-    // The chunk's block offsets: 64 bytes, 16 per quad lane.
-    const uint32_t *b32 = region + kRingDwords + 1 + 4 * ql;
-    *reinterpret_cast<uint4 *>(block_off + c * kBlocksPerChunk + 8 * ql) =
-        make_uint4(b32[0], b32[1], b32[2], b32[3]);
+    // The chunk's block offsets: 64 bytes, 64/G per group lane.
+    const uint32_t *b32 = region + kRingDwords + 1 + (16 / G) * ql;
+    uint4 *outp = reinterpret_cast<uint4 *>(block_off + c * kBlocksPerChunk) + (4 / G) * ql;
+#pragma unroll
+    for (int k = 0; k < 4 / G; ++k)
+      outp[k] = make_uint4(b32[4 * k], b32[4 * k + 1], b32[4 * k + 2], b32[4 * k + 3]);
   }
   if (c < nchunks && ql == 0) {
     const bool chunk_bad = header_bad || (coded && !parsed);
@@ -460,15 +489,6 @@ constexpr int kDecodeBufDwords = kDecodeChunks * kChunkBufDwords;
 constexpr int kDecodeRowDwords = kGroupThreads * kLaneStride;
 constexpr int kDecodeLdsDwords =
     kDecodeBufDwords > kDecodeRowDwords ? kDecodeBufDwords : kDecodeRowDwords;
-
-// The code of an all-zero block (the tag of BX, then one run of all W
-// planes), as it appears in the stream's low bits at the block start.
-template <int W>
-struct ZeroCode {
-  static constexpr uint32_t R = W == 16 ? 4 : 5;
-  static constexpr uint32_t code = (uint32_t)kBX | ((2u | ((uint32_t)(W - 2) << 2)) << 3);
-  static constexpr uint32_t mask = (1u << (3 + 2 + R)) - 1u;
-};
 
 template <int W>
 __global__ __launch_bounds__(kGroupThreads) void decode_kernel(
@@ -782,15 +802,13 @@ hipError_t launch_decompress(int w, const uint8_t *src, uint64_t comp_bytes, uin
     e = hipGetLastError();
   }
   if (e == hipSuccess && nchunks != 0) {
-    const uint64_t groups_a = ntiles_a;
+    const dim3 grid_a((unsigned)ntiles_a);
     if (w == 16)
-      hipLaunchKernelGGL(locate_kernel<16>, dim3((unsigned)groups_a), dim3(kLocateThreads), 0, stream,
-                         src, comp_bytes, raw_bytes, nchunks, ntiles_a, chunk_off, block_off, st,
-                         lb_status, counter);
+      hipLaunchKernelGGL((locate_kernel<16, kLocateLanes>), grid_a, dim3(kLocateThreads), 0, stream, src,
+                         comp_bytes, raw_bytes, nchunks, ntiles_a, chunk_off, block_off, st, lb_status, counter);
     else
-      hipLaunchKernelGGL(locate_kernel<32>, dim3((unsigned)groups_a), dim3(kLocateThreads), 0, stream,
-                         src, comp_bytes, raw_bytes, nchunks, ntiles_a, chunk_off, block_off, st,
-                         lb_status, counter);
+      hipLaunchKernelGGL((locate_kernel<32, kLocateLanes>), grid_a, dim3(kLocateThreads), 0, stream, src,
+                         comp_bytes, raw_bytes, nchunks, ntiles_a, chunk_off, block_off, st, lb_status, counter);
     e = hipGetLastError();
     if (e == hipSuccess) {
       const uint64_t groups_b = (nchunks + kDecodeChunks - 1) / kDecodeChunks;
