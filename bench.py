@@ -3,14 +3,18 @@
 One step = compress and then decompress every tensor of the workload (the
 GPT-2-XL activations at batch 8, sequence 1024: MLP GELU output 8x1024x6400,
 causal softmax 8x25x1024x1024, residual 8x1024x1600, all BF16, ~0.55 GB),
-with inputs already resident in HBM. Prints one JSON line.
+back to back on one stream, with inputs already resident in HBM. Before every
+step (warm-up and timed) a 1 GiB buffer is written, outside the timed region,
+so that no step finds its inputs in the 256 MB last-level cache (MALL); each
+timed step is bracketed by device synchronizations and timed with HIP events.
+Prints one JSON line.
 
-value = raw bytes of the workload / time of one step (each raw byte is both
-compressed and decompressed in a step). The roofline object reports the
-dominant kernel call's algorithmic HBM traffic (read raw + write compressed
-for compression, the reverse for decompression) against MI355X's 8 TB/s.
-The CPU baseline is the oracle (oracle/pzref.c) on a bounded sample of the
-same tensors, on this host's cores.
+value = raw bytes of the workload / mean time of one step (each raw byte is
+both compressed and decompressed in a step). The roofline object reports the
+dominant kernel's algorithmic HBM traffic (read raw + write compressed) per
+unit of its measured time against MI355X's 8 TB/s. The CPU baseline is the
+oracle (oracle/pzref.c) on the same tensors on this host's cores: chunk-
+parallel on the whole workload, and single-threaded on a bounded sample.
 """
 from __future__ import annotations
 
@@ -38,7 +42,9 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--config", type=int, default=5)
-    p.add_argument("--cpu-sample-mb", type=float, default=24.0)
+    p.add_argument("--cpu-sample-mb", type=float, default=24.0,
+                   help="sample of the workload for the single-threaded oracle timing")
+    p.add_argument("--no-flush", action="store_true", help="skip the cache flush before each step")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-verify", action="store_true")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -49,8 +55,9 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}): the codec has no "
-              "cross-GPU path in this build; see DESIGN.md for how it would shard.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}). The codec would shard a "
+              "tensor into contiguous chunk ranges, one per GPU, with one exclusive scan of the "
+              "per-shard stream sizes; only the single-GPU path is built.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -95,6 +102,11 @@ def main():
         it["comp"] = int(it["nbytes"].item())
 
     cur = torch.cuda.current_stream()
+    flush_buf = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def flush():
+        if flush_buf is not None:
+            flush_buf.fill_(0x5A)
 
     def step(events=None):
         for i, it in enumerate(items):
@@ -114,6 +126,7 @@ def main():
                 events[i][3].record(cur)
 
     for _ in range(args.warmup):
+        flush()
         step()
     torch.cuda.synchronize()
 
@@ -125,12 +138,19 @@ def main():
 
     ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in items]
           for _ in range(args.steps)]
+    step_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    start = time.perf_counter()
+    wall = 0.0
     for k in range(args.steps):
+        flush()
+        torch.cuda.synchronize()
+        start = time.perf_counter()
+        step_ev[k][0].record(cur)
         step(ev[k])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - start
+        step_ev[k][1].record(cur)
+        torch.cuda.synchronize()
+        wall += time.perf_counter() - start
+    step_ms = np.array([a.elapsed_time(b) for a, b in step_ev])
 
     raw_total = sum(it["t"].nbytes for it in items)
     comp_total = sum(it["comp"] for it in items)
@@ -142,8 +162,8 @@ def main():
             t_dec[i] += ev[k][i][2].elapsed_time(ev[k][i][3]) / 1e3
     t_comp /= args.steps
     t_dec /= args.steps
-    ms_per_step = wall / args.steps * 1e3
-    value = raw_total / (wall / args.steps) / 1e9
+    ms_per_step = float(step_ms.mean())
+    value = raw_total / (ms_per_step / 1e3) / 1e9
 
     comp_s, dec_s = t_comp.sum(), t_dec.sum()
     algo = raw_total + comp_total  # algorithmic HBM bytes per direction
@@ -167,6 +187,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(tensors, args.cpu_sample_mb)
+    p10, p50, p90 = (float(x) for x in np.percentile(step_ms, [10, 50, 90]))
 
     per_tensor = {it["t"].name: {
         "raw_bytes": it["t"].nbytes, "compressed_bytes": it["comp"],
@@ -196,6 +217,9 @@ def main():
             "ratio": round(raw_total / comp_total, 4),
             "parallelism": "single GPU",
         },
+        "step_ms": {"median": round(p50, 4), "p10": round(p10, 4), "p90": round(p90, 4),
+                    "host_wall_mean": round(wall / args.steps * 1e3, 4),
+                    "cache_flush_before_each_step": flush_buf is not None},
         "compress_raw_gbps": round(raw_total / comp_s / 1e9, 1),
         "decompress_raw_gbps": round(raw_total / dec_s / 1e9, 1),
         "compress_hbm_frac": round(comp_gbps / HBM_PEAK_GBPS, 4),
@@ -207,11 +231,20 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def kernel_source_hash():
+# The sources each kernel is built from: counters taken for a kernel stay
+# valid while these files are unchanged.
+KERNEL_SOURCES = {
+    "compress_kernel": ["pz_device.h", "pz_compress.hip"],
+    "locate_kernel": ["pz_device.h", "pz_decompress.hip"],
+    "decode_kernel": ["pz_device.h", "pz_decompress.hip"],
+}
+
+
+def kernel_source_hash(kernel):
     import hashlib
 
     h = hashlib.sha256()
-    for f in ["pz_device.h", "pz_compress.hip", "pz_decompress.hip"]:
+    for f in KERNEL_SOURCES[kernel.split("<")[0]]:
         with open(os.path.join(ROOT, "lossless_bit_plane_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -227,8 +260,8 @@ def measured_traffic(kernel, tensor_names):
         return None, "no counter summary"
     with open(path) as f:
         prof = json.load(f)
-    if prof.get("source_hash") != kernel_source_hash():
-        return None, "kernels changed since the counters in profiles/ were taken"
+    if prof.get("source_hash", {}).get(kernel.split("<")[0]) != kernel_source_hash(kernel):
+        return None, f"{kernel} changed since the counters in profiles/ were taken"
     total = 0.0
     for name in tensor_names:
         t = prof["traffic"].get(f"{kernel}:{name}")
@@ -239,35 +272,50 @@ def measured_traffic(kernel, tensor_names):
 
 
 def cpu_baseline(tensors, sample_mb):
-    """The oracle, as it stands, on a bounded sample: the same fraction of
-    whole chunks from the start of every tensor, compress then decompress."""
+    """The oracle, as it stands: chunk-parallel over the host cores on the
+    whole workload (the reported value), and single-threaded on the same
+    fraction of whole chunks from the start of every tensor (a bounded
+    sample); compress then decompress, round trip checked."""
     import oracle
 
-    total = sum(t.nbytes for t in tensors)
-    frac = min(1.0, sample_mb * 1e6 / total)
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
-    raw = 0
-    t_c = t_d = 0.0
-    for t in tensors:
-        n = max(4096, int(t.nbytes * frac) // 4096 * 4096)
-        part = t.data[:n]
-        a = time.perf_counter()
-        s = oracle.compress(part, t.elem_bits, threads=threads)
-        b = time.perf_counter()
-        back = oracle.decompress(s, n, t.elem_bits, threads=threads)
-        c = time.perf_counter()
-        assert np.array_equal(back, part)
-        raw += n
-        t_c += b - a
-        t_d += c - b
-    log(f"cpu baseline: {raw / 1e6:.1f} MB sample, {threads} threads, compress {t_c:.2f}s decompress {t_d:.2f}s")
+
+    def run(frac, nthreads):
+        raw = 0
+        t_c = t_d = 0.0
+        for t in tensors:
+            n = max(4096, int(t.nbytes * frac) // 4096 * 4096) if frac < 1.0 else t.nbytes
+            part = t.data[:n]
+            a = time.perf_counter()
+            s = oracle.compress(part, t.elem_bits, threads=nthreads)
+            b = time.perf_counter()
+            back = oracle.decompress(s, n, t.elem_bits, threads=nthreads)
+            c = time.perf_counter()
+            assert np.array_equal(back, part)
+            raw += n
+            t_c += b - a
+            t_d += c - b
+        return raw, t_c, t_d
+
+    total = sum(t.nbytes for t in tensors)
+    raw, t_c, t_d = run(1.0, threads)
+    log(f"cpu baseline: whole workload {raw / 1e6:.1f} MB, {threads} threads, "
+        f"compress {t_c:.2f}s decompress {t_d:.2f}s")
+    frac1 = min(1.0, sample_mb * 1e6 / total)
+    raw1, c1, d1 = run(frac1, 1)
+    log(f"cpu baseline: {raw1 / 1e6:.1f} MB sample, 1 thread, compress {c1:.2f}s decompress {d1:.2f}s")
     return {
         "value": round(raw / (t_c + t_d) / 1e9, 4),
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"first {frac * 100:.1f}% (whole chunks) of each tensor, {raw / 1e6:.1f} MB; "
+        "sample": f"the whole workload ({raw / 1e6:.1f} MB), chunk-parallel on {threads} threads; "
                   f"compress {raw / t_c / 1e6:.1f} MB/s, decompress {raw / t_d / 1e6:.1f} MB/s",
+        "single_thread": {
+            "value": round(raw1 / (c1 + d1) / 1e9, 5), "unit": "GB/s", "cores": 1,
+            "sample": f"first {frac1 * 100:.1f}% (whole chunks) of each tensor, {raw1 / 1e6:.1f} MB; "
+                      f"compress {raw1 / c1 / 1e6:.2f} MB/s, decompress {raw1 / d1 / 1e6:.2f} MB/s",
+        },
     }
 
 
