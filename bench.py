@@ -260,7 +260,8 @@ def measured_traffic(kernel, tensor_names):
         return None, "no counter summary"
     with open(path) as f:
         prof = json.load(f)
-    if prof.get("source_hash", {}).get(kernel.split("<")[0]) != kernel_source_hash(kernel):
+    hashes = prof.get("source_hash")
+    if not isinstance(hashes, dict) or hashes.get(kernel.split("<")[0]) != kernel_source_hash(kernel):
         return None, f"{kernel} changed since the counters in profiles/ were taken"
     total = 0.0
     for name in tensor_names:
