@@ -1,0 +1,44 @@
+"""Host-side logic of bench.py (no GPU): the multi-GPU refusal, the per-kernel
+source hashes and the lookup of committed counter summaries."""
+import json
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_exits_with_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+
+
+def test_kernel_source_hashes_are_per_kernel():
+    hc = bench.kernel_source_hash("compress_kernel<16>")
+    hl = bench.kernel_source_hash("locate_kernel<16, 4>")
+    hd = bench.kernel_source_hash("decode_kernel<16>")
+    assert len(hc) == 16 and hl == hd and hc != hd
+
+
+def test_measured_traffic_never_raises(tmp_path, monkeypatch):
+    names = ["gpt2xl_mlp_gelu", "gpt2xl_attn_probs", "gpt2xl_residual"]
+    total, note = bench.measured_traffic("compress_kernel<16>", names)
+    assert (total is None) == (not isinstance(total, int)) and isinstance(note, str)
+    # A summary in another format, or for other sources, reads as stale.
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    for content in [{"source_hash": "0123456789abcdef", "traffic": {}},
+                    {"source_hash": {"compress_kernel": "x"}, "traffic": {}}]:
+        (prof / "hbm_traffic_gpt2xl_config5.json").write_text(json.dumps(content))
+        monkeypatch.setattr(bench, "kernel_source_hash", lambda k: "y")
+        assert bench.measured_traffic("compress_kernel<16>", names)[0] is None
+    good = {"source_hash": {"compress_kernel": "y"},
+            "traffic": {f"compress_kernel<16>:{n}": {"fetch_bytes": 10.0, "write_bytes": 5.0} for n in names}}
+    (prof / "hbm_traffic_gpt2xl_config5.json").write_text(json.dumps(good))
+    assert bench.measured_traffic("compress_kernel<16>", names)[0] == 45
