@@ -468,8 +468,9 @@ __global__ __launch_bounds__(kGroupThreads, 4) void compress_kernel(
   if (tile >= ntiles) return;
 
   // --- 1. Load block t; find the all-zero blocks. ---
+  // (Block and chunk indices are recomputed where needed rather than kept
+  // live through the statistics, which use every register.)
   const uint64_t block = (uint64_t)tile * kGroupThreads + t;
-  const uint64_t chunk = block >> 5;
   const bool valid = block * kBlockBytes < raw_bytes;
   uint32_t d[32];
   load_block(src, raw_bytes, block * kBlockBytes, d);
@@ -552,19 +553,26 @@ __global__ __launch_bounds__(kGroupThreads, 4) void compress_kernel(
       }
       wave_lds_fence();
       if (want_zbx) {
+        // Every symbol is written at the current rank, which advances only
+        // past non-zero ones: a zero symbol writes 0 where the next non-zero
+        // symbol (or nothing) goes, so there are no branches.
         uint32_t k = 0;
         if constexpr (W == 16) {
           uint16_t *r16 = reinterpret_cast<uint16_t *>(region);
 #pragma unroll
           for (int i = 0; i < 32; ++i) {
             const uint32_t a = d[i] & 0xFFFFu, b = d[i] >> 16;
-            if (a) r16[k++] = (uint16_t)a;
-            if (b) r16[k++] = (uint16_t)b;
+            r16[k] = (uint16_t)a;
+            k += a ? 1u : 0u;
+            r16[k] = (uint16_t)b;
+            k += b ? 1u : 0u;
           }
         } else {
 #pragma unroll
-          for (int i = 0; i < 32; ++i)
-            if (d[i]) region[k++] = d[i];
+          for (int i = 0; i < 32; ++i) {
+            region[k] = d[i];
+            k += d[i] ? 1u : 0u;
+          }
         }
       }
       wave_lds_fence();
@@ -597,6 +605,7 @@ __global__ __launch_bounds__(kGroupThreads, 4) void compress_kernel(
   const uint32_t excl = incl - cost;
   const uint32_t bits = __shfl(incl, (int)((lane & 32) | 31), 64);
   uint32_t raw_len = 0, len = 0;
+  const uint64_t chunk = (uint64_t)tile * kGroupChunks + (t >> 5);
   if (chunk < nchunks) {
     raw_len = (uint32_t)min<uint64_t>(kChunkBytes, raw_bytes - chunk * kChunkBytes);
     len = (bits + 7) / 8;
@@ -634,7 +643,7 @@ __global__ __launch_bounds__(kGroupThreads, 4) void compress_kernel(
   // --- 5. Emission into the chunk buffers (payload bit i at buffer bit i). ---
   // All-zero blocks of coded chunks: their one code. (In a raw chunk their
   // bytes are zeros, which the cleared buffer already holds.)
-  if (valid && !nonzero && !raw_chunk) {
+  if (((uint64_t)tile * kGroupThreads + t) * kBlockBytes < raw_bytes && !nonzero && !raw_chunk) {
     BitSink z;
     z.buf = lds + (t >> 5) * kChunkBufDwords;
     z.off = excl;
