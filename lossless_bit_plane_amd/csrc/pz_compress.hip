@@ -82,13 +82,32 @@ PZ_DEV void fold_counts16(uint32_t t1, uint32_t t2, uint32_t t3, uint32_t &c1, u
   c3 = lo16(t3) | hi16(t3) | (lo16(t2) & hi16(t1)) | (lo16(t1) & hi16(t2));
 }
 
+// Number of non-zero symbols of a block (w = 16: two per dword).
+template <int W>
+PZ_DEV uint32_t count_nonzero(const uint32_t (&d)[32]) {
+  if constexpr (W == 16) {
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) cnt = pk_add_u16(cnt, pk_min_u16(d[i], 0x00010001u));
+    return lo16(cnt) + hi16(cnt);
+  } else {
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) cnt += d[i] != 0 ? 1u : 0u;
+    return cnt;
+  }
+}
+
 // ---------------------------------------------------------------------------
-// Candidate sizes, w = 16. d[i] holds symbols 2i (low half) and 2i+1 (high).
+// Candidate sizes, w = 16. d[i] holds symbols 2i (low half) and 2i+1 (high);
+// n is the block's number of non-zero symbols. zbx (wave-uniform) is false
+// when no lane of the wave holds a block with 0 < n < 64: then ZBX compacts
+// nothing away and its size is the mask plus the BX size.
 // ---------------------------------------------------------------------------
-PZ_DEV void candidate_sizes16(uint32_t (&d)[32], Sizes &out) {
+PZ_DEV void candidate_sizes16(uint32_t (&d)[32], int n, bool zbx, Sizes &out) {
   uint32_t bx_or_s = 0, bx_or = 0, bx_and = ~0u, bx_t2 = 0, bx_t3 = 0, bx_adj = 0, gh_prev = 0;
   uint32_t db_or_s = 0, db_or = 0, db_and = ~0u, db_t2 = 0, db_t3 = 0, db_adj = 0, dgh_prev = 0;
-  uint32_t cnt = 0, b0 = 0, b1 = 0;
+  uint32_t b0 = 0, b1 = 0;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
     const uint32_t s = d[i];
@@ -102,7 +121,6 @@ PZ_DEV void candidate_sizes16(uint32_t (&d)[32], Sizes &out) {
     bx_and &= g;
     bx_adj |= g & (gh | gh_prev);  // pairs (2i, 2i+1) and (2i-1, 2i), low half
     gh_prev = gh;
-    cnt = pk_add_u16(cnt, pk_min_u16(s, 0x00010001u));
 
     // DBX: deltas s[k] - s[k-1] as 17-bit two's complement; the low 16 bits
     // come from a packed subtract, bit 16 is the borrow (bits 15 and 31 of
@@ -132,7 +150,6 @@ PZ_DEV void candidate_sizes16(uint32_t (&d)[32], Sizes &out) {
       b1 = (b1 >> 1) | (bo & 0x80008000u);
   }
 
-  const int n = (int)(lo16(cnt) + hi16(cnt));
   uint32_t c1, c2, c3;
 
   // BX: 16 planes of 64 bits.
@@ -164,23 +181,25 @@ PZ_DEV void candidate_sizes16(uint32_t (&d)[32], Sizes &out) {
 
   // ZBX: the zero, count and pre-XOR masks are those of BX (zero symbols add
   // nothing); "all ones" and adjacency run over the non-zero symbols only.
-  // (Computed for every wave: a wave-uniform skip of this loop costs more in
-  // register pressure than it saves in instructions.)
-  launder_regs(d);
-  uint32_t zb_and = ~0u, zb_adj = 0, zprev = 0;
+  if (zbx) {
+    launder_regs(d);
+    uint32_t zb_and = ~0u, zb_adj = 0, zprev = 0;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const uint32_t s = d[i];
-    const uint32_t g = s ^ ((s >> 1) & 0x7FFF7FFFu);
-    const uint32_t gh = g >> 16;
-    const uint32_t zfill = pk_sub_u16(pk_min_u16(s, 0x00010001u), 0x00010001u);  // 0xFFFF if zero
-    zb_and &= g | zfill;
-    const uint32_t q = g | (zprev & zfill);  // low half: last non-zero g up to symbol 2i
-    zb_adj |= (zprev & g) | (q & gh);
-    zprev = gh | (q & (zfill >> 16));
+    for (int i = 0; i < 32; ++i) {
+      const uint32_t s = d[i];
+      const uint32_t g = s ^ ((s >> 1) & 0x7FFF7FFFu);
+      const uint32_t gh = g >> 16;
+      const uint32_t zfill = pk_sub_u16(pk_min_u16(s, 0x00010001u), 0x00010001u);  // 0xFFFF if zero
+      zb_and &= g | zfill;
+      const uint32_t q = g | (zprev & zfill);  // low half: last non-zero g up to symbol 2i
+      zb_adj |= (zprev & g) | (q & gh);
+      zprev = gh | (q & (zfill >> 16));
+    }
+    out.sz[kZBX] = 64 + plane_code_bits(nz, lo16(zb_and) & hi16(zb_and), pz, exactly2 & lo16(zb_adj),
+                                        single, 16, n, 4);
+  } else {
+    out.sz[kZBX] = 64 + out.sz[kBX];
   }
-  out.sz[kZBX] = 64 + plane_code_bits(nz, lo16(zb_and) & hi16(zb_and), pz, exactly2 & lo16(zb_adj),
-                                      single, 16, n, 4);
 
   out.sz[kZVC] = 64 + 16 * n;
   out.sz[kRAW] = 1024;
@@ -192,11 +211,10 @@ PZ_DEV void candidate_sizes16(uint32_t (&d)[32], Sizes &out) {
 // ---------------------------------------------------------------------------
 // Candidate sizes, w = 32. d[i] is symbol i.
 // ---------------------------------------------------------------------------
-PZ_DEV void candidate_sizes32(uint32_t (&d)[32], Sizes &out) {
+PZ_DEV void candidate_sizes32(uint32_t (&d)[32], int n, bool zbx, Sizes &out) {
   uint32_t bx_or_s = 0, bx_or = 0, bx_and = ~0u, t2 = 0, t3 = 0, adj = 0, gprev = 0;
   uint32_t db_or_s = 0, db_or = 0, db_and = ~0u, u2 = 0, u3 = 0, dadj = 0, dgprev = 0;
   uint32_t bacc = 0;
-  int n = 0;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
     const uint32_t s = d[i];
@@ -208,7 +226,6 @@ PZ_DEV void candidate_sizes32(uint32_t (&d)[32], Sizes &out) {
     bx_and &= g;
     adj |= g & gprev;
     gprev = g;
-    n += s != 0 ? 1 : 0;
     if (i > 0) {
       const uint32_t p = d[i - 1];
       const uint32_t ld = s - p;
@@ -230,7 +247,7 @@ PZ_DEV void candidate_sizes32(uint32_t (&d)[32], Sizes &out) {
   out.sz[kBX] = plane_code_bits(bx_or, bx_and, ~bx_or_s, exactly2 & adj, single, 32, 32, 5);
 
   uint32_t zand = bx_and, zadj = adj;
-  if (__ballot(n > 0 && n < 32)) {
+  if (zbx) {
     launder_regs(d);
     uint32_t za = ~0u, zj = 0, zprev = 0;
 #pragma unroll
@@ -263,11 +280,11 @@ PZ_DEV void candidate_sizes32(uint32_t (&d)[32], Sizes &out) {
 }
 
 template <int W>
-PZ_DEV void candidate_sizes(uint32_t (&d)[32], Sizes &out) {
+PZ_DEV void candidate_sizes(uint32_t (&d)[32], int n, bool zbx, Sizes &out) {
   if constexpr (W == 16)
-    candidate_sizes16(d, out);
+    candidate_sizes16(d, n, zbx, out);
   else
-    candidate_sizes32(d, out);
+    candidate_sizes32(d, n, zbx, out);
 }
 
 // Smallest candidate; equal sizes go to the lowest tag. Returns the tag and
@@ -301,8 +318,9 @@ __global__ __launch_bounds__(kGroupThreads, 4) void size_kernel(
   const bool valid = off < raw_bytes;
   uint32_t d[32];
   load_block(src, raw_bytes, off, d);
+  const int n = (int)count_nonzero<W>(d);
   Sizes s;
-  candidate_sizes<W>(d, s);
+  candidate_sizes<W>(d, n, __ballot(n > 0 && n < 1024 / W) != 0, s);
   int best_size;
   const int tag = select_tag(s, best_size);
   const uint32_t cost = valid ? 3u + (uint32_t)best_size : 0u;
@@ -318,7 +336,7 @@ __global__ __launch_bounds__(kGroupThreads, 4) void size_kernel(
   uint32_t len = 0;
   if (chunk < nchunks) {
     const uint64_t start = chunk * kChunkBytes;
-    const uint32_t raw_len = (uint32_t)min<uint64_t>(kChunkBytes, raw_bytes - start);
+    const uint32_t raw_len = (uint32_t)min_u64(kChunkBytes, raw_bytes - start);
     len = (bits + 7) / 8;
     if (len >= raw_len) len = raw_len;
   }
@@ -455,7 +473,9 @@ __global__ __launch_bounds__(kGroupThreads, 4) void compress_kernel(
   __shared__ __attribute__((aligned(16))) uint32_t lds[kGroupLdsDwords];
   __shared__ uint16_t blk_bits[kGroupThreads];  // per block: its cost, then its bit offset
   __shared__ uint8_t slot_block[kGroupThreads];  // compacted slot -> block of the group
-  __shared__ uint32_t wave_nz[kWavesPerGroup];
+  __shared__ uint8_t slot_n[kGroupThreads];      // compacted slot -> its non-zero symbols
+  __shared__ uint32_t wave_full[kWavesPerGroup];
+  __shared__ uint32_t wave_part[kWavesPerGroup];
   __shared__ uint32_t chunk_len[kGroupChunks];
   __shared__ uint64_t chunk_pay[kGroupChunks];
   __shared__ uint32_t group_tile;
@@ -467,36 +487,44 @@ __global__ __launch_bounds__(kGroupThreads, 4) void compress_kernel(
   const uint32_t tile = group_tile;
   if (tile >= ntiles) return;
 
-  // --- 1. Load block t; find the all-zero blocks. ---
+  // --- 1. Load block t; count its non-zero symbols. ---
   // (Block and chunk indices are recomputed where needed rather than kept
   // live through the statistics, which use every register.)
   const uint64_t block = (uint64_t)tile * kGroupThreads + t;
   const bool valid = block * kBlockBytes < raw_bytes;
   uint32_t d[32];
   load_block(src, raw_bytes, block * kBlockBytes, d);
-  uint32_t any = 0;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) any |= d[i];
-  const bool nonzero = any != 0;  // blocks past the end load as zeros
-  const uint64_t wave_mask = __ballot(nonzero);
-  if (lane == 0) wave_nz[wave] = (uint32_t)popc64(wave_mask);
+  uint32_t sn = count_nonzero<W>(d);  // blocks past the end load as zeros
+  const bool nonzero = sn != 0;
+  const bool partial = nonzero && sn < (uint32_t)N;
+  const uint64_t mfull = __ballot(nonzero && !partial), mpart = __ballot(partial);
+  if (lane == 0) {
+    wave_full[wave] = (uint32_t)popc64(mfull);
+    wave_part[wave] = (uint32_t)popc64(mpart);
+  }
   if (!nonzero) blk_bits[t] = (uint16_t)(valid ? ZeroBlock<W>::bits : 0u);
   __syncthreads();
 
-  // --- 2. Pack the non-zero blocks into slots 0..nnz-1. ---
-  uint32_t nnz = 0, first = 0;
+  // --- 2. Slots: the non-zero blocks are packed through LDS into slots
+  // 0..nnz-1, those without a zero symbol first, so that the ZBX statistics
+  // (needed only when 0 < n < N) run on as few waves as possible. ---
+  uint32_t nfull = 0, npart = 0, ffirst = 0, pfirst = 0;
 #pragma unroll
   for (int k = 0; k < kWavesPerGroup; ++k) {
-    const uint32_t c = wave_nz[k];
-    first += (uint32_t)k < wave ? c : 0u;
-    nnz += c;
+    const uint32_t f = wave_full[k], q = wave_part[k];
+    ffirst += (uint32_t)k < wave ? f : 0u;
+    pfirst += (uint32_t)k < wave ? q : 0u;
+    nfull += f;
+    npart += q;
   }
+  const uint32_t nnz = nfull + npart;
   if (nonzero) {
-    const uint32_t idx = first + lanes_below(wave_mask);
+    const uint32_t idx = partial ? nfull + pfirst + lanes_below(mpart) : ffirst + lanes_below(mfull);
     uint32_t *slot = lds + idx * kLaneStride;
 #pragma unroll
     for (int i = 0; i < 32; ++i) slot[i] = d[i];
     slot_block[idx] = (uint8_t)t;
+    slot_n[idx] = (uint8_t)sn;
   }
   __syncthreads();
 
@@ -516,11 +544,14 @@ __global__ __launch_bounds__(kGroupThreads, 4) void compress_kernel(
   uint32_t e[32];
   if (wave_active) {
     uint32_t *region = lds + slot * kLaneStride;
+    sn = active ? (uint32_t)slot_n[slot] : 0u;
     if (active) {
 #pragma unroll
       for (int i = 0; i < 32; ++i) d[i] = region[i];
     }
-    candidate_sizes<W>(d, s);
+    const bool zbx = __ballot(active && sn < (uint32_t)N) != 0;  // active blocks are non-zero
+    candidate_sizes<W>(d, (int)sn, zbx, s);
+    s.n = (int)sn;
     launder_regs(d);
     int best_size;
     tag = select_tag(s, best_size);
@@ -581,9 +612,11 @@ __global__ __launch_bounds__(kGroupThreads, 4) void compress_kernel(
     // Transform input: the symbols, the deltas (DBX, arranged so that plane
     // element k is delta k+1) or the compacted symbols (ZBX).
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      uint32_t v = d[i];
-      if (want_dbx) {
+    for (int i = 0; i < 32; ++i) e[i] = d[i];
+    if (__ballot(want_dbx)) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        uint32_t v;
         if constexpr (W == 16) {
           // dword i = (delta 2i+1, delta 2i+2); the last slot is empty.
           const uint32_t cur = funnel(i < 31 ? d[i + 1] : 0u, d[i], 16);  // (s 2i+1, s 2i+2)
@@ -592,9 +625,12 @@ __global__ __launch_bounds__(kGroupThreads, 4) void compress_kernel(
         } else {
           v = i < 31 ? d[i + 1] - d[i] : 0u;
         }
+        e[i] = want_dbx ? v : e[i];
       }
-      if (any_zbx && want_zbx) v = region[i];
-      e[i] = v;
+    }
+    if (any_zbx) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) e[i] = want_zbx ? region[i] : e[i];
     }
   }
   __syncthreads();  // costs complete; staging and regions free
@@ -607,7 +643,7 @@ __global__ __launch_bounds__(kGroupThreads, 4) void compress_kernel(
   uint32_t raw_len = 0, len = 0;
   const uint64_t chunk = (uint64_t)tile * kGroupChunks + (t >> 5);
   if (chunk < nchunks) {
-    raw_len = (uint32_t)min<uint64_t>(kChunkBytes, raw_bytes - chunk * kChunkBytes);
+    raw_len = (uint32_t)min_u64(kChunkBytes, raw_bytes - chunk * kChunkBytes);
     len = (bits + 7) / 8;
     if (len >= raw_len) len = raw_len;
   }
@@ -655,7 +691,7 @@ __global__ __launch_bounds__(kGroupThreads, 4) void compress_kernel(
     const uint32_t ch = sb >> 5;
     const uint64_t cchunk = (uint64_t)tile * kGroupChunks + ch;
     const uint32_t craw_len =
-        cchunk < nchunks ? (uint32_t)min<uint64_t>(kChunkBytes, raw_bytes - cchunk * kChunkBytes) : 0u;
+        cchunk < nchunks ? (uint32_t)min_u64(kChunkBytes, raw_bytes - cchunk * kChunkBytes) : 0u;
     const bool craw = chunk_len[ch] == craw_len;
     const bool coded = active && !craw;
     const bool want_raw = active && (craw || tag == kRAW);
@@ -772,31 +808,60 @@ __global__ __launch_bounds__(kGroupThreads, 4) void compress_kernel(
   }
   __syncthreads();
 
-  // --- 6. Store: wave w writes chunks 2w and 2w+1. Payload byte i goes to
-  // dst byte poff + i: with sh = poff & 3, dst dword i of the aligned span
-  // holds buffer bytes 4i - sh .. 4i - sh + 3. ---
+  // --- 6. Store: wave w writes chunks 2w and 2w+1 in 16-byte units.
+  // Payload byte i goes to dst byte poff + i. With sh = poff & 15 =
+  // 4 dsh + bsh, dst dword o of the 16-byte aligned span holds payload bytes
+  // 4o - sh .. 4o - sh + 3: buffer dwords o - dsh - 1 and o - dsh joined by
+  // a funnel shift. Unit u of the span therefore needs buffer dwords
+  // 4u - dsh - 1 .. 4u - dsh + 3, which lie in the aligned quads u - 1 and u
+  // (two conflict-free 16-byte LDS reads; dsh is uniform over the chunk).
+  // Only the first and last units (shared with the neighbouring chunks) are
+  // written piecewise. ---
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const uint32_t c = 2 * wave + (uint32_t)h;
     const uint32_t plen = chunk_len[c];
     if (plen == 0) continue;
     const uint64_t poff = chunk_pay[c];
-    const uint32_t sh = (uint32_t)(poff & 3);
-    const uint64_t gbase = poff - sh;
+    const uint32_t sh = (uint32_t)(poff & 15);
+    const uint32_t dsh = sh >> 2, rs = 32u - 8u * (sh & 3u);
+    uint8_t *span = dst + (poff - sh);
     const uint32_t total = sh + plen;
-    const uint32_t ndw = (total + 3) / 4;
-    const uint32_t *buf = lds + c * kChunkBufDwords;
-    for (uint32_t i = lane; i < ndw; i += kWave) {
-      const uint32_t lo = i > 0 ? buf[i - 1] : 0u;
-      const uint32_t v = sh ? funnel(buf[i], lo, 32u - 8u * sh) : buf[i];
-      const uint32_t b0 = 4 * i, b1 = 4 * i + 4;
-      if (b0 >= sh && b1 <= total) {
-        *reinterpret_cast<uint32_t *>(dst + gbase + b0) = v;
+    const uint32_t nun = (total + 15) / 16;
+    const uint4 *quad = reinterpret_cast<const uint4 *>(lds + c * kChunkBufDwords);
+    for (uint32_t u = lane; u < nun; u += kWave) {
+      const uint4 p = u > 0 ? quad[u - 1] : make_uint4(0, 0, 0, 0);
+      const uint4 q = quad[u];
+      uint32_t w0, w1, w2, w3, w4;  // buffer dwords 4u - dsh - 1 .. 4u - dsh + 3
+      if (dsh == 0) {
+        w0 = p.w; w1 = q.x; w2 = q.y; w3 = q.z; w4 = q.w;
+      } else if (dsh == 1) {
+        w0 = p.z; w1 = p.w; w2 = q.x; w3 = q.y; w4 = q.z;
+      } else if (dsh == 2) {
+        w0 = p.y; w1 = p.z; w2 = p.w; w3 = q.x; w4 = q.y;
+      } else {
+        w0 = p.x; w1 = p.y; w2 = p.z; w3 = p.w; w4 = q.x;
+      }
+      uint32_t v[4];
+      if (rs == 32) {
+        v[0] = w1; v[1] = w2; v[2] = w3; v[3] = w4;
+      } else {
+        v[0] = funnel(w1, w0, rs); v[1] = funnel(w2, w1, rs); v[2] = funnel(w3, w2, rs); v[3] = funnel(w4, w3, rs);
+      }
+      const uint32_t b0 = 16 * u;
+      if (b0 >= sh && b0 + 16 <= total) {
+        *reinterpret_cast<uint4 *>(span + b0) = make_uint4(v[0], v[1], v[2], v[3]);
       } else {
 #pragma unroll
-        for (uint32_t b = 0; b < 4; ++b) {
-          const uint32_t k = b0 + b;
-          if (k >= sh && k < total) dst[gbase + k] = (uint8_t)(v >> (8 * b));
+        for (uint32_t k = 0; k < 4; ++k) {
+          const uint32_t d0 = b0 + 4 * k;
+          if (d0 >= sh && d0 + 4 <= total) {
+            *reinterpret_cast<uint32_t *>(span + d0) = v[k];
+          } else {
+#pragma unroll
+            for (uint32_t b = 0; b < 4; ++b)
+              if (d0 + b >= sh && d0 + b < total) span[d0 + b] = (uint8_t)(v[k] >> (8 * b));
+          }
         }
       }
     }

@@ -345,7 +345,7 @@ __global__ __launch_bounds__(kLocateChunks * G) void locate_kernel(
   const uint64_t off = 2 * nchunks + wave_before + incl - H;
 
   const uint32_t raw_len =
-      c < nchunks ? (uint32_t)min<uint64_t>(kChunkBytes, raw_bytes - c * kChunkBytes) : 0u;
+      c < nchunks ? (uint32_t)min_u64(kChunkBytes, raw_bytes - c * kChunkBytes) : 0u;
   const bool header_bad = c < nchunks && (H > raw_len || off + H > comp_bytes);
   const bool coded = c < nchunks && !header_bad && H < raw_len;
   uint32_t *region = lds + ci * kRingRegion;
@@ -558,7 +558,7 @@ __global__ __launch_bounds__(kGroupThreads) void decode_kernel(
     if (chunk < nchunks) {
       coff = chunk_off[chunk];
       H = hdr[chunk];
-      raw_len = (uint32_t)min<uint64_t>(kChunkBytes, raw_bytes - chunk * kChunkBytes);
+      raw_len = (uint32_t)min_u64(kChunkBytes, raw_bytes - chunk * kChunkBytes);
     }
     const bool ok = block * kBlockBytes < raw_bytes && coff != kBadChunk;
     const bool raw_chunk = ok && H == raw_len;
@@ -746,7 +746,7 @@ __global__ __launch_bounds__(kGroupThreads) void decode_kernel(
   // --- 5. Coalesced store of the group's output span (bytes past raw_bytes
   // are not written). ---
   const uint64_t span0 = gblock0 * kBlockBytes;
-  const uint64_t span_end = min<uint64_t>(raw_bytes, span0 + (uint64_t)kGroupThreads * kBlockBytes);
+  const uint64_t span_end = min_u64(raw_bytes, span0 + (uint64_t)kGroupThreads * kBlockBytes);
   const uint32_t span = (uint32_t)(span_end - span0);
 #pragma unroll
   for (int k = 0; k < kBlocksPerChunk / 4; ++k) {

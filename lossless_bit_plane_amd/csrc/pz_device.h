@@ -66,6 +66,10 @@ PZ_DEV uint32_t lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
+// Integer minimum of two 64-bit values (HIP's templated min goes through
+// floating point for 64-bit integers).
+__host__ __device__ inline uint64_t min_u64(uint64_t a, uint64_t b) { return a < b ? a : b; }
+
 PZ_DEV uint64_t all_ones64(int L) { return L >= 64 ? ~0ull : ((1ull << L) - 1ull); }
 
 // ceil(log2 L) for L >= 2, else 0: width of the position field.
