@@ -509,18 +509,28 @@ __global__ __launch_bounds__(kGroupThreads) void decode_kernel(
   if (gtile * kDecodeChunks >= nchunks) return;
   const uint64_t gblock0 = gtile * kGroupThreads;  // first block of the group
 
-  // --- 1. Stage the 8 payloads (dword-aligned copies); wave w takes 2w, 2w+1. ---
+  // Every thread's metadata at once: its chunk's payload offset and header
+  // and its block's bit offset, so that the staging below waits for one
+  // round trip before its payload loads, and the classification none.
   const uint16_t *hdr = reinterpret_cast<const uint16_t *>(src);
+  const uint64_t block = gblock0 + t;
+  const uint64_t chunk = block >> 5;
+  uint64_t my_coff = kBadChunk;
+  uint32_t my_H = 0, my_boff = 0;
+  if (chunk < nchunks) {
+    my_coff = chunk_off[chunk];
+    my_H = hdr[chunk];
+    my_boff = block_off[block];
+  }
+
+  // --- 1. Stage the 8 payloads (dword-aligned copies); wave w takes 2w, 2w+1
+  // (whose metadata its lanes 0 and 32 hold). ---
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const uint32_t ci = 2 * wave + (uint32_t)h;
-    const uint64_t c = gtile * kDecodeChunks + ci;
-    uint64_t coff = kBadChunk;
-    uint32_t H = 0;
-    if (c < nchunks) {
-      coff = chunk_off[c];
-      H = hdr[c];
-    }
+    const uint64_t coff = (uint64_t)__builtin_amdgcn_readlane((int)(uint32_t)my_coff, 32 * h) |
+                          ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(my_coff >> 32), 32 * h) << 32);
+    const uint32_t H = (uint32_t)__builtin_amdgcn_readlane((int)my_H, 32 * h);
     const uint64_t q0 = (coff >> 2) & ~3ull;
     if (lane == 0) chunk_lead[ci] = coff == kBadChunk ? 0u : (uint32_t)(8 * (coff - 4 * q0));
     if (coff == kBadChunk) continue;
@@ -548,25 +558,19 @@ __global__ __launch_bounds__(kGroupThreads) void decode_kernel(
   __syncthreads();
 
   // --- 2. Block t: all-zero blocks stay here, the rest go to the slot list. ---
-  const uint64_t block = gblock0 + t;
-  const uint64_t chunk = block >> 5;
   bool busy = false;
   {
     const uint32_t ci = t >> 5;
-    uint64_t coff = kBadChunk;
-    uint32_t H = 0, raw_len = 0;
-    if (chunk < nchunks) {
-      coff = chunk_off[chunk];
-      H = hdr[chunk];
-      raw_len = (uint32_t)min_u64(kChunkBytes, raw_bytes - chunk * kChunkBytes);
-    }
+    const uint64_t coff = my_coff;
+    const uint32_t H = my_H;
+    const uint32_t raw_len = chunk < nchunks ? (uint32_t)min_u64(kChunkBytes, raw_bytes - chunk * kChunkBytes) : 0u;
     const bool ok = block * kBlockBytes < raw_bytes && coff != kBadChunk;
     const bool raw_chunk = ok && H == raw_len;
     const bool coded = ok && !raw_chunk;
     uint32_t pos = 1024u * (t & 31), head = 0;
     if (coded) {
       const LdsBits in{lds + ci * kChunkBufDwords, chunk_lead[ci]};
-      pos = block_off[block];
+      pos = my_boff;
       head = in.peek(pos);
       pos += 3;
     }
