@@ -92,6 +92,41 @@ pz_status_t pz_decompress(const void *d_src, size_t comp_bytes, int dtype,
                           int elem_bits, void *d_dst, size_t raw_bytes,
                           int32_t *d_status, void *stream);
 
+/* Codec variants (the single-codec columns the paper compares PlaneZip with,
+ * §V-A and Fig. 3: ZVC as in cDMA, BPC's DBX on every block, BX or ZBX
+ * alone; and PlaneZip with a subset of its candidates). codec_mask allows
+ * candidate t when bit t is set (tags in Fig. 2 order). With tagged = 1 every
+ * block carries the 3-bit tag and takes the smallest allowed candidate, equal
+ * sizes to the lowest tag; with tagged = 0 the mask must hold exactly one
+ * candidate, which every block uses, and no tag is written. In every mode a
+ * chunk that would grow is stored raw (FORMAT.md §4). A stream must be
+ * decompressed with the (codec_mask, tagged) pair it was compressed with;
+ * a tagged decoder accepts any tag 0..4 whatever the mask. An empty mask,
+ * bits above PZ_CODEC_ALL, or an untagged mask with more than one candidate
+ * return PZ_ERROR_INVALID_VALUE. The plain calls above are the same calls
+ * with (PZ_CODEC_ALL, 1). */
+#define PZ_CODEC_ZVC (1u << 0)
+#define PZ_CODEC_DBX (1u << 1)
+#define PZ_CODEC_BX (1u << 2)
+#define PZ_CODEC_ZBX (1u << 3)
+#define PZ_CODEC_RAW (1u << 4)
+#define PZ_CODEC_ALL 0x1Fu
+
+pz_status_t pz_compressed_size_ex(const void *d_src, size_t raw_bytes, int dtype,
+                                  int elem_bits, uint32_t codec_mask, int tagged,
+                                  uint64_t *d_out_bytes, uint16_t *d_chunk_lens,
+                                  void *stream);
+
+pz_status_t pz_compress_ex(const void *d_src, size_t raw_bytes, int dtype,
+                           int elem_bits, uint32_t codec_mask, int tagged,
+                           void *d_dst, size_t dst_capacity,
+                           uint64_t *d_out_bytes, void *stream);
+
+pz_status_t pz_decompress_ex(const void *d_src, size_t comp_bytes, int dtype,
+                             int elem_bits, uint32_t codec_mask, int tagged,
+                             void *d_dst, size_t raw_bytes, int32_t *d_status,
+                             void *stream);
+
 /* Diagnostics of the size pass, per 128-byte block (nblocks =
  * ceil(raw_bytes/128)): d_sizes (nullable) receives the five candidate sizes
  * in bits (ZVC, DBX, BX, ZBX, RAW; payload only, no tag) as 5*nblocks

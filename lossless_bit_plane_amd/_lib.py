@@ -15,7 +15,8 @@ PZ_ERROR_INSUFFICIENT_BUFFER = 2
 PZ_ERROR_CORRUPT_STREAM = 3
 PZ_ERROR_HIP = 4
 
-EXPORTS = ("pz_compressed_size", "pz_compress", "pz_decompress", "pz_block_sizes", "pz_status_string")
+EXPORTS = ("pz_compressed_size", "pz_compress", "pz_decompress", "pz_block_sizes", "pz_status_string",
+           "pz_compressed_size_ex", "pz_compress_ex", "pz_decompress_ex")
 
 
 def _load():
@@ -29,7 +30,12 @@ def _load():
     lib.pz_compress.argtypes = [vp, sz, i, i, vp, sz, vp, vp]
     lib.pz_decompress.argtypes = [vp, sz, i, i, vp, sz, vp, vp]
     lib.pz_block_sizes.argtypes = [vp, sz, i, i, vp, vp, vp]
-    for name in ("pz_compressed_size", "pz_compress", "pz_decompress", "pz_block_sizes"):
+    u32 = ctypes.c_uint32
+    lib.pz_compressed_size_ex.argtypes = [vp, sz, i, i, u32, i, vp, vp, vp]
+    lib.pz_compress_ex.argtypes = [vp, sz, i, i, u32, i, vp, sz, vp, vp]
+    lib.pz_decompress_ex.argtypes = [vp, sz, i, i, u32, i, vp, sz, vp, vp]
+    for name in ("pz_compressed_size", "pz_compress", "pz_decompress", "pz_block_sizes",
+                 "pz_compressed_size_ex", "pz_compress_ex", "pz_decompress_ex"):
         getattr(lib, name).restype = ctypes.c_int
     lib.pz_status_string.argtypes = [ctypes.c_int]
     lib.pz_status_string.restype = ctypes.c_char_p

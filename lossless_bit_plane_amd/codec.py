@@ -10,6 +10,9 @@ import torch
 from ._lib import PZ_ERROR_CORRUPT_STREAM, PlaneZipError, check, lib
 
 BF16, FP32, OTHER = 0, 1, 2
+# Candidate masks of the codec-variant calls (bit t allows tag t).
+CODEC_ZVC, CODEC_DBX, CODEC_BX, CODEC_ZBX, CODEC_RAW = 1, 2, 4, 8, 16
+CODEC_ALL = 0x1F
 _TORCH_DTYPE = {torch.bfloat16: (BF16, 16), torch.float32: (FP32, 32)}
 
 
@@ -98,6 +101,49 @@ def pz_decompress(src: torch.Tensor, comp_bytes: int, raw_bytes: int, dtype: int
         status = torch.empty(1, dtype=torch.int32, device=b.device)
     check(lib.pz_decompress(_ptr(b), comp_bytes, dtype, elem_bits, _ptr(dst), raw_bytes,
                             _ptr(status), _stream(stream)), "pz_decompress")
+    return dst, status
+
+
+def pz_compressed_size_ex(src: torch.Tensor, codec_mask: int, tagged: bool, dtype=None,
+                          elem_bits=None, chunk_lens: bool = False, stream=None):
+    """pz_compressed_size for a codec variant (candidate mask, tagged or not)."""
+    dtype, elem_bits = _kind(src, dtype, elem_bits)
+    b = _byte_view(src)
+    out = torch.empty(1, dtype=torch.int64, device=b.device)
+    lens = torch.empty(num_chunks(b.numel()), dtype=torch.int16, device=b.device) if chunk_lens else None
+    check(lib.pz_compressed_size_ex(_ptr(b), b.numel(), dtype, elem_bits, codec_mask, int(tagged),
+                                    _ptr(out), _ptr(lens), _stream(stream)), "pz_compressed_size_ex")
+    return out, lens
+
+
+def pz_compress_ex(src: torch.Tensor, codec_mask: int, tagged: bool, dtype=None, elem_bits=None,
+                   dst: torch.Tensor | None = None, out_bytes: torch.Tensor | None = None,
+                   stream=None):
+    """pz_compress for a codec variant (candidate mask, tagged or not)."""
+    dtype, elem_bits = _kind(src, dtype, elem_bits)
+    b = _byte_view(src)
+    cap = max_compressed_bytes(b.numel())
+    if dst is None:
+        dst = torch.empty(max(cap, 16), dtype=torch.uint8, device=b.device)
+    if out_bytes is None:
+        out_bytes = torch.empty(1, dtype=torch.int64, device=b.device)
+    check(lib.pz_compress_ex(_ptr(b), b.numel(), dtype, elem_bits, codec_mask, int(tagged), _ptr(dst),
+                             dst.numel(), _ptr(out_bytes), _stream(stream)), "pz_compress_ex")
+    return dst, out_bytes
+
+
+def pz_decompress_ex(src: torch.Tensor, comp_bytes: int, raw_bytes: int, dtype: int, elem_bits: int,
+                     codec_mask: int, tagged: bool, dst: torch.Tensor | None = None,
+                     status: torch.Tensor | None = None, stream=None):
+    """pz_decompress for a stream written by pz_compress_ex with the same
+    (codec_mask, tagged)."""
+    b = _byte_view(src)
+    if dst is None:
+        dst = torch.empty(max(raw_bytes, 16), dtype=torch.uint8, device=b.device)
+    if status is None:
+        status = torch.empty(1, dtype=torch.int32, device=b.device)
+    check(lib.pz_decompress_ex(_ptr(b), comp_bytes, dtype, elem_bits, codec_mask, int(tagged),
+                               _ptr(dst), raw_bytes, _ptr(status), _stream(stream)), "pz_decompress_ex")
     return dst, status
 
 

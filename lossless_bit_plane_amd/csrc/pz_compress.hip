@@ -287,13 +287,14 @@ PZ_DEV void candidate_sizes(uint32_t (&d)[32], int n, bool zbx, Sizes &out) {
     candidate_sizes32(d, n, zbx, out);
 }
 
-// Smallest candidate; equal sizes go to the lowest tag. Returns the tag and
-// its size (no indexing of the size array by a lane-varying tag).
-PZ_DEV int select_tag(const Sizes &s, int &best_size) {
-  int best = 0, bsz = s.sz[0];
+// Smallest allowed candidate (mask bit t = tag t); equal sizes go to the
+// lowest tag. Returns the tag and its size (no indexing of the size array by
+// a lane-varying tag).
+PZ_DEV int select_tag(const Sizes &s, int &best_size, uint32_t mask) {
+  int best = 0, bsz = 0x7FFFFFFF;
 #pragma unroll
-  for (int t = 1; t < 5; ++t) {
-    if (s.sz[t] < bsz) {
+  for (int t = 0; t < 5; ++t) {
+    if (((mask >> t) & 1u) && s.sz[t] < bsz) {
       best = t;
       bsz = s.sz[t];
     }
@@ -309,7 +310,7 @@ template <int W>
 __global__ __launch_bounds__(kGroupThreads, 4) void size_kernel(
     const uint8_t *__restrict__ src, uint64_t raw_bytes, uint64_t nchunks,
     uint64_t *__restrict__ out_bytes, uint16_t *__restrict__ chunk_lens,
-    uint16_t *__restrict__ block_sizes, uint8_t *__restrict__ block_tags) {
+    uint16_t *__restrict__ block_sizes, uint8_t *__restrict__ block_tags, Mode mode) {
   const uint32_t lane = lane_id();
   const uint64_t tile = (uint64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
   if (tile * 2 >= nchunks) return;
@@ -322,8 +323,8 @@ __global__ __launch_bounds__(kGroupThreads, 4) void size_kernel(
   Sizes s;
   candidate_sizes<W>(d, n, __ballot(n > 0 && n < 1024 / W) != 0, s);
   int best_size;
-  const int tag = select_tag(s, best_size);
-  const uint32_t cost = valid ? 3u + (uint32_t)best_size : 0u;
+  const int tag = select_tag(s, best_size, mode.mask);
+  const uint32_t cost = valid ? 3u * mode.tagged + (uint32_t)best_size : 0u;
   if (valid && block_sizes) {
 #pragma unroll
     for (int t = 0; t < 5; ++t) block_sizes[block * 5 + t] = (uint16_t)s.sz[t];
@@ -449,22 +450,28 @@ constexpr int kStageDwords = kGroupThreads * kLaneStride;
 constexpr int kGroupBufDwords = kGroupChunks * kChunkBufDwords;
 constexpr int kGroupLdsDwords = kStageDwords > kGroupBufDwords ? kStageDwords : kGroupBufDwords;
 
-// An all-zero block codes smallest as BX: every XORed plane is zero, so the
-// planes are one zero run (a 2+R-bit code), which is shorter than the ZVC
-// mask (N bits) and than the DBX and ZBX prefixes.
+// An all-zero block under the mode's candidate for it (the smallest allowed;
+// BX in PlaneZip): the tag, a zero mask / base / raw block of zero bits
+// (already present in the cleared buffer), and for the plane encodings one
+// zero run over all planes.
 template <int W>
-struct ZeroBlock {
-  static constexpr uint32_t R = W == 16 ? 4 : 5;
-  static_assert(W - 2 < (1 << R), "a run of all W planes fits the run field");
-  static constexpr uint32_t code = (uint32_t)kBX | ((2u | ((uint32_t)(W - 2) << 2)) << 3);
-  static constexpr uint32_t bits = 3 + 2 + R;
-};
+PZ_DEV void emit_zero_block(uint32_t *buf, uint32_t off, const Mode &m) {
+  constexpr uint32_t N = 1024 / W, R = W == 16 ? 4 : 5;
+  const uint32_t c = m.zc;
+  BitSink z;
+  z.buf = buf;
+  z.off = off;
+  if (m.tagged) z.put(c, 3);
+  z.off += c == 0 ? N : (c == 1 ? (uint32_t)W : (c == 3 ? N : (c == 4 ? 1024u : 0u)));
+  const uint32_t planes = c == 1 ? W + 1 : ((c == 2 || c == 3) ? (uint32_t)W : 0u);
+  if (planes) z.put(2u | ((planes - 2u) << 2), 2 + R);
+}
 
 template <int W>
 __global__ __launch_bounds__(kGroupThreads, 4) void compress_kernel(
     const uint8_t *__restrict__ src, uint64_t raw_bytes, uint64_t nchunks, uint64_t ntiles,
     uint8_t *__restrict__ dst, uint64_t *__restrict__ out_bytes, uint64_t *status,
-    uint32_t *tile_counter) {
+    uint32_t *tile_counter, Mode mode) {
   constexpr int N = 1024 / W;
   constexpr uint32_t R = W == 16 ? 4 : 5;
   using PT = typename std::conditional<W == 16, uint64_t, uint32_t>::type;
@@ -502,7 +509,7 @@ __global__ __launch_bounds__(kGroupThreads, 4) void compress_kernel(
     wave_full[wave] = (uint32_t)popc64(mfull);
     wave_part[wave] = (uint32_t)popc64(mpart);
   }
-  if (!nonzero) blk_bits[t] = (uint16_t)(valid ? ZeroBlock<W>::bits : 0u);
+  if (!nonzero) blk_bits[t] = (uint16_t)(valid ? 3u * mode.tagged + zero_block_size(W, mode.zc) : 0u);
   __syncthreads();
 
   // --- 2. Slots: the non-zero blocks are packed through LDS into slots
@@ -554,8 +561,8 @@ __global__ __launch_bounds__(kGroupThreads, 4) void compress_kernel(
     s.n = (int)sn;
     launder_regs(d);
     int best_size;
-    tag = select_tag(s, best_size);
-    if (active) blk_bits[slot_block[slot]] = (uint16_t)(3 + best_size);
+    tag = select_tag(s, best_size, mode.mask);
+    if (active) blk_bits[slot_block[slot]] = (uint16_t)(3u * mode.tagged + best_size);
 
     const bool want_zvc = active && tag == kZVC;
     const bool want_dbx = active && tag == kDBX;
@@ -680,10 +687,7 @@ __global__ __launch_bounds__(kGroupThreads, 4) void compress_kernel(
   // All-zero blocks of coded chunks: their one code. (In a raw chunk their
   // bytes are zeros, which the cleared buffer already holds.)
   if (((uint64_t)tile * kGroupThreads + t) * kBlockBytes < raw_bytes && !nonzero && !raw_chunk) {
-    BitSink z;
-    z.buf = lds + (t >> 5) * kChunkBufDwords;
-    z.off = excl;
-    z.put(ZeroBlock<W>::code, ZeroBlock<W>::bits);
+    emit_zero_block<W>(lds + (t >> 5) * kChunkBufDwords, excl, mode);
   }
 
   if (wave_active) {
@@ -703,7 +707,7 @@ __global__ __launch_bounds__(kGroupThreads, 4) void compress_kernel(
     BitSink bs;
     bs.buf = lds + ch * kChunkBufDwords;
     bs.off = craw ? 1024u * (sb & 31) : (uint32_t)blk_bits[sb];
-    if (coded) bs.put((uint32_t)tag, 3);
+    if (coded && mode.tagged) bs.put((uint32_t)tag, 3);
 
     if (__ballot(want_raw)) {
       // A raw chunk needs the symbols themselves back where e holds a transform.
@@ -881,9 +885,9 @@ hipError_t fill_u64(uint64_t *p, uint64_t n, uint64_t value, hipStream_t stream)
   return hipGetLastError();
 }
 
-hipError_t launch_size(int w, const uint8_t *src, uint64_t raw_bytes, uint64_t *out_bytes,
-                       uint16_t *chunk_lens, uint16_t *block_sizes, uint8_t *block_tags,
-                       hipStream_t stream) {
+hipError_t launch_size(int w, const uint8_t *src, uint64_t raw_bytes, uint32_t codec_mask, int tagged,
+                       uint64_t *out_bytes, uint16_t *chunk_lens, uint16_t *block_sizes,
+                       uint8_t *block_tags, hipStream_t stream) {
   const uint64_t nchunks = (raw_bytes + kChunkBytes - 1) / kChunkBytes;
   if (out_bytes) {
     hipError_t e = fill_u64(out_bytes, 1, 2 * nchunks, stream);
@@ -892,21 +896,23 @@ hipError_t launch_size(int w, const uint8_t *src, uint64_t raw_bytes, uint64_t *
   if (nchunks == 0) return hipSuccess;
   const uint64_t ntiles = (nchunks + 1) / 2;
   const uint64_t groups = (ntiles + kWavesPerGroup - 1) / kWavesPerGroup;
+  const Mode mode = make_mode(w, codec_mask, tagged);
   if (w == 16)
     hipLaunchKernelGGL(size_kernel<16>, dim3((unsigned)groups), dim3(kGroupThreads), 0, stream,
-                       src, raw_bytes, nchunks, out_bytes, chunk_lens, block_sizes, block_tags);
+                       src, raw_bytes, nchunks, out_bytes, chunk_lens, block_sizes, block_tags, mode);
   else
     hipLaunchKernelGGL(size_kernel<32>, dim3((unsigned)groups), dim3(kGroupThreads), 0, stream,
-                       src, raw_bytes, nchunks, out_bytes, chunk_lens, block_sizes, block_tags);
+                       src, raw_bytes, nchunks, out_bytes, chunk_lens, block_sizes, block_tags, mode);
   return hipGetLastError();
 }
 
-hipError_t launch_compress(int w, const uint8_t *src, uint64_t raw_bytes, uint8_t *dst,
-                           uint64_t *out_bytes, hipStream_t stream) {
+hipError_t launch_compress(int w, const uint8_t *src, uint64_t raw_bytes, uint32_t codec_mask,
+                           int tagged, uint8_t *dst, uint64_t *out_bytes, hipStream_t stream) {
   const uint64_t nchunks = (raw_bytes + kChunkBytes - 1) / kChunkBytes;
   if (nchunks == 0) return fill_u64(out_bytes, 1, 0, stream);
   const uint64_t ntiles = (nchunks + kGroupChunks - 1) / kGroupChunks;
   const uint64_t groups = ntiles;
+  const Mode mode = make_mode(w, codec_mask, tagged);
   // Scratch: one look-back status word per tile, then the tile counter.
   const size_t words = (size_t)ntiles + 1;
   uint64_t *scratch = nullptr;
@@ -917,10 +923,10 @@ hipError_t launch_compress(int w, const uint8_t *src, uint64_t raw_bytes, uint8_
     uint32_t *counter = reinterpret_cast<uint32_t *>(scratch + ntiles);
     if (w == 16)
       hipLaunchKernelGGL(compress_kernel<16>, dim3((unsigned)groups), dim3(kGroupThreads), 0,
-                         stream, src, raw_bytes, nchunks, ntiles, dst, out_bytes, scratch, counter);
+                         stream, src, raw_bytes, nchunks, ntiles, dst, out_bytes, scratch, counter, mode);
     else
       hipLaunchKernelGGL(compress_kernel<32>, dim3((unsigned)groups), dim3(kGroupThreads), 0,
-                         stream, src, raw_bytes, nchunks, ntiles, dst, out_bytes, scratch, counter);
+                         stream, src, raw_bytes, nchunks, ntiles, dst, out_bytes, scratch, counter, mode);
     e = hipGetLastError();
   }
   hipError_t f = hipFreeAsync(scratch, stream);

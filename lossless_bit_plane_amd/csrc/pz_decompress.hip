@@ -52,15 +52,34 @@ struct GlobalBits {
   }
 };
 
-// The code of an all-zero block (the tag of BX, then one run of all W
-// planes), as it appears in the stream's low bits at the block start.
-template <int W>
-struct ZeroCode {
-  static constexpr uint32_t R = W == 16 ? 4 : 5;
-  static constexpr uint32_t code = (uint32_t)kBX | ((2u | ((uint32_t)(W - 2) << 2)) << 3);
-  static constexpr uint32_t bits = 3 + 2 + R;
-  static constexpr uint32_t mask = (1u << bits) - 1u;
+// What the decoder needs of a codec mode: whether blocks carry a tag (else
+// every block is the fixed candidate), and the code of an all-zero block it
+// can settle at once: BX with all planes in one zero run, behind a BX tag or
+// alone in the untagged BX mode, as it appears in the stream's low bits at a
+// block start (zmask = 0: no such shortcut). Any other block, and any stream
+// a tagged decoder is given whatever mask the encoder used, is decoded by
+// its codes.
+struct DMode {
+  uint32_t tagged, fixed;
+  uint32_t zmask, zcode, zbits;
 };
+
+inline DMode make_dmode(int W, uint32_t mask, int tagged) {
+  const uint32_t R = W == 16 ? 4 : 5;
+  const uint32_t run = 2u | ((uint32_t)(W - 2) << 2);  // one zero run over all W planes
+  DMode m{tagged ? 1u : 0u, 0u, 0u, 1u, 0u};
+  for (uint32_t t = 0; t < 5; ++t)
+    if (mask == (1u << t)) m.fixed = t;
+  if (tagged) {
+    m.zbits = 3 + 2 + R;
+    m.zcode = (uint32_t)kBX | (run << 3);
+  } else if (m.fixed == (uint32_t)kBX) {
+    m.zbits = 2 + R;
+    m.zcode = run;
+  }
+  if (m.zbits) m.zmask = (1u << m.zbits) - 1u;
+  return m;
+}
 
 // ---------------------------------------------------------------------------
 // Locate. A workgroup takes a tile of 64 chunks; each chunk is walked by a
@@ -222,7 +241,8 @@ struct ChunkRing {
 // block's plane codes, whose class is the trailing-zero count of the next
 // bits and whose length comes from a per-block table.
 template <int W, int G>
-PZ_DEV bool parse_chunk(ChunkRing<G> &in, bool coded, uint32_t H, uint32_t raw_len, uint16_t *boff) {
+PZ_DEV bool parse_chunk(ChunkRing<G> &in, bool coded, uint32_t H, uint32_t raw_len, uint16_t *boff,
+                        const DMode &mode) {
   constexpr uint32_t N = 1024 / W;
   constexpr uint32_t R = W == 16 ? 4 : 5;
   constexpr uint32_t kSpec = 4 * G;  // codes tried per step
@@ -241,14 +261,15 @@ PZ_DEV bool parse_chunk(ChunkRing<G> &in, bool coded, uint32_t H, uint32_t raw_l
       in.step(pos);
       if (ql == 0) boff[b] = (uint16_t)pos;
       const uint32_t head = in.peek(pos);
-      const uint32_t tag = head & 7u;
-      if ((head & ZeroCode<W>::mask) == ZeroCode<W>::code) {
-        pos += ZeroCode<W>::bits;  // an all-zero block: one run over all planes
+      const uint32_t tag = mode.tagged ? head & 7u : mode.fixed;
+      const uint32_t hb = 3u * mode.tagged;  // tag bits
+      if ((head & mode.zmask) == mode.zcode) {
+        pos += mode.zbits;  // an all-zero block: one run over all planes
       } else {
-        uint32_t n = (uint32_t)popc32(in.peek(pos + 3));
-        if (W == 16) n += (uint32_t)popc32(in.peek(pos + 35));
+        uint32_t n = (uint32_t)popc32(in.peek(pos + hb));
+        if (W == 16) n += (uint32_t)popc32(in.peek(pos + hb + 32));
         const bool masked = tag == kZVC || tag == kZBX;
-        pos += 3 + (tag == kDBX ? W : 0u) + (masked ? N : 0u) + (tag == kZVC ? W * n : 0u) +
+        pos += hb + (tag == kDBX ? W : 0u) + (masked ? N : 0u) + (tag == kZVC ? W * n : 0u) +
                (tag == kRAW ? 1024u : 0u);
         bad |= tag > 4;
         L = tag == kDBX ? N - 1 : (tag == kZBX ? n : N);
@@ -308,7 +329,7 @@ template <int W, int G>
 __global__ __launch_bounds__(kLocateChunks * G) void locate_kernel(
     const uint8_t *__restrict__ src, uint64_t comp_bytes, uint64_t raw_bytes, uint64_t nchunks,
     uint64_t ntiles, uint64_t *__restrict__ chunk_off, uint16_t *__restrict__ block_off,
-    int32_t *status_out, uint64_t *lb_status, uint32_t *tile_counter) {
+    int32_t *status_out, uint64_t *lb_status, uint32_t *tile_counter, DMode mode) {
   constexpr int kWaves = G;  // 64 chunks x G lanes
   __shared__ uint32_t lds[kLocateChunks * kRingRegion];
   __shared__ uint64_t wave_sum[kWaves];
@@ -352,7 +373,7 @@ __global__ __launch_bounds__(kLocateChunks * G) void locate_kernel(
   uint16_t *boff = reinterpret_cast<uint16_t *>(region + kRingDwords + 1);
   ChunkRing<G> in;
   in.start(region, src, comp_bytes, coded ? off : 0, ql);
-  const bool parsed = parse_chunk<W, G>(in, coded, H, raw_len, boff);  // whole wave
+  const bool parsed = parse_chunk<W, G>(in, coded, H, raw_len, boff, mode);  // whole wave
   wave_lds_fence();
   if (coded) {
     // The chunk's block offsets: 64 bytes, 64/G per group lane.
@@ -494,7 +515,7 @@ template <int W>
 __global__ __launch_bounds__(kGroupThreads) void decode_kernel(
     const uint8_t *__restrict__ src, uint64_t comp_bytes, uint64_t raw_bytes, uint64_t nchunks,
     const uint64_t *__restrict__ chunk_off, const uint16_t *__restrict__ block_off,
-    uint8_t *__restrict__ dst) {
+    uint8_t *__restrict__ dst, DMode mode) {
   constexpr int N = 1024 / W;
   constexpr uint32_t WMASK = W == 16 ? 0xFFFFu : 0xFFFFFFFFu;
   __shared__ __attribute__((aligned(16))) uint32_t lds[kDecodeLdsDwords];
@@ -572,11 +593,12 @@ __global__ __launch_bounds__(kGroupThreads) void decode_kernel(
       const LdsBits in{lds + ci * kChunkBufDwords, chunk_lead[ci]};
       pos = my_boff;
       head = in.peek(pos);
-      pos += 3;
+      pos += 3u * mode.tagged;
     }
-    const bool zero = coded && (head & ZeroCode<W>::mask) == ZeroCode<W>::code;
+    const bool zero = coded && (head & mode.zmask) == mode.zcode;
+    const uint32_t tag = mode.tagged ? head & 7u : mode.fixed;
     busy = raw_chunk || (coded && !zero);
-    if (busy) blk_info[t] = pos | ((head & 7u) << 16) | ((uint32_t)raw_chunk << 19);
+    if (busy) blk_info[t] = pos | (tag << 16) | ((uint32_t)raw_chunk << 19);
   }
   const uint64_t bmask = __ballot(busy);
   if (lane == 0) wave_busy[wave] = (uint32_t)popc64(bmask);
@@ -777,8 +799,10 @@ __global__ void clear_scratch_kernel(uint64_t *words, uint64_t n, int32_t *statu
   if (i0 == 0) *status = value;
 }
 
-hipError_t launch_decompress(int w, const uint8_t *src, uint64_t comp_bytes, uint8_t *dst,
-                             uint64_t raw_bytes, int32_t *status, hipStream_t stream) {
+hipError_t launch_decompress(int w, const uint8_t *src, uint64_t comp_bytes, uint32_t codec_mask,
+                             int tagged, uint8_t *dst, uint64_t raw_bytes, int32_t *status,
+                             hipStream_t stream) {
+  const DMode mode = make_dmode(w, codec_mask, tagged);
   const uint64_t nchunks = (raw_bytes + kChunkBytes - 1) / kChunkBytes;
   const uint64_t ntiles_a = (nchunks + kLocateChunks - 1) / kLocateChunks;
   // Scratch (8-byte words): chunk offsets, block offsets, look-back status,
@@ -809,19 +833,21 @@ hipError_t launch_decompress(int w, const uint8_t *src, uint64_t comp_bytes, uin
     const dim3 grid_a((unsigned)ntiles_a);
     if (w == 16)
       hipLaunchKernelGGL((locate_kernel<16, kLocateLanes>), grid_a, dim3(kLocateThreads), 0, stream, src,
-                         comp_bytes, raw_bytes, nchunks, ntiles_a, chunk_off, block_off, st, lb_status, counter);
+                         comp_bytes, raw_bytes, nchunks, ntiles_a, chunk_off, block_off, st, lb_status, counter,
+                         mode);
     else
       hipLaunchKernelGGL((locate_kernel<32, kLocateLanes>), grid_a, dim3(kLocateThreads), 0, stream, src,
-                         comp_bytes, raw_bytes, nchunks, ntiles_a, chunk_off, block_off, st, lb_status, counter);
+                         comp_bytes, raw_bytes, nchunks, ntiles_a, chunk_off, block_off, st, lb_status, counter,
+                         mode);
     e = hipGetLastError();
     if (e == hipSuccess) {
       const uint64_t groups_b = (nchunks + kDecodeChunks - 1) / kDecodeChunks;
       if (w == 16)
         hipLaunchKernelGGL(decode_kernel<16>, dim3((unsigned)groups_b), dim3(kGroupThreads), 0,
-                           stream, src, comp_bytes, raw_bytes, nchunks, chunk_off, block_off, dst);
+                           stream, src, comp_bytes, raw_bytes, nchunks, chunk_off, block_off, dst, mode);
       else
         hipLaunchKernelGGL(decode_kernel<32>, dim3((unsigned)groups_b), dim3(kGroupThreads), 0,
-                           stream, src, comp_bytes, raw_bytes, nchunks, chunk_off, block_off, dst);
+                           stream, src, comp_bytes, raw_bytes, nchunks, chunk_off, block_off, dst, mode);
       e = hipGetLastError();
     }
   }

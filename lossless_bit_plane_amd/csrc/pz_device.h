@@ -38,6 +38,50 @@ constexpr uint64_t kValueMask = kFlagAggregate - 1;
 
 constexpr uint64_t kBadChunk = ~0ull;
 
+// Codec mode (§III-A; the single-codec columns of §V-A and Table III):
+// the candidates a block may use (bit t = tag t) and whether each block
+// carries the 3-bit tag. PlaneZip itself is {all five, tagged}; an untagged
+// mode has exactly one candidate and writes no tags. In every mode a chunk
+// that would grow is stored raw.
+constexpr uint32_t kAllCodecs = 0x1Fu;
+struct Mode {
+  uint32_t mask;    // allowed candidates
+  uint32_t tagged;  // 1: a 3-bit tag per block
+  uint32_t fixed;   // the candidate of an untagged mode
+  uint32_t zc;      // the candidate this mode picks for an all-zero block
+};
+
+// Size in bits (payload, no tag) of an all-zero block under candidate c: a
+// zero mask for ZVC and ZBX, a zero base for DBX, all planes in one zero run
+// for the plane encodings (W planes, W+1 for DBX), 1024 bits for RAW.
+__host__ __device__ inline uint32_t zero_block_size(int W, uint32_t c) {
+  const uint32_t N = 1024u / W, R = W == 16 ? 4u : 5u;
+  switch (c) {
+    case 0: return N;
+    case 1: return W + 2 + R;
+    case 2: return 2 + R;
+    case 3: return N + 2 + R;
+    default: return 1024;
+  }
+}
+
+// The mode for (mask, tagged): the all-zero block's candidate is the
+// smallest allowed one, ties to the lowest tag, as for any block.
+__host__ __device__ inline Mode make_mode(int W, uint32_t mask, int tagged) {
+  Mode m{mask, tagged ? 1u : 0u, 0u, 0u};
+  uint32_t best = 0xFFFFFFFFu;
+  for (uint32_t t = 0; t < 5; ++t) {
+    if (!((mask >> t) & 1u)) continue;
+    if (!tagged) m.fixed = t;
+    const uint32_t z = zero_block_size(W, t);
+    if (z < best) {
+      best = z;
+      m.zc = t;
+    }
+  }
+  return m;
+}
+
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 PZ_DEV uint32_t pk_sub_u16(uint32_t a, uint32_t b) {

@@ -23,8 +23,12 @@
 #define BLOCKS_PER_CHUNK 32
 /* Largest candidate payload is DBX/ZBX at 16 + 17*65 bits; round up. */
 #define CAND_BUF_BYTES 256
-/* A chunk of 32 coded blocks is at most 32 * (3 + 1024) bits. */
-#define CHUNK_BUF_BYTES 4200
+/* A chunk is coded in full before the raw decision (a chunk that would grow
+ * is stored raw, §III-A), so the buffer holds 32 blocks of the largest
+ * candidate plus its tag: with RAW allowed a block is at most 3 + 1024 bits,
+ * but a mode without RAW (a single-codec variant) can reach
+ * 3 + CAND_BUF_BYTES * 8 bits. */
+#define CHUNK_BUF_BYTES (BLOCKS_PER_CHUNK * (CAND_BUF_BYTES + 1))
 
 /* ------------------------------------------------------------------------ */
 /* Bit I/O. Stream bit t is bit (t % 8) of byte (t / 8); a field is written  */

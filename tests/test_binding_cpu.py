@@ -56,3 +56,15 @@ def test_rejects_bad_arguments_on_host(lib):
     assert lib.pz_decompress(fake, 3, 0, 16, fake, 8193, None, None) == _lib.PZ_ERROR_CORRUPT_STREAM
     assert lib.pz_compressed_size(fake, 10, 2, 16, fake, None, None) == _lib.PZ_ERROR_INVALID_VALUE
     assert lib.pz_status_string(3) == b"corrupt stream"
+
+
+def test_rejects_bad_codec_modes_on_host(lib):
+    from lossless_bit_plane_amd import _lib
+
+    fake = 256  # aligned, never dereferenced: every call below fails its checks first
+    bad = _lib.PZ_ERROR_INVALID_VALUE
+    for mask, tagged in [(0, 1), (0x20, 1), (0x3F, 1), (0x03, 0), (0x1F, 0), (0, 0), (0x04, 2)]:
+        assert lib.pz_compress_ex(fake, 100, 0, 16, mask, tagged, fake, 1000, fake, None) == bad
+        assert lib.pz_compressed_size_ex(fake, 100, 0, 16, mask, tagged, fake, None, None) == bad
+        assert lib.pz_decompress_ex(fake, 1000, 0, 16, mask, tagged, fake, 100, None, None) == bad
+
