@@ -49,6 +49,9 @@ def parse():
     p.add_argument("--no-verify", action="store_true")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="run one plain device copy of this many MiB first (HBM counter calibration)")
+    p.add_argument("--variants", action="store_true",
+                   help="also time the codec variants the paper compares PlaneZip with (Fig. 3) "
+                        "on the same tensors and report their ratios")
     return p.parse_args()
 
 
@@ -196,6 +199,8 @@ def main():
         "decompress_raw_gbps": round(it["t"].nbytes / t_dec[i] / 1e9, 1),
     } for i, it in enumerate(items)}
 
+    variants = measure_variants(pz, items, flush, cur) if args.variants else None
+
     out = {
         "metric": "compress & decompress GB/s (raw bytes), % of HBM roofline; ratio = oracle",
         "value": round(value, 2),
@@ -228,7 +233,69 @@ def main():
         "cpu_baseline": cpu,
         "tensors": per_tensor,
     }
+    if variants is not None:
+        out["variants"] = variants
     print(json.dumps(out), flush=True)
+
+
+# The codecs of the paper's comparison (§V-A, Fig. 3) that are defined on the
+# pages, as (candidate mask, tagged, symbol width or None for the tensor's):
+# ZVC alone as in cDMA, BPC's DBX on every block, BX and ZBX alone, PlaneZip,
+# and PlaneZip on BF16 with 32-bit symbols as the original BPC codes blocks.
+VARIANTS = {
+    "ZVC": (0x01, False, None),
+    "BPC (DBX on every block)": (0x02, False, None),
+    "BX": (0x04, False, None),
+    "ZBX": (0x08, False, None),
+    "PlaneZip": (0x1F, True, None),
+    "PlaneZip, 32-bit symbols": (0x1F, True, 32),
+}
+
+
+def measure_variants(pz, items, flush, cur, reps=3):
+    """Ratio and raw GB/s of every variant on the workload's tensors (median
+    of `reps` timed compress and decompress calls per tensor, each after a
+    cache flush), round trip checked."""
+    import torch
+
+    res = {}
+    for name, (mask, tagged, w) in VARIANTS.items():
+        raw = comp = 0
+        tc = td = 0.0
+        per = {}
+        for it in items:
+            t = it["t"]
+            bits = w or t.elem_bits
+            cs, ds = [], []
+            for _ in range(reps):
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+                flush()
+                e[0].record(cur)
+                pz.pz_compress_ex(it["src"], mask, tagged, t.dtype, bits, it["stream"], it["nbytes"])
+                e[1].record(cur)
+                torch.cuda.synchronize()
+                n = int(it["nbytes"].item())
+                flush()
+                e[2].record(cur)
+                pz.pz_decompress_ex(it["stream"], n, t.nbytes, t.dtype, bits, mask, tagged,
+                                    it["out"], it["status"])
+                e[3].record(cur)
+                torch.cuda.synchronize()
+                assert int(it["status"].item()) == 0 and torch.equal(it["out"], it["src"]), name
+                cs.append(e[0].elapsed_time(e[1]) / 1e3)
+                ds.append(e[2].elapsed_time(e[3]) / 1e3)
+            c, d = float(np.median(cs)), float(np.median(ds))
+            raw += t.nbytes
+            comp += n
+            tc += c
+            td += d
+            per[t.name] = round(t.nbytes / n, 4)
+        res[name] = {"ratio": round(raw / comp, 4), "ratio_per_tensor": per,
+                     "compress_raw_gbps": round(raw / tc / 1e9, 1),
+                     "decompress_raw_gbps": round(raw / td / 1e9, 1)}
+        log(f"variant {name}: ratio {raw / comp:.3f}, compress {raw / tc / 1e9:.0f} GB/s, "
+            f"decompress {raw / td / 1e9:.0f} GB/s")
+    return res
 
 
 # The sources each kernel is built from: counters taken for a kernel stay
