@@ -13,16 +13,24 @@
  * Conventions for every entry point:
  *   - All data pointers are device pointers (hipMalloc'd memory or a torch
  *     CUDA/HIP tensor's data_ptr()), owned by the caller, and must be 16-byte
- *     aligned. The library allocates temporary device scratch per call with
- *     hipMallocAsync on the given stream and frees it the same way.
+ *     aligned.
+ *   - Device scratch (look-back words, a tile counter, per-call offsets) is
+ *     kept by the library, one buffer per (device, stream), and reused by the
+ *     calls on that stream, so a call normally allocates and clears nothing.
+ *     A buffer grows, with hipFreeAsync / hipMallocAsync on its stream, when a
+ *     call needs more; buffers live until the process ends (a few tens of
+ *     bytes per 4 KB chunk of the largest tensor seen on the stream). A
+ *     stream handle that is destroyed and handed out again is taken for the
+ *     same stream: finish the PlaneZip work of a stream before destroying it.
  *   - `stream` is a hipStream_t (NULL means the null stream). Every call only
  *     enqueues work and returns; results written to device memory are valid
  *     once the stream has been synchronized.
  *   - Errors that the host can see (bad arguments, a launch failure) are
  *     returned synchronously and nothing is enqueued. Errors that depend on the
  *     data (a corrupt stream) are written to device memory.
- *   - Calls on different streams are independent; the library keeps no state
- *     between calls.
+ *   - Calls on different streams are independent (each stream has its own
+ *     scratch); apart from that scratch, the library keeps no state between
+ *     calls. The calls are safe to make from several host threads.
  */
 #ifndef PLANEZIP_H
 #define PLANEZIP_H

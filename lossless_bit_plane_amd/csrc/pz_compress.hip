@@ -471,7 +471,7 @@ template <int W>
 __global__ __launch_bounds__(kGroupThreads, 4) void compress_kernel(
     const uint8_t *__restrict__ src, uint64_t raw_bytes, uint64_t nchunks, uint64_t ntiles,
     uint8_t *__restrict__ dst, uint64_t *__restrict__ out_bytes, uint64_t *status,
-    uint32_t *tile_counter, Mode mode) {
+    uint32_t *tile_counter, uint32_t counter_base, uint32_t epoch, Mode mode) {
   constexpr int N = 1024 / W;
   constexpr uint32_t R = W == 16 ? 4 : 5;
   using PT = typename std::conditional<W == 16, uint64_t, uint32_t>::type;
@@ -489,7 +489,7 @@ __global__ __launch_bounds__(kGroupThreads, 4) void compress_kernel(
 
   const uint32_t t = threadIdx.x, lane = lane_id();
   const uint32_t wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform: a scalar
-  if (t == 0) group_tile = atomicAdd(tile_counter, 1u);
+  if (t == 0) group_tile = atomicAdd(tile_counter, 1u) - counter_base;
   __syncthreads();
   const uint32_t tile = group_tile;
   if (tile >= ntiles) return;
@@ -680,7 +680,7 @@ __global__ __launch_bounds__(kGroupThreads, 4) void compress_kernel(
       if (lane >= (uint32_t)o) inc += v;
     }
     agg = __shfl(inc, kGroupChunks - 1, 64);
-    lookback_publish(status, tile, agg);
+    lookback_publish(status, tile, agg, epoch);
   }
 
   // --- 5. Emission into the chunk buffers (payload bit i at buffer bit i). ---
@@ -806,7 +806,7 @@ __global__ __launch_bounds__(kGroupThreads, 4) void compress_kernel(
 
   // Device-wide payload offsets of the group's chunks.
   if (wave == 0) {
-    const uint64_t before = lookback_resolve(status, tile, agg);
+    const uint64_t before = lookback_resolve(status, tile, agg, epoch);
     if (lane < (uint32_t)kGroupChunks) chunk_pay[lane] = 2 * nchunks + before + (inc - l);
     if (tile == ntiles - 1 && lane == 0) *out_bytes = 2 * nchunks + before + agg;
   }
@@ -906,31 +906,28 @@ hipError_t launch_size(int w, const uint8_t *src, uint64_t raw_bytes, uint32_t c
   return hipGetLastError();
 }
 
+ScratchNeed compress_scratch_need(uint64_t raw_bytes) {
+  const uint64_t nchunks = (raw_bytes + kChunkBytes - 1) / kChunkBytes;
+  const uint64_t ntiles = (nchunks + kGroupChunks - 1) / kGroupChunks;
+  return ScratchNeed{(size_t)ntiles, 0, (uint32_t)ntiles};
+}
+
 hipError_t launch_compress(int w, const uint8_t *src, uint64_t raw_bytes, uint32_t codec_mask,
-                           int tagged, uint8_t *dst, uint64_t *out_bytes, hipStream_t stream) {
+                           int tagged, uint8_t *dst, uint64_t *out_bytes, const Scratch &scratch,
+                           hipStream_t stream) {
   const uint64_t nchunks = (raw_bytes + kChunkBytes - 1) / kChunkBytes;
   if (nchunks == 0) return fill_u64(out_bytes, 1, 0, stream);
   const uint64_t ntiles = (nchunks + kGroupChunks - 1) / kGroupChunks;
-  const uint64_t groups = ntiles;
   const Mode mode = make_mode(w, codec_mask, tagged);
-  // Scratch: one look-back status word per tile, then the tile counter.
-  const size_t words = (size_t)ntiles + 1;
-  uint64_t *scratch = nullptr;
-  hipError_t e = hipMallocAsync(reinterpret_cast<void **>(&scratch), words * sizeof(uint64_t), stream);
-  if (e != hipSuccess) return e;
-  e = fill_u64(scratch, words, 0, stream);
-  if (e == hipSuccess) {
-    uint32_t *counter = reinterpret_cast<uint32_t *>(scratch + ntiles);
-    if (w == 16)
-      hipLaunchKernelGGL(compress_kernel<16>, dim3((unsigned)groups), dim3(kGroupThreads), 0,
-                         stream, src, raw_bytes, nchunks, ntiles, dst, out_bytes, scratch, counter, mode);
-    else
-      hipLaunchKernelGGL(compress_kernel<32>, dim3((unsigned)groups), dim3(kGroupThreads), 0,
-                         stream, src, raw_bytes, nchunks, ntiles, dst, out_bytes, scratch, counter, mode);
-    e = hipGetLastError();
-  }
-  hipError_t f = hipFreeAsync(scratch, stream);
-  return e != hipSuccess ? e : f;
+  if (w == 16)
+    hipLaunchKernelGGL(compress_kernel<16>, dim3((unsigned)ntiles), dim3(kGroupThreads), 0, stream, src,
+                       raw_bytes, nchunks, ntiles, dst, out_bytes, scratch.words, scratch.counter,
+                       scratch.counter_base, scratch.epoch, mode);
+  else
+    hipLaunchKernelGGL(compress_kernel<32>, dim3((unsigned)ntiles), dim3(kGroupThreads), 0, stream, src,
+                       raw_bytes, nchunks, ntiles, dst, out_bytes, scratch.words, scratch.counter,
+                       scratch.counter_base, scratch.epoch, mode);
+  return hipGetLastError();
 }
 
 }  // namespace pz

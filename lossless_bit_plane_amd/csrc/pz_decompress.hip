@@ -329,7 +329,8 @@ template <int W, int G>
 __global__ __launch_bounds__(kLocateChunks * G) void locate_kernel(
     const uint8_t *__restrict__ src, uint64_t comp_bytes, uint64_t raw_bytes, uint64_t nchunks,
     uint64_t ntiles, uint64_t *__restrict__ chunk_off, uint16_t *__restrict__ block_off,
-    int32_t *status_out, uint64_t *lb_status, uint32_t *tile_counter, DMode mode) {
+    uint32_t *err, uint32_t epoch, uint64_t *lb_status, uint32_t *tile_counter, uint32_t counter_base,
+    DMode mode) {
   constexpr int kWaves = G;  // 64 chunks x G lanes
   __shared__ uint32_t lds[kLocateChunks * kRingRegion];
   __shared__ uint64_t wave_sum[kWaves];
@@ -337,7 +338,7 @@ __global__ __launch_bounds__(kLocateChunks * G) void locate_kernel(
   __shared__ uint32_t group_tile;
   const uint32_t t = threadIdx.x, lane = lane_id(), ql = t & (G - 1);
   const uint32_t wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  if (t == 0) group_tile = atomicAdd(tile_counter, 1u);
+  if (t == 0) group_tile = atomicAdd(tile_counter, 1u) - counter_base;
   __syncthreads();
   const uint32_t tile = group_tile;
   if (tile >= ntiles) return;
@@ -354,10 +355,10 @@ __global__ __launch_bounds__(kLocateChunks * G) void locate_kernel(
     uint64_t agg = 0;
 #pragma unroll
     for (int k = 0; k < kWaves; ++k) agg += wave_sum[k];
-    const uint64_t before = lookback(lb_status, tile, agg);
+    const uint64_t before = lookback(lb_status, tile, agg, epoch);
     if (lane == 0) {
       tile_before = before;
-      if (tile == ntiles - 1 && 2 * nchunks + before + agg != comp_bytes) *status_out = kStatusCorrupt;
+      if (tile == ntiles - 1 && 2 * nchunks + before + agg != comp_bytes) atomicMax(err, epoch);
     }
   }
   __syncthreads();
@@ -386,7 +387,7 @@ __global__ __launch_bounds__(kLocateChunks * G) void locate_kernel(
   if (c < nchunks && ql == 0) {
     const bool chunk_bad = header_bad || (coded && !parsed);
     chunk_off[c] = chunk_bad ? kBadChunk : off;
-    if (chunk_bad) *status_out = kStatusCorrupt;
+    if (chunk_bad) atomicMax(err, epoch);
   }
 }
 
@@ -515,7 +516,7 @@ template <int W>
 __global__ __launch_bounds__(kGroupThreads) void decode_kernel(
     const uint8_t *__restrict__ src, uint64_t comp_bytes, uint64_t raw_bytes, uint64_t nchunks,
     const uint64_t *__restrict__ chunk_off, const uint16_t *__restrict__ block_off,
-    uint8_t *__restrict__ dst, DMode mode) {
+    uint8_t *__restrict__ dst, const uint32_t *err, uint32_t epoch, int32_t *status, DMode mode) {
   constexpr int N = 1024 / W;
   constexpr uint32_t WMASK = W == 16 ? 0xFFFFu : 0xFFFFFFFFu;
   __shared__ __attribute__((aligned(16))) uint32_t lds[kDecodeLdsDwords];
@@ -528,6 +529,10 @@ __global__ __launch_bounds__(kGroupThreads) void decode_kernel(
   const uint32_t wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const uint64_t gtile = blockIdx.x;
   if (gtile * kDecodeChunks >= nchunks) return;
+  // The call's status: locate, which ran before this kernel, marked a
+  // corrupt stream with the call's epoch.
+  if (gtile == 0 && t == 0 && status)
+    *status = __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch ? kStatusCorrupt : 0;
   const uint64_t gblock0 = gtile * kGroupThreads;  // first block of the group
 
   // Every thread's metadata at once: its chunk's payload offset and header
@@ -791,68 +796,54 @@ __global__ __launch_bounds__(kGroupThreads) void decode_kernel(
   }
 }
 
-// Clears the look-back words and the tile counter, and sets the status word,
-// in one launch.
-__global__ void clear_scratch_kernel(uint64_t *words, uint64_t n, int32_t *status, int32_t value) {
-  const uint64_t i0 = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (uint64_t i = i0; i < n; i += (uint64_t)gridDim.x * blockDim.x) words[i] = 0;
-  if (i0 == 0) *status = value;
+// Sets a decompress call's status when it launches no kernel (an empty
+// tensor).
+__global__ void set_status_kernel(int32_t *status, int32_t value) { *status = value; }
+
+ScratchNeed decompress_scratch_need(uint64_t raw_bytes) {
+  const uint64_t nchunks = (raw_bytes + kChunkBytes - 1) / kChunkBytes;
+  const uint64_t ntiles_a = (nchunks + kLocateChunks - 1) / kLocateChunks;
+  // Per call: chunk offsets (8 bytes per chunk), then block offsets (64 bytes
+  // per chunk, 16-byte aligned).
+  const size_t extra = (size_t)(((nchunks + 1) & ~1ull) * 8 + nchunks * kBlocksPerChunk * 2);
+  return ScratchNeed{(size_t)ntiles_a, extra, (uint32_t)ntiles_a};
 }
 
 hipError_t launch_decompress(int w, const uint8_t *src, uint64_t comp_bytes, uint32_t codec_mask,
                              int tagged, uint8_t *dst, uint64_t raw_bytes, int32_t *status,
-                             hipStream_t stream) {
+                             const Scratch &scratch, hipStream_t stream) {
   const DMode mode = make_dmode(w, codec_mask, tagged);
   const uint64_t nchunks = (raw_bytes + kChunkBytes - 1) / kChunkBytes;
+  if (nchunks == 0) {
+    if (!status) return hipSuccess;
+    hipLaunchKernelGGL(set_status_kernel, dim3(1), dim3(1), 0, stream, status,
+                       comp_bytes != 0 ? kStatusCorrupt : 0);
+    return hipGetLastError();
+  }
   const uint64_t ntiles_a = (nchunks + kLocateChunks - 1) / kLocateChunks;
-  // Scratch (8-byte words): chunk offsets, block offsets, look-back status,
-  // tile counter, and a status word when the caller passes none.
-  const uint64_t w_off = (nchunks + 1) & ~1ull;  // keeps the block offsets 16-byte aligned
-  const uint64_t w_boff = (nchunks * kBlocksPerChunk * 2 + 7) / 8;
-  const uint64_t w_lb = ntiles_a;
-  const size_t words = (size_t)(w_off + w_boff + w_lb + 2);
-  uint64_t *scratch = nullptr;
-  hipError_t e = hipMallocAsync(reinterpret_cast<void **>(&scratch), words * sizeof(uint64_t), stream);
+  uint64_t *chunk_off = reinterpret_cast<uint64_t *>(scratch.extra);
+  uint16_t *block_off = reinterpret_cast<uint16_t *>(scratch.extra + ((nchunks + 1) & ~1ull) * 8);
+  const dim3 grid_a((unsigned)ntiles_a);
+  if (w == 16)
+    hipLaunchKernelGGL((locate_kernel<16, kLocateLanes>), grid_a, dim3(kLocateThreads), 0, stream, src,
+                       comp_bytes, raw_bytes, nchunks, ntiles_a, chunk_off, block_off, scratch.err,
+                       scratch.epoch, scratch.words, scratch.counter, scratch.counter_base, mode);
+  else
+    hipLaunchKernelGGL((locate_kernel<32, kLocateLanes>), grid_a, dim3(kLocateThreads), 0, stream, src,
+                       comp_bytes, raw_bytes, nchunks, ntiles_a, chunk_off, block_off, scratch.err,
+                       scratch.epoch, scratch.words, scratch.counter, scratch.counter_base, mode);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  uint64_t *chunk_off = scratch;
-  uint16_t *block_off = reinterpret_cast<uint16_t *>(scratch + w_off);
-  uint64_t *lb_status = scratch + w_off + w_boff;
-  uint32_t *counter = reinterpret_cast<uint32_t *>(lb_status + w_lb);
-  int32_t *own_status = reinterpret_cast<int32_t *>(lb_status + w_lb + 1);
-  int32_t *st = status ? status : own_status;
-
-  {
-    const int32_t first_status = (nchunks == 0 && comp_bytes != 0) ? kStatusCorrupt : 0;
-    const uint64_t n = w_lb + 1;
-    const uint64_t groups = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
-    hipLaunchKernelGGL(clear_scratch_kernel, dim3((unsigned)groups), dim3(256), 0, stream, lb_status, n,
-                       st, first_status);
-    e = hipGetLastError();
-  }
-  if (e == hipSuccess && nchunks != 0) {
-    const dim3 grid_a((unsigned)ntiles_a);
-    if (w == 16)
-      hipLaunchKernelGGL((locate_kernel<16, kLocateLanes>), grid_a, dim3(kLocateThreads), 0, stream, src,
-                         comp_bytes, raw_bytes, nchunks, ntiles_a, chunk_off, block_off, st, lb_status, counter,
-                         mode);
-    else
-      hipLaunchKernelGGL((locate_kernel<32, kLocateLanes>), grid_a, dim3(kLocateThreads), 0, stream, src,
-                         comp_bytes, raw_bytes, nchunks, ntiles_a, chunk_off, block_off, st, lb_status, counter,
-                         mode);
-    e = hipGetLastError();
-    if (e == hipSuccess) {
-      const uint64_t groups_b = (nchunks + kDecodeChunks - 1) / kDecodeChunks;
-      if (w == 16)
-        hipLaunchKernelGGL(decode_kernel<16>, dim3((unsigned)groups_b), dim3(kGroupThreads), 0,
-                           stream, src, comp_bytes, raw_bytes, nchunks, chunk_off, block_off, dst, mode);
-      else
-        hipLaunchKernelGGL(decode_kernel<32>, dim3((unsigned)groups_b), dim3(kGroupThreads), 0,
-                           stream, src, comp_bytes, raw_bytes, nchunks, chunk_off, block_off, dst, mode);
-      e = hipGetLastError();
-    }
-  }
-  hipError_t f = hipFreeAsync(scratch, stream);
-  return e != hipSuccess ? e : f;
+  const uint64_t groups_b = (nchunks + kDecodeChunks - 1) / kDecodeChunks;
+  if (w == 16)
+    hipLaunchKernelGGL(decode_kernel<16>, dim3((unsigned)groups_b), dim3(kGroupThreads), 0, stream, src,
+                       comp_bytes, raw_bytes, nchunks, chunk_off, block_off, dst, scratch.err, scratch.epoch,
+                       status, mode);
+  else
+    hipLaunchKernelGGL(decode_kernel<32>, dim3((unsigned)groups_b), dim3(kGroupThreads), 0, stream, src,
+                       comp_bytes, raw_bytes, nchunks, chunk_off, block_off, dst, scratch.err, scratch.epoch,
+                       status, mode);
+  return hipGetLastError();
 }
 
 }  // namespace pz

@@ -31,10 +31,16 @@ constexpr int kWaveLdsDwords = 2 * kChunkBufDwords > kWave * kLaneStride
                                    ? 2 * kChunkBufDwords
                                    : kWave * kLaneStride;
 
-// Look-back status words: flag in the top two bits, value below.
+// Look-back status words: a flag in the top two bits, then the epoch of the
+// call that wrote the word (22 bits), then the value (40 bits: streams of up
+// to 1 TiB). A word of another epoch reads as not ready, so the words that a
+// reused scratch buffer keeps from earlier calls need no clearing.
 constexpr uint64_t kFlagAggregate = 1ull << 62;
 constexpr uint64_t kFlagPrefix = 2ull << 62;
-constexpr uint64_t kValueMask = kFlagAggregate - 1;
+constexpr int kEpochShift = 40;
+constexpr uint64_t kEpochBits = (1ull << 22) - 1;
+constexpr uint64_t kValueMask = (1ull << kEpochShift) - 1;
+constexpr uint32_t kEpochMax = (uint32_t)kEpochBits;
 
 constexpr uint64_t kBadChunk = ~0ull;
 
@@ -195,19 +201,23 @@ PZ_DEV uint32_t acquire_tile(uint32_t *counter) {
 // publishes its inclusive prefix); lookback_resolve walks back over the
 // predecessors 64 at a time until it meets an inclusive prefix, publishes this
 // tile's inclusive prefix and returns the exclusive prefix of `agg`.
-PZ_DEV void lookback_publish(uint64_t *status, uint32_t tile, uint64_t agg) {
-  if (lane_id() == 0) atomic_store_agent(&status[tile], (tile == 0 ? kFlagPrefix : kFlagAggregate) | agg);
+PZ_DEV void lookback_publish(uint64_t *status, uint32_t tile, uint64_t agg, uint32_t epoch) {
+  if (lane_id() == 0)
+    atomic_store_agent(&status[tile],
+                       (tile == 0 ? kFlagPrefix : kFlagAggregate) | ((uint64_t)epoch << kEpochShift) | agg);
 }
 
-PZ_DEV uint64_t lookback_resolve(uint64_t *status, uint32_t tile, uint64_t agg) {
+PZ_DEV uint64_t lookback_resolve(uint64_t *status, uint32_t tile, uint64_t agg, uint32_t epoch) {
   if (tile == 0) return 0;
   const uint32_t lane = lane_id();
+  const uint64_t stamp = (uint64_t)epoch << kEpochShift;
   uint64_t excl = 0;
   int64_t base = (int64_t)tile - 1;
   while (true) {
     const int64_t idx = base - (int64_t)lane;
-    const uint64_t st = idx >= 0 ? atomic_load_agent(&status[idx]) : kFlagPrefix;
-    const uint64_t flag = st >> 62;
+    const uint64_t st = idx >= 0 ? atomic_load_agent(&status[idx]) : (kFlagPrefix | stamp);
+    const bool current = ((st >> kEpochShift) & kEpochBits) == epoch;
+    const uint64_t flag = current ? st >> 62 : 0;
     const uint64_t not_ready = __ballot(flag == 0);
     const uint64_t prefix = __ballot(flag == 2);
     const uint64_t first = prefix & (~prefix + 1);         // nearest inclusive prefix
@@ -221,13 +231,13 @@ PZ_DEV uint64_t lookback_resolve(uint64_t *status, uint32_t tile, uint64_t agg) 
     if (prefix) break;
     base -= 64;
   }
-  if (lane == 0) atomic_store_agent(&status[tile], kFlagPrefix | (excl + agg));
+  if (lane == 0) atomic_store_agent(&status[tile], kFlagPrefix | stamp | (excl + agg));
   return excl;
 }
 
-PZ_DEV uint64_t lookback(uint64_t *status, uint32_t tile, uint64_t agg) {
-  lookback_publish(status, tile, agg);
-  return lookback_resolve(status, tile, agg);
+PZ_DEV uint64_t lookback(uint64_t *status, uint32_t tile, uint64_t agg, uint32_t epoch) {
+  lookback_publish(status, tile, agg, epoch);
+  return lookback_resolve(status, tile, agg, epoch);
 }
 
 // Orders this wave's LDS accesses before and after (all lanes of a wave run

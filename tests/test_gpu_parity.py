@@ -227,3 +227,36 @@ def test_corrupt_streams_status_matches_oracle(pz):
             assert np.array_equal(back, oracle.decompress(s, data.size, 16))
         agree += 1
     assert agree == len(cases)
+
+
+def test_scratch_reuse_across_calls(pz):
+    """Back-to-back calls on one stream reuse its scratch (epoch-tagged
+    look-back words, a tile counter that keeps counting): sizes that grow and
+    shrink, a corrupt stream between good ones (its status must not leak into
+    the next call), and a second stream interleaved with the first."""
+    import torch
+
+    (base,) = pzinputs.config1()
+    sizes = [base.nbytes, 4096 * 3 + 5, 700_000, 77, base.nbytes - 4096, 4096 * 70, 1]
+    streams = [torch.cuda.current_stream(), torch.cuda.Stream()]
+    for k, n in enumerate(sizes):
+        data = base.data[-n:].copy() if k % 2 else base.data[:n].copy()
+        t = pzinputs.Tensor(f"reuse_{k}", data, 0, 16)
+        s = streams[k % 2]
+        with torch.cuda.stream(s):
+            src = _dev(data)
+            dst, nbytes = pz.pz_compress(src, 0, 16, stream=s)
+            s.synchronize()
+            g = _host(dst[: int(nbytes.item())])
+            assert np.array_equal(g, oracle.compress(data, 16)), t.name
+            if k == 3:
+                bad = g.copy()
+                bad[-1] ^= 0x80  # padding bit or payload bit: either way corrupt or a different decode
+                o = oracle.decompress_status(bad, n, 16)
+                out, status = pz.pz_decompress(_dev(bad), bad.size, n, 0, 16, stream=s)
+                s.synchronize()
+                assert int(status.item()) == (0 if o == oracle.OK else 3)
+            out, status = pz.pz_decompress(_dev(g), g.size, n, 0, 16, stream=s)
+            s.synchronize()
+            assert int(status.item()) == 0, t.name
+            assert np.array_equal(_host(out[:n]), data), t.name
