@@ -406,6 +406,19 @@ struct LdsBits {
   PZ_DEV uint64_t peek64(uint32_t pos) const {
     return (uint64_t)peek(pos) | ((uint64_t)peek(pos + 32) << 32);
   }
+  // A plane code's window and the 64 bits after its first bit (the payload
+  // of a verbatim code), from one read of three dwords.
+  PZ_DEV void peek_code(uint32_t pos, uint32_t &win, uint64_t &after) const {
+    const uint32_t a = lead + pos;
+    uint32_t q = a >> 5;
+    q = q > (uint32_t)kChunkBufDwords - 3 ? (uint32_t)kChunkBufDwords - 3 : q;
+    const uint32_t d0 = buf[q], d1 = buf[q + 1], d2 = buf[q + 2];
+    const uint32_t sh = (a & 31u) + 1u;  // 1..32
+    win = funnel(d1, d0, a & 31u);
+    const uint32_t lo = (uint32_t)((((uint64_t)d1 << 32) | d0) >> sh);
+    const uint32_t hi = (uint32_t)((((uint64_t)d2 << 32) | d1) >> sh);
+    after = (uint64_t)lo | ((uint64_t)hi << 32);
+  }
 };
 
 // Reads the plane code of K planes (top plane first) and leaves the planes in
@@ -431,13 +444,11 @@ PZ_DEV void read_planes(const LdsBits &in, uint32_t &pos, uint32_t (&t)[32], int
   for (int j = W; j >= 0; --j) {
     const bool live = active && j < K;
     const bool fresh = live && run == 0;
-    const uint32_t win = in.peek(pos);
+    uint32_t win;
+    uint64_t after;
+    in.peek_code(pos, win, after);
     const uint32_t tz = min((uint32_t)(__ffs(win) - 1), 5u);  // 5: five or more zeros
-    PT verb;
-    if constexpr (W == 16)
-      verb = (PT)in.peek64(pos + 1) & ones;
-    else
-      verb = (PT)in.peek(pos + 1) & ones;
+    const PT verb = (PT)after & ones;
     const PT one_or_pair = (((win >> 4) & 1u) ? (PT)1 : (PT)3) << ((win >> 5) & pmask);
     PT x = tz >= 5 ? ones : (PT)0;
     x = tz == 0 ? verb : x;
