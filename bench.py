@@ -200,6 +200,7 @@ def main():
     } for i, it in enumerate(items)}
 
     variants = measure_variants(pz, items, flush, cur) if args.variants else None
+    size_only = measure_size_only(pz, items, flush, cur)
 
     out = {
         "metric": "compress & decompress GB/s (raw bytes), % of HBM roofline; ratio = oracle",
@@ -232,6 +233,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "tensors": per_tensor,
+        "size_only": size_only,
     }
     if variants is not None:
         out["variants"] = variants
@@ -295,6 +297,52 @@ def measure_variants(pz, items, flush, cur, reps=3):
                      "decompress_raw_gbps": round(raw / td / 1e9, 1)}
         log(f"variant {name}: ratio {raw / comp:.3f}, compress {raw / tc / 1e9:.0f} GB/s, "
             f"decompress {raw / td / 1e9:.0f} GB/s")
+    return res
+
+
+def measure_size_only(pz, items, flush, cur, stride=4, reps=5):
+    """The runtime's size measurements on the workload (PlaneZip §III-B: a
+    profiling iteration sizes tensors without keeping a stream): the exact
+    size pass and the sampled one over every `stride`-th chunk, as raw GB/s
+    (median of `reps` calls per tensor, each after a cache flush), with the
+    sampled estimate's error against the exact size."""
+    import torch
+
+    sample = torch.zeros(2, dtype=torch.int64, device=items[0]["src"].device)
+    res = {}
+    for name in ("exact", "sampled"):
+        raw = comp = est = 0
+        t_total = 0.0
+        for it in items:
+            t = it["t"]
+            ts = []
+            for _ in range(reps):
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                flush()
+                e[0].record(cur)
+                if name == "exact":
+                    pz.pz_compressed_size(it["src"], t.dtype, t.elem_bits)
+                else:
+                    out, _ = pz.pz_compressed_size_sampled(it["src"], stride, t.dtype, t.elem_bits)
+                e[1].record(cur)
+                torch.cuda.synchronize()
+                ts.append(e[0].elapsed_time(e[1]) / 1e3)
+            if name == "exact":
+                n, _ = pz.pz_compressed_size(it["src"], t.dtype, t.elem_bits)
+                size = int(n.item())
+                assert size == it["comp"], "size pass disagrees with the stream length"
+            else:
+                s_comp, s_raw = (int(v) for v in out.cpu().tolist())
+                size = t.nbytes * s_comp / s_raw
+            raw += t.nbytes
+            comp += it["comp"]
+            est += size
+            t_total += float(np.median(ts))
+        res[name] = {"raw_gbps": round(raw / t_total / 1e9, 1), "us": round(t_total * 1e6, 1)}
+        if name == "sampled":
+            res[name].update(stride=stride, estimate_bytes=round(est), exact_bytes=comp,
+                             estimate_err_pct=round(100 * (est - comp) / comp, 4))
+        log(f"size pass {name}: {raw / t_total / 1e9:.0f} GB/s ({t_total * 1e6:.0f} us)")
     return res
 
 

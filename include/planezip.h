@@ -135,6 +135,63 @@ pz_status_t pz_decompress_ex(const void *d_src, size_t comp_bytes, int dtype,
                              void *d_dst, size_t raw_bytes, int32_t *d_status,
                              void *stream);
 
+/* Sampled size: the pz_compressed_size measurement over chunks 0, stride,
+ * 2*stride, ... only (the paper's methodology sizes tensors above 32 MB on
+ * every fourth 4 KB chunk, §IV "Tensor capture"), at 1/stride of the work.
+ *   chunk_stride  >= 1; 1 sizes every chunk
+ *   d_sample      two uint64: [0] the stream bytes of the sampled chunks
+ *                 (2 header bytes + payload each), [1] their raw bytes; the
+ *                 estimated stream size of the tensor is
+ *                 raw_bytes * d_sample[0] / d_sample[1] (exact for stride 1)
+ *   d_sample_lens nullable; ceil(PZ_NUM_CHUNKS(raw_bytes) / chunk_stride)
+ *                 uint16 header values of the sampled chunks, in order
+ * A stride of 0 or a misaligned d_sample return PZ_ERROR_INVALID_VALUE. */
+pz_status_t pz_compressed_size_sampled(const void *d_src, size_t raw_bytes,
+                                       int dtype, int elem_bits,
+                                       uint32_t chunk_stride, uint64_t *d_sample,
+                                       uint16_t *d_sample_lens, void *stream);
+
+/* Per-tensor compressibility predictor (§III-B "Compressibility Predictor",
+ * accuracy in §V-B and Table IV). Host memory only; no device work. A saved
+ * tensor is named by a 64-bit signature, normally PZ_SIGNATURE(position of
+ * its producing operator in the iteration's operator sequence, output slot).
+ * The table keeps one measurement (raw bytes, compressed bytes) per
+ * signature: the size the engine reported for a swap (d_out_bytes of
+ * pz_compress), or a profiling measurement (pz_compressed_size, or the two
+ * words of pz_compressed_size_sampled). A new measurement overwrites the
+ * previous one. Every call is safe from several host threads. */
+typedef struct pz_predictor pz_predictor_t;
+
+#define PZ_SIGNATURE(op_index, output_slot) \
+    ((((uint64_t)(op_index)) << 16) | ((uint64_t)(output_slot) & 0xFFFFu))
+
+/* A table for up to `capacity` signatures ("a few hundred entries"); NULL for
+ * a capacity of 0 or above 2^40, or when host memory runs out. */
+pz_predictor_t *pz_predictor_create(size_t capacity);
+void pz_predictor_destroy(pz_predictor_t *pred);
+
+/* Records that a tensor of this signature took comp_bytes for raw_bytes.
+ * raw_bytes and comp_bytes must be >= 1 and comp_bytes at most
+ * PZ_MAX_COMPRESSED_BYTES(raw_bytes) (else PZ_ERROR_INVALID_VALUE); a new
+ * signature in a full table returns PZ_ERROR_INSUFFICIENT_BUFFER and changes
+ * nothing. */
+pz_status_t pz_predictor_update(pz_predictor_t *pred, uint64_t signature,
+                                uint64_t raw_bytes, uint64_t comp_bytes);
+
+/* Predicted compressed bytes of a tensor of this signature and raw_bytes:
+ * ceil(raw_bytes * comp / raw) of the signature's last measurement, or
+ * raw_bytes (a ratio of 1) while it has none. *measured (nullable) is set to
+ * 1 or 0 accordingly. A prediction above 2^64-1 returns
+ * PZ_ERROR_INVALID_VALUE. */
+pz_status_t pz_predictor_predict(pz_predictor_t *pred, uint64_t signature,
+                                 uint64_t raw_bytes, uint64_t *pred_bytes,
+                                 int *measured);
+
+/* Signatures held, and forgetting them all (e.g. when the operator sequence
+ * changes and signatures are renumbered). */
+size_t pz_predictor_entries(pz_predictor_t *pred);
+void pz_predictor_clear(pz_predictor_t *pred);
+
 /* Diagnostics of the size pass, per 128-byte block (nblocks =
  * ceil(raw_bytes/128)): d_sizes (nullable) receives the five candidate sizes
  * in bits (ZVC, DBX, BX, ZBX, RAW; payload only, no tag) as 5*nblocks

@@ -5,12 +5,18 @@ device memory and streams. The codec is the one of the PlaneZip paper
 (§III-A, Fig. 2): per 128-byte block the smallest of ZVC, DBX, BX, ZBX and raw
 under a 3-bit tag, 4 KB chunks with 16-bit headers; bit layout FORMAT.md v1.
 The ``*_ex`` calls run the single-codec and reduced-candidate variants the
-paper compares PlaneZip with (§V-A, Fig. 3).
+paper compares PlaneZip with (§V-A, Fig. 3); ``pz_compressed_size_sampled``
+and the ``pz_predictor_*`` table are the runtime's size measurement and
+per-tensor predictor (§III-B).
 """
 from .codec import (  # noqa: F401
     BF16, FP32, OTHER, CODEC_ALL, CODEC_BX, CODEC_DBX, CODEC_RAW, CODEC_ZBX, CODEC_ZVC,
     max_compressed_bytes, num_chunks,
     pz_block_sizes, pz_compress, pz_compressed_size, pz_decompress,
-    pz_compress_ex, pz_compressed_size_ex, pz_decompress_ex,
+    pz_compress_ex, pz_compressed_size_ex, pz_decompress_ex, pz_compressed_size_sampled,
     compress, decompress,
+)
+from .predictor import (  # noqa: F401
+    Predictor, signature, pz_predictor_create, pz_predictor_destroy, pz_predictor_update,
+    pz_predictor_predict, pz_predictor_entries, pz_predictor_clear,
 )

@@ -16,7 +16,9 @@ PZ_ERROR_CORRUPT_STREAM = 3
 PZ_ERROR_HIP = 4
 
 EXPORTS = ("pz_compressed_size", "pz_compress", "pz_decompress", "pz_block_sizes", "pz_status_string",
-           "pz_compressed_size_ex", "pz_compress_ex", "pz_decompress_ex")
+           "pz_compressed_size_ex", "pz_compress_ex", "pz_decompress_ex", "pz_compressed_size_sampled",
+           "pz_predictor_create", "pz_predictor_destroy", "pz_predictor_update", "pz_predictor_predict",
+           "pz_predictor_entries", "pz_predictor_clear")
 
 
 def _load():
@@ -34,8 +36,21 @@ def _load():
     lib.pz_compressed_size_ex.argtypes = [vp, sz, i, i, u32, i, vp, vp, vp]
     lib.pz_compress_ex.argtypes = [vp, sz, i, i, u32, i, vp, sz, vp, vp]
     lib.pz_decompress_ex.argtypes = [vp, sz, i, i, u32, i, vp, sz, vp, vp]
+    lib.pz_compressed_size_sampled.argtypes = [vp, sz, i, i, u32, vp, vp, vp]
+    u64 = ctypes.c_uint64
+    lib.pz_predictor_create.argtypes = [sz]
+    lib.pz_predictor_create.restype = vp
+    lib.pz_predictor_destroy.argtypes = [vp]
+    lib.pz_predictor_destroy.restype = None
+    lib.pz_predictor_update.argtypes = [vp, u64, u64, u64]
+    lib.pz_predictor_predict.argtypes = [vp, u64, u64, ctypes.POINTER(u64), ctypes.POINTER(i)]
+    lib.pz_predictor_entries.argtypes = [vp]
+    lib.pz_predictor_entries.restype = sz
+    lib.pz_predictor_clear.argtypes = [vp]
+    lib.pz_predictor_clear.restype = None
     for name in ("pz_compressed_size", "pz_compress", "pz_decompress", "pz_block_sizes",
-                 "pz_compressed_size_ex", "pz_compress_ex", "pz_decompress_ex"):
+                 "pz_compressed_size_ex", "pz_compress_ex", "pz_decompress_ex", "pz_compressed_size_sampled",
+                 "pz_predictor_update", "pz_predictor_predict"):
         getattr(lib, name).restype = ctypes.c_int
     lib.pz_status_string.argtypes = [ctypes.c_int]
     lib.pz_status_string.restype = ctypes.c_char_p

@@ -61,6 +61,21 @@ def pz_compressed_size(src: torch.Tensor, dtype=None, elem_bits=None, chunk_lens
     return out, lens
 
 
+def pz_compressed_size_sampled(src: torch.Tensor, chunk_stride: int = 4, dtype=None, elem_bits=None,
+                               chunk_lens: bool = False, stream=None):
+    """Device int64 tensor (2,): the stream bytes of chunks 0, stride,
+    2*stride, ... and their raw bytes; optionally their int16 (bit pattern of
+    uint16) header values."""
+    dtype, elem_bits = _kind(src, dtype, elem_bits)
+    b = _byte_view(src)
+    out = torch.empty(2, dtype=torch.int64, device=b.device)
+    n = (num_chunks(b.numel()) + chunk_stride - 1) // chunk_stride if chunk_stride > 0 else 0
+    lens = torch.empty(max(n, 1), dtype=torch.int16, device=b.device) if chunk_lens else None
+    check(lib.pz_compressed_size_sampled(_ptr(b), b.numel(), dtype, elem_bits, chunk_stride, _ptr(out),
+                                         _ptr(lens), _stream(stream)), "pz_compressed_size_sampled")
+    return out, (lens[:n] if lens is not None else None)
+
+
 def pz_block_sizes(src: torch.Tensor, dtype=None, elem_bits=None, stream=None):
     """Per-block candidate sizes (int16 view of uint16, shape (nblocks, 5))
     and chosen tags (uint8, nblocks)."""

@@ -140,9 +140,8 @@ pz_status_t pz_compressed_size_ex(const void *d_src, size_t raw_bytes, int dtype
   if (!aligned16(d_src) || (reinterpret_cast<uintptr_t>(d_out_bytes) & 7u) ||
       (reinterpret_cast<uintptr_t>(d_chunk_lens) & 1u))
     return PZ_ERROR_INVALID_VALUE;
-  return from_hip(pz::launch_size(w, static_cast<const uint8_t *>(d_src), raw_bytes, codec_mask, tagged,
-                                  d_out_bytes, d_chunk_lens, nullptr, nullptr,
-                                  static_cast<hipStream_t>(stream)));
+  return from_hip(pz::launch_size(w, static_cast<const uint8_t *>(d_src), raw_bytes, codec_mask, tagged, 1,
+                                  d_out_bytes, nullptr, d_chunk_lens, static_cast<hipStream_t>(stream)));
 }
 
 pz_status_t pz_compressed_size(const void *d_src, size_t raw_bytes, int dtype, int elem_bits,
@@ -151,13 +150,26 @@ pz_status_t pz_compressed_size(const void *d_src, size_t raw_bytes, int dtype, i
                                d_chunk_lens, stream);
 }
 
+pz_status_t pz_compressed_size_sampled(const void *d_src, size_t raw_bytes, int dtype, int elem_bits,
+                                       uint32_t chunk_stride, uint64_t *d_sample, uint16_t *d_sample_lens,
+                                       void *stream) {
+  const int w = symbol_width(dtype, elem_bits);
+  if (w < 0 || chunk_stride == 0 || !d_sample || (raw_bytes && !d_src)) return PZ_ERROR_INVALID_VALUE;
+  if (!aligned16(d_src) || (reinterpret_cast<uintptr_t>(d_sample) & 7u) ||
+      (reinterpret_cast<uintptr_t>(d_sample_lens) & 1u))
+    return PZ_ERROR_INVALID_VALUE;
+  return from_hip(pz::launch_size(w, static_cast<const uint8_t *>(d_src), raw_bytes, PZ_CODEC_ALL, 1,
+                                  chunk_stride, d_sample, d_sample + 1, d_sample_lens,
+                                  static_cast<hipStream_t>(stream)));
+}
+
 pz_status_t pz_block_sizes(const void *d_src, size_t raw_bytes, int dtype, int elem_bits,
                            uint16_t *d_sizes, uint8_t *d_tags, void *stream) {
   const int w = symbol_width(dtype, elem_bits);
   if (w < 0 || (raw_bytes && !d_src)) return PZ_ERROR_INVALID_VALUE;
   if (!aligned16(d_src) || (reinterpret_cast<uintptr_t>(d_sizes) & 1u)) return PZ_ERROR_INVALID_VALUE;
-  return from_hip(pz::launch_size(w, static_cast<const uint8_t *>(d_src), raw_bytes, PZ_CODEC_ALL, 1,
-                                  nullptr, nullptr, d_sizes, d_tags, static_cast<hipStream_t>(stream)));
+  return from_hip(pz::launch_block_sizes(w, static_cast<const uint8_t *>(d_src), raw_bytes, d_sizes, d_tags,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 pz_status_t pz_compress_ex(const void *d_src, size_t raw_bytes, int dtype, int elem_bits,

@@ -304,46 +304,29 @@ PZ_DEV int select_tag(const Sizes &s, int &best_size, uint32_t mask) {
 }
 
 // ---------------------------------------------------------------------------
-// Size pass: chunk lengths (pz_compressed_size) and per-block diagnostics.
+// Per-block diagnostics (pz_block_sizes): every block's five candidate sizes
+// and its tag, one lane per block.
 // ---------------------------------------------------------------------------
 template <int W>
-__global__ __launch_bounds__(kGroupThreads, 4) void size_kernel(
-    const uint8_t *__restrict__ src, uint64_t raw_bytes, uint64_t nchunks,
-    uint64_t *__restrict__ out_bytes, uint16_t *__restrict__ chunk_lens,
-    uint16_t *__restrict__ block_sizes, uint8_t *__restrict__ block_tags, Mode mode) {
-  const uint32_t lane = lane_id();
-  const uint64_t tile = (uint64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
-  if (tile * 2 >= nchunks) return;
-  const uint64_t block = tile * kWave + lane;
-  const uint64_t off = block * kBlockBytes;
-  const bool valid = off < raw_bytes;
+__global__ __launch_bounds__(kGroupThreads, 4) void block_sizes_kernel(
+    const uint8_t *__restrict__ src, uint64_t raw_bytes, uint64_t nblocks,
+    uint16_t *__restrict__ block_sizes, uint8_t *__restrict__ block_tags) {
+  const uint64_t block = (uint64_t)blockIdx.x * kGroupThreads + threadIdx.x;
+  if ((uint64_t)blockIdx.x * kGroupThreads >= nblocks) return;
   uint32_t d[32];
-  load_block(src, raw_bytes, off, d);
+  load_block(src, raw_bytes, block * kBlockBytes, d);
   const int n = (int)count_nonzero<W>(d);
   Sizes s;
   candidate_sizes<W>(d, n, __ballot(n > 0 && n < 1024 / W) != 0, s);
   int best_size;
-  const int tag = select_tag(s, best_size, mode.mask);
-  const uint32_t cost = valid ? 3u * mode.tagged + (uint32_t)best_size : 0u;
-  if (valid && block_sizes) {
+  const int tag = select_tag(s, best_size, 0x1Fu);
+  if (block < nblocks) {
+    if (block_sizes) {
 #pragma unroll
-    for (int t = 0; t < 5; ++t) block_sizes[block * 5 + t] = (uint16_t)s.sz[t];
+      for (int t = 0; t < 5; ++t) block_sizes[block * 5 + t] = (uint16_t)s.sz[t];
+    }
+    if (block_tags) block_tags[block] = (uint8_t)tag;
   }
-  if (valid && block_tags) block_tags[block] = (uint8_t)tag;
-
-  const uint32_t incl = half_inclusive_scan(cost);
-  const uint32_t bits = __shfl(incl, (int)((lane & 32) | 31), 64);
-  const uint64_t chunk = block >> 5;
-  uint32_t len = 0;
-  if (chunk < nchunks) {
-    const uint64_t start = chunk * kChunkBytes;
-    const uint32_t raw_len = (uint32_t)min_u64(kChunkBytes, raw_bytes - start);
-    len = (bits + 7) / 8;
-    if (len >= raw_len) len = raw_len;
-  }
-  if ((lane & 31) == 0 && chunk < nchunks && chunk_lens) chunk_lens[chunk] = (uint16_t)len;
-  const uint64_t sum = (uint64_t)__shfl(len, 0, 64) + (uint64_t)__shfl(len, 32, 64);
-  if (lane == 0 && out_bytes) atomicAdd((unsigned long long *)out_bytes, (unsigned long long)sum);
 }
 
 // ---------------------------------------------------------------------------
@@ -872,6 +855,107 @@ __global__ __launch_bounds__(kGroupThreads, 4) void compress_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Size pass (pz_compressed_size, pz_compressed_size_sampled): the first four
+// phases of compress_kernel with nothing emitted. A workgroup takes 8 sampled
+// chunks (chunk = sample * stride; stride 1 samples every chunk), loads their
+// 256 blocks one per thread, gives all-zero blocks their fixed cost, packs the
+// other blocks onto the fewest waves for the candidate sizes, and scans each
+// chunk's block costs to its length. Lengths go to chunk_lens; their sum to
+// out_bytes (which holds the headers' bytes beforehand).
+// ---------------------------------------------------------------------------
+template <int W>
+__global__ __launch_bounds__(kGroupThreads, 4) void size_kernel(
+    const uint8_t *__restrict__ src, uint64_t raw_bytes, uint64_t nchunks, uint64_t stride,
+    uint64_t nsampled, uint64_t *__restrict__ out_bytes, uint16_t *__restrict__ chunk_lens, Mode mode) {
+  constexpr int N = 1024 / W;
+  __shared__ __attribute__((aligned(16))) uint32_t lds[kStageDwords];
+  __shared__ uint16_t blk_bits[kGroupThreads];
+  __shared__ uint8_t slot_block[kGroupThreads];
+  __shared__ uint8_t slot_n[kGroupThreads];
+  __shared__ uint32_t wave_full[kWavesPerGroup];
+  __shared__ uint32_t wave_part[kWavesPerGroup];
+  __shared__ uint32_t chunk_len[kGroupChunks];
+
+  const uint32_t t = threadIdx.x, lane = lane_id();
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const uint64_t sample = (uint64_t)blockIdx.x * kGroupChunks + (t >> 5);
+  // Samples past the last one read as zeros (their chunk is past the end).
+  const uint64_t chunk = sample < nsampled ? sample * stride : nchunks;
+  const uint64_t block = chunk * kBlocksPerChunk + (t & 31);
+  const bool valid = block * kBlockBytes < raw_bytes;
+
+  uint32_t d[32];
+  load_block(src, raw_bytes, block * kBlockBytes, d);
+  uint32_t sn = count_nonzero<W>(d);
+  const bool nonzero = sn != 0;
+  const bool partial = nonzero && sn < (uint32_t)N;
+  const uint64_t mfull = __ballot(nonzero && !partial), mpart = __ballot(partial);
+  if (lane == 0) {
+    wave_full[wave] = (uint32_t)popc64(mfull);
+    wave_part[wave] = (uint32_t)popc64(mpart);
+  }
+  if (!nonzero) blk_bits[t] = (uint16_t)(valid ? 3u * mode.tagged + zero_block_size(W, mode.zc) : 0u);
+  __syncthreads();
+
+  uint32_t nfull = 0, npart = 0, ffirst = 0, pfirst = 0;
+#pragma unroll
+  for (int k = 0; k < kWavesPerGroup; ++k) {
+    const uint32_t f = wave_full[k], q = wave_part[k];
+    ffirst += (uint32_t)k < wave ? f : 0u;
+    pfirst += (uint32_t)k < wave ? q : 0u;
+    nfull += f;
+    npart += q;
+  }
+  const uint32_t nnz = nfull + npart;
+  if (nonzero) {
+    const uint32_t idx = partial ? nfull + pfirst + lanes_below(mpart) : ffirst + lanes_below(mfull);
+    uint32_t *slot = lds + idx * kLaneStride;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) slot[i] = d[i];
+    slot_block[idx] = (uint8_t)t;
+    slot_n[idx] = (uint8_t)sn;
+  }
+  __syncthreads();
+
+  const uint32_t slot = (t + kGroupThreads - 64u * (blockIdx.x & 3u)) & (kGroupThreads - 1);
+  const bool active = slot < nnz;
+  if (__ballot(active) != 0) {
+    const uint32_t *region = lds + slot * kLaneStride;
+    sn = active ? (uint32_t)slot_n[slot] : 0u;
+    if (active) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) d[i] = region[i];
+    }
+    Sizes s;
+    candidate_sizes<W>(d, (int)sn, __ballot(active && sn < (uint32_t)N) != 0, s);
+    int best_size;
+    select_tag(s, best_size, mode.mask);
+    if (active) blk_bits[slot_block[slot]] = (uint16_t)(3u * mode.tagged + best_size);
+  }
+  __syncthreads();
+
+  const uint32_t cost = blk_bits[t];
+  const uint32_t bits = __shfl(half_inclusive_scan(cost), (int)((lane & 32) | 31), 64);
+  if ((lane & 31) == 0) {
+    uint32_t len = 0;
+    if (chunk < nchunks) {
+      const uint32_t raw_len = (uint32_t)min_u64(kChunkBytes, raw_bytes - chunk * kChunkBytes);
+      len = (bits + 7) / 8;
+      if (len >= raw_len) len = raw_len;
+      if (chunk_lens) chunk_lens[sample] = (uint16_t)len;
+    }
+    chunk_len[t >> 5] = len;
+  }
+  __syncthreads();
+  if (t == 0 && out_bytes) {
+    uint64_t sum = 0;
+#pragma unroll
+    for (int c = 0; c < kGroupChunks; ++c) sum += chunk_len[c];
+    atomicAdd((unsigned long long *)out_bytes, (unsigned long long)sum);
+  }
+}
+
 __global__ void fill_u64_kernel(uint64_t *p, uint64_t n, uint64_t value) {
   for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (uint64_t)gridDim.x * blockDim.x)
@@ -885,24 +969,52 @@ hipError_t fill_u64(uint64_t *p, uint64_t n, uint64_t value, hipStream_t stream)
   return hipGetLastError();
 }
 
+__global__ void store_size_init_kernel(uint64_t *out_bytes, uint64_t v0, uint64_t *out_raw, uint64_t v1) {
+  if (threadIdx.x == 0) {
+    if (out_bytes) *out_bytes = v0;
+    if (out_raw) *out_raw = v1;
+  }
+}
+
 hipError_t launch_size(int w, const uint8_t *src, uint64_t raw_bytes, uint32_t codec_mask, int tagged,
-                       uint64_t *out_bytes, uint16_t *chunk_lens, uint16_t *block_sizes,
-                       uint8_t *block_tags, hipStream_t stream) {
+                       uint64_t stride, uint64_t *out_bytes, uint64_t *out_raw, uint16_t *chunk_lens,
+                       hipStream_t stream) {
   const uint64_t nchunks = (raw_bytes + kChunkBytes - 1) / kChunkBytes;
-  if (out_bytes) {
-    hipError_t e = fill_u64(out_bytes, 1, 2 * nchunks, stream);
+  const uint64_t nsampled = (nchunks + stride - 1) / stride;
+  if (out_bytes || out_raw) {
+    // Headers of the sampled chunks; their raw bytes: whole chunks except
+    // the tensor's last chunk when it is sampled.
+    const uint64_t last = nsampled ? (nsampled - 1) * stride : 0;
+    const uint64_t sampled_raw =
+        nsampled ? (nsampled - 1) * kChunkBytes + min_u64(kChunkBytes, raw_bytes - last * kChunkBytes) : 0;
+    hipLaunchKernelGGL(store_size_init_kernel, dim3(1), dim3(64), 0, stream, out_bytes, 2 * nsampled,
+                       out_raw, sampled_raw);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (nchunks == 0) return hipSuccess;
-  const uint64_t ntiles = (nchunks + 1) / 2;
-  const uint64_t groups = (ntiles + kWavesPerGroup - 1) / kWavesPerGroup;
+  if (nsampled == 0) return hipSuccess;
+  const uint64_t groups = (nsampled + kGroupChunks - 1) / kGroupChunks;
   const Mode mode = make_mode(w, codec_mask, tagged);
   if (w == 16)
-    hipLaunchKernelGGL(size_kernel<16>, dim3((unsigned)groups), dim3(kGroupThreads), 0, stream,
-                       src, raw_bytes, nchunks, out_bytes, chunk_lens, block_sizes, block_tags, mode);
+    hipLaunchKernelGGL(size_kernel<16>, dim3((unsigned)groups), dim3(kGroupThreads), 0, stream, src,
+                       raw_bytes, nchunks, stride, nsampled, out_bytes, chunk_lens, mode);
   else
-    hipLaunchKernelGGL(size_kernel<32>, dim3((unsigned)groups), dim3(kGroupThreads), 0, stream,
-                       src, raw_bytes, nchunks, out_bytes, chunk_lens, block_sizes, block_tags, mode);
+    hipLaunchKernelGGL(size_kernel<32>, dim3((unsigned)groups), dim3(kGroupThreads), 0, stream, src,
+                       raw_bytes, nchunks, stride, nsampled, out_bytes, chunk_lens, mode);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_sizes(int w, const uint8_t *src, uint64_t raw_bytes, uint16_t *block_sizes,
+                              uint8_t *block_tags, hipStream_t stream) {
+  const uint64_t nblocks = (raw_bytes + kBlockBytes - 1) / kBlockBytes;
+  if (nblocks == 0) return hipSuccess;
+  const uint64_t groups = (nblocks + kGroupThreads - 1) / kGroupThreads;
+  if (w == 16)
+    hipLaunchKernelGGL(block_sizes_kernel<16>, dim3((unsigned)groups), dim3(kGroupThreads), 0, stream, src,
+                       raw_bytes, nblocks, block_sizes, block_tags);
+  else
+    hipLaunchKernelGGL(block_sizes_kernel<32>, dim3((unsigned)groups), dim3(kGroupThreads), 0, stream, src,
+                       raw_bytes, nblocks, block_sizes, block_tags);
   return hipGetLastError();
 }
 

@@ -33,9 +33,15 @@ ScratchNeed decompress_scratch_need(uint64_t raw_bytes);
 
 hipError_t fill_u64(uint64_t *p, uint64_t n, uint64_t value, hipStream_t stream);
 
+// Size pass over chunks 0, stride, 2*stride, ...: out_bytes receives their
+// stream bytes (2 + payload each), out_raw their raw bytes, chunk_lens their
+// header values. Every output is nullable.
 hipError_t launch_size(int w, const uint8_t *src, uint64_t raw_bytes, uint32_t codec_mask, int tagged,
-                       uint64_t *out_bytes, uint16_t *chunk_lens, uint16_t *block_sizes,
-                       uint8_t *block_tags, hipStream_t stream);
+                       uint64_t stride, uint64_t *out_bytes, uint64_t *out_raw, uint16_t *chunk_lens,
+                       hipStream_t stream);
+// Per-block candidate sizes and tags (PlaneZip candidates, tagged).
+hipError_t launch_block_sizes(int w, const uint8_t *src, uint64_t raw_bytes, uint16_t *block_sizes,
+                              uint8_t *block_tags, hipStream_t stream);
 
 hipError_t launch_compress(int w, const uint8_t *src, uint64_t raw_bytes, uint32_t codec_mask,
                            int tagged, uint8_t *dst, uint64_t *out_bytes, const Scratch &scratch,

@@ -254,3 +254,17 @@ def header_table(stream, raw_bytes: int) -> np.ndarray:
     """The u16 header values H[0..C-1] of a stream (no validation)."""
     C = num_chunks(raw_bytes)
     return _as_bytes(stream)[: 2 * C].view("<u2").astype(np.int64)
+
+
+def sampled_size(data, w: int, stride: int, threads: int = 1):
+    """The size measurement over chunks 0, stride, 2*stride, ... of a tensor
+    (the paper's methodology compresses tensors above 32 MB on every fourth
+    4 KB chunk, §IV "Tensor capture"): the whole tensor is compressed and the
+    sampled chunks' stream bytes (2 + H each), raw bytes and header values are
+    read off its header table. Returns (stream bytes, raw bytes, H values)."""
+    src = _as_bytes(data)
+    n = src.size
+    H = header_table(compress(src, w, threads=threads), n)
+    picked = np.arange(0, num_chunks(n), stride, dtype=np.int64)
+    raw = np.minimum(CHUNK_BYTES, n - picked * CHUNK_BYTES)
+    return int((2 + H[picked]).sum()), int(raw.sum()), H[picked]

@@ -15,7 +15,8 @@ def _declared():
     for fn in os.listdir(os.path.join(ROOT, "include")):
         if fn.endswith(".h"):
             text = open(os.path.join(ROOT, "include", fn)).read()
-            names += re.findall(r"^\s*(?:pz_status_t|const char \*)\s*(pz_\w+)\s*\(", text, re.M)
+            names += re.findall(r"^\s*(?:pz_status_t|const char \*|pz_predictor_t \*|void|size_t)\s*(pz_\w+)\s*\(",
+                                text, re.M)
     return sorted(set(names))
 
 
@@ -32,8 +33,13 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     declared = _declared()
     assert set(declared) >= {"pz_compress", "pz_decompress", "pz_compressed_size"}
+    assert {"pz_compressed_size_sampled", "pz_predictor_create", "pz_predictor_update",
+            "pz_predictor_predict", "pz_predictor_destroy"} <= set(declared)
     for name in declared:
         assert hasattr(lib, name), name
+    from lossless_bit_plane_amd import _lib
+
+    assert set(_lib.EXPORTS) == set(declared)
 
 
 def test_rejects_bad_arguments_on_host(lib):
@@ -68,3 +74,16 @@ def test_rejects_bad_codec_modes_on_host(lib):
         assert lib.pz_compressed_size_ex(fake, 100, 0, 16, mask, tagged, fake, None, None) == bad
         assert lib.pz_decompress_ex(fake, 1000, 0, 16, mask, tagged, fake, 100, None, None) == bad
 
+
+
+def test_rejects_bad_sampled_size_arguments_on_host(lib):
+    from lossless_bit_plane_amd import _lib
+
+    fake = 256  # aligned, never dereferenced: every call below fails its checks first
+    bad = _lib.PZ_ERROR_INVALID_VALUE
+    assert lib.pz_compressed_size_sampled(fake, 100, 0, 16, 0, fake, None, None) == bad  # stride 0
+    assert lib.pz_compressed_size_sampled(fake, 100, 0, 16, 4, None, None, None) == bad  # no output
+    assert lib.pz_compressed_size_sampled(fake, 100, 0, 16, 4, fake + 4, None, None) == bad  # misaligned
+    assert lib.pz_compressed_size_sampled(fake, 100, 0, 16, 4, fake, fake + 1, None) == bad
+    assert lib.pz_compressed_size_sampled(fake, 100, 1, 16, 4, fake, None, None) == bad  # FP32 with w=16
+    assert lib.pz_compressed_size_sampled(None, 100, 0, 16, 4, fake, None, None) == bad

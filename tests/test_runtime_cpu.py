@@ -1,0 +1,156 @@
+"""The runtime half of PlaneZip on the host (no GPU): the sampled size
+measurement of the oracle pinned to closed forms, the oracle's predictor
+pinned to what §III-B fixes, and the library's native predictor table checked
+against the oracle's on synthetic signature sequences (PlaneZip paper §III-B
+"Compressibility Predictor"; real signatures would need operator traces)."""
+import os
+import random
+import threading
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle.predictor import RatioTable, wire_error
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# Closed forms of FORMAT.md / the P-5 pins, BF16 (w = 16): an all-zero block
+# costs a 3-bit tag and a 6-bit BX zero run, so a zero chunk of b blocks is
+# ceil(9b / 8) payload bytes; uniform random bytes never beat RAW, so a random
+# chunk is stored raw (payload = its raw length), as is any chunk whose code
+# would not be shorter than its raw bytes.
+ZERO, RANDOM = 0, 1
+
+
+def _chunked_tensor(kinds, tail_kind=None, tail_bytes=0, seed=0):
+    rng = np.random.default_rng(seed)
+    parts = []
+    for k in kinds:
+        parts.append(np.zeros(4096, np.uint8) if k == ZERO else rng.integers(0, 256, 4096, dtype=np.uint8))
+    if tail_bytes:
+        parts.append(np.zeros(tail_bytes, np.uint8) if tail_kind == ZERO
+                     else rng.integers(0, 256, tail_bytes, dtype=np.uint8))
+    return np.concatenate(parts)
+
+
+def _closed_form_H(kind, raw_len):
+    blocks = (raw_len + 127) // 128
+    L = -(-9 * blocks // 8) if kind == ZERO else raw_len
+    return raw_len if L >= raw_len else L  # a chunk that would grow is stored raw
+
+
+@pytest.mark.parametrize("tail_kind,tail_bytes", [(None, 0), (ZERO, 1000), (RANDOM, 1000), (ZERO, 1)])
+@pytest.mark.parametrize("stride", [1, 2, 3, 4, 7, 50])
+def test_oracle_sampled_size_closed_forms(stride, tail_kind, tail_bytes):
+    kinds = [RANDOM if c % 3 == 1 else ZERO for c in range(13)]
+    data = _chunked_tensor(kinds, tail_kind, tail_bytes)
+    all_kinds = kinds + ([tail_kind] if tail_bytes else [])
+    raw_lens = [4096] * len(kinds) + ([tail_bytes] if tail_bytes else [])
+    picked = range(0, len(all_kinds), stride)
+    H = [_closed_form_H(all_kinds[c], raw_lens[c]) for c in picked]
+    comp, raw, lens = oracle.sampled_size(data, 16, stride)
+    assert list(lens) == H
+    assert comp == sum(2 + h for h in H)
+    assert raw == sum(raw_lens[c] for c in picked)
+    if stride == 1:
+        assert comp == oracle.compress(data, 16).size and raw == data.size
+
+
+def test_oracle_sampled_size_empty():
+    comp, raw, lens = oracle.sampled_size(np.zeros(0, np.uint8), 16, 4)
+    assert (comp, raw, lens.size) == (0, 0, 0)
+
+
+def test_oracle_predictor_pins():
+    t = RatioTable()
+    # No measurement yet: a ratio of one.
+    assert t.predict(7, 12345) == (12345, False)
+    t.update(7, 4096, 2048)  # ratio 2
+    assert t.predict(7, 8192) == (4096, True)
+    assert t.predict(8, 8192) == (8192, False)  # signatures are independent
+    t.update(7, 4096, 1024)  # the new measurement overwrites the old one
+    assert t.predict(7, 4096) == (1024, True)
+    t.update(9, 3, 2)
+    assert t.predict(9, 4) == (3, True)  # ceil(4 * 2 / 3)
+    assert wire_error([100, 200], [110, 190]) == pytest.approx(20 / 300)
+    assert wire_error([], []) == 0.0
+
+
+@pytest.fixture(scope="module")
+def pzp():
+    path = os.path.join(ROOT, "lossless_bit_plane_amd", "libplanezip.so")
+    if not os.path.exists(path):
+        pytest.fail("libplanezip.so is not built (run __graft_entry__.build())")
+    from lossless_bit_plane_amd import predictor
+
+    return predictor
+
+
+def test_native_predictor_matches_oracle_on_random_sequence(pzp):
+    rng = random.Random(11)
+    table = pzp.Predictor(512)
+    ref = RatioTable()
+    sigs = [pzp.signature(op, slot) for op in range(150) for slot in range(2)]
+    for step in range(6000):
+        sig = rng.choice(sigs)
+        raw = rng.choice([1, 2, 4095, 4096, 4097, rng.randrange(1, 1 << 20), rng.randrange(1, 1 << 40)])
+        if rng.random() < 0.4:
+            max_comp = 2 * ((raw + 4095) // 4096) + raw
+            comp = rng.choice([1, max_comp, rng.randrange(1, max_comp + 1)])
+            table.update(sig, raw, comp)
+            ref.update(sig, raw, comp)
+        else:
+            assert table.predict(sig, raw) == ref.predict(sig, raw), (step, sig, raw)
+    assert len(table) == len(ref.entries)
+
+
+def test_native_predictor_capacity_clear_and_errors(pzp):
+    from lossless_bit_plane_amd._lib import PZ_ERROR_INSUFFICIENT_BUFFER, PZ_ERROR_INVALID_VALUE, PlaneZipError
+
+    t = pzp.Predictor(4)
+    for k in range(4):
+        t.update(pzp.signature(k, 0), 4096, 100 + k)
+    with pytest.raises(PlaneZipError) as e:
+        t.update(pzp.signature(99, 0), 4096, 100)  # a new signature in a full table
+    assert e.value.status == PZ_ERROR_INSUFFICIENT_BUFFER
+    assert t.predict(pzp.signature(99, 0), 4096) == (4096, False)
+    t.update(pzp.signature(2, 0), 4096, 7)  # existing signatures still update
+    assert t.predict(pzp.signature(2, 0), 4096) == (7, True)
+    assert len(t) == 4
+    for raw, comp in [(0, 1), (10, 0), (4096, 4099), (1, 4)]:  # comp above 2*chunks + raw, or zero sizes
+        with pytest.raises(PlaneZipError) as e:
+            t.update(pzp.signature(1, 0), raw, comp)
+        assert e.value.status == PZ_ERROR_INVALID_VALUE
+    t.update(pzp.signature(1, 0), 1, 3)
+    with pytest.raises(PlaneZipError):  # 3 * 2^63 does not fit 64 bits
+        t.predict(pzp.signature(1, 0), 1 << 63)
+    t.clear()
+    assert len(t) == 0
+    assert t.predict(pzp.signature(2, 0), 4096) == (4096, False)
+    assert pzp.signature(3, 0x1FFFF) == (3 << 16) | 0xFFFF
+    with pytest.raises(ValueError):
+        pzp.Predictor(0)
+
+
+def test_native_predictor_from_several_threads(pzp):
+    t = pzp.Predictor(1024)
+    last = {}
+
+    def worker(k):
+        r = random.Random(k)
+        for i in range(2000):
+            sig = pzp.signature(k * 100 + r.randrange(100), 0)
+            comp = r.randrange(1, 4099)
+            t.update(sig, 4096, comp)
+            last[sig] = comp  # each thread owns its signatures
+            t.predict(pzp.signature(r.randrange(800), 0), 4096)
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(8)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert len(t) == len(last)
+    for sig, comp in last.items():
+        assert t.predict(sig, 4096) == (comp, True)
