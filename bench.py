@@ -49,6 +49,7 @@ def parse():
     p.add_argument("--no-verify", action="store_true")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="run one plain device copy of this many MiB first (HBM counter calibration)")
+    p.add_argument("--no-swap", action="store_true", help="skip the copy-path (swap) measurement")
     p.add_argument("--variants", action="store_true",
                    help="also time the codec variants the paper compares PlaneZip with (Fig. 3) "
                         "on the same tensors and report their ratios")
@@ -201,6 +202,7 @@ def main():
 
     variants = measure_variants(pz, items, flush, cur) if args.variants else None
     size_only = measure_size_only(pz, items, flush, cur)
+    swap = None if args.no_swap else measure_swap(pz, items, flush)
 
     out = {
         "metric": "compress & decompress GB/s (raw bytes), % of HBM roofline; ratio = oracle",
@@ -234,6 +236,7 @@ def main():
         "cpu_baseline": cpu,
         "tensors": per_tensor,
         "size_only": size_only,
+        "swap": swap,
     }
     if variants is not None:
         out["variants"] = variants
@@ -344,6 +347,106 @@ def measure_size_only(pz, items, flush, cur, stride=4, reps=5):
                              estimate_err_pct=round(100 * (est - comp) / comp, 4))
         log(f"size pass {name}: {raw / t_total / 1e9:.0f} GB/s ({t_total * 1e6:.0f} us)")
     return res
+
+
+def measure_swap(pz, items, flush, reps=3, pool_chunk_bytes=2 << 20):
+    """The copy path (PlaneZip §III, Fig. 2) on the workload, against plain
+    copies of the raw tensors between HBM and pinned host memory. Swap-out:
+    every tensor compressed into a staging slot and its stream copied into the
+    pinned pool (the engine's worker issues the copies once each length is
+    known); swap-in: the streams copied back and decompressed. Each figure is
+    the workload's raw bytes over the host wall-clock time from the first
+    call to the last completion (median of `reps`, each after a cache flush),
+    round trip checked."""
+    import torch
+
+    raw_total = sum(it["t"].nbytes for it in items)
+    comp_total = sum(it["comp"] for it in items)
+    cur = torch.cuda.current_stream()
+
+    def timed(fn):
+        ts = []
+        for _ in range(reps):
+            flush()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return float(np.median(ts))
+
+    hosts = [torch.empty(it["t"].nbytes, dtype=torch.uint8, pin_memory=True) for it in items]
+
+    def d2h():
+        for h, it in zip(hosts, items):
+            h.copy_(it["src"], non_blocking=True)
+        torch.cuda.synchronize()
+
+    def h2d():
+        for h, it in zip(hosts, items):
+            it["out"].copy_(h, non_blocking=True)
+        torch.cuda.synchronize()
+
+    t_d2h, t_h2d = timed(d2h), timed(h2d)
+    for it in items:
+        assert torch.equal(it["out"], it["src"]), "plain copy round trip"
+    del hosts
+
+    staging = max(pz.max_compressed_bytes(it["t"].nbytes) for it in items)
+    chunks = sum(-(-it["comp"] // pool_chunk_bytes) for it in items) + 8
+    sw = pz.Swapper(pool_chunk_bytes, chunks, staging, 2)
+    tickets = []
+    try:
+        def swap_out():
+            tickets.clear()
+            for it in items:
+                t = it["t"]
+                tickets.append(sw.swap_out(it["src"], t.dtype, t.elem_bits))
+            for k in tickets:
+                sw.wait(k)
+
+        def swap_in():
+            for k, it in zip(tickets, items):
+                sw.swap_in(k, it["out"], it["status"], cur)
+            torch.cuda.synchronize()
+
+        outs, ins = [], []
+        for _ in range(reps):
+            outs.append(timed_once(swap_out, flush))
+            for k, it in zip(tickets, items):
+                assert sw.wait(k) == it["comp"], "pool stream length"
+            ins.append(timed_once(swap_in, flush))
+            for it in items:
+                assert int(it["status"].item()) == 0 and torch.equal(it["out"], it["src"]), "swap round trip"
+            for k in tickets:
+                sw.release(k)
+        t_out, t_in = float(np.median(outs)), float(np.median(ins))
+    finally:
+        sw.close()
+    res = {
+        "raw_bytes": raw_total, "stream_bytes": comp_total, "pool_chunk_bytes": pool_chunk_bytes,
+        "plain_d2h_gbps": round(raw_total / t_d2h / 1e9, 2),
+        "plain_h2d_gbps": round(raw_total / t_h2d / 1e9, 2),
+        "swap_out_gbps": round(raw_total / t_out / 1e9, 2),
+        "swap_in_gbps": round(raw_total / t_in / 1e9, 2),
+        "swap_out_speedup": round(t_d2h / t_out, 3),
+        "swap_in_speedup": round(t_h2d / t_in, 3),
+        "ms": {"plain_d2h": round(t_d2h * 1e3, 3), "plain_h2d": round(t_h2d * 1e3, 3),
+               "swap_out": round(t_out * 1e3, 3), "swap_in": round(t_in * 1e3, 3)},
+    }
+    log(f"swap: plain D2H {res['plain_d2h_gbps']} GB/s, swap-out {res['swap_out_gbps']} GB/s "
+        f"(x{res['swap_out_speedup']}); plain H2D {res['plain_h2d_gbps']} GB/s, swap-in "
+        f"{res['swap_in_gbps']} GB/s (x{res['swap_in_speedup']})")
+    return res
+
+
+def timed_once(fn, flush):
+    import torch
+
+    flush()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    fn()
+    return time.perf_counter() - t0
 
 
 # The sources each kernel is built from: counters taken for a kernel stay

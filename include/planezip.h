@@ -192,6 +192,63 @@ pz_status_t pz_predictor_predict(pz_predictor_t *pred, uint64_t signature,
 size_t pz_predictor_entries(pz_predictor_t *pred);
 void pz_predictor_clear(pz_predictor_t *pred);
 
+/* Swap engine: the copy path of §III and Fig. 2. A swapped-out tensor is
+ * compressed on the GPU into a device staging slot and its stream's exact
+ * bytes are copied by DMA into fixed-size chunks of a pinned host pool ("On
+ * the host, compressed tensors occupy fixed-size chunks of a pinned pool",
+ * §III-A); swapping in copies the chunks back and decompresses them. The
+ * stream's length is known only after the compression has run, so a worker
+ * thread of the engine waits for each compression, takes pool chunks and
+ * issues the copies on the engine's device-to-host stream; pz_swap_out
+ * returns once the compression is enqueued. The engine belongs to the device
+ * that is current at creation; all its calls are safe from several host
+ * threads. Streams are the callers' (compression and decompression run on
+ * them) plus two copy streams of the engine's own (default priority). */
+typedef struct pz_swapper pz_swapper_t;
+
+/* pool_chunk_bytes (a multiple of 16) x pool_chunks of pinned host memory,
+ * and staging_slots (1..64) device buffers of staging_bytes, which bound the
+ * tensors it takes: PZ_MAX_COMPRESSED_BYTES(raw_bytes) <= staging_bytes.
+ * More slots let more compressions run ahead of the copies. NULL on bad
+ * sizes or when an allocation fails (or there is no device). */
+pz_swapper_t *pz_swapper_create(size_t pool_chunk_bytes, size_t pool_chunks,
+                                size_t staging_bytes, int staging_slots);
+/* Waits for all pending work and frees the pool, the slots and the streams. */
+void pz_swapper_destroy(pz_swapper_t *swapper);
+/* Pool chunks not held by a swapped-out tensor. */
+size_t pz_swapper_free_chunks(pz_swapper_t *swapper);
+
+/* Enqueues the compression of d_src (raw_bytes >= 1, device memory, 16-byte
+ * aligned) on `stream`, after the work already there, and returns a ticket
+ * (>= 1). d_src may be reused once `stream` has passed this point. Blocks
+ * while every staging slot is in use. A tensor above the staging size returns
+ * PZ_ERROR_INSUFFICIENT_BUFFER; argument errors are those of pz_compress. */
+pz_status_t pz_swap_out(pz_swapper_t *swapper, const void *d_src, size_t raw_bytes,
+                        int dtype, int elem_bits, void *stream, uint64_t *ticket);
+
+/* Blocks until the ticket's stream is in the pool. *comp_bytes (nullable):
+ * its length. PZ_ERROR_INSUFFICIENT_BUFFER if the pool had too few free
+ * chunks (the tensor was not swapped; release the ticket), PZ_ERROR_HIP if a
+ * copy failed, PZ_ERROR_INVALID_VALUE for an unknown ticket. */
+pz_status_t pz_swap_wait(pz_swapper_t *swapper, uint64_t ticket, uint64_t *comp_bytes);
+
+/* Enqueues the host-to-device copy of the ticket's chunks (after its
+ * device-to-host copies) into a staging slot and their decompression into
+ * d_dst (raw_bytes of the swap-out) on `stream`; d_status as pz_decompress.
+ * Blocks until the worker has handled the swap-out and while every staging
+ * slot is in use. The chunks stay held: a ticket can be swapped in again. */
+pz_status_t pz_swap_in(pz_swapper_t *swapper, uint64_t ticket, void *d_dst,
+                       int32_t *d_status, void *stream);
+
+/* Returns the ticket's pool chunks, after any copy still reading or writing
+ * them, and forgets the ticket. */
+pz_status_t pz_swap_release(pz_swapper_t *swapper, uint64_t ticket);
+
+/* Copies the ticket's stream (FORMAT.md §5) into h_dst (capacity bytes),
+ * after waiting as pz_swap_wait; *comp_bytes (nullable) its length. */
+pz_status_t pz_swap_read(pz_swapper_t *swapper, uint64_t ticket, void *h_dst,
+                         size_t capacity, uint64_t *comp_bytes);
+
 /* Diagnostics of the size pass, per 128-byte block (nblocks =
  * ceil(raw_bytes/128)): d_sizes (nullable) receives the five candidate sizes
  * in bits (ZVC, DBX, BX, ZBX, RAW; payload only, no tag) as 5*nblocks

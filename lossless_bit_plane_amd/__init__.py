@@ -7,7 +7,9 @@ under a 3-bit tag, 4 KB chunks with 16-bit headers; bit layout FORMAT.md v1.
 The ``*_ex`` calls run the single-codec and reduced-candidate variants the
 paper compares PlaneZip with (§V-A, Fig. 3); ``pz_compressed_size_sampled``
 and the ``pz_predictor_*`` table are the runtime's size measurement and
-per-tensor predictor (§III-B).
+per-tensor predictor (§III-B); ``Swapper`` and ``SwapHooks`` are the copy
+path (§III, Fig. 2): compression into a pinned pool of fixed-size chunks and
+back, under autograd's saved-tensor hooks.
 """
 from .codec import (  # noqa: F401
     BF16, FP32, OTHER, CODEC_ALL, CODEC_BX, CODEC_DBX, CODEC_RAW, CODEC_ZBX, CODEC_ZVC,
@@ -20,3 +22,4 @@ from .predictor import (  # noqa: F401
     Predictor, signature, pz_predictor_create, pz_predictor_destroy, pz_predictor_update,
     pz_predictor_predict, pz_predictor_entries, pz_predictor_clear,
 )
+from .swap import Swapper, SwapHooks  # noqa: F401

@@ -18,7 +18,9 @@ PZ_ERROR_HIP = 4
 EXPORTS = ("pz_compressed_size", "pz_compress", "pz_decompress", "pz_block_sizes", "pz_status_string",
            "pz_compressed_size_ex", "pz_compress_ex", "pz_decompress_ex", "pz_compressed_size_sampled",
            "pz_predictor_create", "pz_predictor_destroy", "pz_predictor_update", "pz_predictor_predict",
-           "pz_predictor_entries", "pz_predictor_clear")
+           "pz_predictor_entries", "pz_predictor_clear",
+           "pz_swapper_create", "pz_swapper_destroy", "pz_swapper_free_chunks", "pz_swap_out", "pz_swap_wait",
+           "pz_swap_in", "pz_swap_release", "pz_swap_read")
 
 
 def _load():
@@ -48,6 +50,19 @@ def _load():
     lib.pz_predictor_entries.restype = sz
     lib.pz_predictor_clear.argtypes = [vp]
     lib.pz_predictor_clear.restype = None
+    lib.pz_swapper_create.argtypes = [sz, sz, sz, i]
+    lib.pz_swapper_create.restype = vp
+    lib.pz_swapper_destroy.argtypes = [vp]
+    lib.pz_swapper_destroy.restype = None
+    lib.pz_swapper_free_chunks.argtypes = [vp]
+    lib.pz_swapper_free_chunks.restype = sz
+    lib.pz_swap_out.argtypes = [vp, vp, sz, i, i, vp, ctypes.POINTER(u64)]
+    lib.pz_swap_wait.argtypes = [vp, u64, ctypes.POINTER(u64)]
+    lib.pz_swap_in.argtypes = [vp, u64, vp, vp, vp]
+    lib.pz_swap_release.argtypes = [vp, u64]
+    lib.pz_swap_read.argtypes = [vp, u64, vp, sz, ctypes.POINTER(u64)]
+    for name in ("pz_swap_out", "pz_swap_wait", "pz_swap_in", "pz_swap_release", "pz_swap_read"):
+        getattr(lib, name).restype = ctypes.c_int
     for name in ("pz_compressed_size", "pz_compress", "pz_decompress", "pz_block_sizes",
                  "pz_compressed_size_ex", "pz_compress_ex", "pz_decompress_ex", "pz_compressed_size_sampled",
                  "pz_predictor_update", "pz_predictor_predict"):

@@ -5,7 +5,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libplanezip.so")
-SOURCES = ["pz_compress.hip", "pz_decompress.hip", "pz_api.hip", "pz_predictor.cpp"]
+SOURCES = ["pz_compress.hip", "pz_decompress.hip", "pz_api.hip", "pz_predictor.cpp", "pz_swap.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

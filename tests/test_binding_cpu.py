@@ -15,7 +15,7 @@ def _declared():
     for fn in os.listdir(os.path.join(ROOT, "include")):
         if fn.endswith(".h"):
             text = open(os.path.join(ROOT, "include", fn)).read()
-            names += re.findall(r"^\s*(?:pz_status_t|const char \*|pz_predictor_t \*|void|size_t)\s*(pz_\w+)\s*\(",
+            names += re.findall(r"^\s*(?:pz_status_t|const char \*|pz_predictor_t \*|pz_swapper_t \*|void|size_t)\s*(pz_\w+)\s*\(",
                                 text, re.M)
     return sorted(set(names))
 
@@ -87,3 +87,17 @@ def test_rejects_bad_sampled_size_arguments_on_host(lib):
     assert lib.pz_compressed_size_sampled(fake, 100, 0, 16, 4, fake, fake + 1, None) == bad
     assert lib.pz_compressed_size_sampled(fake, 100, 1, 16, 4, fake, None, None) == bad  # FP32 with w=16
     assert lib.pz_compressed_size_sampled(None, 100, 0, 16, 4, fake, None, None) == bad
+
+
+def test_swapper_rejects_bad_sizes_without_touching_the_device(lib):
+    # Argument checks come before any allocation; without a GPU every valid
+    # request fails too (NULL, no crash).
+    for args in [(0, 4, 1 << 20, 2), (1000, 4, 1 << 20, 2), (1 << 16, 0, 1 << 20, 2),
+                 (1 << 16, 4, 0, 2), (1 << 16, 4, 1 << 20, 0), (1 << 16, 4, 1 << 20, 65)]:
+        assert not lib.pz_swapper_create(*args)
+    assert lib.pz_swapper_free_chunks(None) == 0
+    lib.pz_swapper_destroy(None)
+    from lossless_bit_plane_amd import _lib
+
+    assert lib.pz_swap_wait(None, 1, None) == _lib.PZ_ERROR_INVALID_VALUE
+    assert lib.pz_swap_release(None, 1) == _lib.PZ_ERROR_INVALID_VALUE
