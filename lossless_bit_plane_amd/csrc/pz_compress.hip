@@ -472,22 +472,18 @@ __global__ __launch_bounds__(kGroupThreads, 4) void compress_kernel(
 
   const uint32_t t = threadIdx.x, lane = lane_id();
   const uint32_t wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform: a scalar
-  // --- 1. Load block t; count its non-zero symbols. ---
-  // The tile is the ticket's, so that every tile a look-back waits on
-  // belongs to a running workgroup. The workgroup loads tile blockIdx.x,
-  // which the ticket normally is, before asking for the ticket, so that the
-  // two round trips overlap; another ticket means loading again.
-  uint32_t d[32];
-  load_block(src, raw_bytes, ((uint64_t)blockIdx.x * kGroupThreads + t) * kBlockBytes, d);
   if (t == 0) group_tile = atomicAdd(tile_counter, 1u) - counter_base;
   __syncthreads();
   const uint32_t tile = group_tile;
   if (tile >= ntiles) return;
-  if (tile != blockIdx.x) load_block(src, raw_bytes, ((uint64_t)tile * kGroupThreads + t) * kBlockBytes, d);
+
+  // --- 1. Load block t; count its non-zero symbols. ---
   // (Block and chunk indices are recomputed where needed rather than kept
   // live through the statistics, which use every register.)
   const uint64_t block = (uint64_t)tile * kGroupThreads + t;
   const bool valid = block * kBlockBytes < raw_bytes;
+  uint32_t d[32];
+  load_block(src, raw_bytes, block * kBlockBytes, d);
   uint32_t sn = count_nonzero<W>(d);  // blocks past the end load as zeros
   const bool nonzero = sn != 0;
   const bool partial = nonzero && sn < (uint32_t)N;

@@ -338,12 +338,6 @@ __global__ __launch_bounds__(kLocateChunks * G) void locate_kernel(
   __shared__ uint32_t group_tile;
   const uint32_t t = threadIdx.x, lane = lane_id(), ql = t & (G - 1);
   const uint32_t wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  // The tile is the ticket's (every tile a look-back waits on belongs to a
-  // running workgroup); the header of tile blockIdx.x, which the ticket
-  // normally is, is read while the ticket is in flight.
-  const uint32_t ci = t / G;  // chunk within the tile
-  const uint64_t sc = (uint64_t)blockIdx.x * kLocateChunks + ci;
-  uint32_t H = sc < nchunks ? reinterpret_cast<const uint16_t *>(src)[sc] : 0u;
   if (t == 0) group_tile = atomicAdd(tile_counter, 1u) - counter_base;
   __syncthreads();
   const uint32_t tile = group_tile;
@@ -351,8 +345,9 @@ __global__ __launch_bounds__(kLocateChunks * G) void locate_kernel(
 
   // Chunk offsets: a scan of the 16-bit headers over the tile, and one
   // look-back per tile for the headers before it.
+  const uint32_t ci = t / G;  // chunk within the tile
   const uint64_t c = (uint64_t)tile * kLocateChunks + ci;
-  if (tile != blockIdx.x) H = c < nchunks ? reinterpret_cast<const uint16_t *>(src)[c] : 0u;
+  const uint32_t H = c < nchunks ? reinterpret_cast<const uint16_t *>(src)[c] : 0u;
   const uint64_t incl = wave_inclusive_scan_u64(ql == 0 ? H : 0u);  // equal over the group
   if (lane == kWave - 1) wave_sum[wave] = incl;
   __syncthreads();
