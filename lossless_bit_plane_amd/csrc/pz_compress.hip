@@ -418,18 +418,23 @@ PZ_DEV void emit_run(BitSink &bs, uint32_t run, uint32_t R) {
 }
 
 // ---------------------------------------------------------------------------
-// Single-pass compression, one workgroup per tile of 8 chunks (256 blocks).
+// Single-pass compression, one workgroup per tile of 16 chunks (512 blocks,
+// eight waves: two such workgroups fill a CU's LDS; tiles of 8 chunks, with
+// twice the workgroups and tile tickets, were 4% slower and tiles of 32
+// slower still).
 //
 // Softmax-like activations hold many all-zero blocks, and a wave runs the
 // candidate statistics and the emission for all its lanes at the cost of
-// the slowest. So the group first loads its 256 blocks one per thread,
+// the slowest. So the group first loads its 512 blocks one per thread,
 // gives every all-zero block its fixed code (below), and packs the non-zero
 // blocks through LDS into the lowest slots: only ceil(nnz / 64) waves then
 // run the statistics and the emission. Chunk offsets come from one decoupled
 // look-back per group.
 // ---------------------------------------------------------------------------
-constexpr int kGroupChunks = kGroupThreads / kBlocksPerChunk;
-constexpr int kStageDwords = kGroupThreads * kLaneStride;
+constexpr int kCWaves = 8;  // waves per compress / size workgroup
+constexpr int kCThreads = kWave * kCWaves;
+constexpr int kGroupChunks = kCThreads / kBlocksPerChunk;
+constexpr int kStageDwords = kCThreads * kLaneStride;
 constexpr int kGroupBufDwords = kGroupChunks * kChunkBufDwords;
 constexpr int kGroupLdsDwords = kStageDwords > kGroupBufDwords ? kStageDwords : kGroupBufDwords;
 
@@ -451,7 +456,7 @@ PZ_DEV void emit_zero_block(uint32_t *buf, uint32_t off, const Mode &m) {
 }
 
 template <int W>
-__global__ __launch_bounds__(kGroupThreads, 4) void compress_kernel(
+__global__ __launch_bounds__(kCThreads, 2) void compress_kernel(
     const uint8_t *__restrict__ src, uint64_t raw_bytes, uint64_t nchunks, uint64_t ntiles,
     uint8_t *__restrict__ dst, uint64_t *__restrict__ out_bytes, uint64_t *status,
     uint32_t *tile_counter, uint32_t counter_base, uint32_t epoch, Mode mode) {
@@ -461,11 +466,11 @@ __global__ __launch_bounds__(kGroupThreads, 4) void compress_kernel(
   // Staging slots / ZBX compaction regions (stride kLaneStride), later the
   // eight chunk buffers.
   __shared__ __attribute__((aligned(16))) uint32_t lds[kGroupLdsDwords];
-  __shared__ uint16_t blk_bits[kGroupThreads];  // per block: its cost, then its bit offset
-  __shared__ uint8_t slot_block[kGroupThreads];  // compacted slot -> block of the group
-  __shared__ uint8_t slot_n[kGroupThreads];      // compacted slot -> its non-zero symbols
-  __shared__ uint32_t wave_full[kWavesPerGroup];
-  __shared__ uint32_t wave_part[kWavesPerGroup];
+  __shared__ uint16_t blk_bits[kCThreads];  // per block: its cost, then its bit offset
+  __shared__ uint16_t slot_block[kCThreads];  // compacted slot -> block of the group
+  __shared__ uint8_t slot_n[kCThreads];      // compacted slot -> its non-zero symbols
+  __shared__ uint32_t wave_full[kCWaves];
+  __shared__ uint32_t wave_part[kCWaves];
   __shared__ uint32_t chunk_len[kGroupChunks];
   __shared__ uint64_t chunk_pay[kGroupChunks];
   __shared__ uint32_t group_tile;
@@ -480,7 +485,7 @@ __global__ __launch_bounds__(kGroupThreads, 4) void compress_kernel(
   // --- 1. Load block t; count its non-zero symbols. ---
   // (Block and chunk indices are recomputed where needed rather than kept
   // live through the statistics, which use every register.)
-  const uint64_t block = (uint64_t)tile * kGroupThreads + t;
+  const uint64_t block = (uint64_t)tile * kCThreads + t;
   const bool valid = block * kBlockBytes < raw_bytes;
   uint32_t d[32];
   load_block(src, raw_bytes, block * kBlockBytes, d);
@@ -500,7 +505,7 @@ __global__ __launch_bounds__(kGroupThreads, 4) void compress_kernel(
   // (needed only when 0 < n < N) run on as few waves as possible. ---
   uint32_t nfull = 0, npart = 0, ffirst = 0, pfirst = 0;
 #pragma unroll
-  for (int k = 0; k < kWavesPerGroup; ++k) {
+  for (int k = 0; k < kCWaves; ++k) {
     const uint32_t f = wave_full[k], q = wave_part[k];
     ffirst += (uint32_t)k < wave ? f : 0u;
     pfirst += (uint32_t)k < wave ? q : 0u;
@@ -513,14 +518,14 @@ __global__ __launch_bounds__(kGroupThreads, 4) void compress_kernel(
     uint32_t *slot = lds + idx * kLaneStride;
 #pragma unroll
     for (int i = 0; i < 32; ++i) slot[i] = d[i];
-    slot_block[idx] = (uint8_t)t;
+    slot_block[idx] = (uint16_t)t;
     slot_n[idx] = (uint8_t)sn;
   }
   __syncthreads();
 
   // Waves take the slots in an order rotated per tile, so that the busy
   // waves of successive groups fall on different SIMDs.
-  const uint32_t slot = (t + kGroupThreads - 64u * (tile & 3u)) & (kGroupThreads - 1);
+  const uint32_t slot = (t + kCThreads - 64u * (tile & (kCWaves - 1u))) & (kCThreads - 1);
   const bool active = slot < nnz;
   const bool wave_active = __ballot(active) != 0;
 
@@ -645,7 +650,7 @@ __global__ __launch_bounds__(kGroupThreads, 4) void compress_kernel(
   }
   {
     uint4 *z = reinterpret_cast<uint4 *>(lds);
-    for (uint32_t i = t; i < (uint32_t)kGroupBufDwords / 4; i += kGroupThreads)
+    for (uint32_t i = t; i < (uint32_t)kGroupBufDwords / 4; i += kCThreads)
       z[i] = make_uint4(0, 0, 0, 0);
   }
   __syncthreads();
@@ -669,7 +674,7 @@ __global__ __launch_bounds__(kGroupThreads, 4) void compress_kernel(
   // --- 5. Emission into the chunk buffers (payload bit i at buffer bit i). ---
   // All-zero blocks of coded chunks: their one code. (In a raw chunk their
   // bytes are zeros, which the cleared buffer already holds.)
-  if (((uint64_t)tile * kGroupThreads + t) * kBlockBytes < raw_bytes && !nonzero && !raw_chunk) {
+  if (((uint64_t)tile * kCThreads + t) * kBlockBytes < raw_bytes && !nonzero && !raw_chunk) {
     emit_zero_block<W>(lds + (t >> 5) * kChunkBufDwords, excl, mode);
   }
 
@@ -696,7 +701,7 @@ __global__ __launch_bounds__(kGroupThreads, 4) void compress_kernel(
       // A raw chunk needs the symbols themselves back where e holds a transform.
       const bool reload = want_raw && (tag == kDBX || tag == kZBX);
       if (__ballot(reload)) {
-        if (reload) load_block(src, raw_bytes, ((uint64_t)tile * kGroupThreads + sb) * kBlockBytes, e);
+        if (reload) load_block(src, raw_bytes, ((uint64_t)tile * kCThreads + sb) * kBlockBytes, e);
       }
       if (want_raw) {
         // 1024 bits: the first and last dwords are shared with neighbours
@@ -857,24 +862,24 @@ __global__ __launch_bounds__(kGroupThreads, 4) void compress_kernel(
 
 // ---------------------------------------------------------------------------
 // Size pass (pz_compressed_size, pz_compressed_size_sampled): the first four
-// phases of compress_kernel with nothing emitted. A workgroup takes 8 sampled
+// phases of compress_kernel with nothing emitted. A workgroup takes 16 sampled
 // chunks (chunk = sample * stride; stride 1 samples every chunk), loads their
-// 256 blocks one per thread, gives all-zero blocks their fixed cost, packs the
+// 512 blocks one per thread, gives all-zero blocks their fixed cost, packs the
 // other blocks onto the fewest waves for the candidate sizes, and scans each
 // chunk's block costs to its length. Lengths go to chunk_lens; their sum to
 // out_bytes (which holds the headers' bytes beforehand).
 // ---------------------------------------------------------------------------
 template <int W>
-__global__ __launch_bounds__(kGroupThreads, 4) void size_kernel(
+__global__ __launch_bounds__(kCThreads, 2) void size_kernel(
     const uint8_t *__restrict__ src, uint64_t raw_bytes, uint64_t nchunks, uint64_t stride,
     uint64_t nsampled, uint64_t *__restrict__ out_bytes, uint16_t *__restrict__ chunk_lens, Mode mode) {
   constexpr int N = 1024 / W;
   __shared__ __attribute__((aligned(16))) uint32_t lds[kStageDwords];
-  __shared__ uint16_t blk_bits[kGroupThreads];
-  __shared__ uint8_t slot_block[kGroupThreads];
-  __shared__ uint8_t slot_n[kGroupThreads];
-  __shared__ uint32_t wave_full[kWavesPerGroup];
-  __shared__ uint32_t wave_part[kWavesPerGroup];
+  __shared__ uint16_t blk_bits[kCThreads];
+  __shared__ uint16_t slot_block[kCThreads];
+  __shared__ uint8_t slot_n[kCThreads];
+  __shared__ uint32_t wave_full[kCWaves];
+  __shared__ uint32_t wave_part[kCWaves];
   __shared__ uint32_t chunk_len[kGroupChunks];
 
   const uint32_t t = threadIdx.x, lane = lane_id();
@@ -900,7 +905,7 @@ __global__ __launch_bounds__(kGroupThreads, 4) void size_kernel(
 
   uint32_t nfull = 0, npart = 0, ffirst = 0, pfirst = 0;
 #pragma unroll
-  for (int k = 0; k < kWavesPerGroup; ++k) {
+  for (int k = 0; k < kCWaves; ++k) {
     const uint32_t f = wave_full[k], q = wave_part[k];
     ffirst += (uint32_t)k < wave ? f : 0u;
     pfirst += (uint32_t)k < wave ? q : 0u;
@@ -913,12 +918,12 @@ __global__ __launch_bounds__(kGroupThreads, 4) void size_kernel(
     uint32_t *slot = lds + idx * kLaneStride;
 #pragma unroll
     for (int i = 0; i < 32; ++i) slot[i] = d[i];
-    slot_block[idx] = (uint8_t)t;
+    slot_block[idx] = (uint16_t)t;
     slot_n[idx] = (uint8_t)sn;
   }
   __syncthreads();
 
-  const uint32_t slot = (t + kGroupThreads - 64u * (blockIdx.x & 3u)) & (kGroupThreads - 1);
+  const uint32_t slot = (t + kCThreads - 64u * (blockIdx.x & (kCWaves - 1u))) & (kCThreads - 1);
   const bool active = slot < nnz;
   if (__ballot(active) != 0) {
     const uint32_t *region = lds + slot * kLaneStride;
@@ -996,10 +1001,10 @@ hipError_t launch_size(int w, const uint8_t *src, uint64_t raw_bytes, uint32_t c
   const uint64_t groups = (nsampled + kGroupChunks - 1) / kGroupChunks;
   const Mode mode = make_mode(w, codec_mask, tagged);
   if (w == 16)
-    hipLaunchKernelGGL(size_kernel<16>, dim3((unsigned)groups), dim3(kGroupThreads), 0, stream, src,
+    hipLaunchKernelGGL(size_kernel<16>, dim3((unsigned)groups), dim3(kCThreads), 0, stream, src,
                        raw_bytes, nchunks, stride, nsampled, out_bytes, chunk_lens, mode);
   else
-    hipLaunchKernelGGL(size_kernel<32>, dim3((unsigned)groups), dim3(kGroupThreads), 0, stream, src,
+    hipLaunchKernelGGL(size_kernel<32>, dim3((unsigned)groups), dim3(kCThreads), 0, stream, src,
                        raw_bytes, nchunks, stride, nsampled, out_bytes, chunk_lens, mode);
   return hipGetLastError();
 }
@@ -1032,11 +1037,11 @@ hipError_t launch_compress(int w, const uint8_t *src, uint64_t raw_bytes, uint32
   const uint64_t ntiles = (nchunks + kGroupChunks - 1) / kGroupChunks;
   const Mode mode = make_mode(w, codec_mask, tagged);
   if (w == 16)
-    hipLaunchKernelGGL(compress_kernel<16>, dim3((unsigned)ntiles), dim3(kGroupThreads), 0, stream, src,
+    hipLaunchKernelGGL(compress_kernel<16>, dim3((unsigned)ntiles), dim3(kCThreads), 0, stream, src,
                        raw_bytes, nchunks, ntiles, dst, out_bytes, scratch.words, scratch.counter,
                        scratch.counter_base, scratch.epoch, mode);
   else
-    hipLaunchKernelGGL(compress_kernel<32>, dim3((unsigned)ntiles), dim3(kGroupThreads), 0, stream, src,
+    hipLaunchKernelGGL(compress_kernel<32>, dim3((unsigned)ntiles), dim3(kCThreads), 0, stream, src,
                        raw_bytes, nchunks, ntiles, dst, out_bytes, scratch.words, scratch.counter,
                        scratch.counter_base, scratch.epoch, mode);
   return hipGetLastError();
