@@ -171,3 +171,70 @@ def test_saved_tensor_hooks_give_identical_gradients(pz):
         assert sw.free_chunks() == 256
     finally:
         sw.close()
+
+
+def test_saved_tensor_hooks_bf16_elementwise(pz):
+    """BF16 activations saved by elementwise operators come back bit-exact."""
+    import torch
+
+    torch.manual_seed(1)
+    x = torch.randn(4096, 1536, device="cuda", dtype=torch.bfloat16).requires_grad_()
+
+    def run():
+        y = torch.nn.functional.gelu(x) * torch.sigmoid(x)
+        z = torch.softmax(y.float(), dim=-1).to(torch.bfloat16)
+        (z * y).sum().backward()
+        g = x.grad.clone()
+        x.grad = None
+        return g
+
+    ref = run()
+    sw = pz.Swapper(1 << 20, 128, 26 << 20, 3)
+    try:
+        with pz.SwapHooks(sw, min_bytes=1 << 20, check=True) as hooks:
+            got = run()
+        torch.cuda.synchronize()
+        assert hooks.swapped >= 3, hooks.swapped
+        assert torch.equal(got, ref)
+    finally:
+        sw.close()
+
+
+def test_swap_from_several_host_threads(pz):
+    """Four host threads share one engine, each on its own stream."""
+    import threading
+
+    import torch
+
+    (c1,) = pzinputs.config1()
+    sw = pz.Swapper(1 << 16, 512, 1 << 21, 3)
+    errors = []
+
+    def worker(k):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                data = np.roll(c1.data, 777 * k)
+                src = torch.from_numpy(data).to("cuda", non_blocking=False)
+                for rep in range(6):
+                    ticket = sw.swap_out(src, 0, 16, stream=s)
+                    out = torch.empty_like(src)
+                    status = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+                    sw.swap_in(ticket, out, status, stream=s)
+                    s.synchronize()
+                    if int(status.item()) != 0 or not torch.equal(out, src):
+                        errors.append((k, rep))
+                    sw.release(ticket)
+        except Exception as e:  # reported below
+            errors.append((k, repr(e)))
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(4)]
+    try:
+        for th in threads:
+            th.start()
+        for th in threads:
+            th.join()
+        assert not errors, errors
+        assert sw.free_chunks() == 512
+    finally:
+        sw.close()
