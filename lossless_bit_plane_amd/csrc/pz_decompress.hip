@@ -456,9 +456,13 @@ PZ_DEV void read_planes(const LdsBits &in, uint32_t &pos, uint32_t (&t)[32], int
     x = tz == 4 ? above : x;  // the plane before the XOR is zero
     x = fresh ? x : (PT)0;
     const uint32_t len = (uint32_t)(lut >> (8 * tz)) & 0xFFu;
-    const uint32_t newrun = tz == 1 ? ((win >> 2) & ((1u << R) - 1u)) + 1u : 0u;
-    pos += fresh ? len : 0u;
-    run = fresh ? newrun : (live ? run - 1u : run);
+    // Planes left in a zero run: a fresh run code sets them, every live
+    // plane uses one (as arithmetic on masks: written as selects, the
+    // update is compiled into exec-mask branches).
+    const uint32_t fm = 0u - (uint32_t)fresh;
+    const uint32_t newrun = (tz == 1 ? ((win >> 2) & ((1u << R) - 1u)) + 1u : 0u) & fm;
+    pos += len & fm;
+    run = newrun | ((run - (uint32_t)live) & ~fm);
     const PT p = live ? (x ^ above) : (PT)0;
     above = live ? p : above;
     if (j < W) {

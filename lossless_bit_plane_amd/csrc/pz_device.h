@@ -96,9 +96,12 @@ PZ_DEV uint32_t pk_sub_u16(uint32_t a, uint32_t b) {
 PZ_DEV uint32_t pk_add_u16(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, a) + __builtin_bit_cast(u16x2, b));
 }
+// One v_pk_min_u16. (Written as an elementwise min, a min with 1 is turned
+// into two 16-bit compares, two selects and a byte permute per call.)
 PZ_DEV uint32_t pk_min_u16(uint32_t a, uint32_t b) {
-  return __builtin_bit_cast(
-      uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, a), __builtin_bit_cast(u16x2, b)));
+  uint32_t r;
+  asm("v_pk_min_u16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
 }
 
 PZ_DEV uint32_t funnel(uint32_t hi, uint32_t lo, uint32_t shift) {
