@@ -569,16 +569,17 @@ __global__ __launch_bounds__(kCThreads, 2) void compress_kernel(
     }
     base = W == 16 ? (d[0] & 0xFFFFu) : d[0];
 
-    // ZBX: move the non-zero symbols to the front of this slot's region
-    // (the slot was read above; no other thread touches it).
-    const bool any_zbx = __ballot(want_zbx) != 0;
-    if (any_zbx) {
-      if (want_zbx) {
+    // ZBX and ZVC: move the non-zero symbols to the front of this slot's
+    // region (the slot was read above; no other thread touches it).
+    const bool want_cmp = want_zbx || want_zvc;
+    const bool any_cmp = __ballot(want_cmp) != 0;
+    if (any_cmp) {
+      if (want_cmp) {
 #pragma unroll
         for (int i = 0; i < 32; ++i) region[i] = 0;
       }
       wave_lds_fence();
-      if (want_zbx) {
+      if (want_cmp) {
         // Every symbol is written at the current rank, which advances only
         // past non-zero ones: a zero symbol writes 0 where the next non-zero
         // symbol (or nothing) goes, so there are no branches.
@@ -623,9 +624,9 @@ __global__ __launch_bounds__(kCThreads, 2) void compress_kernel(
         e[i] = want_dbx ? v : e[i];
       }
     }
-    if (any_zbx) {
+    if (any_cmp) {
 #pragma unroll
-      for (int i = 0; i < 32; ++i) e[i] = want_zbx ? region[i] : e[i];
+      for (int i = 0; i < 32; ++i) e[i] = want_cmp ? region[i] : e[i];
     }
   }
   __syncthreads();  // costs complete; staging and regions free
@@ -699,7 +700,7 @@ __global__ __launch_bounds__(kCThreads, 2) void compress_kernel(
 
     if (__ballot(want_raw)) {
       // A raw chunk needs the symbols themselves back where e holds a transform.
-      const bool reload = want_raw && (tag == kDBX || tag == kZBX);
+      const bool reload = want_raw && (tag == kDBX || tag == kZBX || tag == kZVC);
       if (__ballot(reload)) {
         if (reload) load_block(src, raw_bytes, ((uint64_t)tile * kCThreads + sb) * kBlockBytes, e);
       }
@@ -716,17 +717,16 @@ __global__ __launch_bounds__(kCThreads, 2) void compress_kernel(
     }
 
     if (__ballot(want_zvc)) {
-      if (want_zvc) {
-        bs.put64(nzmask, N);
+      // The mask, then the n non-zero symbols: the compacted symbols in e,
+      // 32 bits (two symbols) at a time, until no lane has any left.
+      if (want_zvc) bs.put64(nzmask, N);
+      const uint32_t bits = want_zvc ? (uint32_t)W * (uint32_t)s.n : 0u;
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          if constexpr (W == 16) {
-            const uint32_t a = e[i] & 0xFFFFu, b = e[i] >> 16;
-            if (a) bs.put(a, 16);
-            if (b) bs.put(b, 16);
-          } else {
-            if (e[i]) bs.put(e[i], 32);
-          }
+      for (int q = 0; q < 32; ++q) {
+        if (!__ballot(32u * q < bits)) break;
+        if (32u * q < bits) {
+          const uint32_t len = bits - 32u * q < 32u ? bits - 32u * q : 32u;
+          bs.put(e[q], len);
         }
       }
     }
