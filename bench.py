@@ -56,6 +56,18 @@ def parse():
     return p.parse_args()
 
 
+# The synthetic workloads (pzinputs), by what they stand in for.
+WORKLOADS = {
+    1: "codec smoke tensor: ReLU(N(0,1)) BF16, 1 MiB, plus 64 corner-case blocks",
+    2: "CNN feature maps, FP32 NCHW 32x64x56x56, ReLU of smoothed noise",
+    3: "GPT-2 (124M) BF16 saved activations, batch 8, seq 1024: MLP GELU 8x1024x3072, "
+       "causal attention probabilities 8x12x1024x1024",
+    4: "ViT-B/16 LayerNorm outputs 64x197x768, BF16 and FP32",
+    5: "GPT-2-XL BF16 saved activations, batch 8, seq 1024: MLP GELU 8x1024x6400, "
+       "causal softmax 8x25x1024x1024, residual 8x1024x1600",
+}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -215,11 +227,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u16 symbols (bf16 bit patterns), integer codec",
+        "dtype": ", ".join(sorted({f"u{t.elem_bits} symbols" for t in tensors})) + ", integer codec",
         "data": "synthetic (seeded generators in pzinputs, stand-ins for captured activations)",
         "config": {
-            "workload": "GPT-2-XL BF16 saved activations, batch 8, seq 1024: MLP GELU 8x1024x6400, "
-                        "causal softmax 8x25x1024x1024, residual 8x1024x1600",
+            "workload": WORKLOADS.get(args.config, f"config {args.config}"),
+            "tensors": [f"{t.name} {list(t.shape)}" for t in tensors],
             "raw_bytes": raw_total,
             "compressed_bytes": comp_total,
             "ratio": round(raw_total / comp_total, 4),
