@@ -565,7 +565,13 @@ __global__ __launch_bounds__(kGroupThreads) void decode_kernel(
   }
 
   // --- 1. Stage the 8 payloads (dword-aligned copies); wave w takes 2w, 2w+1
-  // (whose metadata its lanes 0 and 32 hold). ---
+  // (whose metadata its lanes 0 and 32 hold). A payload is at most 258
+  // 16-byte units, five per lane: every load of both chunks is issued before
+  // any is stored, so that the wave waits for memory once. ---
+  constexpr int kStageUnits = (kChunkBufDwords / 4 + kWave - 1) / kWave;
+  uint4 sv[2][kStageUnits];
+  uint32_t snq[2], sfull[2];
+  uint64_t sq0[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const uint32_t ci = 2 * wave + (uint32_t)h;
@@ -574,26 +580,43 @@ __global__ __launch_bounds__(kGroupThreads) void decode_kernel(
     const uint32_t H = (uint32_t)__builtin_amdgcn_readlane((int)my_H, 32 * h);
     const uint64_t q0 = (coff >> 2) & ~3ull;
     if (lane == 0) chunk_lead[ci] = coff == kBadChunk ? 0u : (uint32_t)(8 * (coff - 4 * q0));
-    if (coff == kBadChunk) continue;
-    const uint32_t lead_bytes = (uint32_t)(coff - 4 * q0);
-    const uint32_t nq = (lead_bytes + H + 15) / 16;  // 16-byte groups, at most 258
-    uint4 *buf4 = reinterpret_cast<uint4 *>(lds + ci * kChunkBufDwords);
-    const uint8_t *g = src + 4 * q0;
-    for (uint32_t i = lane; i < nq; i += kWave) {
-      const uint64_t b = 4 * q0 + 16ull * i;
-      uint4 v;
-      if (b + 16 <= comp_bytes) {
-        v = reinterpret_cast<const uint4 *>(g)[i];
-      } else {
+    const uint32_t nq = coff == kBadChunk ? 0u : ((uint32_t)(coff - 4 * q0) + H + 15) / 16;
+    // Units wholly inside the stream (the others, at its very end, are read
+    // byte by byte below); the loads are unconditional, clamped to the last
+    // such unit, so that none waits for another.
+    const uint64_t inside = comp_bytes > 4 * q0 ? (comp_bytes - 4 * q0) / 16 : 0;
+    const uint32_t nfull = nq < inside ? nq : (uint32_t)inside;
+    snq[h] = nq;
+    sfull[h] = nfull;
+    sq0[h] = q0;
+    const uint4 *g = reinterpret_cast<const uint4 *>(src + 4 * q0);
+    if (nfull > 0) {  // wave-uniform
+#pragma unroll
+      for (int k = 0; k < kStageUnits; ++k) {
+        const uint32_t u = lane + (uint32_t)kWave * k;
+        sv[h][k] = g[u < nfull ? u : nfull - 1];
+      }
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint4 *buf4 = reinterpret_cast<uint4 *>(lds + (2 * wave + (uint32_t)h) * kChunkBufDwords);
+#pragma unroll
+    for (int k = 0; k < kStageUnits; ++k) {
+      const uint32_t u = lane + (uint32_t)kWave * k;
+      if (u >= snq[h]) continue;
+      const uint64_t b = 4 * sq0[h] + 16ull * u;
+      if (u >= sfull[h]) {
+        // The stream's last bytes: byte loads below comp_bytes, zeros above.
         uint32_t tv[4] = {0, 0, 0, 0};
 #pragma unroll 1
-        for (uint32_t k = 0; k < 16 && b + k < comp_bytes; ++k) {
-          const uint32_t x = (uint32_t)src[b + k] << (8 * (k & 3));
-          if (k < 4) tv[0] |= x; else if (k < 8) tv[1] |= x; else if (k < 12) tv[2] |= x; else tv[3] |= x;
+        for (uint32_t q = 0; q < 16 && b + q < comp_bytes; ++q) {
+          const uint32_t x = (uint32_t)src[b + q] << (8 * (q & 3));
+          if (q < 4) tv[0] |= x; else if (q < 8) tv[1] |= x; else if (q < 12) tv[2] |= x; else tv[3] |= x;
         }
-        v = make_uint4(tv[0], tv[1], tv[2], tv[3]);
+        sv[h][k] = make_uint4(tv[0], tv[1], tv[2], tv[3]);
       }
-      buf4[i] = v;
+      buf4[u] = sv[h][k];
     }
   }
   __syncthreads();
