@@ -28,30 +28,6 @@ namespace pz {
 
 constexpr int32_t kStatusCorrupt = 3;
 
-// Bits of the stream in global memory, read through dword loads that never
-// touch a byte at or past `limit`.
-struct GlobalBits {
-  const uint8_t *src;
-  uint64_t limit;     // comp_bytes
-  uint64_t base_bit;  // bit offset of the chunk payload in the stream
-
-  PZ_DEV uint32_t dword(uint64_t q) const {
-    const uint64_t b = q * 4;
-    if (b + 4 <= limit) return *reinterpret_cast<const uint32_t *>(src + b);
-    uint32_t v = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      if (b + k < limit) v |= (uint32_t)src[b + k] << (8 * k);
-    return v;
-  }
-  // 32 stream bits starting at payload bit `pos`; bit 0 is the first.
-  PZ_DEV uint32_t peek(uint32_t pos) const {
-    const uint64_t a = base_bit + pos;
-    const uint64_t q = a >> 5;
-    return funnel(dword(q + 1), dword(q), (uint32_t)(a & 31));
-  }
-};
-
 // What the decoder needs of a codec mode: whether blocks carry a tag (else
 // every block is the fixed candidate), and the code of an all-zero block it
 // can settle at once: BX with all planes in one zero run, behind a BX tag or
@@ -474,43 +450,6 @@ PZ_DEV void read_planes(const LdsBits &in, uint32_t &pos, uint32_t (&t)[32], int
         t[j] = (uint32_t)ps;
       }
     }
-  }
-}
-
-// Stores a decoded block; the tensor's last block only up to raw_bytes.
-PZ_DEV void store_block(uint8_t *__restrict__ dst, uint64_t off, uint64_t raw_bytes,
-                        const uint32_t (&d)[32]) {
-  if (off + kBlockBytes <= raw_bytes) {
-    uint4 *p = reinterpret_cast<uint4 *>(dst + off);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) p[q] = make_uint4(d[4 * q], d[4 * q + 1], d[4 * q + 2], d[4 * q + 3]);
-  } else {
-    const uint64_t n = raw_bytes - off;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-        if (4 * (uint64_t)i + b < n) dst[off + 4 * i + b] = (uint8_t)(d[i] >> (8 * b));
-    }
-  }
-}
-
-// Inverse of the w = 16 plane construction: 16 planes of 64 bits to packed
-// symbols d[i] = sym 2i | sym 2i+1 << 16.
-PZ_DEV void symbols_from_planes16(const uint64_t (&P)[17], uint32_t (&d)[32]) {
-  uint32_t e[32];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    e[j] = (uint32_t)P[j];
-    e[j + 16] = (uint32_t)(P[j] >> 32);
-  }
-  transpose32(e);  // e[r] = sym r | sym r+32 << 16
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    if (i < 16)
-      d[i] = (e[2 * i] & 0xFFFFu) | (e[2 * i + 1] << 16);
-    else
-      d[i] = (e[2 * i - 32] >> 16) | (e[2 * i - 31] & 0xFFFF0000u);
   }
 }
 
