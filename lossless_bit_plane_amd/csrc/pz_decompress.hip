@@ -111,11 +111,11 @@ PZ_DEV uint32_t group_or(uint32_t v) {
 }
 
 // A chunk's stream, read by the chunk's group through the LDS ring. The ring
-// is topped up only at block starts: the 32 dwords requested at the previous
-// block start are stored, and the next 32 are requested if the ring will have
-// room for them; only if fewer than one block's worth of dwords is then
-// buffered does the group wait for a load on the spot. Each of the G lanes
-// holds and stores 32/G of the 32 dwords.
+// is topped up only at block starts, and only when some group of the wave has
+// fewer than one block's worth of dwords buffered: then every group stores the
+// 32 dwords it requested at the last such round and requests the next 32 if
+// the ring will have room for them, and a group still short waits for a load
+// on the spot. Each of the G lanes holds and stores 32/G of the 32 dwords.
 template <int G>
 struct ChunkRing {
   static constexpr int kPart = kGroupDwords / G;  // dwords per lane per refill
@@ -193,13 +193,19 @@ struct ChunkRing {
   // dwords [dword of pos, +kBlockAhead) available and requests the next group.
   PZ_DEV void step(uint32_t pos) {
     const uint32_t cur = (lead + pos) >> 5;
-    if (pending) commit();
-    while (fill < cur + kBlockAhead) {
-      issue();
-      commit();
+    // A wave waits for all its loads at once, so the groups of a wave store
+    // and request in common rounds, and a round is held only when some group
+    // is short of buffered dwords: the loads of the last round have then had
+    // every step since to arrive.
+    if (__ballot(fill < cur + kBlockAhead)) {
+      if (pending) commit();
+      while (fill < cur + kBlockAhead) {
+        issue();
+        commit();
+      }
+      // Stored dwords at or above cur stay in the ring until the group passes them.
+      if (fill + kGroupDwords <= cur + kRingDwords) issue();
     }
-    // Stored dwords at or above cur stay in the ring until the group passes them.
-    if (fill + kGroupDwords <= cur + kRingDwords) issue();
     wave_lds_fence();  // the group's stores before its reads
   }
   PZ_DEV uint32_t peek(uint32_t pos) const {
