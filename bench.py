@@ -3,11 +3,16 @@
 One step = compress and then decompress every tensor of the workload (the
 GPT-2-XL activations at batch 8, sequence 1024: MLP GELU output 8x1024x6400,
 causal softmax 8x25x1024x1024, residual 8x1024x1600, all BF16, ~0.55 GB),
-back to back on one stream, with inputs already resident in HBM. Before every
-step (warm-up and timed) a 1 GiB buffer is written, outside the timed region,
-so that no step finds its inputs in the 256 MB last-level cache (MALL); each
-timed step is bracketed by device synchronizations and timed with HIP events.
-Prints one JSON line.
+each tensor into and out of its own stream, on one HIP stream, with inputs
+already resident in HBM: one pz_compress_batch call and then one
+pz_decompress_batch call over the tensors (one launch per kernel). The same
+step made of one pz_compress / pz_decompress call per tensor is timed as well
+(`per_call`, and the per-tensor rates). Before every step (warm-up and timed)
+a 1 GiB buffer is written, outside the timed region, so that no step finds
+its inputs in the 256 MB last-level cache (MALL); each timed step is
+bracketed by device synchronizations and timed with HIP events recorded
+behind the flush (so the host has enqueued the step before the GPU starts
+it). Prints one JSON line.
 
 value = raw bytes of the workload / mean time of one step (each raw byte is
 both compressed and decompressed in a step). The roofline object reports the
@@ -124,7 +129,30 @@ def main():
         if flush_buf is not None:
             flush_buf.fill_(0x5A)
 
+    # Batched step: one call per direction for each (dtype, width) group of
+    # tensors (the bench workload is one group).
+    groups = {}
+    for it in items:
+        groups.setdefault((it["t"].dtype, it["t"].elem_bits), []).append(it)
+    for (dt, w), g in groups.items():
+        g[0]["group_out"] = torch.zeros(len(g), dtype=torch.int64, device=dev)
+        g[0]["group_status"] = torch.zeros(len(g), dtype=torch.int32, device=dev)
+
     def step(events=None):
+        if events is not None:
+            events[0].record(cur)
+        for (dt, w), g in groups.items():
+            pz.pz_compress_batch([it["src"] for it in g], dt, w, [it["stream"] for it in g], g[0]["group_out"])
+        if events is not None:
+            events[1].record(cur)
+        for (dt, w), g in groups.items():
+            pz.pz_decompress_batch([it["stream"] for it in g], [it["comp"] for it in g],
+                                   [it["t"].nbytes for it in g], dt, w, [it["out"] for it in g],
+                                   g[0]["group_status"])
+        if events is not None:
+            events[2].record(cur)
+
+    def step_calls(events=None):
         for i, it in enumerate(items):
             t = it["t"]
             if events is not None:
@@ -141,32 +169,51 @@ def main():
             if events is not None:
                 events[i][3].record(cur)
 
+    def verify(what):
+        for it in items:
+            assert int(it["status"].item()) == 0, f"{what}: decompress reported a corrupt stream"
+            assert torch.equal(it["out"], it["src"]), f"{what}: round trip mismatch on {it['t'].name}"
+        for g in groups.values():
+            assert not g[0]["group_status"].any().item(), f"{what}: decompress reported a corrupt stream"
+            assert [int(v) for v in g[0]["group_out"].tolist()] == [it["comp"] for it in g], what
+        log(f"{what}: round trip verified on the device")
+
     for _ in range(args.warmup):
+        flush()
+        step_calls()
         flush()
         step()
     torch.cuda.synchronize()
-
     if not args.no_verify:
-        for it in items:
-            assert int(it["status"].item()) == 0, "decompress reported a corrupt stream"
-            assert torch.equal(it["out"], it["src"]), f"round trip mismatch on {it['t'].name}"
-        log("round trip verified on the device")
+        verify("warm-up")
 
-    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in items]
-          for _ in range(args.steps)]
-    step_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    wall = 0.0
-    for k in range(args.steps):
-        flush()
+    def timed_steps(fn, nev):
+        # Each step sits between two device synchronizations. The cache flush
+        # is enqueued first and the step's start event behind it, so the
+        # host has enqueued the whole step by the time the GPU reaches it
+        # (the events time the GPU's work, not the host's submission).
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+        step_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
         torch.cuda.synchronize()
-        start = time.perf_counter()
-        step_ev[k][0].record(cur)
-        step(ev[k])
-        step_ev[k][1].record(cur)
-        torch.cuda.synchronize()
-        wall += time.perf_counter() - start
-    step_ms = np.array([a.elapsed_time(b) for a, b in step_ev])
+        enqueue = 0.0
+        for k in range(args.steps):
+            torch.cuda.synchronize()
+            flush()
+            start = time.perf_counter()
+            step_ev[k][0].record(cur)
+            fn(ev[k])
+            step_ev[k][1].record(cur)
+            enqueue += time.perf_counter() - start
+            torch.cuda.synchronize()
+        return ev, np.array([a.elapsed_time(b) for a, b in step_ev]), enqueue
+
+    # One pz_compress / pz_decompress call per tensor: per-tensor rates.
+    ev_c, step_ms_c, _ = timed_steps(
+        lambda e: step_calls([[e[4 * i + j] for j in range(4)] for i in range(len(items))]), 4 * len(items))
+    # The batched step: the bench line.
+    ev, step_ms, wall = timed_steps(step, 3)
+    if not args.no_verify:
+        verify("timed steps")
 
     raw_total = sum(it["t"].nbytes for it in items)
     comp_total = sum(it["comp"] for it in items)
@@ -174,23 +221,25 @@ def main():
     t_dec = np.zeros(len(items))
     for k in range(args.steps):
         for i in range(len(items)):
-            t_comp[i] += ev[k][i][0].elapsed_time(ev[k][i][1]) / 1e3
-            t_dec[i] += ev[k][i][2].elapsed_time(ev[k][i][3]) / 1e3
+            t_comp[i] += ev_c[k][4 * i].elapsed_time(ev_c[k][4 * i + 1]) / 1e3
+            t_dec[i] += ev_c[k][4 * i + 2].elapsed_time(ev_c[k][4 * i + 3]) / 1e3
     t_comp /= args.steps
     t_dec /= args.steps
     ms_per_step = float(step_ms.mean())
     value = raw_total / (ms_per_step / 1e3) / 1e9
 
-    comp_s, dec_s = t_comp.sum(), t_dec.sum()
+    comp_s = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) / 1e3
+    dec_s = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) / 1e3
     algo = raw_total + comp_total  # algorithmic HBM bytes per direction
     comp_gbps = algo / comp_s / 1e9
     dec_gbps = algo / dec_s / 1e9
-    # The dominant kernel is compress_kernel (the pz_compress call is that
-    # kernel plus a scratch-clearing fill): it reads R and writes C per tensor.
-    traffic, traffic_note = measured_traffic("compress_kernel<16>", [it["t"].name for it in items])
+    # The dominant kernel is compress_kernel (a pz_compress_batch call is
+    # one launch of it over the group's tensors): it reads R and writes C.
+    traffic, traffic_note = measured_traffic(
+        "compress_kernel<16>", [batch_name([it["t"].name for it in g]) for g in groups.values()])
     roofline = {
         "bound": "hbm",
-        "kernel": "compress_kernel (pz_compress call, one launch per tensor)",
+        "kernel": "compress_kernel (one pz_compress_batch launch over the workload's tensors)",
         "achieved": round(comp_gbps, 1),
         "peak": HBM_PEAK_GBPS,
         "unit": "GB/s",
@@ -216,6 +265,15 @@ def main():
     size_only = measure_size_only(pz, items, flush, cur)
     swap = None if args.no_swap else measure_swap(pz, items, flush)
 
+    ms_calls = float(step_ms_c.mean())
+    per_call = {
+        "ms_per_step": round(ms_calls, 4),
+        "value": round(raw_total / (ms_calls / 1e3) / 1e9, 2),
+        "compress_raw_gbps": round(raw_total / t_comp.sum() / 1e9, 1),
+        "decompress_raw_gbps": round(raw_total / t_dec.sum() / 1e9, 1),
+        "step_ms_median": round(float(np.median(step_ms_c)), 4),
+    }
+
     out = {
         "metric": "compress & decompress GB/s (raw bytes), % of HBM roofline; ratio = oracle",
         "value": round(value, 2),
@@ -236,15 +294,18 @@ def main():
             "compressed_bytes": comp_total,
             "ratio": round(raw_total / comp_total, 4),
             "parallelism": "single GPU",
+            "calls": "pz_compress_batch then pz_decompress_batch over the tensors (separate streams, "
+                     "one launch per kernel); per_call: one call per tensor and direction",
         },
         "step_ms": {"median": round(p50, 4), "p10": round(p10, 4), "p90": round(p90, 4),
-                    "host_wall_mean": round(wall / args.steps * 1e3, 4),
+                    "host_enqueue_ms_mean": round(wall / args.steps * 1e3, 4),
                     "cache_flush_before_each_step": flush_buf is not None},
         "compress_raw_gbps": round(raw_total / comp_s / 1e9, 1),
         "decompress_raw_gbps": round(raw_total / dec_s / 1e9, 1),
         "compress_hbm_frac": round(comp_gbps / HBM_PEAK_GBPS, 4),
         "decompress_hbm_frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
         "roofline": roofline,
+        "per_call": per_call,
         "cpu_baseline": cpu,
         "tensors": per_tensor,
         "size_only": size_only,
@@ -480,11 +541,16 @@ def kernel_source_hash(kernel):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel, tensor_names):
+def batch_name(tensor_names):
+    """Name of a batched launch over these tensors in the profile summaries."""
+    return "batch(" + ",".join(tensor_names) + ")"
+
+
+def measured_traffic(kernel, launch_names):
     """HBM bytes (FETCH_SIZE + WRITE_SIZE, calibrated against a plain copy)
-    of one launch of `kernel` per tensor, summed over the workload's tensors,
-    from the committed rocprofv3 summary; None when the kernels changed since
-    the counters were taken."""
+    of the named launches of `kernel` (a tensor's name, or batch_name of a
+    batched launch), summed, from the committed rocprofv3 summary; None when
+    the kernels changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic_gpt2xl_config5.json")
     if not os.path.exists(path):
         return None, "no counter summary"
@@ -494,12 +560,12 @@ def measured_traffic(kernel, tensor_names):
     if not isinstance(hashes, dict) or hashes.get(kernel.split("<")[0]) != kernel_source_hash(kernel):
         return None, f"{kernel} changed since the counters in profiles/ were taken"
     total = 0.0
-    for name in tensor_names:
+    for name in launch_names:
         t = prof["traffic"].get(f"{kernel}:{name}")
         if t is None:
             return None, f"no counters for {kernel} on {name}"
         total += t["fetch_bytes"] + t["write_bytes"]
-    return round(total), "profiles/hbm_traffic_gpt2xl_config5.json (sum over the tensors' launches)"
+    return round(total), "profiles/hbm_traffic_gpt2xl_config5.json (the batched launch)"
 
 
 def cpu_baseline(tensors, sample_mb):

@@ -135,6 +135,38 @@ pz_status_t pz_decompress_ex(const void *d_src, size_t comp_bytes, int dtype,
                              void *d_dst, size_t raw_bytes, int32_t *d_status,
                              void *stream);
 
+/* Batched calls: pz_compress / pz_decompress on `count` separate tensors of
+ * one (dtype, elem_bits) in as few launches as possible (up to 8 tensors per
+ * launch), for callers that code several tensors at once — the swaps waiting
+ * on a copy queue, or every saved tensor measured in the profiling iteration
+ * (PlaneZip paper, §III-B and §III-C). Tensor i gets exactly the stream (or
+ * output and status) that the single call would give it; streams are not
+ * concatenated.
+ *   count            >= 0 (0: nothing is enqueued)
+ *   d_srcs, d_dsts   host arrays of count device pointers (16-byte aligned;
+ *                    a tensor's pointers may be null when its size is 0)
+ *   raw_bytes,       host arrays of count sizes, as in the single calls
+ *   comp_bytes,
+ *   dst_capacities
+ *   d_out_bytes      device array of count uint64 (compress)
+ *   d_status         nullable device array of count int32 (decompress)
+ * Every tensor is checked before anything is enqueued: the first failing
+ * check's status is returned (PZ_ERROR_INVALID_VALUE,
+ * PZ_ERROR_INSUFFICIENT_BUFFER, or PZ_ERROR_CORRUPT_STREAM for a comp_bytes
+ * below 2*chunks) and no tensor is coded. The host arrays are read before
+ * the call returns; device buffers follow the single calls' rules, and the
+ * tensors of one call must not overlap one another's outputs. */
+pz_status_t pz_compress_batch(int count, const void *const *d_srcs,
+                              const size_t *raw_bytes, int dtype, int elem_bits,
+                              void *const *d_dsts, const size_t *dst_capacities,
+                              uint64_t *d_out_bytes, void *stream);
+
+pz_status_t pz_decompress_batch(int count, const void *const *d_srcs,
+                                const size_t *comp_bytes, int dtype,
+                                int elem_bits, void *const *d_dsts,
+                                const size_t *raw_bytes, int32_t *d_status,
+                                void *stream);
+
 /* Sampled size: the pz_compressed_size measurement over chunks 0, stride,
  * 2*stride, ... only (the paper's methodology sizes tensors above 32 MB on
  * every fourth 4 KB chunk, §IV "Tensor capture"), at 1/stride of the work.

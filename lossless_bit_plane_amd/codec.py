@@ -5,6 +5,8 @@ torch stream. Every call only enqueues work, like the C functions.
 """
 from __future__ import annotations
 
+import ctypes
+
 import torch
 
 from ._lib import PZ_ERROR_CORRUPT_STREAM, PlaneZipError, check, lib
@@ -160,6 +162,52 @@ def pz_decompress_ex(src: torch.Tensor, comp_bytes: int, raw_bytes: int, dtype: 
     check(lib.pz_decompress_ex(_ptr(b), comp_bytes, dtype, elem_bits, codec_mask, int(tagged),
                                _ptr(dst), raw_bytes, _ptr(status), _stream(stream)), "pz_decompress_ex")
     return dst, status
+
+
+def _ptr_array(ts):
+    return (ctypes.c_void_p * max(1, len(ts)))(*[_ptr(t) for t in ts])
+
+
+def _size_array(vals):
+    return (ctypes.c_size_t * max(1, len(vals)))(*[int(v) for v in vals])
+
+
+def pz_compress_batch(srcs, dtype: int, elem_bits: int, dsts=None, out_bytes: torch.Tensor | None = None,
+                      stream=None):
+    """pz_compress on several tensors of one (dtype, elem_bits) in as few
+    launches as possible. Returns (dsts, out_bytes): a list of uint8 streams
+    (capacity max_compressed_bytes each) and a device int64 tensor (n,)."""
+    bs = [_byte_view(t) for t in srcs]
+    if not bs:
+        raise ValueError("pz_compress_batch: no tensors")
+    dev = bs[0].device
+    if dsts is None:
+        dsts = [torch.empty(max(max_compressed_bytes(b.numel()), 16), dtype=torch.uint8, device=dev) for b in bs]
+    if out_bytes is None:
+        out_bytes = torch.empty(len(bs), dtype=torch.int64, device=dev)
+    check(lib.pz_compress_batch(len(bs), _ptr_array(bs), _size_array([b.numel() for b in bs]), dtype, elem_bits,
+                                _ptr_array(dsts), _size_array([d.numel() for d in dsts]), _ptr(out_bytes),
+                                _stream(stream)), "pz_compress_batch")
+    return dsts, out_bytes
+
+
+def pz_decompress_batch(srcs, comp_bytes, raw_bytes, dtype: int, elem_bits: int, dsts=None,
+                        status: torch.Tensor | None = None, stream=None):
+    """pz_decompress on several streams of one (dtype, elem_bits). Returns
+    (dsts, status): a list of uint8 tensors (raw_bytes each) and a device
+    int32 tensor (n,)."""
+    bs = [_byte_view(t) for t in srcs]
+    if not bs or len(comp_bytes) != len(bs) or len(raw_bytes) != len(bs):
+        raise ValueError("pz_decompress_batch: one comp_bytes and raw_bytes per stream")
+    dev = bs[0].device
+    if dsts is None:
+        dsts = [torch.empty(max(int(r), 16), dtype=torch.uint8, device=dev) for r in raw_bytes]
+    if status is None:
+        status = torch.empty(len(bs), dtype=torch.int32, device=dev)
+    check(lib.pz_decompress_batch(len(bs), _ptr_array(bs), _size_array(comp_bytes), dtype, elem_bits,
+                                  _ptr_array(dsts), _size_array(raw_bytes), _ptr(status), _stream(stream)),
+          "pz_decompress_batch")
+    return dsts, status
 
 
 def compress(t: torch.Tensor, dtype=None, elem_bits=None):

@@ -41,8 +41,8 @@ pz_status_t from_hip(hipError_t e) { return e == hipSuccess ? PZ_SUCCESS : PZ_ER
 // and the tile counter keeps counting (a call counts its tiles from where the
 // previous one left it). The buffer grows (stream-ordered free and
 // allocation, then one clearing) when a call needs more, and is cleared again
-// when the epoch wraps. Buffer layout: the tile counter and the error word
-// (16 bytes), the look-back words, the per-call bytes.
+// when the epoch wraps. Buffer layout: the tile counter and the error words
+// of a launch's tensors (48 bytes), the look-back words, the per-call bytes.
 // ---------------------------------------------------------------------------
 struct ScratchEntry {
   int device;
@@ -55,7 +55,8 @@ struct ScratchEntry {
   bool clear;         // the header and words must be cleared before the next call
 };
 
-constexpr size_t kScratchHeader = 16;
+constexpr size_t kScratchHeader = 48;
+static_assert(4 + 4 * pz::kMaxBatch <= kScratchHeader, "counter and error words");
 
 std::mutex g_scratch_mu;
 std::vector<ScratchEntry> g_scratch;
@@ -114,6 +115,124 @@ hipError_t with_scratch(hipStream_t stream, const pz::ScratchNeed &need, F launc
   else
     ent->clear = true;
   return e;
+}
+
+// Compress calls: every tensor is checked first (nothing is enqueued if one
+// fails); then tensors with chunks go out in launches of up to kMaxBatch,
+// and an empty tensor's size is set to 0.
+pz_status_t compress_many(int dtype, int elem_bits, uint32_t codec_mask, int tagged, int count,
+                          const void *const *srcs, const size_t *raw, void *const *dsts, const size_t *caps,
+                          uint64_t *d_out_bytes, void *stream) {
+  const int w = symbol_width(dtype, elem_bits);
+  if (w < 0 || !valid_mode(codec_mask, tagged) || count < 0 || (reinterpret_cast<uintptr_t>(d_out_bytes) & 7u))
+    return PZ_ERROR_INVALID_VALUE;
+  if (count > 0 && (!srcs || !raw || !dsts || !caps || !d_out_bytes)) return PZ_ERROR_INVALID_VALUE;
+  for (int i = 0; i < count; ++i) {
+    if (raw[i] && (!srcs[i] || !dsts[i])) return PZ_ERROR_INVALID_VALUE;
+    if (!aligned16(srcs[i]) || !aligned16(dsts[i])) return PZ_ERROR_INVALID_VALUE;
+  }
+  for (int i = 0; i < count; ++i)
+    if (caps[i] < PZ_MAX_COMPRESSED_BYTES(raw[i])) return PZ_ERROR_INSUFFICIENT_BUFFER;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int i = 0;
+  while (i < count) {
+    pz::CBatch b{};
+    while (i < count && b.n < (uint32_t)pz::kMaxBatch) {
+      if (raw[i] == 0) {
+        const hipError_t e = pz::fill_u64(d_out_bytes + i, 1, 0, s);
+        if (e != hipSuccess) return from_hip(e);
+        ++i;
+        continue;
+      }
+      pz::CTensor &x = b.t[b.n++];
+      x.src = static_cast<const uint8_t *>(srcs[i]);
+      x.dst = static_cast<uint8_t *>(dsts[i]);
+      x.out_bytes = d_out_bytes + i;
+      x.raw_bytes = raw[i];
+      x.nchunks = PZ_NUM_CHUNKS(raw[i]);
+      x.tile_begin = b.total_tiles;
+      x.ntiles = pz::compress_tiles(raw[i]);
+      b.total_tiles += x.ntiles;
+      ++i;
+    }
+    if (b.n == 0) continue;
+    const pz::ScratchNeed need{b.total_tiles, 0, b.total_tiles};
+    const hipError_t e = with_scratch(s, need, [&](const pz::Scratch &sc) {
+      return pz::launch_compress(w, b, codec_mask, tagged, sc, s);
+    });
+    if (e != hipSuccess) return from_hip(e);
+  }
+  return PZ_SUCCESS;
+}
+
+// Decompress calls, checked and launched as compress_many; an empty tensor
+// gets its status from comp_bytes alone. Within a launch the densest streams
+// (most stream bytes per raw byte) come first, so that the longest chunk
+// walks start first.
+pz_status_t decompress_many(int dtype, int elem_bits, uint32_t codec_mask, int tagged, int count,
+                            const void *const *srcs, const size_t *comp, void *const *dsts, const size_t *raw,
+                            int32_t *d_status, void *stream) {
+  const int w = symbol_width(dtype, elem_bits);
+  if (w < 0 || !valid_mode(codec_mask, tagged) || count < 0 || (reinterpret_cast<uintptr_t>(d_status) & 3u))
+    return PZ_ERROR_INVALID_VALUE;
+  if (count > 0 && (!srcs || !comp || !dsts || !raw)) return PZ_ERROR_INVALID_VALUE;
+  for (int i = 0; i < count; ++i) {
+    if ((comp[i] && !srcs[i]) || (raw[i] && !dsts[i])) return PZ_ERROR_INVALID_VALUE;
+    if (!aligned16(srcs[i]) || !aligned16(dsts[i])) return PZ_ERROR_INVALID_VALUE;
+  }
+  for (int i = 0; i < count; ++i)
+    if (comp[i] < 2 * PZ_NUM_CHUNKS(raw[i])) return PZ_ERROR_CORRUPT_STREAM;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int i = 0;
+  while (i < count) {
+    int idx[pz::kMaxBatch];
+    int n = 0;
+    while (i < count && n < pz::kMaxBatch) {
+      if (raw[i] == 0) {
+        const hipError_t e = pz::launch_empty_status(d_status ? d_status + i : nullptr, comp[i], s);
+        if (e != hipSuccess) return from_hip(e);
+      } else {
+        idx[n++] = i;
+      }
+      ++i;
+    }
+    if (n == 0) continue;
+    // Densest first (insertion sort on comp / raw, compared as products).
+    for (int a = 1; a < n; ++a)
+      for (int c = a; c > 0; --c) {
+        const unsigned __int128 l = (unsigned __int128)comp[idx[c]] * raw[idx[c - 1]];
+        const unsigned __int128 r = (unsigned __int128)comp[idx[c - 1]] * raw[idx[c]];
+        if (l <= r) break;
+        const int tmp = idx[c];
+        idx[c] = idx[c - 1];
+        idx[c - 1] = tmp;
+      }
+    pz::DBatch b{};
+    size_t extra = 0;
+    for (int a = 0; a < n; ++a) {
+      const int j = idx[a];
+      pz::DTensor &x = b.t[b.n++];
+      x.src = static_cast<const uint8_t *>(srcs[j]);
+      x.dst = static_cast<uint8_t *>(dsts[j]);
+      x.status = d_status ? d_status + j : nullptr;
+      x.comp_bytes = comp[j];
+      x.raw_bytes = raw[j];
+      x.nchunks = PZ_NUM_CHUNKS(raw[j]);
+      x.tile_begin = b.total_tiles;
+      x.ntiles = pz::locate_tiles(raw[j]);
+      x.group_begin = b.total_groups;
+      x.ngroups = pz::decode_groups(raw[j]);
+      b.total_tiles += x.ntiles;
+      b.total_groups += x.ngroups;
+      extra += pz::decompress_extra(raw[j]);
+    }
+    const pz::ScratchNeed need{b.total_tiles, extra, b.total_tiles};
+    const hipError_t e = with_scratch(s, need, [&](const pz::Scratch &sc) {
+      return pz::launch_decompress(w, b, codec_mask, tagged, sc, s);
+    });
+    if (e != hipSuccess) return from_hip(e);
+  }
+  return PZ_SUCCESS;
 }
 
 }  // namespace
@@ -175,17 +294,8 @@ pz_status_t pz_block_sizes(const void *d_src, size_t raw_bytes, int dtype, int e
 pz_status_t pz_compress_ex(const void *d_src, size_t raw_bytes, int dtype, int elem_bits,
                            uint32_t codec_mask, int tagged, void *d_dst, size_t dst_capacity,
                            uint64_t *d_out_bytes, void *stream) {
-  const int w = symbol_width(dtype, elem_bits);
-  if (w < 0 || !valid_mode(codec_mask, tagged) || !d_out_bytes || (raw_bytes && (!d_src || !d_dst)))
-    return PZ_ERROR_INVALID_VALUE;
-  if (!aligned16(d_src) || !aligned16(d_dst) || (reinterpret_cast<uintptr_t>(d_out_bytes) & 7u))
-    return PZ_ERROR_INVALID_VALUE;
-  if (dst_capacity < PZ_MAX_COMPRESSED_BYTES(raw_bytes)) return PZ_ERROR_INSUFFICIENT_BUFFER;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  return from_hip(with_scratch(s, pz::compress_scratch_need(raw_bytes), [&](const pz::Scratch &sc) {
-    return pz::launch_compress(w, static_cast<const uint8_t *>(d_src), raw_bytes, codec_mask, tagged,
-                               static_cast<uint8_t *>(d_dst), d_out_bytes, sc, s);
-  }));
+  return compress_many(dtype, elem_bits, codec_mask, tagged, 1, &d_src, &raw_bytes, &d_dst, &dst_capacity,
+                       d_out_bytes, stream);
 }
 
 pz_status_t pz_compress(const void *d_src, size_t raw_bytes, int dtype, int elem_bits, void *d_dst,
@@ -194,26 +304,31 @@ pz_status_t pz_compress(const void *d_src, size_t raw_bytes, int dtype, int elem
                         d_out_bytes, stream);
 }
 
+pz_status_t pz_compress_batch(int count, const void *const *d_srcs, const size_t *raw_bytes, int dtype,
+                              int elem_bits, void *const *d_dsts, const size_t *dst_capacities,
+                              uint64_t *d_out_bytes, void *stream) {
+  return compress_many(dtype, elem_bits, PZ_CODEC_ALL, 1, count, d_srcs, raw_bytes, d_dsts, dst_capacities,
+                       d_out_bytes, stream);
+}
+
 pz_status_t pz_decompress_ex(const void *d_src, size_t comp_bytes, int dtype, int elem_bits,
                              uint32_t codec_mask, int tagged, void *d_dst, size_t raw_bytes,
                              int32_t *d_status, void *stream) {
-  const int w = symbol_width(dtype, elem_bits);
-  if (w < 0 || !valid_mode(codec_mask, tagged) || (comp_bytes && !d_src) || (raw_bytes && !d_dst))
-    return PZ_ERROR_INVALID_VALUE;
-  if (!aligned16(d_src) || !aligned16(d_dst) || (reinterpret_cast<uintptr_t>(d_status) & 3u))
-    return PZ_ERROR_INVALID_VALUE;
-  if (comp_bytes < 2 * PZ_NUM_CHUNKS(raw_bytes)) return PZ_ERROR_CORRUPT_STREAM;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  return from_hip(with_scratch(s, pz::decompress_scratch_need(raw_bytes), [&](const pz::Scratch &sc) {
-    return pz::launch_decompress(w, static_cast<const uint8_t *>(d_src), comp_bytes, codec_mask, tagged,
-                                 static_cast<uint8_t *>(d_dst), raw_bytes, d_status, sc, s);
-  }));
+  return decompress_many(dtype, elem_bits, codec_mask, tagged, 1, &d_src, &comp_bytes, &d_dst, &raw_bytes,
+                         d_status, stream);
 }
 
 pz_status_t pz_decompress(const void *d_src, size_t comp_bytes, int dtype, int elem_bits,
                           void *d_dst, size_t raw_bytes, int32_t *d_status, void *stream) {
   return pz_decompress_ex(d_src, comp_bytes, dtype, elem_bits, PZ_CODEC_ALL, 1, d_dst, raw_bytes,
                           d_status, stream);
+}
+
+pz_status_t pz_decompress_batch(int count, const void *const *d_srcs, const size_t *comp_bytes, int dtype,
+                                int elem_bits, void *const *d_dsts, const size_t *raw_bytes,
+                                int32_t *d_status, void *stream) {
+  return decompress_many(dtype, elem_bits, PZ_CODEC_ALL, 1, count, d_srcs, comp_bytes, d_dsts, raw_bytes,
+                         d_status, stream);
 }
 
 }  // extern "C"

@@ -456,10 +456,9 @@ PZ_DEV void emit_zero_block(uint32_t *buf, uint32_t off, const Mode &m) {
 }
 
 template <int W>
-__global__ __launch_bounds__(kCThreads, 2) void compress_kernel(
-    const uint8_t *__restrict__ src, uint64_t raw_bytes, uint64_t nchunks, uint64_t ntiles,
-    uint8_t *__restrict__ dst, uint64_t *__restrict__ out_bytes, uint64_t *status,
-    uint32_t *tile_counter, uint32_t counter_base, uint32_t epoch, Mode mode) {
+__global__ __launch_bounds__(kCThreads, 2) void compress_kernel(const CBatch batch, uint64_t *lb_words,
+                                                                 uint32_t *tile_counter, uint32_t counter_base,
+                                                                 uint32_t epoch, Mode mode) {
   constexpr int N = 1024 / W;
   constexpr uint32_t R = W == 16 ? 4 : 5;
   using PT = typename std::conditional<W == 16, uint64_t, uint32_t>::type;
@@ -479,8 +478,18 @@ __global__ __launch_bounds__(kCThreads, 2) void compress_kernel(
   const uint32_t wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform: a scalar
   if (t == 0) group_tile = atomicAdd(tile_counter, 1u) - counter_base;
   __syncthreads();
-  const uint32_t tile = group_tile;
-  if (tile >= ntiles) return;
+  // The launch's tile -> the tensor it belongs to and the tile within it.
+  const uint32_t gtile = __builtin_amdgcn_readfirstlane(group_tile);
+  if (gtile >= batch.total_tiles) return;
+  uint32_t k = 0;
+#pragma unroll
+  for (uint32_t i = 1; i < (uint32_t)kMaxBatch; ++i) k += i < batch.n && gtile >= batch.t[i].tile_begin ? 1u : 0u;
+  const uint8_t *__restrict__ src = batch.t[k].src;
+  uint8_t *__restrict__ dst = batch.t[k].dst;
+  const uint64_t raw_bytes = batch.t[k].raw_bytes, nchunks = batch.t[k].nchunks;
+  const uint32_t ntiles = batch.t[k].ntiles;
+  const uint32_t tile = gtile - batch.t[k].tile_begin;
+  uint64_t *status = lb_words + batch.t[k].tile_begin;
 
   // --- 1. Load block t; count its non-zero symbols. ---
   // (Block and chunk indices are recomputed where needed rather than kept
@@ -796,7 +805,7 @@ __global__ __launch_bounds__(kCThreads, 2) void compress_kernel(
   if (wave == 0) {
     const uint64_t before = lookback_resolve(status, tile, agg, epoch);
     if (lane < (uint32_t)kGroupChunks) chunk_pay[lane] = 2 * nchunks + before + (inc - l);
-    if (tile == ntiles - 1 && lane == 0) *out_bytes = 2 * nchunks + before + agg;
+    if (tile == ntiles - 1 && lane == 0) *batch.t[k].out_bytes = 2 * nchunks + before + agg;
   }
   __syncthreads();
 
@@ -1023,27 +1032,20 @@ hipError_t launch_block_sizes(int w, const uint8_t *src, uint64_t raw_bytes, uin
   return hipGetLastError();
 }
 
-ScratchNeed compress_scratch_need(uint64_t raw_bytes) {
+uint32_t compress_tiles(uint64_t raw_bytes) {
   const uint64_t nchunks = (raw_bytes + kChunkBytes - 1) / kChunkBytes;
-  const uint64_t ntiles = (nchunks + kGroupChunks - 1) / kGroupChunks;
-  return ScratchNeed{(size_t)ntiles, 0, (uint32_t)ntiles};
+  return (uint32_t)((nchunks + kGroupChunks - 1) / kGroupChunks);
 }
 
-hipError_t launch_compress(int w, const uint8_t *src, uint64_t raw_bytes, uint32_t codec_mask,
-                           int tagged, uint8_t *dst, uint64_t *out_bytes, const Scratch &scratch,
-                           hipStream_t stream) {
-  const uint64_t nchunks = (raw_bytes + kChunkBytes - 1) / kChunkBytes;
-  if (nchunks == 0) return fill_u64(out_bytes, 1, 0, stream);
-  const uint64_t ntiles = (nchunks + kGroupChunks - 1) / kGroupChunks;
+hipError_t launch_compress(int w, const CBatch &batch, uint32_t codec_mask, int tagged,
+                           const Scratch &scratch, hipStream_t stream) {
   const Mode mode = make_mode(w, codec_mask, tagged);
   if (w == 16)
-    hipLaunchKernelGGL(compress_kernel<16>, dim3((unsigned)ntiles), dim3(kCThreads), 0, stream, src,
-                       raw_bytes, nchunks, ntiles, dst, out_bytes, scratch.words, scratch.counter,
-                       scratch.counter_base, scratch.epoch, mode);
+    hipLaunchKernelGGL(compress_kernel<16>, dim3(batch.total_tiles), dim3(kCThreads), 0, stream, batch,
+                       scratch.words, scratch.counter, scratch.counter_base, scratch.epoch, mode);
   else
-    hipLaunchKernelGGL(compress_kernel<32>, dim3((unsigned)ntiles), dim3(kCThreads), 0, stream, src,
-                       raw_bytes, nchunks, ntiles, dst, out_bytes, scratch.words, scratch.counter,
-                       scratch.counter_base, scratch.epoch, mode);
+    hipLaunchKernelGGL(compress_kernel<32>, dim3(batch.total_tiles), dim3(kCThreads), 0, stream, batch,
+                       scratch.words, scratch.counter, scratch.counter_base, scratch.epoch, mode);
   return hipGetLastError();
 }
 

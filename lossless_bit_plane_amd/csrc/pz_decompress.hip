@@ -308,11 +308,10 @@ PZ_DEV bool parse_chunk(ChunkRing<G> &in, bool coded, uint32_t H, uint32_t raw_l
 }
 
 template <int W, int G>
-__global__ __launch_bounds__(kLocateChunks * G) void locate_kernel(
-    const uint8_t *__restrict__ src, uint64_t comp_bytes, uint64_t raw_bytes, uint64_t nchunks,
-    uint64_t ntiles, uint64_t *__restrict__ chunk_off, uint16_t *__restrict__ block_off,
-    uint32_t *err, uint32_t epoch, uint64_t *lb_status, uint32_t *tile_counter, uint32_t counter_base,
-    DMode mode) {
+__global__ __launch_bounds__(kLocateChunks * G) void locate_kernel(const DBatch batch, uint32_t *err_words,
+                                                                    uint32_t epoch, uint64_t *lb_words,
+                                                                    uint32_t *tile_counter,
+                                                                    uint32_t counter_base, DMode mode) {
   constexpr int kWaves = G;  // 64 chunks x G lanes
   __shared__ uint32_t lds[kLocateChunks * kRingRegion];
   __shared__ uint64_t wave_sum[kWaves];
@@ -322,8 +321,21 @@ __global__ __launch_bounds__(kLocateChunks * G) void locate_kernel(
   const uint32_t wave = __builtin_amdgcn_readfirstlane(t >> 6);
   if (t == 0) group_tile = atomicAdd(tile_counter, 1u) - counter_base;
   __syncthreads();
-  const uint32_t tile = group_tile;
-  if (tile >= ntiles) return;
+  // The launch's tile -> the tensor it belongs to and the tile within it.
+  const uint32_t gtile = __builtin_amdgcn_readfirstlane(group_tile);
+  if (gtile >= batch.total_tiles) return;
+  uint32_t k = 0;
+#pragma unroll
+  for (uint32_t i = 1; i < (uint32_t)kMaxBatch; ++i) k += i < batch.n && gtile >= batch.t[i].tile_begin ? 1u : 0u;
+  const uint8_t *__restrict__ src = batch.t[k].src;
+  const uint64_t comp_bytes = batch.t[k].comp_bytes, raw_bytes = batch.t[k].raw_bytes;
+  const uint64_t nchunks = batch.t[k].nchunks;
+  const uint32_t ntiles = batch.t[k].ntiles;
+  uint64_t *__restrict__ chunk_off = batch.t[k].chunk_off;
+  uint16_t *__restrict__ block_off = batch.t[k].block_off;
+  uint32_t *err = err_words + k;
+  const uint32_t tile = gtile - batch.t[k].tile_begin;
+  uint64_t *lb_status = lb_words + batch.t[k].tile_begin;
 
   // Chunk offsets: a scan of the 16-bit headers over the tile, and one
   // look-back per tile for the headers before it.
@@ -473,10 +485,8 @@ constexpr int kDecodeLdsDwords =
     kDecodeBufDwords > kDecodeRowDwords ? kDecodeBufDwords : kDecodeRowDwords;
 
 template <int W>
-__global__ __launch_bounds__(kGroupThreads) void decode_kernel(
-    const uint8_t *__restrict__ src, uint64_t comp_bytes, uint64_t raw_bytes, uint64_t nchunks,
-    const uint64_t *__restrict__ chunk_off, const uint16_t *__restrict__ block_off,
-    uint8_t *__restrict__ dst, const uint32_t *err, uint32_t epoch, int32_t *status, DMode mode) {
+__global__ __launch_bounds__(kGroupThreads) void decode_kernel(const DBatch batch, const uint32_t *err_words,
+                                                               uint32_t epoch, DMode mode) {
   constexpr int N = 1024 / W;
   constexpr uint32_t WMASK = W == 16 ? 0xFFFFu : 0xFFFFFFFFu;
   __shared__ __attribute__((aligned(16))) uint32_t lds[kDecodeLdsDwords];
@@ -487,7 +497,19 @@ __global__ __launch_bounds__(kGroupThreads) void decode_kernel(
 
   const uint32_t t = threadIdx.x, lane = lane_id();
   const uint32_t wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const uint64_t gtile = blockIdx.x;
+  // The launch's group -> the tensor it belongs to and the group within it.
+  uint32_t k = 0;
+#pragma unroll
+  for (uint32_t i = 1; i < (uint32_t)kMaxBatch; ++i) k += i < batch.n && blockIdx.x >= batch.t[i].group_begin ? 1u : 0u;
+  const uint8_t *__restrict__ src = batch.t[k].src;
+  uint8_t *__restrict__ dst = batch.t[k].dst;
+  const uint64_t comp_bytes = batch.t[k].comp_bytes, raw_bytes = batch.t[k].raw_bytes;
+  const uint64_t nchunks = batch.t[k].nchunks;
+  const uint64_t *__restrict__ chunk_off = batch.t[k].chunk_off;
+  const uint16_t *__restrict__ block_off = batch.t[k].block_off;
+  const uint32_t *err = err_words + k;
+  int32_t *status = batch.t[k].status;
+  const uint64_t gtile = blockIdx.x - batch.t[k].group_begin;
   if (gtile * kDecodeChunks >= nchunks) return;
   // The call's status: locate, which ran before this kernel, marked a
   // corrupt stream with the call's epoch.
@@ -783,49 +805,56 @@ __global__ __launch_bounds__(kGroupThreads) void decode_kernel(
 // tensor).
 __global__ void set_status_kernel(int32_t *status, int32_t value) { *status = value; }
 
-ScratchNeed decompress_scratch_need(uint64_t raw_bytes) {
-  const uint64_t nchunks = (raw_bytes + kChunkBytes - 1) / kChunkBytes;
-  const uint64_t ntiles_a = (nchunks + kLocateChunks - 1) / kLocateChunks;
-  // Per call: chunk offsets (8 bytes per chunk), then block offsets (64 bytes
-  // per chunk, 16-byte aligned).
-  const size_t extra = (size_t)(((nchunks + 1) & ~1ull) * 8 + nchunks * kBlocksPerChunk * 2);
-  return ScratchNeed{(size_t)ntiles_a, extra, (uint32_t)ntiles_a};
+hipError_t launch_empty_status(int32_t *status, uint64_t comp_bytes, hipStream_t stream) {
+  if (!status) return hipSuccess;
+  hipLaunchKernelGGL(set_status_kernel, dim3(1), dim3(1), 0, stream, status,
+                     comp_bytes != 0 ? kStatusCorrupt : 0);
+  return hipGetLastError();
 }
 
-hipError_t launch_decompress(int w, const uint8_t *src, uint64_t comp_bytes, uint32_t codec_mask,
-                             int tagged, uint8_t *dst, uint64_t raw_bytes, int32_t *status,
+uint32_t locate_tiles(uint64_t raw_bytes) {
+  const uint64_t nchunks = (raw_bytes + kChunkBytes - 1) / kChunkBytes;
+  return (uint32_t)((nchunks + kLocateChunks - 1) / kLocateChunks);
+}
+
+uint32_t decode_groups(uint64_t raw_bytes) {
+  const uint64_t nchunks = (raw_bytes + kChunkBytes - 1) / kChunkBytes;
+  return (uint32_t)((nchunks + kDecodeChunks - 1) / kDecodeChunks);
+}
+
+// Per tensor: chunk offsets (8 bytes per chunk), then block offsets (64 bytes
+// per chunk), each 16-byte aligned.
+size_t decompress_extra(uint64_t raw_bytes) {
+  const uint64_t nchunks = (raw_bytes + kChunkBytes - 1) / kChunkBytes;
+  return (size_t)(((nchunks + 1) & ~1ull) * 8 + nchunks * kBlocksPerChunk * 2);
+}
+
+hipError_t launch_decompress(int w, DBatch &batch, uint32_t codec_mask, int tagged,
                              const Scratch &scratch, hipStream_t stream) {
   const DMode mode = make_dmode(w, codec_mask, tagged);
-  const uint64_t nchunks = (raw_bytes + kChunkBytes - 1) / kChunkBytes;
-  if (nchunks == 0) {
-    if (!status) return hipSuccess;
-    hipLaunchKernelGGL(set_status_kernel, dim3(1), dim3(1), 0, stream, status,
-                       comp_bytes != 0 ? kStatusCorrupt : 0);
-    return hipGetLastError();
+  uint8_t *extra = scratch.extra;
+  for (uint32_t k = 0; k < batch.n; ++k) {
+    DTensor &x = batch.t[k];
+    x.chunk_off = reinterpret_cast<uint64_t *>(extra);
+    x.block_off = reinterpret_cast<uint16_t *>(extra + ((x.nchunks + 1) & ~1ull) * 8);
+    extra += decompress_extra(x.raw_bytes);
   }
-  const uint64_t ntiles_a = (nchunks + kLocateChunks - 1) / kLocateChunks;
-  uint64_t *chunk_off = reinterpret_cast<uint64_t *>(scratch.extra);
-  uint16_t *block_off = reinterpret_cast<uint16_t *>(scratch.extra + ((nchunks + 1) & ~1ull) * 8);
-  const dim3 grid_a((unsigned)ntiles_a);
+  const dim3 grid_a(batch.total_tiles);
   if (w == 16)
-    hipLaunchKernelGGL((locate_kernel<16, kLocateLanes>), grid_a, dim3(kLocateThreads), 0, stream, src,
-                       comp_bytes, raw_bytes, nchunks, ntiles_a, chunk_off, block_off, scratch.err,
-                       scratch.epoch, scratch.words, scratch.counter, scratch.counter_base, mode);
+    hipLaunchKernelGGL((locate_kernel<16, kLocateLanes>), grid_a, dim3(kLocateThreads), 0, stream, batch,
+                       scratch.err, scratch.epoch, scratch.words, scratch.counter, scratch.counter_base, mode);
   else
-    hipLaunchKernelGGL((locate_kernel<32, kLocateLanes>), grid_a, dim3(kLocateThreads), 0, stream, src,
-                       comp_bytes, raw_bytes, nchunks, ntiles_a, chunk_off, block_off, scratch.err,
-                       scratch.epoch, scratch.words, scratch.counter, scratch.counter_base, mode);
+    hipLaunchKernelGGL((locate_kernel<32, kLocateLanes>), grid_a, dim3(kLocateThreads), 0, stream, batch,
+                       scratch.err, scratch.epoch, scratch.words, scratch.counter, scratch.counter_base, mode);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const uint64_t groups_b = (nchunks + kDecodeChunks - 1) / kDecodeChunks;
+  const dim3 grid_b(batch.total_groups);
   if (w == 16)
-    hipLaunchKernelGGL(decode_kernel<16>, dim3((unsigned)groups_b), dim3(kGroupThreads), 0, stream, src,
-                       comp_bytes, raw_bytes, nchunks, chunk_off, block_off, dst, scratch.err, scratch.epoch,
-                       status, mode);
+    hipLaunchKernelGGL(decode_kernel<16>, grid_b, dim3(kGroupThreads), 0, stream, batch, scratch.err,
+                       scratch.epoch, mode);
   else
-    hipLaunchKernelGGL(decode_kernel<32>, dim3((unsigned)groups_b), dim3(kGroupThreads), 0, stream, src,
-                       comp_bytes, raw_bytes, nchunks, chunk_off, block_off, dst, scratch.err, scratch.epoch,
-                       status, mode);
+    hipLaunchKernelGGL(decode_kernel<32>, grid_b, dim3(kGroupThreads), 0, stream, batch, scratch.err,
+                       scratch.epoch, mode);
   return hipGetLastError();
 }
 

@@ -7,14 +7,19 @@
 
 namespace pz {
 
-// The device scratch of one compress or decompress call: a buffer reused by
+// Tensors coded by one launch (a batch call is split into launches of at
+// most this many).
+constexpr int kMaxBatch = 8;
+
+// The device scratch of one compress or decompress launch: a buffer reused by
 // the calls on one (device, stream) (see the scratch cache of pz_api.hip).
 // Its look-back words carry the call's epoch, and its tile counter is never
 // reset: a call's tiles are counted from counter_base, so no call clears it.
 struct Scratch {
   uint64_t *words;        // look-back status words
   uint32_t *counter;      // tile counter
-  uint32_t *err;          // epoch of the last decompress call that found a corrupt stream
+  uint32_t *err;          // per tensor of a launch (kMaxBatch words): the epoch of
+                          // the last decompress launch that found its stream corrupt
   uint8_t *extra;         // per-call buffers (decompress: chunk and block offsets)
   uint32_t epoch;         // this call's epoch, 1..kEpochMax
   uint32_t counter_base;  // tile counter at the start of this call
@@ -28,8 +33,55 @@ struct ScratchNeed {
   uint32_t counted;
 };
 
-ScratchNeed compress_scratch_need(uint64_t raw_bytes);
-ScratchNeed decompress_scratch_need(uint64_t raw_bytes);
+// The tensors of one compress launch. The launch numbers its tiles across the
+// tensors (tensor k holds tiles tile_begin .. tile_begin + ntiles - 1, in
+// increasing order of k) and takes them from the tile counter in that order;
+// tensor k's look-back words are words[tile_begin ..].
+struct CTensor {
+  const uint8_t *src;
+  uint8_t *dst;
+  uint64_t *out_bytes;
+  uint64_t raw_bytes;
+  uint64_t nchunks;
+  uint32_t tile_begin;
+  uint32_t ntiles;
+};
+struct CBatch {
+  uint32_t n;
+  uint32_t total_tiles;
+  CTensor t[kMaxBatch];
+};
+
+// The tensors of one decompress launch: locate tiles numbered across the
+// tensors as in CBatch, decode groups likewise; tensor k reports corruption
+// in error word k.
+struct DTensor {
+  const uint8_t *src;
+  uint8_t *dst;
+  int32_t *status;
+  uint64_t *chunk_off;
+  uint16_t *block_off;
+  uint64_t comp_bytes;
+  uint64_t raw_bytes;
+  uint64_t nchunks;
+  uint32_t tile_begin;
+  uint32_t ntiles;
+  uint32_t group_begin;
+  uint32_t ngroups;
+};
+struct DBatch {
+  uint32_t n;
+  uint32_t total_tiles;
+  uint32_t total_groups;
+  DTensor t[kMaxBatch];
+};
+
+// Compress: tiles of the tensors (CTensor::ntiles). Decompress: locate tiles
+// and decode groups of a tensor, and its per-call bytes (16-byte multiple).
+uint32_t compress_tiles(uint64_t raw_bytes);
+uint32_t locate_tiles(uint64_t raw_bytes);
+uint32_t decode_groups(uint64_t raw_bytes);
+size_t decompress_extra(uint64_t raw_bytes);
 
 hipError_t fill_u64(uint64_t *p, uint64_t n, uint64_t value, hipStream_t stream);
 
@@ -43,12 +95,14 @@ hipError_t launch_size(int w, const uint8_t *src, uint64_t raw_bytes, uint32_t c
 hipError_t launch_block_sizes(int w, const uint8_t *src, uint64_t raw_bytes, uint16_t *block_sizes,
                               uint8_t *block_tags, hipStream_t stream);
 
-hipError_t launch_compress(int w, const uint8_t *src, uint64_t raw_bytes, uint32_t codec_mask,
-                           int tagged, uint8_t *dst, uint64_t *out_bytes, const Scratch &scratch,
-                           hipStream_t stream);
-
-hipError_t launch_decompress(int w, const uint8_t *src, uint64_t comp_bytes, uint32_t codec_mask,
-                             int tagged, uint8_t *dst, uint64_t raw_bytes, int32_t *status,
+// One launch per kernel for the batch's tensors (each with at least one
+// chunk; the batch has at least one tile). Decompress points each tensor's
+// chunk_off and block_off into scratch.extra itself.
+hipError_t launch_compress(int w, const CBatch &batch, uint32_t codec_mask, int tagged,
+                           const Scratch &scratch, hipStream_t stream);
+hipError_t launch_decompress(int w, DBatch &batch, uint32_t codec_mask, int tagged,
                              const Scratch &scratch, hipStream_t stream);
+// Status of a decompress call with no chunks: corrupt unless comp_bytes is 0.
+hipError_t launch_empty_status(int32_t *status, uint64_t comp_bytes, hipStream_t stream);
 
 }  // namespace pz

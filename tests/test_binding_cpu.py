@@ -89,6 +89,46 @@ def test_rejects_bad_sampled_size_arguments_on_host(lib):
     assert lib.pz_compressed_size_sampled(None, 100, 0, 16, 4, fake, None, None) == bad
 
 
+def test_batch_calls_check_every_tensor_before_enqueueing(lib):
+    from lossless_bit_plane_amd import _lib
+
+    fake = 256  # aligned, never dereferenced: every call below fails its checks first
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+
+    def ptrs(*v):
+        return (vp * len(v))(*v)
+
+    def sizes(*v):
+        return (sz * len(v))(*v)
+
+    bad, short = _lib.PZ_ERROR_INVALID_VALUE, _lib.PZ_ERROR_INSUFFICIENT_BUFFER
+    # An empty batch enqueues nothing and succeeds (no device needed).
+    assert lib.pz_compress_batch(0, None, None, 0, 16, None, None, None, None) == 0
+    assert lib.pz_decompress_batch(0, None, None, 0, 16, None, None, None, None) == 0
+    assert lib.pz_compress_batch(-1, None, None, 0, 16, None, None, None, None) == bad
+    assert lib.pz_compress_batch(2, None, sizes(1, 1), 0, 16, ptrs(fake, fake), sizes(9, 9), fake, None) == bad
+    # The second tensor fails: misaligned source, null destination, short
+    # capacity, a bad (dtype, width) pair for all.
+    ok_cap = 2 + 4096
+    assert lib.pz_compress_batch(2, ptrs(fake, fake + 4), sizes(4096, 4096), 0, 16, ptrs(fake, fake),
+                                 sizes(ok_cap, ok_cap), fake, None) == bad
+    assert lib.pz_compress_batch(2, ptrs(fake, fake), sizes(4096, 4096), 0, 16, ptrs(fake, None),
+                                 sizes(ok_cap, ok_cap), fake, None) == bad
+    assert lib.pz_compress_batch(2, ptrs(fake, fake), sizes(4096, 4097), 0, 16, ptrs(fake, fake),
+                                 sizes(ok_cap, ok_cap), fake, None) == short
+    assert lib.pz_compress_batch(2, ptrs(fake, fake), sizes(4096, 4096), 1, 16, ptrs(fake, fake),
+                                 sizes(ok_cap, ok_cap), fake, None) == bad
+    assert lib.pz_compress_batch(1, ptrs(fake), sizes(4096), 0, 16, ptrs(fake), sizes(ok_cap), fake + 4,
+                                 None) == bad  # misaligned sizes array
+    # Decompress: a stream shorter than its header table, a misaligned status.
+    assert lib.pz_decompress_batch(2, ptrs(fake, fake), sizes(100, 3), 0, 16, ptrs(fake, fake),
+                                   sizes(4096, 8193), None, None) == _lib.PZ_ERROR_CORRUPT_STREAM
+    assert lib.pz_decompress_batch(1, ptrs(fake), sizes(100), 0, 16, ptrs(fake), sizes(4096), fake + 2,
+                                   None) == bad
+    assert lib.pz_decompress_batch(2, ptrs(fake, None), sizes(100, 100), 0, 16, ptrs(fake, fake),
+                                   sizes(4096, 4096), None, None) == bad
+
+
 def test_swapper_rejects_bad_sizes_without_touching_the_device(lib):
     # Argument checks come before any allocation; without a GPU every valid
     # request fails too (NULL, no crash).
