@@ -1,9 +1,10 @@
 """Randomized parity with the oracle (needs a GPU): seeded tensors of random
 length whose chunks mix the structures the codec distinguishes (all-zero,
 sparse, random bits, smooth values, constant runs, sign alternation), every
-allowed (dtype, symbol width) pair, the plain calls and random codec
-variants. Bar: stream, size pass and sampled size bit-exact with the oracle;
-the round trip restores the bytes."""
+allowed (dtype, symbol width) pair, the plain calls, random codec variants
+and batched calls on random sets of such tensors. Bar: stream, size pass and
+sampled size bit-exact with the oracle; the round trip restores the
+bytes."""
 import os
 
 import numpy as np
@@ -95,3 +96,30 @@ def test_random_tensors_bitexact(pz, seed):
         out, status = pz.pz_decompress_ex(dst, n, data.size, dtype, bits, mask, tagged)
         assert int(status.item()) == 0
         assert np.array_equal(out[: data.size].cpu().numpy(), data), (seed, case)
+
+
+@pytest.mark.parametrize("seed", list(range(4)))
+def test_random_batches_bitexact(pz, seed):
+    """Batched calls on 1-11 random tensors of one (dtype, width) pair, some
+    empty: every stream bit-exact with the oracle, every round trip exact."""
+    import torch
+
+    rng = np.random.default_rng(2000 + seed)
+    for case in range(3):
+        count = int(rng.integers(1, 12))
+        datas = [_tensor(rng) if rng.random() < 0.85 else np.zeros(0, np.uint8) for _ in range(count)]
+        dtype, bits = PAIRS[int(rng.integers(0, len(PAIRS)))]
+        print(f"[random batch] seed={seed} case={case} sizes={[d.size for d in datas]} dtype={dtype} w={bits}",
+              flush=True)
+        srcs = [torch.from_numpy(d).to("cuda") if d.size else torch.zeros(16, dtype=torch.uint8, device="cuda")[:0]
+                for d in datas]
+        dsts, nb = pz.pz_compress_batch(srcs, dtype, bits)
+        n = [int(v) for v in nb.cpu().tolist()]
+        for i, d in enumerate(datas):
+            o = oracle.compress(d, bits, threads=THREADS)
+            g = dsts[i][: n[i]].cpu().numpy()
+            assert g.size == o.size and np.array_equal(g, o), (seed, case, i)
+        outs, status = pz.pz_decompress_batch(dsts, n, [d.size for d in datas], dtype, bits)
+        assert status.cpu().tolist() == [0] * count
+        for i, d in enumerate(datas):
+            assert np.array_equal(outs[i][: d.size].cpu().numpy(), d), (seed, case, i)
