@@ -46,7 +46,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--config", type=int, default=5)
+    p.add_argument("--workload", default="gpt2-xl", choices=sorted(WORKLOAD_NAMES))
     p.add_argument("--cpu-sample-mb", type=float, default=24.0,
                    help="sample of the workload for the single-threaded oracle timing")
     p.add_argument("--no-flush", action="store_true", help="skip the cache flush before each step")
@@ -63,14 +63,15 @@ def parse():
 
 # The synthetic workloads (pzinputs), by what they stand in for.
 WORKLOADS = {
-    1: "codec smoke tensor: ReLU(N(0,1)) BF16, 1 MiB, plus 64 corner-case blocks",
-    2: "CNN feature maps, FP32 NCHW 32x64x56x56, ReLU of smoothed noise",
-    3: "GPT-2 (124M) BF16 saved activations, batch 8, seq 1024: MLP GELU 8x1024x3072, "
-       "causal attention probabilities 8x12x1024x1024",
-    4: "ViT-B/16 LayerNorm outputs 64x197x768, BF16 and FP32",
-    5: "GPT-2-XL BF16 saved activations, batch 8, seq 1024: MLP GELU 8x1024x6400, "
-       "causal softmax 8x25x1024x1024, residual 8x1024x1600",
+    "relu-smoke": "codec smoke tensor: ReLU(N(0,1)) BF16, 1 MiB, plus 64 corner-case blocks",
+    "cnn-fp32": "CNN feature maps, FP32 NCHW 32x64x56x56, ReLU of smoothed noise",
+    "gpt2-small": "GPT-2 (124M) BF16 saved activations, batch 8, seq 1024: MLP GELU 8x1024x3072, "
+                  "causal attention probabilities 8x12x1024x1024",
+    "vit-layernorm": "ViT-B/16 LayerNorm outputs 64x197x768, BF16 and FP32",
+    "gpt2-xl": "GPT-2-XL BF16 saved activations, batch 8, seq 1024: MLP GELU 8x1024x6400, "
+               "causal softmax 8x25x1024x1024, residual 8x1024x1600",
 }
+WORKLOAD_NAMES = tuple(WORKLOADS)
 
 
 def main():
@@ -97,8 +98,8 @@ def main():
         log(f"calibration copy: {n} bytes read, {n} bytes written")
         del a, b
     t0 = time.time()
-    tensors = pzinputs.config(args.config)
-    log(f"generated config {args.config} in {time.time() - t0:.1f}s: "
+    tensors = pzinputs.workload(args.workload)
+    log(f"generated workload {args.workload} in {time.time() - t0:.1f}s: "
         + ", ".join(f"{t.name} {t.nbytes / 1e6:.1f} MB" for t in tensors))
 
     # Device buffers, allocated once.
@@ -288,7 +289,7 @@ def main():
         "dtype": ", ".join(sorted({f"u{t.elem_bits} symbols" for t in tensors})) + ", integer codec",
         "data": "synthetic (seeded generators in pzinputs, stand-ins for captured activations)",
         "config": {
-            "workload": WORKLOADS.get(args.config, f"config {args.config}"),
+            "workload": WORKLOADS[args.workload],
             "tensors": [f"{t.name} {list(t.shape)}" for t in tensors],
             "raw_bytes": raw_total,
             "compressed_bytes": comp_total,
@@ -551,7 +552,7 @@ def measured_traffic(kernel, launch_names):
     of the named launches of `kernel` (a tensor's name, or batch_name of a
     batched launch), summed, from the committed rocprofv3 summary; None when
     the kernels changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", "hbm_traffic_gpt2xl_config5.json")
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_gpt2xl_activations.json")
     if not os.path.exists(path):
         return None, "no counter summary"
     with open(path) as f:
@@ -565,7 +566,7 @@ def measured_traffic(kernel, launch_names):
         if t is None:
             return None, f"no counters for {kernel} on {name}"
         total += t["fetch_bytes"] + t["write_bytes"]
-    return round(total), "profiles/hbm_traffic_gpt2xl_config5.json (the batched launch)"
+    return round(total), "profiles/hbm_traffic_gpt2xl_activations.json (the batched launch)"
 
 
 def cpu_baseline(tensors, sample_mb):

@@ -153,7 +153,7 @@ def corner_blocks(seed: int = 100) -> np.ndarray:
     return out
 
 
-def config1() -> list[Tensor]:
+def relu_smoke() -> list[Tensor]:
     """Codec smoke test (BF16): ReLU(N(0,1)), 524,288 values from seed 0,
     followed by the 64 corner-case blocks (chunks 256 and 257)."""
     rng = np.random.default_rng(0)
@@ -176,7 +176,7 @@ def _box3x3(z: np.ndarray) -> np.ndarray:
     return acc / np.float32(9.0)
 
 
-def config2() -> list[Tensor]:
+def cnn_feature_maps_fp32() -> list[Tensor]:
     """FP32 CNN feature maps: NCHW 32x64x56x56, ReLU(0.5 * box3x3(N(0,1)))
     from seed 1; about half the values are exact zeros and neighbours share
     exponent bits."""
@@ -186,7 +186,7 @@ def config2() -> list[Tensor]:
     return [_fp32_tensor("cnn_relu_fp32", y)]
 
 
-def config3() -> list[Tensor]:
+def gpt2_small_activations() -> list[Tensor]:
     """GPT-2 (124M) saved activations at batch 8, sequence 1024 (BF16), seed 2:
     MLP GELU output 8x1024x3072 and causal attention probabilities
     8x12x1024x1024 (exact zeros above the diagonal)."""
@@ -199,7 +199,7 @@ def config3() -> list[Tensor]:
     return [gelu, attn]
 
 
-def config4() -> list[Tensor]:
+def vit_layernorm() -> list[Tensor]:
     """ViT-B/16 LayerNorm output 64x197x768, x*g + b with x ~ N(0,1),
     g ~ U(0.5, 1.5) and b ~ N(0, 0.1) per channel (0.1 read as the standard
     deviation), seed 3; as BF16 (RNE) and as FP32. Dense and nearly
@@ -212,7 +212,7 @@ def config4() -> list[Tensor]:
     return [_bf16_tensor("vit_layernorm_bf16", y), _fp32_tensor("vit_layernorm_fp32", y)]
 
 
-def config5() -> list[Tensor]:
+def gpt2xl_activations() -> list[Tensor]:
     """GPT-2-XL saved activations at batch 8, sequence 1024, hidden 1600
     (BF16), seed 4: MLP GELU output 8x1024x6400, causal softmax scores
     8x25x1024x1024 and the residual stream 8x1024x1600 ~ N(0,1); about
@@ -228,19 +228,20 @@ def config5() -> list[Tensor]:
     return [gelu, attn, resid]
 
 
-CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
-
-CONFIG_NAMES = {
-    1: "codec smoke test: BF16 ReLU(N(0,1)) 1 MiB + 64 corner blocks",
-    2: "FP32 CNN feature maps NCHW 32x64x56x56, ReLU(0.5*box3x3(N(0,1)))",
-    3: "GPT-2 124M BF16 activations, batch 8 seq 1024: GELU 8x1024x3072 + causal attention 8x12x1024x1024",
-    4: "ViT-B/16 LayerNorm output 64x197x768, BF16 and FP32",
-    5: "GPT-2-XL BF16 activations, batch 8 seq 1024: GELU 8x1024x6400 + causal softmax 8x25x1024x1024 + residual 8x1024x1600",
+# The workloads by name: generator and description.
+WORKLOADS = {
+    "relu-smoke": (relu_smoke, "codec smoke test: BF16 ReLU(N(0,1)) 1 MiB + 64 corner blocks"),
+    "cnn-fp32": (cnn_feature_maps_fp32, "FP32 CNN feature maps NCHW 32x64x56x56, ReLU(0.5*box3x3(N(0,1)))"),
+    "gpt2-small": (gpt2_small_activations, "GPT-2 124M BF16 activations, batch 8 seq 1024: GELU 8x1024x3072 "
+                   "+ causal attention 8x12x1024x1024"),
+    "vit-layernorm": (vit_layernorm, "ViT-B/16 LayerNorm output 64x197x768, BF16 and FP32"),
+    "gpt2-xl": (gpt2xl_activations, "GPT-2-XL BF16 activations, batch 8 seq 1024: GELU 8x1024x6400 "
+                "+ causal softmax 8x25x1024x1024 + residual 8x1024x1600"),
 }
 
 
-def config(k: int) -> list[Tensor]:
-    return CONFIGS[k]()
+def workload(name: str) -> list[Tensor]:
+    return WORKLOADS[name][0]()
 
 
 def sample_blocks(t: Tensor, count: int, seed: int = 0) -> np.ndarray:
@@ -253,7 +254,7 @@ def sample_blocks(t: Tensor, count: int, seed: int = 0) -> np.ndarray:
 
 
 def edge_tensors(seed: int = 5) -> list[Tensor]:
-    """Tensors that are not configs: ragged tails, whole raw chunks, all-zero
+    """Tensors outside the workloads: ragged tails, whole raw chunks, all-zero
     data, and random/ReLU data of awkward lengths, for both widths."""
     rng = np.random.default_rng(seed)
     out = []

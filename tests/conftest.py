@@ -10,21 +10,21 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
-    config.addinivalue_line("markers", "slow: generates the large synthetic configs")
+    config.addinivalue_line("markers", "slow: generates the large synthetic workloads")
 
 
 _CACHE = {}
 
 
-def load_config(k):
-    """Synthetic config k, generated once per test session."""
+def load_workload(name):
+    """The named synthetic workload, generated once per test session."""
     import pzinputs
 
-    if k not in _CACHE:
-        _CACHE[k] = pzinputs.config(k)
-    return _CACHE[k]
+    if name not in _CACHE:
+        _CACHE[name] = pzinputs.workload(name)
+    return _CACHE[name]
 
 
 @pytest.fixture(scope="session")
-def config_tensors():
-    return load_config
+def workload_tensors():
+    return load_workload

@@ -35,13 +35,13 @@ def test_measured_traffic_never_raises(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     for content in [{"source_hash": "0123456789abcdef", "traffic": {}},
                     {"source_hash": {"compress_kernel": "x"}, "traffic": {}}]:
-        (prof / "hbm_traffic_gpt2xl_config5.json").write_text(json.dumps(content))
+        (prof / "hbm_traffic_gpt2xl_activations.json").write_text(json.dumps(content))
         monkeypatch.setattr(bench, "kernel_source_hash", lambda k: "y")
         assert bench.measured_traffic("compress_kernel<16>", names)[0] is None
     good = {"source_hash": {"compress_kernel": "y"},
             "traffic": {f"compress_kernel<16>:{n}": {"fetch_bytes": 10.0, "write_bytes": 5.0} for n in names}}
     good["traffic"][f"compress_kernel<16>:{bench.batch_name(names)}"] = {"fetch_bytes": 20.0, "write_bytes": 7.0}
-    (prof / "hbm_traffic_gpt2xl_config5.json").write_text(json.dumps(good))
+    (prof / "hbm_traffic_gpt2xl_activations.json").write_text(json.dumps(good))
     assert bench.measured_traffic("compress_kernel<16>", names)[0] == 45
     assert bench.measured_traffic("compress_kernel<16>", [bench.batch_name(names)])[0] == 27
     assert bench.measured_traffic("compress_kernel<16>", [bench.batch_name(names[:2])])[0] is None

@@ -56,8 +56,8 @@ def _check_batch(pz, datas, dtype, w):
 def test_batch_bench_workload_bitexact(pz):
     """The GPT-2-XL BF16 workload (MLP GELU 8x1024x6400, causal softmax
     8x25x1024x1024, residual 8x1024x1600) at full size in one batch per
-    direction: the bench's launch configuration."""
-    ts = pzinputs.config5()
+    direction, as the bench launches it."""
+    ts = pzinputs.gpt2xl_activations()
     print("[batch] gpt2-xl workload", [t.nbytes for t in ts], flush=True)
     _check_batch(pz, [t.data for t in ts], ts[0].dtype, ts[0].elem_bits)
 
@@ -65,7 +65,7 @@ def test_batch_bench_workload_bitexact(pz):
 def test_batch_fp32_tensors(pz):
     """FP32 with 32-bit symbols: CNN feature maps and the ViT LayerNorm
     output."""
-    ts = [t for t in pzinputs.config2() + pzinputs.config4() if t.elem_bits == 32]
+    ts = [t for t in pzinputs.cnn_feature_maps_fp32() + pzinputs.vit_layernorm() if t.elem_bits == 32]
     print("[batch] fp32", [t.name for t in ts], flush=True)
     _check_batch(pz, [t.data for t in ts], pzinputs.FP32, 32)
 
@@ -76,7 +76,7 @@ def test_batch_ragged_empty_and_split(pz, w):
     zero and smooth bytes: two launches of up to eight tensors, empty tensors
     set directly, streams ordered densest first inside a launch."""
     rng = np.random.default_rng(70 + w)
-    (base,) = pzinputs.config1()
+    (base,) = pzinputs.relu_smoke()
     sizes = [0, 1, 127, 128, 4095, 4096, 4097, 65836, 0, 12345, 3 * 4096, 200000, 0, 5]
     datas = []
     for k, n in enumerate(sizes):
@@ -100,7 +100,7 @@ def test_batch_corrupt_stream_flags_only_its_tensor(pz):
 
     from lossless_bit_plane_amd._lib import PlaneZipError
 
-    (base,) = pzinputs.config1()
+    (base,) = pzinputs.relu_smoke()
     datas = [base.data[: 20 * 4096], base.data[100000: 100000 + 9 * 4096 + 55], base.data[300000: 300000 + 40000]]
     streams = [oracle.compress(d, 16) for d in datas]
     rng = np.random.default_rng(5)

@@ -47,8 +47,8 @@ def _dev(data):
 
 
 def _tensors():
-    (c1,) = pzinputs.config1()
-    fp32 = pzinputs.config2()[0]
+    (c1,) = pzinputs.relu_smoke()
+    fp32 = pzinputs.cnn_feature_maps_fp32()[0]
     ts = [
         c1,
         pzinputs.Tensor("bf16_as_w32", c1.data, 0, 32),
@@ -82,7 +82,7 @@ def test_mode_streams_bitexact(pz, mask, tagged):
 
 @pytest.mark.parametrize("mask,tagged", [(BX, False), (DBX, False), (ZVC | RAW, True)])
 def test_mode_corrupt_streams_status_matches_oracle(pz, mask, tagged):
-    (base,) = pzinputs.config1()
+    (base,) = pzinputs.relu_smoke()
     data = base.data[: 24 * 4096 + 777].copy()
     stream = oracle.compress(data, 16, mask, tagged)
     rng = np.random.default_rng(11)

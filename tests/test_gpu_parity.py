@@ -1,7 +1,7 @@
 """Parity of the HIP codec with the CPU oracle, through the C ABI (needs a GPU).
 
 The bar is bit-exactness: integer work, no tolerance. Checked on every
-synthetic config tensor at full size (stream bytes, header values, per-block
+synthetic workload tensor at full size (stream bytes, header values, per-block
 candidate sizes and tags, round trip), on ragged and degenerate tensors, and
 on corrupt streams (status agreement with the oracle).
 """
@@ -87,8 +87,8 @@ def test_library_symbols(pz):
         assert getattr(_lib.lib, name)
 
 
-def test_block_sizes_match_oracle_config1(pz):
-    (t,) = pzinputs.config1()
+def test_block_sizes_match_oracle_relu_smoke(pz):
+    (t,) = pzinputs.relu_smoke()
     sizes, tags = pz.pz_block_sizes(_dev(t.data), t.dtype, t.elem_bits)
     g = _host(sizes).view(np.uint16).astype(np.int64)
     model = size_model.candidate_sizes(t.data.reshape(-1, 128), 16)
@@ -137,14 +137,14 @@ def test_block_sizes_match_oracle_structured(pz, w):
     _check_tensor(pz, t)
 
 
-def test_config1_stream_bitexact(pz):
-    (t,) = pzinputs.config1()
+def test_relu_smoke_stream_bitexact(pz):
+    (t,) = pzinputs.relu_smoke()
     _check_tensor(pz, t)
 
 
-@pytest.mark.parametrize("k", [2, 3, 4, 5])
-def test_config_streams_bitexact(pz, config_tensors, k):
-    for t in config_tensors(k):
+@pytest.mark.parametrize("name", ["cnn-fp32", "gpt2-small", "vit-layernorm", "gpt2-xl"])
+def test_workload_streams_bitexact(pz, workload_tensors, name):
+    for t in workload_tensors(name):
         _check_tensor(pz, t)
 
 
@@ -170,10 +170,10 @@ def test_empty_tensor(pz):
     assert int(status.item()) == 3
 
 
-def test_deterministic_streams(pz, config_tensors):
+def test_deterministic_streams(pz, workload_tensors):
     """Repeated runs give byte-identical streams (catches look-back and LDS
     races)."""
-    t = config_tensors(3)[1]
+    t = workload_tensors("gpt2-small")[1]
     src = _dev(t.data)
     first = None
     for _ in range(5):
@@ -185,10 +185,10 @@ def test_deterministic_streams(pz, config_tensors):
             assert np.array_equal(cur, first)
 
 
-def test_oracle_streams_decode_on_gpu(pz, config_tensors):
+def test_oracle_streams_decode_on_gpu(pz, workload_tensors):
     """The GPU decoder reads the oracle's streams (the same bytes if parity
     holds, decoded independently here)."""
-    for t in config_tensors(2) + config_tensors(4):
+    for t in workload_tensors("cnn-fp32") + workload_tensors("vit-layernorm"):
         o_stream = oracle.compress(t.data, t.elem_bits, threads=THREADS)
         st, back = _gpu_decompress(pz, o_stream, t)
         assert st == 0 and np.array_equal(back, t.data)
@@ -197,7 +197,7 @@ def test_oracle_streams_decode_on_gpu(pz, config_tensors):
 def test_corrupt_streams_status_matches_oracle(pz):
     """Random bit flips, truncations and header edits: the GPU status equals
     the oracle's, and a good stream decodes."""
-    (base,) = pzinputs.config1()
+    (base,) = pzinputs.relu_smoke()
     data = base.data[: 24 * 4096 + 777].copy()
     t = pzinputs.Tensor("corrupt_base", data, 0, 16)
     stream = oracle.compress(data, 16)
@@ -236,7 +236,7 @@ def test_scratch_reuse_across_calls(pz):
     the next call), and a second stream interleaved with the first."""
     import torch
 
-    (base,) = pzinputs.config1()
+    (base,) = pzinputs.relu_smoke()
     sizes = [base.nbytes, 4096 * 3 + 5, 700_000, 77, base.nbytes - 4096, 4096 * 70, 1]
     streams = [torch.cuda.current_stream(), torch.cuda.Stream()]
     for k, n in enumerate(sizes):

@@ -67,8 +67,8 @@ def _chunk_mix(n_chunks, tail, seed=3):
 def test_sampled_size_small_tensors(pz, stride):
     ts = [pzinputs.Tensor(f"mix{n}_{tail}", _chunk_mix(n, tail), 0, 16)
           for n, tail in [(1, 0), (2, 0), (13, 0), (13, 1), (13, 1000), (14, 4095), (40, 130), (0, 77)]]
-    (c1,) = pzinputs.config1()
-    fp32 = pzinputs.config2()[0]
+    (c1,) = pzinputs.relu_smoke()
+    fp32 = pzinputs.cnn_feature_maps_fp32()[0]
     ts += [c1, pzinputs.Tensor("bf16_as_w32", c1.data, 0, 32),
            pzinputs.Tensor("fp32_slice", fp32.data[: (1 << 20) + 4100].copy(), 1, 32)]
     ts += [t for t in pzinputs.edge_tensors() if t.nbytes <= (1 << 16)]
@@ -77,7 +77,7 @@ def test_sampled_size_small_tensors(pz, stride):
 
 
 def test_sampled_size_stride1_is_exact_size(pz):
-    (t,) = pzinputs.config1()
+    (t,) = pzinputs.relu_smoke()
     src = _dev(t.data)
     comp, raw = _check(pz, t, 1, src)
     size, _ = pz.pz_compressed_size(src, t.dtype, t.elem_bits)
@@ -92,9 +92,9 @@ def test_sampled_size_empty(pz):
     assert out.cpu().tolist() == [0, 0] and lens.numel() == 0
 
 
-@pytest.mark.parametrize("k", [2, 3, 4, 5])
-def test_sampled_size_full_configs(pz, config_tensors, k):
-    for t in config_tensors(k):
+@pytest.mark.parametrize("name", ["cnn-fp32", "gpt2-small", "vit-layernorm", "gpt2-xl"])
+def test_sampled_size_full_workloads(pz, workload_tensors, name):
+    for t in workload_tensors(name):
         src = _dev(t.data)
         comp, raw = _check(pz, t, 4, src)
         size, _ = pz.pz_compressed_size(src, t.dtype, t.elem_bits)

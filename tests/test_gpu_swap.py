@@ -57,9 +57,9 @@ def _roundtrip(pz, sw, tensors):
     return tickets
 
 
-def test_swap_round_trip_configs(pz, config_tensors):
-    (c1,) = pzinputs.config1()
-    ts = [c1, config_tensors(2)[0], config_tensors(3)[0]]
+def test_swap_round_trip_workloads(pz, workload_tensors):
+    (c1,) = pzinputs.relu_smoke()
+    ts = [c1, workload_tensors("cnn-fp32")[0], workload_tensors("gpt2-small")[0]]
     sw = pz.Swapper(1 << 20, 256, 52 << 20, 3)
     try:
         tickets = _roundtrip(pz, sw, ts)
@@ -74,7 +74,7 @@ def test_swap_round_trip_configs(pz, config_tensors):
 def test_swap_scattered_chunks_and_slot_reuse(pz):
     """64 KB pool chunks, two staging slots, many tensors in flight, and
     releases in random order, so that later streams land in scattered chunks."""
-    (c1,) = pzinputs.config1()
+    (c1,) = pzinputs.relu_smoke()
     rng = random.Random(5)
     sizes = [1, 100, 4096, 4097, 65536, 65537, 300000, 1 << 20, 1056768]
     ts = []
@@ -206,7 +206,7 @@ def test_swap_from_several_host_threads(pz):
 
     import torch
 
-    (c1,) = pzinputs.config1()
+    (c1,) = pzinputs.relu_smoke()
     sw = pz.Swapper(1 << 16, 512, 1 << 21, 3)
     errors = []
 

@@ -120,7 +120,7 @@ def test_arbitrary_bytes(data, w):
     _check_blocks(np.frombuffer(data, dtype=np.uint8), w, explicit=True)
 
 
-def test_corner_blocks_of_smoke_config():
+def test_corner_blocks_of_smoke_tensor():
     import pzinputs
 
     _check_blocks(pzinputs.corner_blocks(100).view(np.uint8), 16, explicit=True)

@@ -1,7 +1,7 @@
-"""Whole-stream checks of the CPU oracle on the synthetic configs (no GPU).
+"""Whole-stream checks of the CPU oracle on the synthetic workloads (no GPU).
 
-* round trip of every config tensor (config 1 in full, block samples of the
-  larger ones) and of the edge tensors;
+* round trip of every workload tensor (the smoke tensor in full, block
+  samples of the larger ones) and of the edge tensors;
 * the numpy size model equals the C encoder's bit counts for every sampled
   block, and the stream length equals 2C plus the padded chunk lengths;
 * corrupt streams (FORMAT.md §6) are rejected;
@@ -23,8 +23,8 @@ def _roundtrip_with_model(data, w):
     return stream, tags, bits
 
 
-def test_config1_full(config_tensors):
-    (t,) = config_tensors(1)
+def test_relu_smoke_full(workload_tensors):
+    (t,) = workload_tensors("relu-smoke")
     assert t.nbytes == 1056768
     stream, tags, bits = _roundtrip_with_model(t.data, 16)
     blocks = t.data.reshape(-1, 128)
@@ -37,11 +37,11 @@ def test_config1_full(config_tensors):
     assert {1, 2, 3, 4} <= set(int(v) for v in np.unique(tags))
 
 
-@pytest.mark.parametrize("k", [2, 3, 4, 5])
-def test_config_block_samples(config_tensors, k):
+@pytest.mark.parametrize("k,name", [(2, "cnn-fp32"), (3, "gpt2-small"), (4, "vit-layernorm"), (5, "gpt2-xl")])
+def test_workload_block_samples(workload_tensors, k, name):
     """Two implementations agree on 3,000 sampled blocks of every tensor, and
     sampled whole chunks round-trip."""
-    for i, t in enumerate(config_tensors(k)):
+    for i, t in enumerate(workload_tensors(name)):
         blocks = pzinputs.sample_blocks(t, 3000, seed=k * 10 + i)
         model = size_model.candidate_sizes(blocks, t.elem_bits)
         np.testing.assert_array_equal(oracle.blocks_sizes(blocks, t.elem_bits), model)
@@ -57,8 +57,8 @@ def test_edge_tensors():
         _roundtrip_with_model(t.data, t.elem_bits)
 
 
-def test_threaded_driver_matches(config_tensors):
-    (t,) = config_tensors(1)
+def test_threaded_driver_matches(workload_tensors):
+    (t,) = workload_tensors("relu-smoke")
     s1 = oracle.compress(t.data, 16)
     s4 = oracle.compress(t.data, 16, threads=4)
     assert s1.tobytes() == s4.tobytes()
@@ -66,9 +66,9 @@ def test_threaded_driver_matches(config_tensors):
 
 
 @pytest.mark.parametrize("cand", [0, 1, 2, 3, 4])
-def test_single_codec_variants(config_tensors, cand):
+def test_single_codec_variants(workload_tensors, cand):
     """One fixed encoding, no tag (the paper's per-codec columns)."""
-    (t,) = config_tensors(1)
+    (t,) = workload_tensors("relu-smoke")
     data = t.data[: 64 * 4096]
     mask = 1 << cand
     s = oracle.compress(data, 16, codec_mask=mask, tagged=False)
@@ -78,10 +78,10 @@ def test_single_codec_variants(config_tensors, cand):
     assert s.size == size_model.stream_bytes(data.size, model[:, cand])
 
 
-def test_bf16_as_32_bit_symbols(config_tensors):
+def test_bf16_as_32_bit_symbols(workload_tensors):
     """BF16 data coded with w = 32 (§V-A ablation) round-trips and compresses
     less than with w = 16 on ReLU data."""
-    (t,) = config_tensors(1)
+    (t,) = workload_tensors("relu-smoke")
     s16 = oracle.compress(t.data, 16)
     s32, _, _ = _roundtrip_with_model(t.data, 32)
     assert s32.size > s16.size
@@ -92,7 +92,7 @@ def test_bf16_as_32_bit_symbols(config_tensors):
 # --------------------------------------------------------------------------
 
 def _good_stream():
-    (t,) = [pzinputs.config1()[0]]
+    (t,) = [pzinputs.relu_smoke()[0]]
     data = t.data[: 3 * 4096 + 1000].copy()
     return data, oracle.compress(data, 16)
 
