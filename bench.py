@@ -420,6 +420,26 @@ def measure_size_only(pz, items, flush, cur, stride=4, reps=5):
             res[name].update(stride=stride, estimate_bytes=round(est), exact_bytes=comp,
                              estimate_err_pct=round(100 * (est - comp) / comp, 4))
         log(f"size pass {name}: {raw / t_total / 1e9:.0f} GB/s ({t_total * 1e6:.0f} us)")
+    # The exact sizes of every tensor in one pz_compressed_size_batch call per
+    # (dtype, width) group.
+    groups = {}
+    for it in items:
+        groups.setdefault((it["t"].dtype, it["t"].elem_bits), []).append(it)
+    ts = []
+    for _ in range(reps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        flush()
+        e[0].record(cur)
+        outs = [pz.pz_compressed_size_batch([it["src"] for it in g], dt, w)[0] for (dt, w), g in groups.items()]
+        e[1].record(cur)
+        torch.cuda.synchronize()
+        ts.append(e[0].elapsed_time(e[1]) / 1e3)
+    for out, g in zip(outs, groups.values()):
+        assert [int(v) for v in out.tolist()] == [it["comp"] for it in g], "batched size pass disagrees"
+    raw = sum(it["t"].nbytes for it in items)
+    t_b = float(np.median(ts))
+    res["exact_batched"] = {"raw_gbps": round(raw / t_b / 1e9, 1), "us": round(t_b * 1e6, 1)}
+    log(f"size pass exact, batched: {raw / t_b / 1e9:.0f} GB/s ({t_b * 1e6:.0f} us)")
     return res
 
 

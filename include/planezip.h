@@ -161,6 +161,20 @@ pz_status_t pz_compress_batch(int count, const void *const *d_srcs,
                               void *const *d_dsts, const size_t *dst_capacities,
                               uint64_t *d_out_bytes, void *stream);
 
+/* pz_compressed_size on `count` tensors of one (dtype, elem_bits) in as few
+ * launches as possible (up to 8 tensors per launch): the profiling
+ * iteration's measurement of every saved tensor (PlaneZip paper, §III-B).
+ *   d_srcs, raw_bytes  host arrays of count device pointers (16-byte aligned)
+ *                      and sizes
+ *   d_out_bytes        device array of count uint64: tensor i's stream bytes
+ *   d_chunk_lens       nullable host array of count nullable device pointers:
+ *                      tensor i's PZ_NUM_CHUNKS(raw_bytes[i]) header values
+ * Every tensor is checked before anything is enqueued. */
+pz_status_t pz_compressed_size_batch(int count, const void *const *d_srcs,
+                                     const size_t *raw_bytes, int dtype,
+                                     int elem_bits, uint64_t *d_out_bytes,
+                                     uint16_t *const *d_chunk_lens, void *stream);
+
 pz_status_t pz_decompress_batch(int count, const void *const *d_srcs,
                                 const size_t *comp_bytes, int dtype,
                                 int elem_bits, void *const *d_dsts,

@@ -20,7 +20,8 @@ EXPORTS = ("pz_compressed_size", "pz_compress", "pz_decompress", "pz_block_sizes
            "pz_predictor_create", "pz_predictor_destroy", "pz_predictor_update", "pz_predictor_predict",
            "pz_predictor_entries", "pz_predictor_clear",
            "pz_swapper_create", "pz_swapper_destroy", "pz_swapper_free_chunks", "pz_swap_out", "pz_swap_wait",
-           "pz_swap_in", "pz_swap_release", "pz_swap_read", "pz_compress_batch", "pz_decompress_batch")
+           "pz_swap_in", "pz_swap_release", "pz_swap_read", "pz_compress_batch", "pz_decompress_batch",
+           "pz_compressed_size_batch")
 
 
 def _load():
@@ -43,6 +44,8 @@ def _load():
                                       ctypes.POINTER(sz), vp, vp]
     lib.pz_decompress_batch.argtypes = [i, ctypes.POINTER(vp), ctypes.POINTER(sz), i, i, ctypes.POINTER(vp),
                                         ctypes.POINTER(sz), vp, vp]
+    lib.pz_compressed_size_batch.argtypes = [i, ctypes.POINTER(vp), ctypes.POINTER(sz), i, i, vp,
+                                             ctypes.POINTER(vp), vp]
     u64 = ctypes.c_uint64
     lib.pz_predictor_create.argtypes = [sz]
     lib.pz_predictor_create.restype = vp
@@ -69,7 +72,8 @@ def _load():
         getattr(lib, name).restype = ctypes.c_int
     for name in ("pz_compressed_size", "pz_compress", "pz_decompress", "pz_block_sizes",
                  "pz_compressed_size_ex", "pz_compress_ex", "pz_decompress_ex", "pz_compressed_size_sampled",
-                 "pz_predictor_update", "pz_predictor_predict", "pz_compress_batch", "pz_decompress_batch"):
+                 "pz_predictor_update", "pz_predictor_predict", "pz_compress_batch", "pz_decompress_batch",
+                 "pz_compressed_size_batch"):
         getattr(lib, name).restype = ctypes.c_int
     lib.pz_status_string.argtypes = [ctypes.c_int]
     lib.pz_status_string.restype = ctypes.c_char_p

@@ -191,6 +191,24 @@ def pz_compress_batch(srcs, dtype: int, elem_bits: int, dsts=None, out_bytes: to
     return dsts, out_bytes
 
 
+def pz_compressed_size_batch(srcs, dtype: int, elem_bits: int, chunk_lens: bool = False, stream=None):
+    """pz_compressed_size on several tensors of one (dtype, elem_bits) in as
+    few launches as possible. Returns (out_bytes, lens): a device int64
+    tensor (n,) and, with chunk_lens, a list of int16 header tensors."""
+    bs = [_byte_view(t) for t in srcs]
+    if not bs:
+        raise ValueError("pz_compressed_size_batch: no tensors")
+    dev = bs[0].device
+    out = torch.empty(len(bs), dtype=torch.int64, device=dev)
+    lens = [torch.empty(max(1, num_chunks(b.numel())), dtype=torch.int16, device=dev) for b in bs] if chunk_lens else None
+    check(lib.pz_compressed_size_batch(len(bs), _ptr_array(bs), _size_array([b.numel() for b in bs]), dtype,
+                                       elem_bits, _ptr(out), _ptr_array(lens) if lens else None, _stream(stream)),
+          "pz_compressed_size_batch")
+    if lens is not None:
+        lens = [ln[: num_chunks(b.numel())] for ln, b in zip(lens, bs)]
+    return out, lens
+
+
 def pz_decompress_batch(srcs, comp_bytes, raw_bytes, dtype: int, elem_bits: int, dsts=None,
                         status: torch.Tensor | None = None, stream=None):
     """pz_decompress on several streams of one (dtype, elem_bits). Returns

@@ -259,8 +259,17 @@ pz_status_t pz_compressed_size_ex(const void *d_src, size_t raw_bytes, int dtype
   if (!aligned16(d_src) || (reinterpret_cast<uintptr_t>(d_out_bytes) & 7u) ||
       (reinterpret_cast<uintptr_t>(d_chunk_lens) & 1u))
     return PZ_ERROR_INVALID_VALUE;
-  return from_hip(pz::launch_size(w, static_cast<const uint8_t *>(d_src), raw_bytes, codec_mask, tagged, 1,
-                                  d_out_bytes, nullptr, d_chunk_lens, static_cast<hipStream_t>(stream)));
+  pz::SBatch b{};
+  b.n = 1;
+  pz::STensor &x = b.t[0];
+  x.src = static_cast<const uint8_t *>(d_src);
+  x.out_bytes = d_out_bytes;
+  x.chunk_lens = d_chunk_lens;
+  x.raw_bytes = raw_bytes;
+  x.stride = 1;
+  pz::size_plan(x);
+  b.total_groups = x.ngroups;
+  return from_hip(pz::launch_size(w, b, codec_mask, tagged, static_cast<hipStream_t>(stream)));
 }
 
 pz_status_t pz_compressed_size(const void *d_src, size_t raw_bytes, int dtype, int elem_bits,
@@ -277,9 +286,48 @@ pz_status_t pz_compressed_size_sampled(const void *d_src, size_t raw_bytes, int 
   if (!aligned16(d_src) || (reinterpret_cast<uintptr_t>(d_sample) & 7u) ||
       (reinterpret_cast<uintptr_t>(d_sample_lens) & 1u))
     return PZ_ERROR_INVALID_VALUE;
-  return from_hip(pz::launch_size(w, static_cast<const uint8_t *>(d_src), raw_bytes, PZ_CODEC_ALL, 1,
-                                  chunk_stride, d_sample, d_sample + 1, d_sample_lens,
-                                  static_cast<hipStream_t>(stream)));
+  pz::SBatch b{};
+  b.n = 1;
+  pz::STensor &x = b.t[0];
+  x.src = static_cast<const uint8_t *>(d_src);
+  x.out_bytes = d_sample;
+  x.out_raw = d_sample + 1;
+  x.chunk_lens = d_sample_lens;
+  x.raw_bytes = raw_bytes;
+  x.stride = chunk_stride;
+  pz::size_plan(x);
+  b.total_groups = x.ngroups;
+  return from_hip(pz::launch_size(w, b, PZ_CODEC_ALL, 1, static_cast<hipStream_t>(stream)));
+}
+
+pz_status_t pz_compressed_size_batch(int count, const void *const *d_srcs, const size_t *raw_bytes, int dtype,
+                                     int elem_bits, uint64_t *d_out_bytes, uint16_t *const *d_chunk_lens,
+                                     void *stream) {
+  const int w = symbol_width(dtype, elem_bits);
+  if (w < 0 || count < 0 || (reinterpret_cast<uintptr_t>(d_out_bytes) & 7u)) return PZ_ERROR_INVALID_VALUE;
+  if (count > 0 && (!d_srcs || !raw_bytes || !d_out_bytes)) return PZ_ERROR_INVALID_VALUE;
+  for (int i = 0; i < count; ++i) {
+    if ((raw_bytes[i] && !d_srcs[i]) || !aligned16(d_srcs[i])) return PZ_ERROR_INVALID_VALUE;
+    if (d_chunk_lens && (reinterpret_cast<uintptr_t>(d_chunk_lens[i]) & 1u)) return PZ_ERROR_INVALID_VALUE;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int i = 0; i < count;) {
+    pz::SBatch b{};
+    for (; i < count && b.n < (uint32_t)pz::kMaxBatch; ++i) {
+      pz::STensor &x = b.t[b.n++];
+      x.src = static_cast<const uint8_t *>(d_srcs[i]);
+      x.out_bytes = d_out_bytes + i;
+      x.chunk_lens = d_chunk_lens ? d_chunk_lens[i] : nullptr;
+      x.raw_bytes = raw_bytes[i];
+      x.stride = 1;
+      pz::size_plan(x);
+      x.group_begin = b.total_groups;
+      b.total_groups += x.ngroups;
+    }
+    const hipError_t e = pz::launch_size(w, b, PZ_CODEC_ALL, 1, s);
+    if (e != hipSuccess) return from_hip(e);
+  }
+  return PZ_SUCCESS;
 }
 
 pz_status_t pz_block_sizes(const void *d_src, size_t raw_bytes, int dtype, int elem_bits,

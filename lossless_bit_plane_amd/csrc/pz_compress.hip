@@ -482,8 +482,10 @@ __global__ __launch_bounds__(kCThreads, 2) void compress_kernel(const CBatch bat
   const uint32_t gtile = __builtin_amdgcn_readfirstlane(group_tile);
   if (gtile >= batch.total_tiles) return;
   uint32_t k = 0;
+  if (batch.n > 1) {  // a single tensor's fields load at once
 #pragma unroll
-  for (uint32_t i = 1; i < (uint32_t)kMaxBatch; ++i) k += i < batch.n && gtile >= batch.t[i].tile_begin ? 1u : 0u;
+    for (uint32_t i = 1; i < (uint32_t)kMaxBatch; ++i) k += i < batch.n && gtile >= batch.t[i].tile_begin ? 1u : 0u;
+  }
   const uint8_t *__restrict__ src = batch.t[k].src;
   uint8_t *__restrict__ dst = batch.t[k].dst;
   const uint64_t raw_bytes = batch.t[k].raw_bytes, nchunks = batch.t[k].nchunks;
@@ -879,9 +881,7 @@ __global__ __launch_bounds__(kCThreads, 2) void compress_kernel(const CBatch bat
 // out_bytes (which holds the headers' bytes beforehand).
 // ---------------------------------------------------------------------------
 template <int W>
-__global__ __launch_bounds__(kCThreads, 2) void size_kernel(
-    const uint8_t *__restrict__ src, uint64_t raw_bytes, uint64_t nchunks, uint64_t stride,
-    uint64_t nsampled, uint64_t *__restrict__ out_bytes, uint16_t *__restrict__ chunk_lens, Mode mode) {
+__global__ __launch_bounds__(kCThreads, 2) void size_kernel(const SBatch batch, Mode mode) {
   constexpr int N = 1024 / W;
   __shared__ __attribute__((aligned(16))) uint32_t lds[kStageDwords];
   __shared__ uint16_t blk_bits[kCThreads];
@@ -893,7 +893,19 @@ __global__ __launch_bounds__(kCThreads, 2) void size_kernel(
 
   const uint32_t t = threadIdx.x, lane = lane_id();
   const uint32_t wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const uint64_t sample = (uint64_t)blockIdx.x * kGroupChunks + (t >> 5);
+  // The launch's group -> the tensor it belongs to (the last one starting at
+  // or before it: a tensor without chunks has no groups).
+  uint32_t k = 0;
+  if (batch.n > 1) {  // a single tensor's fields load at once
+#pragma unroll
+    for (uint32_t i = 1; i < (uint32_t)kMaxBatch; ++i) k += i < batch.n && blockIdx.x >= batch.t[i].group_begin ? 1u : 0u;
+  }
+  const uint8_t *__restrict__ src = batch.t[k].src;
+  const uint64_t raw_bytes = batch.t[k].raw_bytes, nchunks = batch.t[k].nchunks;
+  const uint64_t stride = batch.t[k].stride, nsampled = batch.t[k].nsampled;
+  uint64_t *__restrict__ out_bytes = batch.t[k].out_bytes;
+  uint16_t *__restrict__ chunk_lens = batch.t[k].chunk_lens;
+  const uint64_t sample = (uint64_t)(blockIdx.x - batch.t[k].group_begin) * kGroupChunks + (t >> 5);
   // Samples past the last one read as zeros (their chunk is past the end).
   const uint64_t chunk = sample < nsampled ? sample * stride : nchunks;
   const uint64_t block = chunk * kBlocksPerChunk + (t & 31);
@@ -983,38 +995,35 @@ hipError_t fill_u64(uint64_t *p, uint64_t n, uint64_t value, hipStream_t stream)
   return hipGetLastError();
 }
 
-__global__ void store_size_init_kernel(uint64_t *out_bytes, uint64_t v0, uint64_t *out_raw, uint64_t v1) {
-  if (threadIdx.x == 0) {
-    if (out_bytes) *out_bytes = v0;
-    if (out_raw) *out_raw = v1;
-  }
+// Starting values of a size launch's outputs: the sampled chunks' headers
+// (2 bytes each) and their raw bytes (whole chunks except the tensor's last
+// chunk when it is sampled); thread k sets tensor k's.
+__global__ void store_size_init_kernel(const SBatch batch) {
+  const uint32_t k = threadIdx.x;
+  if (k >= batch.n) return;
+  const STensor &x = batch.t[k];
+  const uint64_t last = x.nsampled ? (x.nsampled - 1) * x.stride : 0;
+  const uint64_t sampled_raw =
+      x.nsampled ? (x.nsampled - 1) * kChunkBytes + min_u64(kChunkBytes, x.raw_bytes - last * kChunkBytes) : 0;
+  if (x.out_bytes) *x.out_bytes = 2 * x.nsampled;
+  if (x.out_raw) *x.out_raw = sampled_raw;
 }
 
-hipError_t launch_size(int w, const uint8_t *src, uint64_t raw_bytes, uint32_t codec_mask, int tagged,
-                       uint64_t stride, uint64_t *out_bytes, uint64_t *out_raw, uint16_t *chunk_lens,
-                       hipStream_t stream) {
-  const uint64_t nchunks = (raw_bytes + kChunkBytes - 1) / kChunkBytes;
-  const uint64_t nsampled = (nchunks + stride - 1) / stride;
-  if (out_bytes || out_raw) {
-    // Headers of the sampled chunks; their raw bytes: whole chunks except
-    // the tensor's last chunk when it is sampled.
-    const uint64_t last = nsampled ? (nsampled - 1) * stride : 0;
-    const uint64_t sampled_raw =
-        nsampled ? (nsampled - 1) * kChunkBytes + min_u64(kChunkBytes, raw_bytes - last * kChunkBytes) : 0;
-    hipLaunchKernelGGL(store_size_init_kernel, dim3(1), dim3(64), 0, stream, out_bytes, 2 * nsampled,
-                       out_raw, sampled_raw);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (nsampled == 0) return hipSuccess;
-  const uint64_t groups = (nsampled + kGroupChunks - 1) / kGroupChunks;
+void size_plan(STensor &x) {
+  x.nchunks = (x.raw_bytes + kChunkBytes - 1) / kChunkBytes;
+  x.nsampled = (x.nchunks + x.stride - 1) / x.stride;
+  x.ngroups = (uint32_t)((x.nsampled + kGroupChunks - 1) / kGroupChunks);
+}
+
+hipError_t launch_size(int w, const SBatch &batch, uint32_t codec_mask, int tagged, hipStream_t stream) {
+  hipLaunchKernelGGL(store_size_init_kernel, dim3(1), dim3(64), 0, stream, batch);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || batch.total_groups == 0) return e;
   const Mode mode = make_mode(w, codec_mask, tagged);
   if (w == 16)
-    hipLaunchKernelGGL(size_kernel<16>, dim3((unsigned)groups), dim3(kCThreads), 0, stream, src,
-                       raw_bytes, nchunks, stride, nsampled, out_bytes, chunk_lens, mode);
+    hipLaunchKernelGGL(size_kernel<16>, dim3(batch.total_groups), dim3(kCThreads), 0, stream, batch, mode);
   else
-    hipLaunchKernelGGL(size_kernel<32>, dim3((unsigned)groups), dim3(kCThreads), 0, stream, src,
-                       raw_bytes, nchunks, stride, nsampled, out_bytes, chunk_lens, mode);
+    hipLaunchKernelGGL(size_kernel<32>, dim3(batch.total_groups), dim3(kCThreads), 0, stream, batch, mode);
   return hipGetLastError();
 }
 

@@ -325,8 +325,10 @@ __global__ __launch_bounds__(kLocateChunks * G) void locate_kernel(const DBatch 
   const uint32_t gtile = __builtin_amdgcn_readfirstlane(group_tile);
   if (gtile >= batch.total_tiles) return;
   uint32_t k = 0;
+  if (batch.n > 1) {  // a single tensor's fields load at once
 #pragma unroll
-  for (uint32_t i = 1; i < (uint32_t)kMaxBatch; ++i) k += i < batch.n && gtile >= batch.t[i].tile_begin ? 1u : 0u;
+    for (uint32_t i = 1; i < (uint32_t)kMaxBatch; ++i) k += i < batch.n && gtile >= batch.t[i].tile_begin ? 1u : 0u;
+  }
   const uint8_t *__restrict__ src = batch.t[k].src;
   const uint64_t comp_bytes = batch.t[k].comp_bytes, raw_bytes = batch.t[k].raw_bytes;
   const uint64_t nchunks = batch.t[k].nchunks;
@@ -499,8 +501,10 @@ __global__ __launch_bounds__(kGroupThreads) void decode_kernel(const DBatch batc
   const uint32_t wave = __builtin_amdgcn_readfirstlane(t >> 6);
   // The launch's group -> the tensor it belongs to and the group within it.
   uint32_t k = 0;
+  if (batch.n > 1) {  // a single tensor's fields load at once
 #pragma unroll
-  for (uint32_t i = 1; i < (uint32_t)kMaxBatch; ++i) k += i < batch.n && blockIdx.x >= batch.t[i].group_begin ? 1u : 0u;
+    for (uint32_t i = 1; i < (uint32_t)kMaxBatch; ++i) k += i < batch.n && blockIdx.x >= batch.t[i].group_begin ? 1u : 0u;
+  }
   const uint8_t *__restrict__ src = batch.t[k].src;
   uint8_t *__restrict__ dst = batch.t[k].dst;
   const uint64_t comp_bytes = batch.t[k].comp_bytes, raw_bytes = batch.t[k].raw_bytes;

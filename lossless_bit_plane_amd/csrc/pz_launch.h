@@ -85,12 +85,33 @@ size_t decompress_extra(uint64_t raw_bytes);
 
 hipError_t fill_u64(uint64_t *p, uint64_t n, uint64_t value, hipStream_t stream);
 
-// Size pass over chunks 0, stride, 2*stride, ...: out_bytes receives their
-// stream bytes (2 + payload each), out_raw their raw bytes, chunk_lens their
-// header values. Every output is nullable.
-hipError_t launch_size(int w, const uint8_t *src, uint64_t raw_bytes, uint32_t codec_mask, int tagged,
-                       uint64_t stride, uint64_t *out_bytes, uint64_t *out_raw, uint16_t *chunk_lens,
-                       hipStream_t stream);
+// The tensors of one size launch. The size pass of tensor k covers its
+// chunks 0, stride, 2*stride, ... (nsampled of them, 16 per workgroup, the
+// launch's groups group_begin .. group_begin + ngroups - 1): out_bytes
+// receives their stream bytes (2 + payload each), out_raw their raw bytes,
+// chunk_lens their header values. Every output is nullable; a tensor with no
+// chunks has no groups and gets zeros.
+struct STensor {
+  const uint8_t *src;
+  uint64_t *out_bytes;
+  uint64_t *out_raw;
+  uint16_t *chunk_lens;
+  uint64_t raw_bytes;
+  uint64_t nchunks;
+  uint64_t stride;
+  uint64_t nsampled;
+  uint32_t group_begin;
+  uint32_t ngroups;
+};
+struct SBatch {
+  uint32_t n;
+  uint32_t total_groups;
+  STensor t[kMaxBatch];
+};
+
+// Fills in nchunks, nsampled and ngroups of a tensor from raw_bytes and stride.
+void size_plan(STensor &x);
+hipError_t launch_size(int w, const SBatch &batch, uint32_t codec_mask, int tagged, hipStream_t stream);
 // Per-block candidate sizes and tags (PlaneZip candidates, tagged).
 hipError_t launch_block_sizes(int w, const uint8_t *src, uint64_t raw_bytes, uint16_t *block_sizes,
                               uint8_t *block_tags, hipStream_t stream);

@@ -127,6 +127,13 @@ def test_batch_calls_check_every_tensor_before_enqueueing(lib):
                                    None) == bad
     assert lib.pz_decompress_batch(2, ptrs(fake, None), sizes(100, 100), 0, 16, ptrs(fake, fake),
                                    sizes(4096, 4096), None, None) == bad
+    # Size batches: empty, bad pair, misaligned source or outputs.
+    assert lib.pz_compressed_size_batch(0, None, None, 0, 16, None, None, None) == 0
+    assert lib.pz_compressed_size_batch(1, ptrs(fake), sizes(100), 1, 16, fake, None, None) == bad
+    assert lib.pz_compressed_size_batch(2, ptrs(fake, fake + 8), sizes(100, 100), 0, 16, fake, None, None) == bad
+    assert lib.pz_compressed_size_batch(1, ptrs(fake), sizes(100), 0, 16, fake + 4, None, None) == bad
+    assert lib.pz_compressed_size_batch(1, ptrs(fake), sizes(100), 0, 16, fake, ptrs(fake + 1), None) == bad
+    assert lib.pz_compressed_size_batch(1, ptrs(None), sizes(100), 0, 16, fake, None, None) == bad
 
 
 def test_swapper_rejects_bad_sizes_without_touching_the_device(lib):

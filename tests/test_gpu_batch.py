@@ -1,6 +1,7 @@
-"""Batched calls through the C ABI (needs a GPU): pz_compress_batch and
-pz_decompress_batch give every tensor exactly the stream, output and status
-that the oracle fixes for it alone. Bar: bit-exact streams and round trips,
+"""Batched calls through the C ABI (needs a GPU): pz_compress_batch,
+pz_compressed_size_batch and pz_decompress_batch give every tensor exactly
+the stream, size, header values, output and status that the oracle fixes
+for it alone. Bar: bit-exact streams and round trips,
 corruption reported for the corrupt tensor only, host-side rejection of a
 whole call before anything is enqueued."""
 import os
@@ -41,11 +42,15 @@ def _check_batch(pz, datas, dtype, w):
     oracle, decompress them in one batch call and compare the bytes."""
     srcs = [_dev(d) for d in datas]
     dsts, nb = pz.pz_compress_batch(srcs, dtype, w)
+    sizes, lens = pz.pz_compressed_size_batch(srcs, dtype, w, chunk_lens=True)
     n = [int(v) for v in nb.cpu().tolist()]
+    assert [int(v) for v in sizes.cpu().tolist()] == n
     for i, d in enumerate(datas):
         o = oracle.compress(d, w, threads=THREADS)
         g = dsts[i][: n[i]].cpu().numpy()
         assert g.size == o.size and np.array_equal(g, o), (i, d.size, g.size, o.size)
+        np.testing.assert_array_equal(lens[i].cpu().numpy().view(np.uint16).astype(np.int64),
+                                      oracle.header_table(o, d.size))
     outs, status = pz.pz_decompress_batch(dsts, n, [d.size for d in datas], dtype, w)
     assert status.cpu().tolist() == [0] * len(datas)
     for i, d in enumerate(datas):
