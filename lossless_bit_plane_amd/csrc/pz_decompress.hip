@@ -423,6 +423,7 @@ struct LdsBits {
 // 0 := 0); DBX's top plane (the borrow plane) only feeds the XOR chain. Every
 // plane is decoded with selects rather than branches: the class comes from the
 // trailing-zero count of the next 32 bits, and a pending zero run yields X = 0.
+// A lane with `active` false keeps its pos; its planes are unspecified.
 template <int W>
 PZ_DEV void read_planes(const LdsBits &in, uint32_t &pos, uint32_t (&t)[32], int K, uint32_t L,
                         bool dbx, bool active) {
@@ -438,7 +439,11 @@ PZ_DEV void read_planes(const LdsBits &in, uint32_t &pos, uint32_t (&t)[32], int
   uint32_t run = 0;
 #pragma unroll
   for (int j = W; j >= 0; --j) {
-    const bool live = active && j < K;
+    // Only the top plane can be absent (K is W or W + 1). Below it every
+    // plane of a decoding lane is live, and the other lanes' planes are
+    // never used, so those planes need no liveness selects (only their
+    // position must not move).
+    const bool live = j < W || (active && j < K);
     const bool fresh = live && run == 0;
     uint32_t win;
     uint64_t after;
@@ -455,7 +460,7 @@ PZ_DEV void read_planes(const LdsBits &in, uint32_t &pos, uint32_t (&t)[32], int
     // Planes left in a zero run: a fresh run code sets them, every live
     // plane uses one (as arithmetic on masks: written as selects, the
     // update is compiled into exec-mask branches).
-    const uint32_t fm = 0u - (uint32_t)fresh;
+    const uint32_t fm = 0u - (uint32_t)(fresh && active);  // other lanes keep their position
     const uint32_t newrun = (tz == 1 ? ((win >> 2) & ((1u << R) - 1u)) + 1u : 0u) & fm;
     pos += len & fm;
     run = newrun | ((run - (uint32_t)live) & ~fm);
