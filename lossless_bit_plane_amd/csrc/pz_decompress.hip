@@ -237,8 +237,8 @@ PZ_DEV bool parse_chunk(ChunkRing<G> &in, bool coded, uint32_t H, uint32_t raw_l
     const bool live = coded && !bad && b < nb;
     if (!__ballot(live)) break;
     int left = 0;
-    uint32_t L = N, pmask = 0;
-    uint64_t lut = 0;
+    uint32_t L = N, pmask = 0, V = 0;
+    uint32_t lut = 0;  // short-code lengths by class: byte tz - 1 for tz = 1..4
     if (live) {
       in.step(pos);
       if (ql == 0) boff[b] = (uint16_t)pos;
@@ -260,11 +260,10 @@ PZ_DEV bool parse_chunk(ChunkRing<G> &in, bool coded, uint32_t H, uint32_t raw_l
         // verbatim 1+L, run 2+R, lone zero 3, pair/single 5+PW, other 5.
         const uint32_t pw = (uint32_t)position_bits((int)L);
         pmask = (1u << pw) - 1u;
-        lut = (uint64_t)(1 + L) | ((uint64_t)(2 + R) << 8) | (3ull << 16) |
-              ((uint64_t)(5 + pw) << 24) | (5ull << 32);
+        V = 1 + L;
+        lut = (2 + R) | (3u << 8) | ((5 + pw) << 16) | (5u << 24);
       }
     }
-    const uint32_t V = (uint32_t)(lut & 0xFFu);
     const uint32_t spec = 4 * ql * V;  // this lane tries codes 4 ql .. 4 ql + 3
     const uint32_t runf = (1u << R) - 1u;
     // Straight-line steps (selects, no branches): a lone wave pays for every
@@ -286,7 +285,7 @@ PZ_DEV bool parse_chunk(ChunkRing<G> &in, bool coded, uint32_t H, uint32_t raw_l
       for (int m = 0; m < 2; ++m) {
         take = take && left > 0 && (win & 1u) == 0u;  // a short code (at most 11 bits)
         const uint32_t tz = (uint32_t)__builtin_ctz(win | 16u);  // trailing zeros, capped at 4
-        const uint32_t len = (uint32_t)(lut >> (8 * tz)) & 0xFFu;
+        const uint32_t len = __builtin_amdgcn_ubfe(lut, 8u * tz - 8u, 8u);  // tz = 0 is never taken
         const int planes = tz == 1 ? (int)((win >> 2) & runf) + 2 : 1;  // a run past the end: left < 0
         // A position must lie inside the plane: p <= L-1 (single), L-2 (pair).
         const bool badpos = tz == 3 && ((win >> 5) & pmask) + 2 > L + ((win >> 4) & 1u);
@@ -448,7 +447,7 @@ PZ_DEV void read_planes(const LdsBits &in, uint32_t &pos, uint32_t (&t)[32], int
     uint32_t win;
     uint64_t after;
     in.peek_code(pos, win, after);
-    const uint32_t tz = min((uint32_t)(__ffs(win) - 1), 5u);  // 5: five or more zeros
+    const uint32_t tz = (uint32_t)__builtin_ctz(win | 32u);  // 5: five or more zeros
     const PT verb = (PT)after & ones;
     const PT one_or_pair = (((win >> 4) & 1u) ? (PT)1 : (PT)3) << ((win >> 5) & pmask);
     PT x = tz >= 5 ? ones : (PT)0;
