@@ -78,7 +78,9 @@ hipError_t with_scratch(hipStream_t stream, const pz::ScratchNeed &need, F launc
     ent = &g_scratch.back();
   }
   if (ent->words < need.words || ent->extra < need.extra || !ent->base) {
-    const size_t words = need.words > ent->words ? need.words + need.words / 4 + 64 : ent->words;
+    // An even word count keeps the per-call bytes 16-byte aligned (locate
+    // stores block offsets in 16-byte units).
+    const size_t words = need.words > ent->words ? (need.words + need.words / 4 + 64 + 1) & ~size_t(1) : ent->words;
     const size_t extra = ((need.extra > ent->extra ? need.extra + need.extra / 4 : ent->extra) + 15) & ~size_t(15);
     if (ent->base) {
       e = hipFreeAsync(ent->base, stream);
