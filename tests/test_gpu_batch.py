@@ -100,6 +100,21 @@ def test_batch_ragged_empty_and_split(pz, w):
     assert [n[i] for i, d in enumerate(datas) if d.size == 0] == [0, 0, 0]
 
 
+def test_batch_tile_edges(pz):
+    """Tensors ending exactly at, one byte before and one byte after the
+    tiles' edges (8 chunks per decode group, 16 per compress tile, 64 per
+    locate tile), so that one tensor's last tile and the next one's first
+    meet at every kind of edge in one launch."""
+    (base,) = pzinputs.relu_smoke()
+    sizes = []
+    for chunks in (8, 16, 64, 1, 63, 65, 17, 7):
+        for d in (-1, 0, 1):
+            sizes.append(chunks * 4096 + d)
+    datas = [np.ascontiguousarray(base.data[(977 * i) % 4096:][:n]) for i, n in enumerate(sizes)]
+    print("[batch] tile edges", sizes, flush=True)
+    _check_batch(pz, datas, pzinputs.BF16, 16)
+
+
 def test_batch_corrupt_stream_flags_only_its_tensor(pz):
     import torch
 
