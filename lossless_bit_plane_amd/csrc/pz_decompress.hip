@@ -205,8 +205,8 @@ struct ChunkRing {
       }
       // Stored dwords at or above cur stay in the ring until the group passes them.
       if (fill + kGroupDwords <= cur + kRingDwords) issue();
+      wave_lds_fence();  // the group's stores before its reads
     }
-    wave_lds_fence();  // the group's stores before its reads
   }
   PZ_DEV uint32_t peek(uint32_t pos) const {
     const uint32_t a = lead + pos;
@@ -248,9 +248,13 @@ PZ_DEV bool parse_chunk(ChunkRing<G> &in, bool coded, uint32_t H, uint32_t raw_l
       if ((head & mode.zmask) == mode.zcode) {
         pos += mode.zbits;  // an all-zero block: one run over all planes
       } else {
-        uint32_t n = (uint32_t)popc32(in.peek(pos + hb));
-        if (W == 16) n += (uint32_t)popc32(in.peek(pos + hb + 32));
         const bool masked = tag == kZVC || tag == kZBX;
+        // The zero mask's count, read only when some chunk of the wave needs it.
+        uint32_t n = 0;
+        if (__ballot(masked)) {
+          n = (uint32_t)popc32(in.peek(pos + hb));
+          if (W == 16) n += (uint32_t)popc32(in.peek(pos + hb + 32));
+        }
         pos += hb + (tag == kDBX ? W : 0u) + (masked ? N : 0u) + (tag == kZVC ? W * n : 0u) +
                (tag == kRAW ? 1024u : 0u);
         bad |= tag > 4;
