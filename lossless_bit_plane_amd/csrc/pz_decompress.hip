@@ -453,12 +453,14 @@ PZ_DEV void read_planes(const LdsBits &in, uint32_t &pos, uint32_t (&t)[32], int
     in.peek_code(pos, win, after);
     const uint32_t tz = (uint32_t)__builtin_ctz(win | 32u);  // 5: five or more zeros
     const PT verb = (PT)after & ones;
-    const PT one_or_pair = (((win >> 4) & 1u) ? (PT)1 : (PT)3) << ((win >> 5) & pmask);
-    PT x = tz >= 5 ? ones : (PT)0;
-    x = tz == 0 ? verb : x;
-    x = tz == 3 ? one_or_pair : x;
-    x = tz == 4 ? above : x;  // the plane before the XOR is zero
-    x = fresh ? x : (PT)0;
+    // Single (bit 4 set): one 1; pair: two adjacent 1s.
+    const PT one_or_pair = (PT)(3u - 2u * ((win >> 4) & 1u)) << ((win >> 5) & pmask);
+    // Within a zero run (not fresh) the class reads as a run (X = 0).
+    const uint32_t cls = fresh ? tz : 1u;
+    PT x = cls >= 5 ? ones : (PT)0;
+    x = cls == 0 ? verb : x;
+    x = cls == 3 ? one_or_pair : x;
+    x = cls == 4 ? above : x;  // the plane before the XOR is zero
     const uint32_t len = (uint32_t)(lut >> (8 * tz)) & 0xFFu;
     // Planes left in a zero run: a fresh run code sets them, every live
     // plane uses one (as arithmetic on masks: written as selects, the
