@@ -1,11 +1,15 @@
 """Python entry points with the names of the C ABI (argument marshalling only).
 
 Tensors must be contiguous device tensors; the stream defaults to the current
-torch stream. Every call only enqueues work, like the C functions.
+torch stream. Every call only enqueues work, like the C functions (except
+with the PZ_DEBUG environment variable set, when pz_compressed_size also
+prints the size pass's per-block tags and sizes and synchronizes).
 """
 from __future__ import annotations
 
 import ctypes
+import os
+import sys
 
 import torch
 
@@ -26,9 +30,12 @@ def max_compressed_bytes(raw_bytes: int) -> int:
     return 2 * num_chunks(raw_bytes) + raw_bytes
 
 
+def _stream_obj(stream):
+    return torch.cuda.current_stream() if stream is None else stream
+
+
 def _stream(stream):
-    s = torch.cuda.current_stream() if stream is None else stream
-    return s.cuda_stream
+    return _stream_obj(stream).cuda_stream
 
 
 def _ptr(t):
@@ -60,7 +67,34 @@ def pz_compressed_size(src: torch.Tensor, dtype=None, elem_bits=None, chunk_lens
     lens = torch.empty(num_chunks(b.numel()), dtype=torch.int16, device=b.device) if chunk_lens else None
     check(lib.pz_compressed_size(_ptr(b), b.numel(), dtype, elem_bits, _ptr(out), _ptr(lens),
                                  _stream(stream)), "pz_compressed_size")
+    if os.environ.get("PZ_DEBUG"):
+        _debug_dump(src, dtype, elem_bits, out, stream)
     return out, lens
+
+
+_TAG_NAMES = ("ZVC", "DBX", "BX", "ZBX", "RAW")
+
+
+def _debug_dump(src, dtype, elem_bits, out, stream):
+    """PZ_DEBUG=1: the size pass's per-block tags (a histogram) and the mean
+    size of every candidate, on stderr; PZ_DEBUG=2: also one line per block
+    (tag and the five candidate sizes in bits). Synchronizes the stream."""
+    sizes, tags = pz_block_sizes(src, dtype, elem_bits, stream=stream)
+    s = _stream_obj(stream)
+    s.synchronize()
+    sz = sizes.cpu().view(torch.uint16).to(torch.int64) if sizes.numel() else torch.zeros((0, 5), dtype=torch.int64)
+    tg = tags.cpu().to(torch.int64)
+    nb = tg.numel()
+    hist = torch.bincount(tg, minlength=5).tolist() if nb else [0] * 5
+    mean = (sz.double().mean(dim=0).tolist() if nb else [0.0] * 5)
+    print(f"[PZ_DEBUG] {nb} blocks, w={elem_bits}, stream {int(out.item())} bytes; tags "
+          + ", ".join(f"{n} {c}" for n, c in zip(_TAG_NAMES, hist))
+          + "; mean candidate bits " + ", ".join(f"{n} {m:.1f}" for n, m in zip(_TAG_NAMES, mean)),
+          file=sys.stderr, flush=True)
+    if os.environ.get("PZ_DEBUG") == "2":
+        for i in range(nb):
+            print(f"[PZ_DEBUG] block {i}: {_TAG_NAMES[int(tg[i])]} "
+                  + " ".join(str(int(v)) for v in sz[i].tolist()), file=sys.stderr)
 
 
 def pz_compressed_size_sampled(src: torch.Tensor, chunk_stride: int = 4, dtype=None, elem_bits=None,

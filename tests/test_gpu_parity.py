@@ -137,6 +137,21 @@ def test_block_sizes_match_oracle_structured(pz, w):
     _check_tensor(pz, t)
 
 
+def test_pz_debug_dump_matches_oracle_tags(pz, monkeypatch, capfd):
+    """PZ_DEBUG=1 prints the size pass's tag histogram; it equals the
+    oracle's size model on the smoke tensor."""
+    (t,) = pzinputs.relu_smoke()
+    monkeypatch.setenv("PZ_DEBUG", "1")
+    pz.pz_compressed_size(_dev(t.data), t.dtype, t.elem_bits)
+    err = capfd.readouterr().err
+    line = [l for l in err.splitlines() if l.startswith("[PZ_DEBUG]")][0]
+    model = size_model.candidate_sizes(t.data.reshape(-1, 128), 16)
+    want = np.bincount(size_model.select(model), minlength=5)
+    names = ("ZVC", "DBX", "BX", "ZBX", "RAW")
+    assert "tags " + ", ".join(f"{n} {c}" for n, c in zip(names, want.tolist())) in line, line
+    assert f"{t.nbytes // 128} blocks" in line
+
+
 def test_relu_smoke_stream_bitexact(pz):
     (t,) = pzinputs.relu_smoke()
     _check_tensor(pz, t)
