@@ -9,14 +9,18 @@
 // Mapping to the hardware: one lane owns one 128-byte block, so a wave holds
 // two 4 KB chunks. A lane sizes the four plane encodings without transposing:
 // the XORed planes of BX are the bit-planes of s ^ (s >> 1), so "plane j is
-// zero / all ones / holds one 1 / holds two 1s" are OR, AND and saturating
-// count reductions over the block's symbols, evaluated bit-parallel on all
-// planes at once (two BF16 symbols per 32-bit register). Only the chosen
-// encoding is transposed (a 32x32 bit-matrix butterfly in registers) and
-// emitted: every code is OR-ed into a per-chunk LDS buffer at its bit offset,
-// with no branches on the bit position. Chunk offsets come from a single-pass
-// decoupled look-back over per-wave chunk-length sums, so the input is read
-// once and the stream written once.
+// zero / all ones / holds one 1 / holds two adjacent 1s" are OR, AND, a
+// saturating per-bit population count and an adjacency OR over the block's
+// symbols, evaluated on all planes at once. For w = 16 a register holds
+// symbols i and i + 32 (the "split" layout), so that neighbouring symbols sit
+// in neighbouring registers at the same bit positions and one packed 16-bit
+// subtraction yields two of DBX's deltas. Only the chosen encoding is
+// transposed (a 32x32 bit-matrix butterfly in registers) and emitted: each
+// code is OR-ed into a per-chunk LDS buffer at its bit offset. Planes that
+// every lane of a wave codes verbatim, or that are zero in every lane, take
+// short uniform paths; the others go through a branch-free classifier. Chunk
+// offsets come from a single-pass decoupled look-back over per-workgroup
+// stream lengths, so the input is read once and the stream written once.
 #include <type_traits>
 
 #include "pz_device.h"
@@ -56,39 +60,49 @@ PZ_DEV void load_block(const uint8_t *__restrict__ src, uint64_t raw_bytes, uint
   }
 }
 
-// Makes the compiler treat the block's registers as new values, so that
-// expressions of one phase are recomputed in the next instead of being kept
-// alive across it (which would double the register footprint).
-PZ_DEV void launder_regs(uint32_t (&d)[32]) {
-#pragma unroll
-  for (int i = 0; i < 32; ++i) asm volatile("" : "+v"(d[i]));
-}
-
 PZ_DEV uint32_t lo16(uint32_t x) { return x & 0xFFFFu; }
 PZ_DEV uint32_t hi16(uint32_t x) { return x >> 16; }
 
-struct Sizes {
-  int sz[5];
-  int n;         // non-zero symbols
-  uint32_t b0;   // DBX borrow bits (layout: candidate_sizes16 / 32)
-  uint32_t b1;
-};
-
-// Merges per-half saturating counters (>=1, >=2, >=3 ones) of the two halves.
-PZ_DEV void fold_counts16(uint32_t t1, uint32_t t2, uint32_t t3, uint32_t &c1, uint32_t &c2,
-                          uint32_t &c3) {
-  c1 = lo16(t1) | hi16(t1);
-  c2 = lo16(t2) | hi16(t2) | (lo16(t1) & hi16(t1));
-  c3 = lo16(t3) | hi16(t3) | (lo16(t2) & hi16(t1)) | (lo16(t1) & hi16(t2));
+// Both 16-bit halves shifted right by one (bits 15 and 31 become zero).
+PZ_DEV uint32_t pk_shr1(uint32_t x) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, x) >> (unsigned short)1);
 }
 
-// Number of non-zero symbols of a block (w = 16: two per dword).
+// One v_bitop3_b32: bit i of the result is IMM's bit (4 a_i + 2 b_i + c_i),
+// so an IMM is written as the function applied to a = 0xF0, b = 0xCC,
+// c = 0xAA. (Spelled out, some of the statistics below were compiled into
+// two or three instructions each.)
+template <uint32_t IMM>
+PZ_DEV uint32_t b3(uint32_t a, uint32_t b, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(a, b, c, IMM);
+}
+constexpr uint32_t kAnd3 = 0xF0 & 0xCC & 0xAA;            // a & b & c
+constexpr uint32_t kOrAnd = 0xF0 | (0xCC & 0xAA);         // a | (b & c)
+constexpr uint32_t kCount0 = (0xF0 ^ 0xCC) | (0xF0 & 0xAA);  // (a ^ b) | (a & c)
+constexpr uint32_t kCount1 = (0xF0 & 0xCC) | 0xAA;        // (a & b) | c
+constexpr uint32_t kBorrow = (~0xF0 & 0xCC) | (~(0xF0 ^ 0xCC) & 0xAA);  // borrow out of a - b = c
+constexpr uint32_t kSelect = (0xF0 & 0xCC) | (~0xF0 & 0xAA);  // a ? b : c, bitwise
+
+// w = 16: the natural layout holds symbols 2q and 2q+1 in dword q; the split
+// layout holds symbol i in the low half of dword i and symbol i + 32 in its
+// high half.
+PZ_DEV void to_split16(uint32_t (&d)[32]) {
+  uint32_t s[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i)
+    s[i] = __builtin_amdgcn_perm(d[16 + (i >> 1)], d[i >> 1], (i & 1) ? 0x07060302u : 0x05040100u);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) d[i] = s[i];
+}
+
+// Number of non-zero symbols of a block (either layout).
 template <int W>
 PZ_DEV uint32_t count_nonzero(const uint32_t (&d)[32]) {
   if constexpr (W == 16) {
     uint32_t cnt = 0;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) cnt = pk_add_u16(cnt, pk_min_u16(d[i], 0x00010001u));
+    for (int i = 0; i < 32; i += 2)
+      cnt = cnt + pk_min_u16(d[i], 0x00010001u) + pk_min_u16(d[i + 1], 0x00010001u);
     return lo16(cnt) + hi16(cnt);
   } else {
     uint32_t cnt = 0;
@@ -98,157 +112,214 @@ PZ_DEV uint32_t count_nonzero(const uint32_t (&d)[32]) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// Candidate sizes, w = 16. d[i] holds symbols 2i (low half) and 2i+1 (high);
-// n is the block's number of non-zero symbols. zbx (wave-uniform) is false
-// when no lane of the wave holds a block with 0 < n < 64: then ZBX compacts
-// nothing away and its size is the mask plus the BX size.
-// ---------------------------------------------------------------------------
-PZ_DEV void candidate_sizes16(uint32_t (&d)[32], int n, bool zbx, Sizes &out) {
-  uint32_t bx_or_s = 0, bx_or = 0, bx_and = ~0u, bx_t2 = 0, bx_t3 = 0, bx_adj = 0, gh_prev = 0;
-  uint32_t db_or_s = 0, db_or = 0, db_and = ~0u, db_t2 = 0, db_t3 = 0, db_adj = 0, dgh_prev = 0;
-  uint32_t b0 = 0, b1 = 0;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const uint32_t s = d[i];
-    // BX: the XORed planes are the bit-planes of s ^ (s >> 1) per symbol.
-    const uint32_t g = s ^ ((s >> 1) & 0x7FFF7FFFu);
-    const uint32_t gh = g >> 16;
-    bx_or_s |= s;
-    bx_t3 |= bx_t2 & g;
-    bx_t2 |= bx_or & g;
-    bx_or |= g;
-    bx_and &= g;
-    bx_adj |= g & (gh | gh_prev);  // pairs (2i, 2i+1) and (2i-1, 2i), low half
-    gh_prev = gh;
+// Per-bit population count saturating at 3, over the values fed to it: the
+// pair (c0, c1) reads 0 = (0,0), 1 = (1,0), 2 = (0,1), 3 or more = (1,1).
+PZ_DEV void count4(uint32_t &c0, uint32_t &c1, uint32_t g) {
+  const uint32_t n0 = b3<kCount0 & 0xFF>(c0, g, c1);  // (c0 ^ g) | (c0 & c1)
+  c1 = b3<kCount1 & 0xFF>(c0, g, c1);                 // (c0 & g) | c1
+  c0 = n0;
+}
 
-    // DBX: deltas s[k] - s[k-1] as 17-bit two's complement; the low 16 bits
-    // come from a packed subtract, bit 16 is the borrow (bits 15 and 31 of
-    // bo). The XORed planes are the bits of D ^ (D >> 1).
-    const uint32_t prevp = i == 0 ? (s << 16) : funnel(s, d[i - 1], 16);
-    uint32_t ld = pk_sub_u16(s, prevp);
-    uint32_t bo = (~s & prevp) | (~(s ^ prevp) & ld);
-    uint32_t gd = ld ^ (((ld >> 1) & 0x7FFF7FFFu) | (bo & 0x80008000u));
-    if (i == 0) {  // symbol 0 is the base, not a delta
-      ld &= 0xFFFF0000u;
-      gd &= 0xFFFF0000u;
-      bo &= 0x80000000u;
-    }
-    const uint32_t dgh = gd >> 16;
-    db_or_s |= ld;
-    db_t3 |= db_t2 & gd;
-    db_t2 |= db_or & gd;
-    db_or |= gd;
-    db_and &= (i == 0) ? (gd | 0xFFFFu) : gd;
-    db_adj |= gd & (dgh | dgh_prev);
-    dgh_prev = dgh;
-    // Borrow bits, shifted in from the top: b0 bit i = borrow of delta 2i,
-    // bit 16+i = borrow of delta 2i+1 (i < 16); b1 likewise for deltas 32+.
-    if (i < 16)
-      b0 = (b0 >> 1) | (bo & 0x80008000u);
-    else
-      b1 = (b1 >> 1) | (bo & 0x80008000u);
-  }
-
-  uint32_t c1, c2, c3;
-
-  // BX: 16 planes of 64 bits.
-  fold_counts16(bx_or, bx_t2, bx_t3, c1, c2, c3);
-  const uint32_t nz = c1;
-  const uint32_t pz = ~(lo16(bx_or_s) | hi16(bx_or_s)) & 0xFFFFu;
-  const uint32_t single = c1 & ~c2;
-  const uint32_t exactly2 = c2 & ~c3;
-  out.sz[kBX] = plane_code_bits(nz, lo16(bx_and) & hi16(bx_and), pz, exactly2 & lo16(bx_adj), single,
-                                16, 64, 4);
-
-  // DBX: base, then 17 planes of 63 bits; plane 16 is the borrow plane.
-  fold_counts16(db_or, db_t2, db_t3, c1, c2, c3);
-  uint64_t dnz = c1;
-  uint64_t dones = lo16(db_and) & hi16(db_and);
-  const uint64_t dpz = ~(lo16(db_or_s) | hi16(db_or_s)) & 0xFFFFu;
-  uint64_t dsingle = c1 & ~c2;
-  uint64_t dpair = c2 & ~c3 & lo16(db_adj);
-  const int bc = popc32(b0) + popc32(b1);
-  // Adjacent borrows: deltas (2i, 2i+1), (2i+1, 2i+2), and (31, 32).
-  const uint32_t badj = ((b0 & (b0 >> 16)) & 0xFFFFu) | (((b0 >> 16) & (b0 >> 1)) & 0x7FFFu) |
-                        ((b1 & (b1 >> 16)) & 0xFFFFu) | (((b1 >> 16) & (b1 >> 1)) & 0x7FFFu) |
-                        ((b0 >> 31) & b1 & 1u);
-  dnz |= (uint64_t)(bc != 0) << 16;
-  dones |= (uint64_t)(bc == 63) << 16;
-  dsingle |= (uint64_t)(bc == 1) << 16;
-  dpair |= (uint64_t)(bc == 2 && badj != 0) << 16;
-  out.sz[kDBX] = 16 + plane_code_bits(dnz, dones, dpz, dpair, dsingle, 17, 63, 4);
-
-  // ZBX: the zero, count and pre-XOR masks are those of BX (zero symbols add
-  // nothing); "all ones" and adjacency run over the non-zero symbols only.
-  if (zbx) {
-    launder_regs(d);
-    uint32_t zb_and = ~0u, zb_adj = 0, zprev = 0;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const uint32_t s = d[i];
-      const uint32_t g = s ^ ((s >> 1) & 0x7FFF7FFFu);
-      const uint32_t gh = g >> 16;
-      const uint32_t zfill = pk_sub_u16(pk_min_u16(s, 0x00010001u), 0x00010001u);  // 0xFFFF if zero
-      zb_and &= g | zfill;
-      const uint32_t q = g | (zprev & zfill);  // low half: last non-zero g up to symbol 2i
-      zb_adj |= (zprev & g) | (q & gh);
-      zprev = gh | (q & (zfill >> 16));
-    }
-    out.sz[kZBX] = 64 + plane_code_bits(nz, lo16(zb_and) & hi16(zb_and), pz, exactly2 & lo16(zb_adj),
-                                        single, 16, n, 4);
-  } else {
-    out.sz[kZBX] = 64 + out.sz[kBX];
-  }
-
-  out.sz[kZVC] = 64 + 16 * n;
-  out.sz[kRAW] = 1024;
-  out.n = n;
-  out.b0 = b0;
-  out.b1 = b1;
+// Per-plane "at least 1 / 2 / 3 ones" of a w = 16 counter whose two halves
+// count symbols 0..31 and 32..63 of the same plane.
+PZ_DEV void fold4_16(uint32_t c0, uint32_t c1, uint32_t &ge1, uint32_t &ge2, uint32_t &ge3) {
+  const uint32_t a = c0 | c1, b = c1, c = c0 & c1;
+  ge1 = lo16(a) | hi16(a);
+  ge2 = lo16(b) | hi16(b) | (lo16(a) & hi16(a));
+  ge3 = lo16(c) | hi16(c) | (lo16(b) & hi16(a)) | (lo16(a) & hi16(b));
 }
 
 // ---------------------------------------------------------------------------
-// Candidate sizes, w = 32. d[i] is symbol i.
+// Plane-code size from per-plane class masks (bit j describes plane j):
+// nz: XORed plane non-zero; ones: XORed plane all ones; pz: plane before the
+// XOR is zero; pair: exactly two adjacent ones; single: exactly one one.
+// Codes of §III-A: a lone zero plane 3 bits, a run of zero planes 2+R bits,
+// all-ones and pre-XOR-zero planes 5 bits, pair and single 5 + PW bits, any
+// other plane 1 + L bits; the first matching class wins, in that order. Also
+// returns the masks of the verbatim and of the zero planes.
 // ---------------------------------------------------------------------------
-PZ_DEV void candidate_sizes32(uint32_t (&d)[32], int n, bool zbx, Sizes &out) {
-  uint32_t bx_or_s = 0, bx_or = 0, bx_and = ~0u, t2 = 0, t3 = 0, adj = 0, gprev = 0;
-  uint32_t db_or_s = 0, db_or = 0, db_and = ~0u, u2 = 0, u3 = 0, dadj = 0, dgprev = 0;
-  uint32_t bacc = 0;
+PZ_DEV int plane_code_bits(uint64_t nz, uint64_t ones, uint64_t pz, uint64_t pair, uint64_t single, int K,
+                           int L, int R, uint64_t &verb, uint64_t &zero) {
+  const uint64_t kmask = (K >= 64) ? ~0ull : ((1ull << K) - 1ull);
+  nz &= kmask;
+  const uint64_t a = nz & ones;
+  const uint64_t b = nz & ~a & pz;
+  const uint64_t rest = nz & ~a & ~b;
+  const uint64_t cd = rest & (pair | single);
+  const uint64_t e = rest & ~cd;
+  const uint64_t z = ~nz & kmask;
+  const uint64_t starts = z & ~(z >> 1);
+  const uint64_t lone = starts & ~(z << 1);
+  const int runs = popc64(starts), lones = popc64(lone);
+  const int pw = position_bits(L);
+  verb = e;
+  zero = z;
+  return 5 * popc64(a | b) + (5 + pw) * popc64(cd) + (1 + L) * popc64(e) + 3 * lones + (2 + R) * (runs - lones);
+}
+
+// What the statistics of a block give the selection and the emission: the
+// five candidate sizes (payload bits, no tag), and for the plane encodings
+// (index 0 DBX, 1 BX, 2 ZBX) the masks of their verbatim and zero planes;
+// and DBX's top plane (the borrows of the deltas).
+struct Stats {
+  int sz[5];
+  uint64_t verb[3];
+  uint64_t zero[3];
+  uint32_t bm_lo, bm_hi;
+};
+
+// ---------------------------------------------------------------------------
+// Candidate sizes, w = 16, split layout: d[i] holds symbols i (low half) and
+// i + 32 (high half). DBX's deltas are taken as delta[k] = s[k] - s[k-1] in
+// the arrangement (delta[i+1], delta[i+33]) = d[i+1] - d[i], so that the
+// register of delta k+1 is the one the transpose turns into plane bit k.
+// zbx (wave-uniform) is false when no lane of the wave holds a block with
+// 0 < n < 64: then ZBX compacts nothing away and its size is the mask plus
+// the BX size.
+// ---------------------------------------------------------------------------
+PZ_DEV void candidate_sizes16(const uint32_t (&d)[32], int n, bool zbx, Stats &o) {
+  uint32_t os = 0, an = ~0u, c0 = 0, c1 = 0, aj = 0, gp = 0, g0 = 0;
+  uint32_t dos = 0, dan = ~0u, e0 = 0, e1 = 0, daj = 0, dp = 0, dg0 = 0, bw0 = 0, bw1 = 0;
+  const uint32_t s32 = hi16(d[0]);
+#pragma unroll
+  for (int i = 0; i < 32; i += 2) {
+    uint32_t g[2], gd[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int k = i + h;
+      const uint32_t s = d[k];
+      // BX: the XORed planes are the bit-planes of s ^ (s >> 1) per symbol.
+      g[h] = s ^ pk_shr1(s);
+      count4(c0, c1, g[h]);
+      if (k == 0)
+        g0 = g[h];
+      else
+        aj = b3<kOrAnd & 0xFF>(aj, g[h], gp);  // symbols (k-1, k) and (k+31, k+32)
+      gp = g[h];
+      // DBX: deltas (k+1, k+33) as 17-bit two's complement; the low 16 bits
+      // come from a packed subtraction, bit 16 is the borrow (bits 15 and
+      // 31 of bo). The XORed planes are the bits of D ^ (D >> 1). The last
+      // register holds delta 32 (symbol 32 - symbol 31) alone.
+      const uint32_t cur = k < 31 ? d[k + 1] : s32;
+      const uint32_t prv = k < 31 ? s : lo16(s);
+      const uint32_t ld = pk_sub_u16(cur, prv);
+      const uint32_t bo = b3<kBorrow & 0xFF>(cur, prv, ld);
+      gd[h] = ld ^ b3<kSelect & 0xFF>(0x80008000u, bo, pk_shr1(ld));
+      count4(e0, e1, gd[h]);
+      if (k == 0)
+        dg0 = gd[h];
+      else
+        daj = b3<kOrAnd & 0xFF>(daj, gd[h], dp);
+      dp = gd[h];
+      dos |= ld;
+      // Borrow bits, shifted in from the top: bw0 bit k = borrow of delta
+      // k+1, bit 16+k = borrow of delta k+33 (k < 16); bw1 likewise for 16..31.
+      if (k < 16)
+        bw0 = b3<kOrAnd & 0xFF>(bw0 >> 1, bo, 0x80008000u);
+      else
+        bw1 = b3<kOrAnd & 0xFF>(bw1 >> 1, bo, 0x80008000u);
+    }
+    os = os | d[i] | d[i + 1];
+    an = b3<kAnd3 & 0xFF>(an, g[0], g[1]);
+    // The high half of the last register holds no delta: all ones for the AND.
+    dan = b3<kAnd3 & 0xFF>(dan, gd[0], i + 1 == 31 ? (gd[1] | 0xFFFF0000u) : gd[1]);
+  }
+  aj |= gp & (g0 >> 16);    // symbols 31 and 32 (low half of gp, high half of g0)
+  daj |= dp & (dg0 >> 16);  // deltas 32 and 33
+
+  uint32_t ge1, ge2, bge3;
+  // BX: 16 planes of 64 bits.
+  fold4_16(c0, c1, ge1, ge2, bge3);
+  const uint32_t nz = ge1, single = ge1 & ~ge2;
+  const uint32_t pair = (lo16(aj) | hi16(aj)) & ~bge3;
+  const uint32_t ones = lo16(an) & hi16(an);
+  const uint32_t pz = ~(lo16(os) | hi16(os)) & 0xFFFFu;
+  o.sz[kBX] = plane_code_bits(nz, ones, pz, pair, single, 16, 64, 4, o.verb[1], o.zero[1]);
+
+  // DBX: base, then 17 planes of 63 bits; plane 16 is the borrow plane.
+  uint32_t dge1, dge2, dge3;
+  fold4_16(e0, e1, dge1, dge2, dge3);
+  uint64_t dnz = dge1, dsingle = dge1 & ~dge2;
+  uint64_t dpair = (lo16(daj) | hi16(daj)) & ~dge3;
+  uint64_t dones = lo16(dan) & hi16(dan);
+  const uint64_t dpz = ~(lo16(dos) | hi16(dos)) & 0xFFFFu;
+  const uint32_t bl = __builtin_amdgcn_perm(bw1, bw0, 0x05040100u);  // plane bits 0..31
+  const uint32_t bh = __builtin_amdgcn_perm(bw1, bw0, 0x07060302u);  // plane bits 32..63
+  const int bc = popc32(bl) + popc32(bh);
+  const bool badj = ((bl & (bl >> 1)) | (bh & (bh >> 1)) | ((bl >> 31) & bh & 1u)) != 0;
+  dnz |= (uint64_t)(bc != 0) << 16;
+  dones |= (uint64_t)(bc == 63) << 16;
+  dsingle |= (uint64_t)(bc == 1) << 16;
+  dpair |= (uint64_t)(bc == 2 && badj) << 16;
+  o.sz[kDBX] = 16 + plane_code_bits(dnz, dones, dpz, dpair, dsingle, 17, 63, 4, o.verb[0], o.zero[0]);
+  o.bm_lo = bl;
+  o.bm_hi = bh;
+
+  // ZBX: the zero, count and pre-XOR masks are those of BX (zero symbols add
+  // nothing); "all ones" and adjacency run over the non-zero symbols only,
+  // in order: symbols 0..31 (low halves), then 32..63 (high halves).
+  if (zbx) {
+    uint32_t zan = ~0u, zaj = 0, zp = 0, zf = 0, seen = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const uint32_t s = d[i];
+      const uint32_t g = s ^ pk_shr1(s);
+      const uint32_t zfill = pk_sub_u16(pk_min_u16(s, 0x00010001u), 0x00010001u);  // 0xFFFF if zero
+      zan &= g | zfill;
+      zaj |= zp & g;                      // last non-zero symbol before this one
+      zp = (zp & zfill) | g;
+      zf |= g & ~seen;                    // first non-zero symbol of each half
+      seen |= ~zfill;
+    }
+    zaj |= zp & (zf >> 16);  // last non-zero of 0..31 and first of 32..63
+    const uint32_t zpair = (lo16(zaj) | hi16(zaj)) & ~bge3;
+    o.sz[kZBX] = 64 + plane_code_bits(nz, lo16(zan) & hi16(zan), pz, zpair, single, 16, n, 4, o.verb[2],
+                                      o.zero[2]);
+  } else {
+    o.sz[kZBX] = 64 + o.sz[kBX];
+    o.verb[2] = o.verb[1];
+    o.zero[2] = o.zero[1];
+  }
+
+  o.sz[kZVC] = 64 + 16 * n;
+  o.sz[kRAW] = 1024;
+}
+
+// ---------------------------------------------------------------------------
+// Candidate sizes, w = 32. d[i] is symbol i; delta k+1 = d[k+1] - d[k] is
+// plane bit k.
+// ---------------------------------------------------------------------------
+PZ_DEV void candidate_sizes32(const uint32_t (&d)[32], int n, bool zbx, Stats &o) {
+  uint32_t os = 0, an = ~0u, c0 = 0, c1 = 0, aj = 0, gp = 0;
+  uint32_t dos = 0, dan = ~0u, e0 = 0, e1 = 0, daj = 0, dp = 0, bacc = 0;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
     const uint32_t s = d[i];
     const uint32_t g = s ^ (s >> 1);
-    bx_or_s |= s;
-    t3 |= t2 & g;
-    t2 |= bx_or & g;
-    bx_or |= g;
-    bx_and &= g;
-    adj |= g & gprev;
-    gprev = g;
-    if (i > 0) {
-      const uint32_t p = d[i - 1];
-      const uint32_t ld = s - p;
-      const uint32_t bo = (~s & p) | (~(s ^ p) & ld);  // borrow in bit 31
+    os |= s;
+    an &= g;
+    count4(c0, c1, g);
+    if (i > 0) aj |= g & gp;
+    gp = g;
+    if (i < 31) {
+      const uint32_t cur = d[i + 1];
+      const uint32_t ld = cur - s;
+      const uint32_t bo = (~cur & s) | (~(cur ^ s) & ld);  // borrow in bit 31
       const uint32_t gd = ld ^ ((ld >> 1) | (bo & 0x80000000u));
-      db_or_s |= ld;
-      u3 |= u2 & gd;
-      u2 |= db_or & gd;
-      db_or |= gd;
-      db_and &= gd;
-      dadj |= gd & dgprev;
-      dgprev = gd;
-      bacc = (bacc >> 1) | (bo & 0x80000000u);  // ends with delta i's borrow at bit i
+      dos |= ld;
+      dan &= gd;
+      count4(e0, e1, gd);
+      if (i > 0) daj |= gd & dp;
+      dp = gd;
+      bacc = (bacc >> 1) | (bo & 0x80000000u);  // ends with delta k+1's borrow at bit k+1
     }
   }
-  const uint32_t bm = bacc >> 1;  // plane element k = borrow of delta k+1
-  const uint32_t single = bx_or & ~t2;
-  const uint32_t exactly2 = t2 & ~t3;
-  out.sz[kBX] = plane_code_bits(bx_or, bx_and, ~bx_or_s, exactly2 & adj, single, 32, 32, 5);
+  const uint32_t bm = bacc >> 1;  // plane bit k = borrow of delta k+1
+  const uint32_t ge1 = c0 | c1, ge3 = c0 & c1;
+  const uint32_t single = ge1 & ~c1;
+  o.sz[kBX] = plane_code_bits(ge1, an, ~os, aj & ~ge3, single, 32, 32, 5, o.verb[1], o.zero[1]);
 
-  uint32_t zand = bx_and, zadj = adj;
   if (zbx) {
-    launder_regs(d);
     uint32_t za = ~0u, zj = 0, zprev = 0;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
@@ -258,29 +329,30 @@ PZ_DEV void candidate_sizes32(uint32_t (&d)[32], int n, bool zbx, Sizes &out) {
       zj |= zprev & g;
       zprev = s != 0 ? g : zprev;
     }
-    zand = za;
-    zadj = zj;
+    o.sz[kZBX] = 32 + plane_code_bits(ge1, za, ~os, zj & ~ge3, single, 32, n, 5, o.verb[2], o.zero[2]);
+  } else {
+    o.sz[kZBX] = 32 + o.sz[kBX];
+    o.verb[2] = o.verb[1];
+    o.zero[2] = o.zero[1];
   }
-  out.sz[kZBX] = 32 + plane_code_bits(bx_or, zand, ~bx_or_s, exactly2 & zadj, single, 32, n, 5);
 
+  const uint32_t dge1 = e0 | e1, dge3 = e0 & e1;
   const int bc = popc32(bm);
-  const uint64_t dnz = (uint64_t)db_or | ((uint64_t)(bm != 0) << 32);
-  const uint64_t dones = (uint64_t)db_and | ((uint64_t)(bm == 0x7FFFFFFFu) << 32);
-  const uint64_t dpz = (uint64_t)(~db_or_s);
-  const uint64_t dsingle = (uint64_t)(db_or & ~u2) | ((uint64_t)(bc == 1) << 32);
-  const uint64_t dpair =
-      (uint64_t)(u2 & ~u3 & dadj) | ((uint64_t)(bc == 2 && (bm & (bm >> 1)) != 0) << 32);
-  out.sz[kDBX] = 32 + plane_code_bits(dnz, dones, dpz, dpair, dsingle, 33, 31, 5);
+  const uint64_t dnz = (uint64_t)dge1 | ((uint64_t)(bm != 0) << 32);
+  const uint64_t dones = (uint64_t)dan | ((uint64_t)(bm == 0x7FFFFFFFu) << 32);
+  const uint64_t dpz = (uint64_t)(~dos);
+  const uint64_t dsingle = (uint64_t)(dge1 & ~e1) | ((uint64_t)(bc == 1) << 32);
+  const uint64_t dpair = (uint64_t)(daj & ~dge3) | ((uint64_t)(bc == 2 && (bm & (bm >> 1)) != 0) << 32);
+  o.sz[kDBX] = 32 + plane_code_bits(dnz, dones, dpz, dpair, dsingle, 33, 31, 5, o.verb[0], o.zero[0]);
+  o.bm_lo = bm;
+  o.bm_hi = 0;
 
-  out.sz[kZVC] = 32 + 32 * n;
-  out.sz[kRAW] = 1024;
-  out.n = n;
-  out.b0 = bm;
-  out.b1 = 0;
+  o.sz[kZVC] = 32 + 32 * n;
+  o.sz[kRAW] = 1024;
 }
 
 template <int W>
-PZ_DEV void candidate_sizes(uint32_t (&d)[32], int n, bool zbx, Sizes &out) {
+PZ_DEV void candidate_sizes(const uint32_t (&d)[32], int n, bool zbx, Stats &out) {
   if constexpr (W == 16)
     candidate_sizes16(d, n, zbx, out);
   else
@@ -290,7 +362,7 @@ PZ_DEV void candidate_sizes(uint32_t (&d)[32], int n, bool zbx, Sizes &out) {
 // Smallest allowed candidate (mask bit t = tag t); equal sizes go to the
 // lowest tag. Returns the tag and its size (no indexing of the size array by
 // a lane-varying tag).
-PZ_DEV int select_tag(const Sizes &s, int &best_size, uint32_t mask) {
+PZ_DEV int select_tag(const Stats &s, int &best_size, uint32_t mask) {
   int best = 0, bsz = 0x7FFFFFFF;
 #pragma unroll
   for (int t = 0; t < 5; ++t) {
@@ -301,6 +373,16 @@ PZ_DEV int select_tag(const Sizes &s, int &best_size, uint32_t mask) {
   }
   best_size = bsz;
   return best;
+}
+
+// AND of a value over the 64 lanes of the wave (every lane must be active).
+PZ_DEV uint32_t wave_and32(uint32_t v) {
+  v &= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);   // quad: lanes 1,0,3,2
+  v &= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);   // quad: lanes 2,3,0,1
+  v &= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false);  // half-row mirror
+  v &= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false);  // row mirror
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 0) & (uint32_t)__builtin_amdgcn_readlane((int)v, 16) &
+         (uint32_t)__builtin_amdgcn_readlane((int)v, 32) & (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
 }
 
 // ---------------------------------------------------------------------------
@@ -316,7 +398,8 @@ __global__ __launch_bounds__(kGroupThreads, 4) void block_sizes_kernel(
   uint32_t d[32];
   load_block(src, raw_bytes, block * kBlockBytes, d);
   const int n = (int)count_nonzero<W>(d);
-  Sizes s;
+  if constexpr (W == 16) to_split16(d);
+  Stats s;
   candidate_sizes<W>(d, n, __ballot(n > 0 && n < 1024 / W) != 0, s);
   int best_size;
   const int tag = select_tag(s, best_size, 0x1Fu);
@@ -330,108 +413,120 @@ __global__ __launch_bounds__(kGroupThreads, 4) void block_sizes_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Emission helpers: fields are OR-ed into the zeroed LDS chunk buffer at an
-// explicit bit offset (stream bit t = bit t%32 of dword t/32).
+// Emission: fields are OR-ed into the zeroed LDS chunk buffer at an explicit
+// bit offset (stream bit t = bit t%32 of dword t/32). A write may touch a
+// dword past its last bit with a zero value.
 // ---------------------------------------------------------------------------
-struct BitSink {
-  uint32_t *buf;
-  uint32_t off;  // next bit
-
-  // n <= 32 bits of v (v < 2^n).
-  PZ_DEV void put(uint32_t v, uint32_t n) {
-    const uint32_t q = off >> 5, sh = off & 31u;
-    atomicOr(&buf[q], v << sh);
-    atomicOr(&buf[q + 1], (v >> 1) >> (31u - sh));  // v >> (32 - sh); 0 when sh == 0
-    off += n;
-  }
-  // n <= 64 bits of v (v < 2^n).
-  PZ_DEV void put64(uint64_t v, uint32_t n) {
-    const uint32_t q = off >> 5, sh = off & 31u;
-    const uint64_t lowpart = v << sh;
-    atomicOr(&buf[q], (uint32_t)lowpart);
-    atomicOr(&buf[q + 1], (uint32_t)(lowpart >> 32));
-    atomicOr(&buf[q + 2], ((uint32_t)(v >> 32) >> 1) >> (31u - sh));
-    off += n;
-  }
-};
-
-// Morton spread: bit i of the low 16 bits goes to bit 2i.
-PZ_DEV uint32_t spread16(uint32_t v) {
-  v &= 0xFFFFu;
-  v = (v | (v << 8)) & 0x00FF00FFu;
-  v = (v | (v << 4)) & 0x0F0F0F0Fu;
-  v = (v | (v << 2)) & 0x33333333u;
-  v = (v | (v << 1)) & 0x55555555u;
-  return v;
+// v (below 2^32) at bit off: dwords off/32 and off/32 + 1.
+PZ_DEV void or32(uint32_t *buf, uint32_t off, uint32_t v) {
+  uint32_t *p = buf + (off >> 5);
+  const uint32_t sh = off & 31u;
+  atomicOr(p, v << sh);
+  atomicOr(p + 1, (v >> 1) >> (31u - sh));  // v >> (32 - sh); 0 when sh == 0
 }
 
-// One plane's code: the pending zero run (if any) and this plane's code in one
-// field, then the verbatim payload. x is the XORed plane, p the plane itself.
-template <typename PT>
-PZ_DEV void emit_plane(BitSink &bs, PT x, PT p, PT ones, uint32_t L, uint32_t pw, uint32_t R,
-                       uint32_t &run) {
-  if (x == 0) {
-    ++run;
-    return;
-  }
-  uint32_t rcode = 0, rlen = 0;
-  if (run) {
-    rlen = run == 1 ? 3u : 2u + R;
-    rcode = run == 1 ? 4u : (2u | ((run - 2u) << 2));
-  }
-  run = 0;
-  int cnt;
-  uint32_t low;
+// 64 bits (hi:lo) at bit off: dwords off/32 .. off/32 + 2.
+PZ_DEV void or64(uint32_t *buf, uint32_t off, uint32_t lo, uint32_t hi) {
+  uint32_t *p = buf + (off >> 5);
+  const uint32_t sh = off & 31u;
+  const uint64_t v = (((uint64_t)hi << 32) | lo) << sh;
+  atomicOr(p, (uint32_t)v);
+  atomicOr(p + 1, (uint32_t)(v >> 32));
+  atomicOr(p + 2, (hi >> 1) >> (31u - sh));
+}
+
+// A verbatim plane code: the bit 1, then the plane (hi:lo) at bit off + 1.
+PZ_DEV void or_verbatim(uint32_t *buf, uint32_t off, uint32_t lo, uint32_t hi) {
+  uint32_t *p = buf + (off >> 5);
+  const uint32_t sh = off & 31u, nsh = 31u - sh;
+  atomicOr(p, ((lo << 1) | 1u) << sh);
+  atomicOr(p + 1, funnel(hi, lo, nsh));  // bits 32..63 of (plane << (sh + 1))
+  atomicOr(p + 2, hi >> nsh);            // bits 64..95
+}
+PZ_DEV void or_verbatim(uint32_t *buf, uint32_t off, uint32_t x) {
+  uint32_t *p = buf + (off >> 5);
+  const uint32_t sh = off & 31u;
+  atomicOr(p, ((x << 1) | 1u) << sh);
+  atomicOr(p + 1, x >> (31u - sh));
+}
+
+// Code of a run of `run` zero planes (0: none) and its length: '001' for one
+// plane, '01' and run - 2 in R bits for more. Written as arithmetic on
+// min(run, 2): as selects on run, the compiler turned it into branches.
+template <uint32_t R>
+PZ_DEV void run_code(uint32_t run, uint32_t &code, uint32_t &len) {
+  const uint32_t m = run < 2u ? run : 2u;  // 0, 1, 2
+  const uint32_t two = m >> 1;            // run >= 2
+  len = 3u * m + (R - 4u) * two;          // 0, 3, 2 + R
+  code = (run << 2) - 6u * two;           // 0, 4, 2 | (run - 2) << 2
+}
+
+// One plane, any class, without branches: x is the XORed plane, pz whether
+// the plane before the XOR is zero, ones the all-ones value of the plane
+// width L, cs = 5 + PW the length of a pair or single code. A zero plane
+// extends the pending run; a non-zero one writes the pending run's code and
+// its own code, and, if verbatim, the plane itself.
+template <typename PT, uint32_t R>
+PZ_DEV void emit_plane(uint32_t *buf, uint32_t &off, uint32_t &run, PT x, bool pz, PT ones, uint32_t L,
+                       uint32_t cs) {
+  uint32_t xlo, xhi;
   if constexpr (sizeof(PT) == 8) {
-    cnt = popc64((uint64_t)x);
-    low = (uint32_t)__builtin_ctzll((uint64_t)x);
+    xlo = (uint32_t)x;
+    xhi = (uint32_t)((uint64_t)x >> 32);
   } else {
-    cnt = popc32((uint32_t)x);
-    low = (uint32_t)__builtin_ctz((uint32_t)x);
+    xlo = (uint32_t)x;
+    xhi = 0;
   }
+  const bool nz = (xlo | xhi) != 0;
+  const uint32_t cnt = (uint32_t)popc32(xlo) + (uint32_t)popc32(xhi);
+  // Lowest set bit (a zero half gives ffbl = ~0, which min ignores).
+  const uint32_t flo = (uint32_t)__ffs(xlo) - 1u, fhi = (uint32_t)__ffs(xhi) - 1u;
+  const uint32_t low = sizeof(PT) == 8 ? min(flo, 32u + fhi) : flo;
+  const uint32_t tl = (uint32_t)(x >> (low & (8 * sizeof(PT) - 1)));
+  // One 1, or two adjacent 1s: cnt minus "bit low+1 set" is then 1.
+  const bool shortc = cnt - ((tl >> 1) & 1u) == 1u;
   const bool is_ones = x == ones;
-  const bool is_pz = p == 0;
-  const bool is_pair = cnt == 2 && (x >> low) == (PT)3;
-  const bool is_single = cnt == 1;
-  uint32_t code, clen;
-  if (is_ones || is_pz) {
-    code = is_ones ? 0u : 16u;
-    clen = 5;
-  } else if (is_pair || is_single) {
-    code = (is_pair ? 8u : 24u) | (low << 5);
-    clen = 5 + pw;
-  } else {
-    code = 1u;
-    clen = 1;
-  }
-  bs.put(rcode | (code << rlen), rlen + clen);
-  if (!(is_ones || is_pz || is_pair || is_single)) {
+  // Code and length by the first matching class (all ones, pre-XOR zero,
+  // pair or single, verbatim).
+  uint32_t code = shortc ? ((24u - ((tl & 2u) << 3)) | (low << 5)) : 1u;
+  uint32_t clen = shortc ? cs : 1u;
+  code = pz ? 16u : code;
+  clen = pz ? 5u : clen;
+  code = is_ones ? 0u : code;
+  clen = is_ones ? 5u : clen;
+  uint32_t rcode, rlen;
+  run_code<R>(run, rcode, rlen);
+  const uint32_t item = nz ? rcode | (code << rlen) : 0u;
+  or32(buf, off, item);
+  off += nz ? rlen + clen : 0u;
+  run = nz ? 0u : run + 1u;
+  const bool verb = nz && !(shortc || pz || is_ones);
+  if (verb) {
     if constexpr (sizeof(PT) == 8)
-      bs.put64((uint64_t)x, L);
+      or64(buf, off, xlo, xhi);
     else
-      bs.put((uint32_t)x, L);
+      or32(buf, off, xlo);
+    off += L;
   }
-}
-
-PZ_DEV void emit_run(BitSink &bs, uint32_t run, uint32_t R) {
-  if (run) bs.put(run == 1 ? 4u : (2u | ((run - 2u) << 2)), run == 1 ? 3u : 2u + R);
 }
 
 // ---------------------------------------------------------------------------
 // Single-pass compression, one workgroup per tile of 16 chunks (512 blocks,
-// eight waves: two such workgroups fill a CU's LDS; tiles of 8 chunks, with
-// twice the workgroups and tile tickets, were 4% slower and tiles of 32
-// slower still).
+// eight waves: two such workgroups fill a CU's LDS).
 //
 // Softmax-like activations hold many all-zero blocks, and a wave runs the
 // candidate statistics and the emission for all its lanes at the cost of
 // the slowest. So the group first loads its 512 blocks one per thread,
-// gives every all-zero block its fixed code (below), and packs the non-zero
-// blocks through LDS into the lowest slots: only ceil(nnz / 64) waves then
-// run the statistics and the emission. Chunk offsets come from one decoupled
-// look-back per group.
+// gives every all-zero block its fixed code (below), and, when some block is
+// all zero, packs the non-zero blocks through LDS into the lowest slots: only
+// ceil(nnz / 64) waves then run the statistics and the emission. Chunk
+// offsets come from one decoupled look-back per group.
 // ---------------------------------------------------------------------------
 constexpr int kCWaves = 8;  // waves per compress / size workgroup
+constexpr int kCGroupsPerCU = 16 / kCWaves;  // workgroups a CU holds (LDS and VGPRs both allow)
+// The second launch bound is the minimum number of waves per SIMD: four caps
+// a lane at 128 VGPRs, so that a CU holds the 16 waves above.
+constexpr int kCWavesPerSimd = 4;
 constexpr int kCThreads = kWave * kCWaves;
 constexpr int kGroupChunks = kCThreads / kBlocksPerChunk;
 constexpr int kStageDwords = kCThreads * kLaneStride;
@@ -446,33 +541,71 @@ template <int W>
 PZ_DEV void emit_zero_block(uint32_t *buf, uint32_t off, const Mode &m) {
   constexpr uint32_t N = 1024 / W, R = W == 16 ? 4 : 5;
   const uint32_t c = m.zc;
-  BitSink z;
-  z.buf = buf;
-  z.off = off;
-  if (m.tagged) z.put(c, 3);
-  z.off += c == 0 ? N : (c == 1 ? (uint32_t)W : (c == 3 ? N : (c == 4 ? 1024u : 0u)));
+  uint32_t v = 0, len = 0;
+  if (m.tagged) {
+    v = c;
+    len = 3;
+  }
+  len += c == 0 ? N : (c == 1 ? (uint32_t)W : (c == 3 ? N : (c == 4 ? 1024u : 0u)));
   const uint32_t planes = c == 1 ? W + 1 : ((c == 2 || c == 3) ? (uint32_t)W : 0u);
-  if (planes) z.put(2u | ((planes - 2u) << 2), 2 + R);
+  if (m.tagged) or32(buf, off, v);
+  if (planes) or32(buf, off + len, 2u | ((planes - 2u) << 2));
+}
+
+// The (ZVC / ZBX) mask of a block: bit k = symbol k non-zero.
+template <int W>
+PZ_DEV void nonzero_mask(const uint32_t (&d)[32], uint32_t &mlo, uint32_t &mhi) {
+  mlo = mhi = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    if constexpr (W == 16) {
+      const uint32_t z = pk_min_u16(d[i], 0x00010001u);
+      mlo |= (z & 1u) << i;
+      mhi |= (z >> 16) << i;
+    } else {
+      mlo |= (uint32_t)(d[i] != 0) << i;
+    }
+  }
+}
+
+// The tensor of a launch's tile (the last one whose first tile is at or
+// before it: a tensor without chunks has no tiles).
+PZ_DEV uint32_t tensor_of(const CBatch &batch, uint32_t gtile) {
+  uint32_t k = 0;
+  if (batch.n > 1) {  // a single tensor's fields load at once
+#pragma unroll
+    for (uint32_t i = 1; i < (uint32_t)kMaxBatch; ++i) k += i < batch.n && gtile >= batch.t[i].tile_begin ? 1u : 0u;
+  }
+  return k;
+}
+
+// Block t of the launch's tile gtile, into registers.
+PZ_DEV void load_tile_block(const CBatch &batch, uint32_t gtile, uint32_t t, uint32_t (&d)[32]) {
+  const uint32_t k = tensor_of(batch, gtile);
+  const uint64_t block = (uint64_t)(gtile - batch.t[k].tile_begin) * kCThreads + t;
+  load_block(batch.t[k].src, batch.t[k].raw_bytes, block * kBlockBytes, d);
 }
 
 template <int W>
-__global__ __launch_bounds__(kCThreads, 2) void compress_kernel(const CBatch batch, uint64_t *lb_words,
+__global__ __launch_bounds__(kCThreads, kCWavesPerSimd) void compress_kernel(const CBatch batch, uint64_t *lb_words,
                                                                  uint32_t *tile_counter, uint32_t counter_base,
                                                                  uint32_t epoch, Mode mode) {
   constexpr int N = 1024 / W;
   constexpr uint32_t R = W == 16 ? 4 : 5;
+  constexpr int KT = W;  // index of DBX's top plane (the borrow plane) in the plane masks
   using PT = typename std::conditional<W == 16, uint64_t, uint32_t>::type;
-  // Staging slots / ZBX compaction regions (stride kLaneStride), later the
-  // eight chunk buffers.
+  // Staging slots / compaction regions (stride kLaneStride), later the
+  // sixteen chunk buffers.
   __shared__ __attribute__((aligned(16))) uint32_t lds[kGroupLdsDwords];
-  __shared__ uint16_t blk_bits[kCThreads];  // per block: its cost, then its bit offset
+  __shared__ uint16_t blk_bits[kCThreads];    // per block: its cost, then its bit offset
   __shared__ uint16_t slot_block[kCThreads];  // compacted slot -> block of the group
-  __shared__ uint8_t slot_n[kCThreads];      // compacted slot -> its non-zero symbols
+  __shared__ uint8_t slot_n[kCThreads];       // compacted slot -> its non-zero symbols
   __shared__ uint32_t wave_full[kCWaves];
   __shared__ uint32_t wave_part[kCWaves];
   __shared__ uint32_t chunk_len[kGroupChunks];
   __shared__ uint64_t chunk_pay[kGroupChunks];
   __shared__ uint32_t group_tile;
+  __shared__ uint32_t done_waves;  // waves done with the emission
 
   const uint32_t t = threadIdx.x, lane = lane_id();
   const uint32_t wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform: a scalar
@@ -481,25 +614,19 @@ __global__ __launch_bounds__(kCThreads, 2) void compress_kernel(const CBatch bat
   // The launch's tile -> the tensor it belongs to and the tile within it.
   const uint32_t gtile = __builtin_amdgcn_readfirstlane(group_tile);
   if (gtile >= batch.total_tiles) return;
-  uint32_t k = 0;
-  if (batch.n > 1) {  // a single tensor's fields load at once
-#pragma unroll
-    for (uint32_t i = 1; i < (uint32_t)kMaxBatch; ++i) k += i < batch.n && gtile >= batch.t[i].tile_begin ? 1u : 0u;
-  }
+  const uint32_t k = tensor_of(batch, gtile);
   const uint8_t *__restrict__ src = batch.t[k].src;
   uint8_t *__restrict__ dst = batch.t[k].dst;
   const uint64_t raw_bytes = batch.t[k].raw_bytes, nchunks = batch.t[k].nchunks;
   const uint32_t ntiles = batch.t[k].ntiles;
   const uint32_t tile = gtile - batch.t[k].tile_begin;
   uint64_t *status = lb_words + batch.t[k].tile_begin;
+  uint32_t d[32];
+  load_tile_block(batch, gtile, t, d);
 
-  // --- 1. Load block t; count its non-zero symbols. ---
-  // (Block and chunk indices are recomputed where needed rather than kept
-  // live through the statistics, which use every register.)
+  // --- 1. Count block t's non-zero symbols (loaded before). ---
   const uint64_t block = (uint64_t)tile * kCThreads + t;
   const bool valid = block * kBlockBytes < raw_bytes;
-  uint32_t d[32];
-  load_block(src, raw_bytes, block * kBlockBytes, d);
   uint32_t sn = count_nonzero<W>(d);  // blocks past the end load as zeros
   const bool nonzero = sn != 0;
   const bool partial = nonzero && sn < (uint32_t)N;
@@ -511,135 +638,162 @@ __global__ __launch_bounds__(kCThreads, 2) void compress_kernel(const CBatch bat
   if (!nonzero) blk_bits[t] = (uint16_t)(valid ? 3u * mode.tagged + zero_block_size(W, mode.zc) : 0u);
   __syncthreads();
 
-  // --- 2. Slots: the non-zero blocks are packed through LDS into slots
-  // 0..nnz-1, those without a zero symbol first, so that the ZBX statistics
-  // (needed only when 0 < n < N) run on as few waves as possible. ---
+  // --- 2. Slots. When some block is all zero, or full and partial blocks
+  // (those with a zero symbol) are mixed, the non-zero blocks are packed
+  // through LDS into slots 0..nnz-1, full blocks first, so that the
+  // statistics (and ZBX's, needed only when 0 < n < N) run on as few waves
+  // as possible. Otherwise every thread keeps its own block. ---
   uint32_t nfull = 0, npart = 0, ffirst = 0, pfirst = 0;
 #pragma unroll
-  for (int k = 0; k < kCWaves; ++k) {
-    const uint32_t f = wave_full[k], q = wave_part[k];
-    ffirst += (uint32_t)k < wave ? f : 0u;
-    pfirst += (uint32_t)k < wave ? q : 0u;
+  for (int q = 0; q < kCWaves; ++q) {
+    const uint32_t f = wave_full[q], p = wave_part[q];
+    ffirst += (uint32_t)q < wave ? f : 0u;
+    pfirst += (uint32_t)q < wave ? p : 0u;
     nfull += f;
-    npart += q;
+    npart += p;
   }
   const uint32_t nnz = nfull + npart;
-  if (nonzero) {
-    const uint32_t idx = partial ? nfull + pfirst + lanes_below(mpart) : ffirst + lanes_below(mfull);
-    uint32_t *slot = lds + idx * kLaneStride;
+  const bool staged = !(nnz == (uint32_t)kCThreads && (npart == 0 || nfull == 0));
+  if (staged) {
+    if (nonzero) {
+      const uint32_t idx = partial ? nfull + pfirst + lanes_below(mpart) : ffirst + lanes_below(mfull);
+      uint32_t *slotp = lds + idx * kLaneStride;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) slot[i] = d[i];
-    slot_block[idx] = (uint16_t)t;
-    slot_n[idx] = (uint8_t)sn;
+      for (int i = 0; i < 32; ++i) slotp[i] = d[i];
+      slot_block[idx] = (uint16_t)t;
+      slot_n[idx] = (uint8_t)sn;
+    }
+    __syncthreads();
   }
-  __syncthreads();
 
   // Waves take the slots in an order rotated per tile, so that the busy
   // waves of successive groups fall on different SIMDs.
-  const uint32_t slot = (t + kCThreads - 64u * (tile & (kCWaves - 1u))) & (kCThreads - 1);
+  const uint32_t slot = staged ? (t + kCThreads - 64u * (tile & (kCWaves - 1u))) & (kCThreads - 1) : t;
   const bool active = slot < nnz;
   const bool wave_active = __ballot(active) != 0;
+  const uint32_t sblock = staged ? (active ? (uint32_t)slot_block[slot] : 0u) : t;  // the slot's block
 
-  // --- 3. Sizes, selection and the transform input of the packed blocks. ---
-  Sizes s;
-  s.n = 0;
-  s.b0 = s.b1 = 0;
+  // --- 3. Sizes, selection and the transform input of the slot's block. ---
   int tag = kRAW;
-  uint64_t nzmask = 0;
-  uint32_t base = 0;
+  uint32_t bm_lo = 0, bm_hi = 0, mlo = 0, mhi = 0, base = 0;
+  uint64_t fv = ~0ull, zr = ~0ull;  // this lane's fast-verbatim and zero plane masks
   uint32_t e[32];
   if (wave_active) {
     uint32_t *region = lds + slot * kLaneStride;
-    sn = active ? (uint32_t)slot_n[slot] : 0u;
-    if (active) {
+    if (staged) {
+      sn = active ? (uint32_t)slot_n[slot] : 0u;
+      if (active) {
 #pragma unroll
-      for (int i = 0; i < 32; ++i) d[i] = region[i];
+        for (int i = 0; i < 32; ++i) d[i] = region[i];
+      }
     }
+    if constexpr (W == 16) to_split16(d);
     const bool zbx = __ballot(active && sn < (uint32_t)N) != 0;  // active blocks are non-zero
+    Stats s;
     candidate_sizes<W>(d, (int)sn, zbx, s);
-    s.n = (int)sn;
-    launder_regs(d);
     int best_size;
     tag = select_tag(s, best_size, mode.mask);
-    if (active) blk_bits[slot_block[slot]] = (uint16_t)(3u * mode.tagged + best_size);
+    if (active) blk_bits[sblock] = (uint16_t)(3u * mode.tagged + best_size);
+    if (!active) tag = kRAW;  // inactive lanes code nothing
+    bm_lo = s.bm_lo;
+    bm_hi = s.bm_hi;
+
+    // Fast-path masks: plane j (bit j; bit KT = DBX's top plane) is verbatim
+    // with no zero run pending above it, or zero.
+    if (active && (tag == kDBX || tag == kBX || tag == kZBX)) {
+      const int ci = tag == kDBX ? 0 : (tag == kBX ? 1 : 2);
+      const uint64_t vb = ci == 0 ? s.verb[0] : (ci == 1 ? s.verb[1] : s.verb[2]);
+      const uint64_t zo = ci == 0 ? s.zero[0] : (ci == 1 ? s.zero[1] : s.zero[2]);
+      fv = vb & ~(zo >> 1);
+      zr = zo;
+      if (tag != kDBX) {
+        fv |= 1ull << KT;
+        zr |= 1ull << KT;
+      }
+    }
 
     const bool want_zvc = active && tag == kZVC;
     const bool want_dbx = active && tag == kDBX;
     const bool want_zbx = active && tag == kZBX;
-    // Non-zero mask (ZVC and ZBX prefix), bit i = symbol i non-zero.
-    if (__ballot(want_zvc || want_zbx)) {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        if constexpr (W == 16) {
-          nzmask |= (uint64_t)((d[i] & 0xFFFFu) != 0) << (2 * i);
-          nzmask |= (uint64_t)((d[i] >> 16) != 0) << (2 * i + 1);
-        } else {
-          nzmask |= (uint64_t)(d[i] != 0) << i;
-        }
-      }
-    }
-    base = W == 16 ? (d[0] & 0xFFFFu) : d[0];
-
-    // ZBX and ZVC: move the non-zero symbols to the front of this slot's
-    // region (the slot was read above; no other thread touches it).
     const bool want_cmp = want_zbx || want_zvc;
+    if (__ballot(want_cmp)) {
+      if (want_cmp) nonzero_mask<W>(d, mlo, mhi);
+    }
+    base = W == 16 ? lo16(d[0]) : d[0];
+
+    // ZBX and ZVC: the non-zero symbols, in order, at the front of this
+    // slot's region (the slot was read above; no other thread touches it).
     const bool any_cmp = __ballot(want_cmp) != 0;
     if (any_cmp) {
       if (want_cmp) {
 #pragma unroll
-        for (int i = 0; i < 32; ++i) region[i] = 0;
+        for (int i = 0; i < 33; ++i) region[i] = 0;
       }
       wave_lds_fence();
       if (want_cmp) {
         // Every symbol is written at the current rank, which advances only
         // past non-zero ones: a zero symbol writes 0 where the next non-zero
         // symbol (or nothing) goes, so there are no branches.
-        uint32_t k = 0;
+        uint32_t r = 0;
         if constexpr (W == 16) {
           uint16_t *r16 = reinterpret_cast<uint16_t *>(region);
 #pragma unroll
-          for (int i = 0; i < 32; ++i) {
-            const uint32_t a = d[i] & 0xFFFFu, b = d[i] >> 16;
-            r16[k] = (uint16_t)a;
-            k += a ? 1u : 0u;
-            r16[k] = (uint16_t)b;
-            k += b ? 1u : 0u;
+          for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int i = 0; i < 32; ++i) {
+              const uint32_t a = h ? hi16(d[i]) : lo16(d[i]);
+              r16[r] = (uint16_t)a;
+              r += a ? 1u : 0u;
+            }
           }
         } else {
 #pragma unroll
           for (int i = 0; i < 32; ++i) {
-            region[k] = d[i];
-            k += d[i] ? 1u : 0u;
+            region[r] = d[i];
+            r += d[i] ? 1u : 0u;
           }
         }
       }
       wave_lds_fence();
     }
 
-    // Transform input: the symbols, the deltas (DBX, arranged so that plane
-    // element k is delta k+1) or the compacted symbols (ZBX).
-#pragma unroll
-    for (int i = 0; i < 32; ++i) e[i] = d[i];
+    // Transform input, in place: the symbols (BX), the deltas (DBX), the
+    // compacted symbols (ZBX: split layout for w = 16; ZVC: in order).
     if (__ballot(want_dbx)) {
+      const uint32_t s32 = hi16(d[0]);
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
         uint32_t v;
-        if constexpr (W == 16) {
-          // dword i = (delta 2i+1, delta 2i+2); the last slot is empty.
-          const uint32_t cur = funnel(i < 31 ? d[i + 1] : 0u, d[i], 16);  // (s 2i+1, s 2i+2)
-          v = pk_sub_u16(cur, d[i]);
-          if (i == 31) v &= 0xFFFFu;
-        } else {
+        if constexpr (W == 16)
+          v = i < 31 ? pk_sub_u16(d[i + 1], d[i]) : lo16(s32 - lo16(d[31]));
+        else
           v = i < 31 ? d[i + 1] - d[i] : 0u;
-        }
-        e[i] = want_dbx ? v : e[i];
+        d[i] = want_dbx ? v : d[i];
       }
     }
     if (any_cmp) {
 #pragma unroll
-      for (int i = 0; i < 32; ++i) e[i] = want_cmp ? region[i] : e[i];
+      for (int i = 0; i < 32; ++i) e[i] = region[i];
+      if constexpr (W == 16) {
+        if (__ballot(want_zbx)) {
+          uint32_t sp[32];
+#pragma unroll
+          for (int i = 0; i < 32; ++i) sp[i] = e[i];
+          to_split16(sp);
+#pragma unroll
+          for (int i = 0; i < 32; ++i) e[i] = want_zbx ? sp[i] : e[i];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 32; ++i) d[i] = want_cmp ? e[i] : d[i];
     }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) e[i] = d[i];
   }
+  const uint64_t FV = W == 16 ? (uint64_t)wave_and32((uint32_t)fv)
+                              : ((uint64_t)wave_and32((uint32_t)(fv >> 32)) << 32) | wave_and32((uint32_t)fv);
+  const uint64_t ZR = W == 16 ? (uint64_t)wave_and32((uint32_t)zr)
+                              : ((uint64_t)wave_and32((uint32_t)(zr >> 32)) << 32) | wave_and32((uint32_t)zr);
   __syncthreads();  // costs complete; staging and regions free
 
   // --- 4. Chunk assembly in block order: bit offsets, lengths, headers. ---
@@ -656,158 +810,193 @@ __global__ __launch_bounds__(kCThreads, 2) void compress_kernel(const CBatch bat
   }
   const bool raw_chunk = len == raw_len;
   blk_bits[t] = (uint16_t)excl;
+  if (t == 0) done_waves = 0;
   if ((lane & 31) == 0) {
     chunk_len[t >> 5] = len;
     if (chunk < nchunks) reinterpret_cast<uint16_t *>(dst)[chunk] = (uint16_t)len;
   }
   {
     uint4 *z = reinterpret_cast<uint4 *>(lds);
-    for (uint32_t i = t; i < (uint32_t)kGroupBufDwords / 4; i += kCThreads)
-      z[i] = make_uint4(0, 0, 0, 0);
+    for (uint32_t i = t; i < (uint32_t)kGroupBufDwords / 4; i += kCThreads) z[i] = make_uint4(0, 0, 0, 0);
   }
   __syncthreads();
 
   // The group's aggregate goes out now; the device-wide offsets are resolved
   // after the emission (which works at byte alignment 0), so that waiting on
-  // the predecessors overlaps with it.
-  uint32_t l = 0, inc = 0, agg = 0;
+  // the predecessors overlaps with the other waves' emission.
   if (wave == 0) {
-    l = lane < (uint32_t)kGroupChunks ? chunk_len[lane] : 0u;
-    inc = l;
+    uint32_t inc = lane < (uint32_t)kGroupChunks ? chunk_len[lane] : 0u;
 #pragma unroll
     for (int o = 1; o < kGroupChunks; o <<= 1) {
       const uint32_t v = __shfl_up(inc, o, 64);
       if (lane >= (uint32_t)o) inc += v;
     }
-    agg = __shfl(inc, kGroupChunks - 1, 64);
-    lookback_publish(status, tile, agg, epoch);
+    lookback_publish(status, tile, __shfl(inc, kGroupChunks - 1, 64), epoch);
   }
 
   // --- 5. Emission into the chunk buffers (payload bit i at buffer bit i). ---
   // All-zero blocks of coded chunks: their one code. (In a raw chunk their
   // bytes are zeros, which the cleared buffer already holds.)
-  if (((uint64_t)tile * kCThreads + t) * kBlockBytes < raw_bytes && !nonzero && !raw_chunk) {
-    emit_zero_block<W>(lds + (t >> 5) * kChunkBufDwords, excl, mode);
-  }
+  if (valid && !nonzero && !raw_chunk) emit_zero_block<W>(lds + (t >> 5) * kChunkBufDwords, excl, mode);
 
   if (wave_active) {
-    const uint32_t sb = active ? (uint32_t)slot_block[slot] : 0u;  // the slot's block in the group
-    const uint32_t ch = sb >> 5;
+    const uint32_t ch = sblock >> 5;
     const uint64_t cchunk = (uint64_t)tile * kGroupChunks + ch;
     const uint32_t craw_len =
         cchunk < nchunks ? (uint32_t)min_u64(kChunkBytes, raw_bytes - cchunk * kChunkBytes) : 0u;
     const bool craw = chunk_len[ch] == craw_len;
     const bool coded = active && !craw;
-    const bool want_raw = active && (craw || tag == kRAW);
     const bool want_zvc = coded && tag == kZVC;
     const bool want_dbx = coded && tag == kDBX;
     const bool want_zbx = coded && tag == kZBX;
     const bool want_planes = coded && (tag == kDBX || tag == kBX || tag == kZBX);
+    uint32_t *buf = lds + ch * kChunkBufDwords;
 
-    BitSink bs;
-    bs.buf = lds + ch * kChunkBufDwords;
-    bs.off = craw ? 1024u * (sb & 31) : (uint32_t)blk_bits[sb];
-    if (coded && mode.tagged) bs.put((uint32_t)tag, 3);
-
-    if (__ballot(want_raw)) {
-      // A raw chunk needs the symbols themselves back where e holds a transform.
-      const bool reload = want_raw && (tag == kDBX || tag == kZBX || tag == kZVC);
-      if (__ballot(reload)) {
-        if (reload) load_block(src, raw_bytes, ((uint64_t)tile * kCThreads + sb) * kBlockBytes, e);
-      }
-      if (want_raw) {
-        // 1024 bits: the first and last dwords are shared with neighbours
-        // (OR), the 31 between belong to this block alone.
-        const uint32_t q = bs.off >> 5, sh = bs.off & 31u;
-        atomicOr(&bs.buf[q], e[0] << sh);
+    // Raw chunks: the block's bytes at its place (dword aligned).
+    if (__ballot(active && craw)) {
+      if (active && craw) {
+        uint32_t r[32];
+        load_block(src, raw_bytes, ((uint64_t)tile * kCThreads + sblock) * kBlockBytes, r);
+        uint4 *q = reinterpret_cast<uint4 *>(buf + 32 * (sblock & 31));
 #pragma unroll
-        for (int i = 1; i < 32; ++i) bs.buf[q + i] = (e[i] << sh) | ((e[i - 1] >> 1) >> (31u - sh));
-        atomicOr(&bs.buf[q + 32], (e[31] >> 1) >> (31u - sh));
-        bs.off += 1024;
+        for (int i = 0; i < 8; ++i) q[i] = make_uint4(r[4 * i], r[4 * i + 1], r[4 * i + 2], r[4 * i + 3]);
       }
     }
 
+    uint32_t off = coded ? (uint32_t)blk_bits[sblock] : 0u;
+    // Tag, then the DBX base or the ZVC / ZBX mask.
+    if (coded) {
+      uint32_t hv = 0, hl = 0;
+      if (mode.tagged) {
+        hv = (uint32_t)tag;
+        hl = 3;
+      }
+      if (W == 16 && want_dbx) {
+        hv |= base << hl;
+        hl += 16;
+      }
+      or32(buf, off, hv);
+      off += hl;
+      if (W == 32 && want_dbx) {
+        or32(buf, off, base);
+        off += 32;
+      }
+    }
+    if (__ballot(want_zvc || want_zbx)) {
+      if (want_zvc || want_zbx) {
+        if constexpr (W == 16)
+          or64(buf, off, mlo, mhi);
+        else
+          or32(buf, off, mlo);
+        off += N;
+      }
+    }
+
+    // RAW blocks of coded chunks: 1024 bits at an arbitrary bit offset.
+    const bool want_rawblk = coded && tag == kRAW;
+    if (__ballot(want_rawblk)) {
+      if (want_rawblk) {
+        uint32_t r[32];
+        load_block(src, raw_bytes, ((uint64_t)tile * kCThreads + sblock) * kBlockBytes, r);
+        const uint32_t q = off >> 5, sh = off & 31u;
+        atomicOr(&buf[q], r[0] << sh);
+#pragma unroll
+        for (int i = 1; i < 32; ++i) buf[q + i] = (r[i] << sh) | ((r[i - 1] >> 1) >> (31u - sh));
+        atomicOr(&buf[q + 32], (r[31] >> 1) >> (31u - sh));
+      }
+    }
+
+    // ZVC: the n non-zero symbols, in order, 32 bits (two w = 16 symbols) at
+    // a time, until no lane has any left.
     if (__ballot(want_zvc)) {
-      // The mask, then the n non-zero symbols: the compacted symbols in e,
-      // 32 bits (two symbols) at a time, until no lane has any left.
-      if (want_zvc) bs.put64(nzmask, N);
-      const uint32_t bits = want_zvc ? (uint32_t)W * (uint32_t)s.n : 0u;
+      const uint32_t zbits = want_zvc ? (uint32_t)W * sn : 0u;
 #pragma unroll
       for (int q = 0; q < 32; ++q) {
-        if (!__ballot(32u * q < bits)) break;
-        if (32u * q < bits) {
-          const uint32_t len = bits - 32u * q < 32u ? bits - 32u * q : 32u;
-          bs.put(e[q], len);
-        }
+        if (!__ballot(32u * q < zbits)) break;
+        if (32u * q < zbits) or32(buf, off + 32u * q, e[q]);  // words past n hold zeros
       }
     }
 
+    // Plane encodings: DBX's top plane (the borrows), then planes W-1..0 of
+    // the transposed input; each plane takes the zero path, the verbatim
+    // path or the general classifier, as the whole wave allows.
     if (__ballot(want_planes)) {
-      if (want_dbx) bs.put(base, W);
-      if (want_zbx) bs.put64(nzmask, N);
-      const uint32_t L = want_dbx ? (uint32_t)(N - 1) : (want_zbx ? (uint32_t)s.n : (uint32_t)N);
-      const uint32_t pw = (uint32_t)position_bits((int)L);
+      const uint32_t L = want_dbx ? (uint32_t)(N - 1) : (want_zbx ? sn : (uint32_t)N);
+      const uint32_t L1 = L + 1;
+      const uint32_t cs = 5u + (uint32_t)position_bits((int)L);
       const PT ones = (PT)all_ones64((int)L);
       uint32_t run = 0;
       PT above = 0;
-      // DBX's top plane: the borrow bits of the deltas.
       if (__ballot(want_dbx)) {
         PT bm;
-        if constexpr (W == 16) {
-          const uint32_t m0 = spread16(s.b0) | (spread16(s.b0 >> 16) << 1);  // bit m: delta m
-          const uint32_t m1 = spread16(s.b1) | (spread16(s.b1 >> 16) << 1);  // bit m: delta 32+m
-          bm = (((uint64_t)m1 << 32) | m0) >> 1;
+        if constexpr (W == 16)
+          bm = ((uint64_t)bm_hi << 32) | bm_lo;
+        else
+          bm = bm_lo;
+        if ((ZR >> KT) & 1u) {
+          if (want_dbx) run = 1;
+        } else if ((FV >> KT) & 1u) {
+          if (want_dbx) {
+            if constexpr (W == 16)
+              or_verbatim(buf, off, bm_lo, bm_hi);
+            else
+              or_verbatim(buf, off, bm_lo);
+            off += L1;
+          }
         } else {
-          bm = s.b0;
+          if (want_dbx) emit_plane<PT, R>(buf, off, run, bm, false, ones, L, cs);
         }
-        if (want_dbx) {
-          emit_plane<PT>(bs, bm, bm, ones, L, pw, R, run);
-          above = bm;
+        above = want_dbx ? bm : (PT)0;
+      }
+      transpose32(e);
+#pragma unroll
+      for (int j = W - 1; j >= 0; --j) {
+        PT pj;
+        if constexpr (W == 16)
+          pj = ((uint64_t)e[16 + j] << 32) | e[j];
+        else
+          pj = e[j];
+        const PT x = pj ^ above;
+        above = pj;
+        if ((ZR >> j) & 1u) {
+          if (want_planes) ++run;
+        } else if ((FV >> j) & 1u) {
+          if (want_planes) {
+            if constexpr (W == 16)
+              or_verbatim(buf, off, (uint32_t)x, (uint32_t)((uint64_t)x >> 32));
+            else
+              or_verbatim(buf, off, (uint32_t)x);
+            off += L1;
+          }
+        } else {
+          if (want_planes) emit_plane<PT, R>(buf, off, run, x, pj == 0, ones, L, cs);
         }
       }
-      if constexpr (W == 16) {
-        uint64_t P[16];
-        {
-          // Symbols k and k+32 share a dword, so one 32x32 transpose yields
-          // the low and high halves of every 64-bit plane.
-          uint32_t tr[32];
-#pragma unroll
-          for (int r = 0; r < 32; ++r) {
-            const uint32_t a = e[r >> 1], b = e[16 + (r >> 1)];
-            tr[r] = ((r & 1) ? (a >> 16) : (a & 0xFFFFu)) | ((r & 1) ? (b & 0xFFFF0000u) : (b << 16));
-          }
-          transpose32(tr);
-#pragma unroll
-          for (int j = 0; j < 16; ++j) P[j] = (uint64_t)tr[j] | ((uint64_t)tr[j + 16] << 32);
-        }
-#pragma unroll
-        for (int j = 15; j >= 0; --j) {
-          if (want_planes) {
-            const uint64_t p = P[j];
-            emit_plane<uint64_t>(bs, p ^ above, p, ones, L, pw, R, run);
-            above = p;
-          }
-        }
-      } else {
-        transpose32(e);
-#pragma unroll
-        for (int j = 31; j >= 0; --j) {
-          if (want_planes) {
-            const uint32_t p = e[j];
-            emit_plane<uint32_t>(bs, p ^ above, p, ones, L, pw, R, run);
-            above = p;
-          }
-        }
+      if (want_planes && run) {
+        uint32_t rcode, rlen;
+        run_code<R>(run, rcode, rlen);
+        or32(buf, off, rcode);
       }
-      if (want_planes) emit_run(bs, run, R);
     }
   }
 
-  // Device-wide payload offsets of the group's chunks.
-  if (wave == 0) {
-    const uint64_t before = lookback_resolve(status, tile, agg, epoch);
-    if (lane < (uint32_t)kGroupChunks) chunk_pay[lane] = 2 * nchunks + before + (inc - l);
-    if (tile == ntiles - 1 && lane == 0) *batch.t[k].out_bytes = 2 * nchunks + before + agg;
+  // Device-wide payload offsets of the group's chunks: the first wave done
+  // with its emission resolves the look-back (waves with little or no
+  // emission, as in a tile of mostly zero blocks, start waiting at once).
+  uint32_t first = 0;
+  if (lane == 0) first = atomicAdd(&done_waves, 1u);
+  if (__builtin_amdgcn_readfirstlane(__shfl(first, 0, 64)) == 0) {
+    const uint32_t cl = lane < (uint32_t)kGroupChunks ? chunk_len[lane] : 0u;
+    uint32_t cinc = cl;
+#pragma unroll
+    for (int o = 1; o < kGroupChunks; o <<= 1) {
+      const uint32_t v = __shfl_up(cinc, o, 64);
+      if (lane >= (uint32_t)o) cinc += v;
+    }
+    const uint32_t total = __shfl(cinc, kGroupChunks - 1, 64);
+    const uint64_t before = lookback_resolve(status, tile, total, epoch);
+    if (lane < (uint32_t)kGroupChunks) chunk_pay[lane] = 2 * nchunks + before + (cinc - cl);
+    if (tile == ntiles - 1 && lane == 0) *batch.t[k].out_bytes = 2 * nchunks + before + total;
   }
   __syncthreads();
 
@@ -818,8 +1007,9 @@ __global__ __launch_bounds__(kCThreads, 2) void compress_kernel(const CBatch bat
   // a funnel shift. Unit u of the span therefore needs buffer dwords
   // 4u - dsh - 1 .. 4u - dsh + 3, which lie in the aligned quads u - 1 and u
   // (two conflict-free 16-byte LDS reads; dsh is uniform over the chunk).
-  // Only the first and last units (shared with the neighbouring chunks) are
-  // written piecewise. ---
+  // A lane's units are u = lane + 64 m (a chunk spans at most 257); all
+  // their LDS reads are issued before the first store. Only the first and
+  // last units (shared with the neighbouring chunks) are written piecewise. ---
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const uint32_t c = 2 * wave + (uint32_t)h;
@@ -856,14 +1046,14 @@ __global__ __launch_bounds__(kCThreads, 2) void compress_kernel(const CBatch bat
         *reinterpret_cast<uint4 *>(span + b0) = make_uint4(v[0], v[1], v[2], v[3]);
       } else {
 #pragma unroll
-        for (uint32_t k = 0; k < 4; ++k) {
-          const uint32_t d0 = b0 + 4 * k;
+        for (uint32_t kk = 0; kk < 4; ++kk) {
+          const uint32_t d0 = b0 + 4 * kk;
           if (d0 >= sh && d0 + 4 <= total) {
-            *reinterpret_cast<uint32_t *>(span + d0) = v[k];
+            *reinterpret_cast<uint32_t *>(span + d0) = v[kk];
           } else {
 #pragma unroll
-            for (uint32_t b = 0; b < 4; ++b)
-              if (d0 + b >= sh && d0 + b < total) span[d0 + b] = (uint8_t)(v[k] >> (8 * b));
+            for (uint32_t bb = 0; bb < 4; ++bb)
+              if (d0 + bb >= sh && d0 + bb < total) span[d0 + bb] = (uint8_t)(v[kk] >> (8 * bb));
           }
         }
       }
@@ -881,7 +1071,7 @@ __global__ __launch_bounds__(kCThreads, 2) void compress_kernel(const CBatch bat
 // out_bytes (which holds the headers' bytes beforehand).
 // ---------------------------------------------------------------------------
 template <int W>
-__global__ __launch_bounds__(kCThreads, 2) void size_kernel(const SBatch batch, Mode mode) {
+__global__ __launch_bounds__(kCThreads, kCWavesPerSimd) void size_kernel(const SBatch batch, Mode mode) {
   constexpr int N = 1024 / W;
   __shared__ __attribute__((aligned(16))) uint32_t lds[kStageDwords];
   __shared__ uint16_t blk_bits[kCThreads];
@@ -926,38 +1116,45 @@ __global__ __launch_bounds__(kCThreads, 2) void size_kernel(const SBatch batch, 
 
   uint32_t nfull = 0, npart = 0, ffirst = 0, pfirst = 0;
 #pragma unroll
-  for (int k = 0; k < kCWaves; ++k) {
-    const uint32_t f = wave_full[k], q = wave_part[k];
-    ffirst += (uint32_t)k < wave ? f : 0u;
-    pfirst += (uint32_t)k < wave ? q : 0u;
+  for (int q = 0; q < kCWaves; ++q) {
+    const uint32_t f = wave_full[q], p = wave_part[q];
+    ffirst += (uint32_t)q < wave ? f : 0u;
+    pfirst += (uint32_t)q < wave ? p : 0u;
     nfull += f;
-    npart += q;
+    npart += p;
   }
   const uint32_t nnz = nfull + npart;
-  if (nonzero) {
-    const uint32_t idx = partial ? nfull + pfirst + lanes_below(mpart) : ffirst + lanes_below(mfull);
-    uint32_t *slot = lds + idx * kLaneStride;
+  const bool staged = !(nnz == (uint32_t)kCThreads && (npart == 0 || nfull == 0));
+  if (staged) {
+    if (nonzero) {
+      const uint32_t idx = partial ? nfull + pfirst + lanes_below(mpart) : ffirst + lanes_below(mfull);
+      uint32_t *slotp = lds + idx * kLaneStride;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) slot[i] = d[i];
-    slot_block[idx] = (uint16_t)t;
-    slot_n[idx] = (uint8_t)sn;
+      for (int i = 0; i < 32; ++i) slotp[i] = d[i];
+      slot_block[idx] = (uint16_t)t;
+      slot_n[idx] = (uint8_t)sn;
+    }
+    __syncthreads();
   }
-  __syncthreads();
 
-  const uint32_t slot = (t + kCThreads - 64u * (blockIdx.x & (kCWaves - 1u))) & (kCThreads - 1);
+  const uint32_t slot = staged ? (t + kCThreads - 64u * (blockIdx.x & (kCWaves - 1u))) & (kCThreads - 1) : t;
   const bool active = slot < nnz;
   if (__ballot(active) != 0) {
-    const uint32_t *region = lds + slot * kLaneStride;
-    sn = active ? (uint32_t)slot_n[slot] : 0u;
-    if (active) {
+    if (staged) {
+      const uint32_t *region = lds + slot * kLaneStride;
+      sn = active ? (uint32_t)slot_n[slot] : 0u;
+      if (active) {
 #pragma unroll
-      for (int i = 0; i < 32; ++i) d[i] = region[i];
+        for (int i = 0; i < 32; ++i) d[i] = region[i];
+      }
     }
-    Sizes s;
+    if constexpr (W == 16) to_split16(d);
+    Stats s;
     candidate_sizes<W>(d, (int)sn, __ballot(active && sn < (uint32_t)N) != 0, s);
     int best_size;
     select_tag(s, best_size, mode.mask);
-    if (active) blk_bits[slot_block[slot]] = (uint16_t)(3u * mode.tagged + best_size);
+    const uint32_t sb = staged ? (uint32_t)slot_block[slot] : t;
+    if (active) blk_bits[sb] = (uint16_t)(3u * mode.tagged + best_size);
   }
   __syncthreads();
 
@@ -1046,15 +1243,16 @@ uint32_t compress_tiles(uint64_t raw_bytes) {
   return (uint32_t)((nchunks + kGroupChunks - 1) / kGroupChunks);
 }
 
+
 hipError_t launch_compress(int w, const CBatch &batch, uint32_t codec_mask, int tagged,
                            const Scratch &scratch, hipStream_t stream) {
   const Mode mode = make_mode(w, codec_mask, tagged);
   if (w == 16)
-    hipLaunchKernelGGL(compress_kernel<16>, dim3(batch.total_tiles), dim3(kCThreads), 0, stream, batch,
-                       scratch.words, scratch.counter, scratch.counter_base, scratch.epoch, mode);
+    hipLaunchKernelGGL(compress_kernel<16>, dim3(batch.total_tiles), dim3(kCThreads), 0, stream, batch, scratch.words,
+                       scratch.counter, scratch.counter_base, scratch.epoch, mode);
   else
-    hipLaunchKernelGGL(compress_kernel<32>, dim3(batch.total_tiles), dim3(kCThreads), 0, stream, batch,
-                       scratch.words, scratch.counter, scratch.counter_base, scratch.epoch, mode);
+    hipLaunchKernelGGL(compress_kernel<32>, dim3(batch.total_tiles), dim3(kCThreads), 0, stream, batch, scratch.words,
+                       scratch.counter, scratch.counter_base, scratch.epoch, mode);
   return hipGetLastError();
 }
 
