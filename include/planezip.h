@@ -181,6 +181,26 @@ pz_status_t pz_decompress_batch(int count, const void *const *d_srcs,
                                 const size_t *raw_bytes, int32_t *d_status,
                                 void *stream);
 
+/* Compression that allocates nothing, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid allocation. Same arguments, checks and stream as
+ * pz_compress (PlaneZip with all five candidates, tagged), but its scratch
+ * (a tile counter and one look-back word per 64 KB tile) lives in a fixed
+ * 128 KiB device array that the library holds on each GPU it runs on until
+ * the process ends; the call allocates and frees nothing (no hipMalloc,
+ * hipMallocAsync, hipFree or allocating library routine) and clears the
+ * array with a kernel, not a memset.
+ *   raw_bytes  at most PZ_NOALLOC_MAX_BYTES; larger sizes return
+ *              PZ_ERROR_INVALID_VALUE with nothing enqueued
+ * Every call on a GPU shares that GPU's array, which keeps the last call's
+ * contents: calls that overlap on one GPU (two streams, two host threads)
+ * race and must be serialized by the caller. The first call with a device
+ * current looks the array's device address up once (hipGetSymbolAddress). */
+#define PZ_NOALLOC_MAX_BYTES ((size_t)1073348608) /* 16378 tiles of 64 KB */
+pz_status_t pz_compress_noalloc(const void *d_src, size_t raw_bytes, int dtype,
+                                int elem_bits, void *d_dst, size_t dst_capacity,
+                                uint64_t *d_out_bytes, void *stream);
+
 /* Sampled size: the pz_compressed_size measurement over chunks 0, stride,
  * 2*stride, ... only (the paper's methodology sizes tensors above 32 MB on
  * every fourth 4 KB chunk, §IV "Tensor capture"), at 1/stride of the work.

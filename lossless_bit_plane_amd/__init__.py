@@ -16,7 +16,7 @@ from .codec import (  # noqa: F401
     max_compressed_bytes, num_chunks,
     pz_block_sizes, pz_compress, pz_compressed_size, pz_decompress,
     pz_compress_ex, pz_compressed_size_ex, pz_decompress_ex, pz_compressed_size_sampled,
-    pz_compress_batch, pz_decompress_batch, pz_compressed_size_batch, compress, decompress,
+    pz_compress_batch, pz_decompress_batch, pz_compressed_size_batch, pz_compress_noalloc, compress, decompress,
 )
 from .predictor import (  # noqa: F401
     Predictor, signature, pz_predictor_create, pz_predictor_destroy, pz_predictor_update,

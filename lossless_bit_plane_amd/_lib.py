@@ -14,6 +14,7 @@ PZ_ERROR_INVALID_VALUE = 1
 PZ_ERROR_INSUFFICIENT_BUFFER = 2
 PZ_ERROR_CORRUPT_STREAM = 3
 PZ_ERROR_HIP = 4
+PZ_NOALLOC_MAX_BYTES = 1073348608
 
 EXPORTS = ("pz_compressed_size", "pz_compress", "pz_decompress", "pz_block_sizes", "pz_status_string",
            "pz_compressed_size_ex", "pz_compress_ex", "pz_decompress_ex", "pz_compressed_size_sampled",
@@ -21,7 +22,7 @@ EXPORTS = ("pz_compressed_size", "pz_compress", "pz_decompress", "pz_block_sizes
            "pz_predictor_entries", "pz_predictor_clear",
            "pz_swapper_create", "pz_swapper_destroy", "pz_swapper_free_chunks", "pz_swap_out", "pz_swap_wait",
            "pz_swap_in", "pz_swap_release", "pz_swap_read", "pz_compress_batch", "pz_decompress_batch",
-           "pz_compressed_size_batch")
+           "pz_compressed_size_batch", "pz_compress_noalloc")
 
 
 def _load():
@@ -33,6 +34,7 @@ def _load():
     vp, sz, i = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
     lib.pz_compressed_size.argtypes = [vp, sz, i, i, vp, vp, vp]
     lib.pz_compress.argtypes = [vp, sz, i, i, vp, sz, vp, vp]
+    lib.pz_compress_noalloc.argtypes = [vp, sz, i, i, vp, sz, vp, vp]
     lib.pz_decompress.argtypes = [vp, sz, i, i, vp, sz, vp, vp]
     lib.pz_block_sizes.argtypes = [vp, sz, i, i, vp, vp, vp]
     u32 = ctypes.c_uint32
@@ -70,10 +72,10 @@ def _load():
     lib.pz_swap_read.argtypes = [vp, u64, vp, sz, ctypes.POINTER(u64)]
     for name in ("pz_swap_out", "pz_swap_wait", "pz_swap_in", "pz_swap_release", "pz_swap_read"):
         getattr(lib, name).restype = ctypes.c_int
-    for name in ("pz_compressed_size", "pz_compress", "pz_decompress", "pz_block_sizes",
+    for name in ("pz_compressed_size", "pz_compress", "pz_compress_noalloc", "pz_decompress", "pz_block_sizes",
                  "pz_compressed_size_ex", "pz_compress_ex", "pz_decompress_ex", "pz_compressed_size_sampled",
                  "pz_predictor_update", "pz_predictor_predict", "pz_compress_batch", "pz_decompress_batch",
-                 "pz_compressed_size_batch"):
+                 "pz_compressed_size_batch", "pz_compress_noalloc"):
         getattr(lib, name).restype = ctypes.c_int
     lib.pz_status_string.argtypes = [ctypes.c_int]
     lib.pz_status_string.restype = ctypes.c_char_p

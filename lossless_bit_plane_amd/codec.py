@@ -141,6 +141,19 @@ def pz_compress(src: torch.Tensor, dtype=None, elem_bits=None, dst: torch.Tensor
     return dst, out_bytes
 
 
+def pz_compress_noalloc(src: torch.Tensor, dst: torch.Tensor, out_bytes: torch.Tensor, dtype=None,
+                        elem_bits=None, stream=None):
+    """pz_compress into caller-provided ``dst`` (uint8, capacity >=
+    max_compressed_bytes) and ``out_bytes`` (int64, 1) through the entry
+    point that allocates nothing (tensors up to PZ_NOALLOC_MAX_BYTES; calls
+    that overlap on one GPU race). Returns (dst, out_bytes)."""
+    dtype, elem_bits = _kind(src, dtype, elem_bits)
+    b = _byte_view(src)
+    check(lib.pz_compress_noalloc(_ptr(b), b.numel(), dtype, elem_bits, _ptr(dst), dst.numel(),
+                                  _ptr(out_bytes), _stream(stream)), "pz_compress_noalloc")
+    return dst, out_bytes
+
+
 def pz_decompress(src: torch.Tensor, comp_bytes: int, raw_bytes: int, dtype: int, elem_bits: int,
                   dst: torch.Tensor | None = None, status: torch.Tensor | None = None, stream=None):
     """Decompress ``comp_bytes`` of ``src`` into ``dst`` (uint8, raw_bytes).

@@ -237,9 +237,82 @@ pz_status_t decompress_many(int dtype, int elem_bits, uint32_t codec_mask, int t
   return PZ_SUCCESS;
 }
 
+// ---------------------------------------------------------------------------
+// Compression without allocation (pz_compress_noalloc). Its scratch (the tile
+// counter and one look-back word per tile) is a fixed array in device
+// memory, one copy per GPU, that lives until the process ends. Host code
+// never passes the array's name to a kernel: its name is a host-side stand-in,
+// not a device address. The device address comes from hipGetSymbolAddress,
+// once per device, on the first call made with that device current, and is
+// kept per device.
+// ---------------------------------------------------------------------------
+constexpr size_t kNoAllocWords = 16384;  // 128 KiB: header + look-back words
+constexpr size_t kNoAllocHeaderWords = kScratchHeader / 8;
+static __device__ __align__(256) uint64_t scratch[kNoAllocWords];
+
+std::mutex g_noalloc_mu;
+uint64_t *g_noalloc_ptr[64];
+
+hipError_t noalloc_scratch(uint64_t **out) {
+  int device = 0;
+  hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess) return e;
+  if (device < 0 || device >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  if (!g_noalloc_ptr[device]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_noalloc_ptr[device] = static_cast<uint64_t *>(ptr);
+  }
+  *out = g_noalloc_ptr[device];
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
+
+pz_status_t pz_compress_noalloc(const void *d_src, size_t raw_bytes, int dtype, int elem_bits, void *d_dst,
+                                size_t dst_capacity, uint64_t *d_out_bytes, void *stream) {
+  const int w = symbol_width(dtype, elem_bits);
+  if (w < 0 || !d_out_bytes || (reinterpret_cast<uintptr_t>(d_out_bytes) & 7u)) return PZ_ERROR_INVALID_VALUE;
+  if (raw_bytes && (!d_src || !d_dst)) return PZ_ERROR_INVALID_VALUE;
+  if (!aligned16(d_src) || !aligned16(d_dst)) return PZ_ERROR_INVALID_VALUE;
+  if (dst_capacity < PZ_MAX_COMPRESSED_BYTES(raw_bytes)) return PZ_ERROR_INSUFFICIENT_BUFFER;
+  if (raw_bytes > PZ_NOALLOC_MAX_BYTES || pz::compress_tiles(raw_bytes) > kNoAllocWords - kNoAllocHeaderWords)
+    return PZ_ERROR_INVALID_VALUE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (raw_bytes == 0) return from_hip(pz::fill_u64(d_out_bytes, 1, 0, s));
+  uint64_t *base = nullptr;
+  hipError_t e = noalloc_scratch(&base);
+  if (e != hipSuccess) return from_hip(e);
+  pz::CBatch b{};
+  b.n = 1;
+  pz::CTensor &x = b.t[0];
+  x.src = static_cast<const uint8_t *>(d_src);
+  x.dst = static_cast<uint8_t *>(d_dst);
+  x.out_bytes = d_out_bytes;
+  x.raw_bytes = raw_bytes;
+  x.nchunks = PZ_NUM_CHUNKS(raw_bytes);
+  x.tile_begin = 0;
+  x.ntiles = pz::compress_tiles(raw_bytes);
+  b.total_tiles = x.ntiles;
+  // The previous call's counter and look-back words are still there: clear
+  // them (a kernel, not a memset) and count this call's tiles from 0 under
+  // epoch 1.
+  e = pz::fill_u64(base, kNoAllocHeaderWords + x.ntiles, 0, s);
+  if (e != hipSuccess) return from_hip(e);
+  pz::Scratch sc;
+  sc.counter = reinterpret_cast<uint32_t *>(base);
+  sc.err = reinterpret_cast<uint32_t *>(base) + 1;
+  sc.words = base + kNoAllocHeaderWords;
+  sc.extra = nullptr;
+  sc.epoch = 1;
+  sc.counter_base = 0;
+  return from_hip(pz::launch_compress(w, b, PZ_CODEC_ALL, 1, sc, s));
+}
+
 
 const char *pz_status_string(int status) {
   switch (status) {

@@ -148,3 +148,20 @@ def test_swapper_rejects_bad_sizes_without_touching_the_device(lib):
 
     assert lib.pz_swap_wait(None, 1, None) == _lib.PZ_ERROR_INVALID_VALUE
     assert lib.pz_swap_release(None, 1) == _lib.PZ_ERROR_INVALID_VALUE
+
+
+def test_noalloc_compress_rejects_on_host(lib):
+    """The allocation-free compress call checks its arguments and its size
+    limit before it touches the device (none of these pointers is read)."""
+    from lossless_bit_plane_amd import _lib
+
+    fake = 256
+    big = _lib.PZ_NOALLOC_MAX_BYTES + 1
+    cap = 2 * ((big + 4095) // 4096) + big
+    assert lib.pz_compress_noalloc(fake, big, 0, 16, fake, cap, fake, None) == _lib.PZ_ERROR_INVALID_VALUE
+    assert lib.pz_compress_noalloc(fake, 100, 0, 8, fake, 1000, fake, None) == _lib.PZ_ERROR_INVALID_VALUE
+    assert lib.pz_compress_noalloc(None, 100, 0, 16, fake, 1000, fake, None) == _lib.PZ_ERROR_INVALID_VALUE
+    assert lib.pz_compress_noalloc(fake, 100, 0, 16, fake, 1000, None, None) == _lib.PZ_ERROR_INVALID_VALUE
+    assert lib.pz_compress_noalloc(fake, 100, 0, 16, fake, 1000, fake + 4, None) == _lib.PZ_ERROR_INVALID_VALUE
+    assert lib.pz_compress_noalloc(fake + 4, 100, 0, 16, fake, 1000, fake, None) == _lib.PZ_ERROR_INVALID_VALUE
+    assert lib.pz_compress_noalloc(fake, 4097, 0, 16, fake, 4100, fake, None) == _lib.PZ_ERROR_INSUFFICIENT_BUFFER
