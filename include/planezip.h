@@ -185,8 +185,8 @@ pz_status_t pz_decompress_batch(int count, const void *const *d_srcs,
  * device memory: code under HIP graph capture, tight serving loops, and
  * harnesses that forbid allocation. Same arguments, checks and stream as
  * pz_compress (PlaneZip with all five candidates, tagged), but its scratch
- * (a tile counter and one look-back word per 64 KB tile) lives in a fixed
- * 128 KiB device array that the library holds on each GPU it runs on until
+ * (a tile counter and one look-back word per 32 KB tile) lives in a fixed
+ * 256 KiB device array that the library holds on each GPU it runs on until
  * the process ends; the call allocates and frees nothing (no hipMalloc,
  * hipMallocAsync, hipFree or allocating library routine) and clears the
  * array with a kernel, not a memset.
@@ -196,7 +196,7 @@ pz_status_t pz_decompress_batch(int count, const void *const *d_srcs,
  * contents: calls that overlap on one GPU (two streams, two host threads)
  * race and must be serialized by the caller. The first call with a device
  * current looks the array's device address up once (hipGetSymbolAddress). */
-#define PZ_NOALLOC_MAX_BYTES ((size_t)1073348608) /* 16378 tiles of 64 KB */
+#define PZ_NOALLOC_MAX_BYTES ((size_t)1073545216) /* 32762 tiles of 32 KB */
 pz_status_t pz_compress_noalloc(const void *d_src, size_t raw_bytes, int dtype,
                                 int elem_bits, void *d_dst, size_t dst_capacity,
                                 uint64_t *d_out_bytes, void *stream);

@@ -246,7 +246,7 @@ pz_status_t decompress_many(int dtype, int elem_bits, uint32_t codec_mask, int t
 // once per device, on the first call made with that device current, and is
 // kept per device.
 // ---------------------------------------------------------------------------
-constexpr size_t kNoAllocWords = 16384;  // 128 KiB: header + look-back words
+constexpr size_t kNoAllocWords = 32768;  // 256 KiB: header + look-back words
 constexpr size_t kNoAllocHeaderWords = kScratchHeader / 8;
 static __device__ __align__(256) uint64_t scratch[kNoAllocWords];
 

@@ -511,19 +511,19 @@ PZ_DEV void emit_plane(uint32_t *buf, uint32_t &off, uint32_t &run, PT x, bool p
 }
 
 // ---------------------------------------------------------------------------
-// Single-pass compression, one workgroup per tile of 16 chunks (512 blocks,
-// eight waves: two such workgroups fill a CU's LDS).
+// Single-pass compression, one workgroup per tile of 8 chunks (256 blocks,
+// four waves: four such workgroups fill a CU, whose phases interleave better
+// than those of two groups of eight waves).
 //
 // Softmax-like activations hold many all-zero blocks, and a wave runs the
 // candidate statistics and the emission for all its lanes at the cost of
-// the slowest. So the group first loads its 512 blocks one per thread,
+// the slowest. So the group first loads its 256 blocks one per thread,
 // gives every all-zero block its fixed code (below), and, when some block is
 // all zero, packs the non-zero blocks through LDS into the lowest slots: only
 // ceil(nnz / 64) waves then run the statistics and the emission. Chunk
 // offsets come from one decoupled look-back per group.
 // ---------------------------------------------------------------------------
-constexpr int kCWaves = 8;  // waves per compress / size workgroup
-constexpr int kCGroupsPerCU = 16 / kCWaves;  // workgroups a CU holds (LDS and VGPRs both allow)
+constexpr int kCWaves = 4;  // waves per compress workgroup
 // The second launch bound is the minimum number of waves per SIMD: four caps
 // a lane at 128 VGPRs, so that a CU holds the 16 waves above.
 constexpr int kCWavesPerSimd = 4;
@@ -595,7 +595,7 @@ __global__ __launch_bounds__(kCThreads, kCWavesPerSimd) void compress_kernel(con
   constexpr int KT = W;  // index of DBX's top plane (the borrow plane) in the plane masks
   using PT = typename std::conditional<W == 16, uint64_t, uint32_t>::type;
   // Staging slots / compaction regions (stride kLaneStride), later the
-  // sixteen chunk buffers.
+  // chunk buffers.
   __shared__ __attribute__((aligned(16))) uint32_t lds[kGroupLdsDwords];
   __shared__ uint16_t blk_bits[kCThreads];    // per block: its cost, then its bit offset
   __shared__ uint16_t slot_block[kCThreads];  // compacted slot -> block of the group
@@ -1070,16 +1070,25 @@ __global__ __launch_bounds__(kCThreads, kCWavesPerSimd) void compress_kernel(con
 // chunk's block costs to its length. Lengths go to chunk_lens; their sum to
 // out_bytes (which holds the headers' bytes beforehand).
 // ---------------------------------------------------------------------------
+// The size pass keeps tiles of 16 chunks (eight waves): it adds each
+// workgroup's bytes to the tensor's total with one atomic on a single
+// address, and such atomics complete one after another (about 6 ns each), so
+// twice the workgroups cost about 50 us more on the GPT-2-XL workload.
+constexpr int kSWaves = 8;
+constexpr int kSThreads = kWave * kSWaves;
+constexpr int kSGroupChunks = kSThreads / kBlocksPerChunk;
+constexpr int kSStageDwords = kSThreads * kLaneStride;
+
 template <int W>
-__global__ __launch_bounds__(kCThreads, kCWavesPerSimd) void size_kernel(const SBatch batch, Mode mode) {
+__global__ __launch_bounds__(kSThreads, kCWavesPerSimd) void size_kernel(const SBatch batch, Mode mode) {
   constexpr int N = 1024 / W;
-  __shared__ __attribute__((aligned(16))) uint32_t lds[kStageDwords];
-  __shared__ uint16_t blk_bits[kCThreads];
-  __shared__ uint16_t slot_block[kCThreads];
-  __shared__ uint8_t slot_n[kCThreads];
-  __shared__ uint32_t wave_full[kCWaves];
-  __shared__ uint32_t wave_part[kCWaves];
-  __shared__ uint32_t chunk_len[kGroupChunks];
+  __shared__ __attribute__((aligned(16))) uint32_t lds[kSStageDwords];
+  __shared__ uint16_t blk_bits[kSThreads];
+  __shared__ uint16_t slot_block[kSThreads];
+  __shared__ uint8_t slot_n[kSThreads];
+  __shared__ uint32_t wave_full[kSWaves];
+  __shared__ uint32_t wave_part[kSWaves];
+  __shared__ uint32_t chunk_len[kSGroupChunks];
 
   const uint32_t t = threadIdx.x, lane = lane_id();
   const uint32_t wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -1095,7 +1104,7 @@ __global__ __launch_bounds__(kCThreads, kCWavesPerSimd) void size_kernel(const S
   const uint64_t stride = batch.t[k].stride, nsampled = batch.t[k].nsampled;
   uint64_t *__restrict__ out_bytes = batch.t[k].out_bytes;
   uint16_t *__restrict__ chunk_lens = batch.t[k].chunk_lens;
-  const uint64_t sample = (uint64_t)(blockIdx.x - batch.t[k].group_begin) * kGroupChunks + (t >> 5);
+  const uint64_t sample = (uint64_t)(blockIdx.x - batch.t[k].group_begin) * kSGroupChunks + (t >> 5);
   // Samples past the last one read as zeros (their chunk is past the end).
   const uint64_t chunk = sample < nsampled ? sample * stride : nchunks;
   const uint64_t block = chunk * kBlocksPerChunk + (t & 31);
@@ -1116,7 +1125,7 @@ __global__ __launch_bounds__(kCThreads, kCWavesPerSimd) void size_kernel(const S
 
   uint32_t nfull = 0, npart = 0, ffirst = 0, pfirst = 0;
 #pragma unroll
-  for (int q = 0; q < kCWaves; ++q) {
+  for (int q = 0; q < kSWaves; ++q) {
     const uint32_t f = wave_full[q], p = wave_part[q];
     ffirst += (uint32_t)q < wave ? f : 0u;
     pfirst += (uint32_t)q < wave ? p : 0u;
@@ -1124,7 +1133,7 @@ __global__ __launch_bounds__(kCThreads, kCWavesPerSimd) void size_kernel(const S
     npart += p;
   }
   const uint32_t nnz = nfull + npart;
-  const bool staged = !(nnz == (uint32_t)kCThreads && (npart == 0 || nfull == 0));
+  const bool staged = !(nnz == (uint32_t)kSThreads && (npart == 0 || nfull == 0));
   if (staged) {
     if (nonzero) {
       const uint32_t idx = partial ? nfull + pfirst + lanes_below(mpart) : ffirst + lanes_below(mfull);
@@ -1137,7 +1146,7 @@ __global__ __launch_bounds__(kCThreads, kCWavesPerSimd) void size_kernel(const S
     __syncthreads();
   }
 
-  const uint32_t slot = staged ? (t + kCThreads - 64u * (blockIdx.x & (kCWaves - 1u))) & (kCThreads - 1) : t;
+  const uint32_t slot = staged ? (t + kSThreads - 64u * (blockIdx.x & (kSWaves - 1u))) & (kSThreads - 1) : t;
   const bool active = slot < nnz;
   if (__ballot(active) != 0) {
     if (staged) {
@@ -1174,7 +1183,7 @@ __global__ __launch_bounds__(kCThreads, kCWavesPerSimd) void size_kernel(const S
   if (t == 0 && out_bytes) {
     uint64_t sum = 0;
 #pragma unroll
-    for (int c = 0; c < kGroupChunks; ++c) sum += chunk_len[c];
+    for (int c = 0; c < kSGroupChunks; ++c) sum += chunk_len[c];
     atomicAdd((unsigned long long *)out_bytes, (unsigned long long)sum);
   }
 }
@@ -1209,7 +1218,7 @@ __global__ void store_size_init_kernel(const SBatch batch) {
 void size_plan(STensor &x) {
   x.nchunks = (x.raw_bytes + kChunkBytes - 1) / kChunkBytes;
   x.nsampled = (x.nchunks + x.stride - 1) / x.stride;
-  x.ngroups = (uint32_t)((x.nsampled + kGroupChunks - 1) / kGroupChunks);
+  x.ngroups = (uint32_t)((x.nsampled + kSGroupChunks - 1) / kSGroupChunks);
 }
 
 hipError_t launch_size(int w, const SBatch &batch, uint32_t codec_mask, int tagged, hipStream_t stream) {
@@ -1218,9 +1227,9 @@ hipError_t launch_size(int w, const SBatch &batch, uint32_t codec_mask, int tagg
   if (e != hipSuccess || batch.total_groups == 0) return e;
   const Mode mode = make_mode(w, codec_mask, tagged);
   if (w == 16)
-    hipLaunchKernelGGL(size_kernel<16>, dim3(batch.total_groups), dim3(kCThreads), 0, stream, batch, mode);
+    hipLaunchKernelGGL(size_kernel<16>, dim3(batch.total_groups), dim3(kSThreads), 0, stream, batch, mode);
   else
-    hipLaunchKernelGGL(size_kernel<32>, dim3(batch.total_groups), dim3(kCThreads), 0, stream, batch, mode);
+    hipLaunchKernelGGL(size_kernel<32>, dim3(batch.total_groups), dim3(kSThreads), 0, stream, batch, mode);
   return hipGetLastError();
 }
 
