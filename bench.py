@@ -320,7 +320,7 @@ def main():
 # The codecs of the paper's comparison (§V-A, Fig. 3) that are defined on the
 # pages, as (candidate mask, tagged, symbol width or None for the tensor's):
 # ZVC alone as in cDMA, BPC's DBX on every block, BX and ZBX alone, PlaneZip,
-# and PlaneZip on BF16 with 32-bit symbols as the original BPC codes blocks.
+# and PlaneZip on BF16 coded as 32-bit symbols (the width BPC itself uses).
 VARIANTS = {
     "ZVC": (0x01, False, None),
     "BPC (DBX on every block)": (0x02, False, None),

@@ -3,12 +3,13 @@
  *
  * The codec is the one of "PlaneZip: Lossless Bit-Plane Compression of
  * Training Activations Offloaded over PCIe" (arXiv:2610.25033), §III-A
- * "Codec" and its "Stream format" paragraph, and Fig. 2: every 128-byte block
- * of a tensor is read as N symbols of w bits, sized under four encodings
- * (ZVC, DBX, BX, ZBX) and as a raw block, and the smallest is kept under a
- * 3-bit tag; 32 blocks form a 4 KB chunk with a 16-bit size header, and a
- * chunk that would grow is stored raw. The exact bit layout (which the paper
- * leaves partly open) is the repository's FORMAT.md, version 1.
+ * "Codec" and its "Stream format" paragraph, and Fig. 2: a tensor is cut into
+ * 128-byte blocks of N w-bit symbols; each block is coded with whichever of
+ * ZVC, DBX, BX, ZBX or a verbatim copy is shortest, marked by a 3-bit tag;
+ * every 4 KB (32 blocks) is a chunk with a 16-bit length header, and a chunk
+ * whose coded form is not shorter than its raw bytes is kept uncompressed.
+ * The exact bit layout (which the paper leaves partly open) is the
+ * repository's FORMAT.md, version 1.
  *
  * Conventions for every entry point:
  *   - All data pointers are device pointers (hipMalloc'd memory or a torch
@@ -25,12 +26,23 @@
  *   - `stream` is a hipStream_t (NULL means the null stream). Every call only
  *     enqueues work and returns; results written to device memory are valid
  *     once the stream has been synchronized.
- *   - Errors that the host can see (bad arguments, a launch failure) are
- *     returned synchronously and nothing is enqueued. Errors that depend on the
- *     data (a corrupt stream) are written to device memory.
+ *   - Because that scratch is found by the stream handle and the look-back
+ *     bookkeeping is fixed when a call is enqueued, the compress and
+ *     decompress calls (single and batched) refuse, with
+ *     PZ_ERROR_INVALID_VALUE and nothing enqueued, hipStreamPerThread (one
+ *     handle for a different stream in every host thread) and a stream that
+ *     is being captured into a HIP graph (replays would reuse the captured
+ *     bookkeeping). Code under graph capture uses pz_compress_noalloc.
+ *   - Argument errors are returned synchronously, before anything is
+ *     enqueued. A call that needs several launches (a batch of more than 8
+ *     tensors, or empty tensors whose sizes are set by a small kernel) may
+ *     have enqueued its earlier launches when a later HIP call fails with
+ *     PZ_ERROR_HIP. Errors that depend on the data (a corrupt stream) are
+ *     written to device memory.
  *   - Calls on different streams are independent (each stream has its own
  *     scratch); apart from that scratch, the library keeps no state between
- *     calls. The calls are safe to make from several host threads.
+ *     calls. Calls on different streams may be made from several host
+ *     threads; calls that share a stream are ordered by it.
  */
 #ifndef PLANEZIP_H
 #define PLANEZIP_H
@@ -42,8 +54,8 @@
 extern "C" {
 #endif
 
-/* Element type of the tensor, as carried in the paper's copy descriptor
- * (§III-A: "The runtime passes the element type in the copy descriptor"). */
+/* Element type of the tensor. In the paper the copy descriptor carries it to
+ * the engine (§III-A). */
 typedef enum {
     PZ_DTYPE_BF16 = 0,
     PZ_DTYPE_FP32 = 1,
@@ -66,13 +78,14 @@ typedef enum {
 
 /* Allowed (dtype, elem_bits) pairs; elem_bits is the symbol width w:
  *   BF16 with 16 (the paper's w for BF16) or 32 (BPC's original width, the
- *   §V-A ablation); FP32 with 32; OTHER with 32 ("other types use w = 32").
+ *   §V-A ablation); FP32 with 32; OTHER with 32 (§III-A codes every
+ *   type other than BF16 and FP32 as 32-bit symbols).
  * Any other pair returns PZ_ERROR_INVALID_VALUE. */
 
 /* Exact size in bytes of the stream pz_compress would write for the same
  * input, computed without writing a stream — the paper's profiling-iteration
- * measurement (§III-B: the engine "compresses them into a scratch buffer and
- * discards the output"; the reported size is the sum of the chunk headers).
+ * measurement (§III-B: during profiling the engine codes each saved tensor
+ * only to learn its size, whose value is the sum of the chunk headers).
  *   d_src        raw tensor bytes, raw_bytes long (any length, including 0)
  *   d_out_bytes  one uint64: 2*chunks + sum of chunk payload lengths
  *   d_chunk_lens nullable; PZ_NUM_CHUNKS(raw_bytes) uint16 header values */
@@ -107,7 +120,7 @@ pz_status_t pz_decompress(const void *d_src, size_t comp_bytes, int dtype,
  * block carries the 3-bit tag and takes the smallest allowed candidate, equal
  * sizes to the lowest tag; with tagged = 0 the mask must hold exactly one
  * candidate, which every block uses, and no tag is written. In every mode a
- * chunk that would grow is stored raw (FORMAT.md §4). A stream must be
+ * chunk that does not shrink is kept raw (FORMAT.md §4). A stream must be
  * decompressed with the (codec_mask, tagged) pair it was compressed with;
  * a tagged decoder accepts any tag 0..4 whatever the mask. An empty mask,
  * bits above PZ_CODEC_ALL, or an untagged mask with more than one candidate
@@ -231,8 +244,9 @@ typedef struct pz_predictor pz_predictor_t;
 #define PZ_SIGNATURE(op_index, output_slot) \
     ((((uint64_t)(op_index)) << 16) | ((uint64_t)(output_slot) & 0xFFFFu))
 
-/* A table for up to `capacity` signatures ("a few hundred entries"); NULL for
- * a capacity of 0 or above 2^40, or when host memory runs out. */
+/* A table for up to `capacity` signatures (§III-B sizes it at a few hundred
+ * entries); NULL for a capacity of 0 or above 2^40, or when host memory runs
+ * out. */
 pz_predictor_t *pz_predictor_create(size_t capacity);
 void pz_predictor_destroy(pz_predictor_t *pred);
 
@@ -260,9 +274,9 @@ void pz_predictor_clear(pz_predictor_t *pred);
 
 /* Swap engine: the copy path of §III and Fig. 2. A swapped-out tensor is
  * compressed on the GPU into a device staging slot and its stream's exact
- * bytes are copied by DMA into fixed-size chunks of a pinned host pool ("On
- * the host, compressed tensors occupy fixed-size chunks of a pinned pool",
- * §III-A); swapping in copies the chunks back and decompresses them. The
+ * bytes are copied by DMA into equal-sized pieces of a pinned host pool (the
+ * host-side layout of §III-A); swapping in copies the pieces back and
+ * decompresses them. The
  * stream's length is known only after the compression has run, so a worker
  * thread of the engine waits for each compression, takes pool chunks and
  * issues the copies on the engine's device-to-host stream; pz_swap_out

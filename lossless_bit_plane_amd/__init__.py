@@ -2,8 +2,9 @@
 
 Thin Python binding of the C ABI in ``include/planezip.h``; PyTorch supplies
 device memory and streams. The codec is the one of the PlaneZip paper
-(§III-A, Fig. 2): per 128-byte block the smallest of ZVC, DBX, BX, ZBX and raw
-under a 3-bit tag, 4 KB chunks with 16-bit headers; bit layout FORMAT.md v1.
+(§III-A, Fig. 2): every 128-byte block takes the shortest of its ZVC, DBX, BX,
+ZBX and verbatim codings behind a 3-bit tag, and 4 KB chunks carry 16-bit
+length headers; bit layout FORMAT.md v1.
 The ``*_ex`` calls run the single-codec and reduced-candidate variants the
 paper compares PlaneZip with (§V-A, Fig. 3); ``pz_compressed_size_sampled``
 and the ``pz_predictor_*`` table are the runtime's size measurement and

@@ -12,9 +12,9 @@
 
 namespace {
 
-// Symbol width w for (dtype, elem_bits), or -1. PlaneZip paper §III-A: w is
-// 16 for BF16 and 32 for FP32 and every other type; BF16 may also use w = 32
-// (BPC's original width, §V-A).
+// Symbol width w for (dtype, elem_bits), or -1. PlaneZip paper §III-A: BF16
+// uses 16-bit symbols, FP32 and all other element types 32-bit ones; BF16 may
+// also be coded as 32-bit symbols (BPC's own width, §V-A).
 int symbol_width(int dtype, int elem_bits) {
   if (dtype == PZ_DTYPE_BF16 && (elem_bits == 16 || elem_bits == 32)) return elem_bits;
   if ((dtype == PZ_DTYPE_FP32 || dtype == PZ_DTYPE_OTHER) && elem_bits == 32) return 32;
@@ -119,6 +119,19 @@ hipError_t with_scratch(hipStream_t stream, const pz::ScratchNeed &need, F launc
   return e;
 }
 
+// The scratch cache identifies a stream by its handle, and its look-back
+// epochs and tile-counter bases are host values fixed when a call is
+// enqueued. So it serves only streams whose calls the stream itself orders
+// and that run once as enqueued: not hipStreamPerThread (one handle, a
+// different stream in every host thread), and not a stream under graph
+// capture (a replay would reuse the captured epoch and counter base).
+pz_status_t check_stream(hipStream_t s) {
+  if (s == hipStreamPerThread) return PZ_ERROR_INVALID_VALUE;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess) return PZ_ERROR_HIP;
+  return cs == hipStreamCaptureStatusNone ? PZ_SUCCESS : PZ_ERROR_INVALID_VALUE;
+}
+
 // Compress calls: every tensor is checked first (nothing is enqueued if one
 // fails); then tensors with chunks go out in launches of up to kMaxBatch,
 // and an empty tensor's size is set to 0.
@@ -136,6 +149,10 @@ pz_status_t compress_many(int dtype, int elem_bits, uint32_t codec_mask, int tag
   for (int i = 0; i < count; ++i)
     if (caps[i] < PZ_MAX_COMPRESSED_BYTES(raw[i])) return PZ_ERROR_INSUFFICIENT_BUFFER;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (count > 0) {
+    const pz_status_t st = check_stream(s);
+    if (st != PZ_SUCCESS) return st;
+  }
   int i = 0;
   while (i < count) {
     pz::CBatch b{};
@@ -185,6 +202,10 @@ pz_status_t decompress_many(int dtype, int elem_bits, uint32_t codec_mask, int t
   for (int i = 0; i < count; ++i)
     if (comp[i] < 2 * PZ_NUM_CHUNKS(raw[i])) return PZ_ERROR_CORRUPT_STREAM;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (count > 0) {
+    const pz_status_t st = check_stream(s);
+    if (st != PZ_SUCCESS) return st;
+  }
   int i = 0;
   while (i < count) {
     int idx[pz::kMaxBatch];

@@ -1,10 +1,11 @@
 // PlaneZip compression on gfx950.
 //
-// Method: PlaneZip paper, §III-A "Codec" and "Stream format", Fig. 2. Every
-// 128-byte block is read as N symbols of w bits (N = 64 for w = 16, 32 for
-// w = 32) and sized under ZVC, DBX, BX, ZBX and raw; the smallest is kept
-// under a 3-bit tag; 32 blocks form a chunk with a 16-bit header and a chunk
-// that would grow is stored raw. Bit layout: FORMAT.md version 1.
+// Method: PlaneZip paper, §III-A "Codec" and "Stream format", Fig. 2. A
+// 128-byte block holds N w-bit symbols (N = 64 for w = 16, 32 for w = 32);
+// its ZVC, DBX, BX, ZBX and verbatim encodings are sized and the shortest is
+// kept behind a 3-bit tag; each 32 blocks make a chunk with a 16-bit length
+// header, and a chunk that does not shrink is kept raw. Bit layout:
+// FORMAT.md version 1.
 //
 // Mapping to the hardware: one lane owns one 128-byte block, so a wave holds
 // two 4 KB chunks. A lane sizes the four plane encodings without transposing:

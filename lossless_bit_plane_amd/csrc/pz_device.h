@@ -48,7 +48,7 @@ constexpr uint64_t kBadChunk = ~0ull;
 // the candidates a block may use (bit t = tag t) and whether each block
 // carries the 3-bit tag. PlaneZip itself is {all five, tagged}; an untagged
 // mode has exactly one candidate and writes no tags. In every mode a chunk
-// that would grow is stored raw.
+// that does not shrink is kept raw.
 constexpr uint32_t kAllCodecs = 0x1Fu;
 struct Mode {
   uint32_t mask;    // allowed candidates

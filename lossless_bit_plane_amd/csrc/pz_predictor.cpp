@@ -1,8 +1,9 @@
 // Per-tensor compressibility predictor of the PlaneZip runtime (PlaneZip
 // paper, §III-B "Compressibility Predictor"; accuracy in §V-B and Table IV).
 //
-// A saved tensor is named by a signature: the position of its producing
-// operator in the repeating operator sequence and its output slot. The table
+// A saved tensor is named by a signature: where its producing operator sits
+// in the sequence that every training iteration repeats, and which of that
+// operator's outputs it is. The table
 // keeps, per signature, the last measurement (raw bytes, compressed bytes):
 // the size the engine reported for a swap, or a profiling-iteration
 // measurement such as pz_compressed_size or pz_compressed_size_sampled. A new

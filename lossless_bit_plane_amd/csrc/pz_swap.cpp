@@ -1,8 +1,8 @@
 // Swap engine: the copy path of the PlaneZip paper (§III, Fig. 2; the pinned
 // pool of §III-A "Stream format"). A swapped-out tensor is compressed on the
 // GPU into a device staging slot, and its stream's exact bytes go to host
-// memory by DMA, into fixed-size chunks of a pinned pool, so that streams of
-// any size never fragment the host allocator. Swapping in copies the chunks
+// memory by DMA, into equal-sized pieces of a pinned pool, so that streams of
+// any size never fragment the host allocator. Swapping in copies the pieces
 // back into a staging slot and decompresses them into the caller's tensor.
 //
 // The stream's length is known only once the compression has run, so a

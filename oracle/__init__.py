@@ -6,8 +6,8 @@ HIP library and its binding) must never import it.
 
 The C library follows the PlaneZip paper, §III-A ("Codec" and "Stream format")
 and Fig. 2; ``size_model`` is a second, independent implementation of the
-candidate sizes, as the paper's validation paragraph describes (a vectorized
-size model next to a bit-exact encoder and decoder).
+candidate sizes, as in the paper's validation (there, an array-based size
+calculation was checked against an exact encoder and decoder).
 """
 from __future__ import annotations
 

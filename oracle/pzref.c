@@ -8,8 +8,9 @@
  * Everything here is written for obviousness, not speed: bits are moved one
  * at a time, planes are built one bit at a time, and a block is encoded in all
  * five ways before the smallest is kept, exactly as the paper describes the
- * engine (PlaneZip paper, §III-A and Fig. 2: "encodes each 128 B block in four
- * ways in parallel and keeps the smallest output or the raw block").
+ * engine (PlaneZip paper, §III-A and Fig. 2: the engine tries all four
+ * encodings on every 128-byte block at once and keeps the shortest, or the
+ * block itself).
  * The bit layout is FORMAT.md version 1.
  */
 #include "pzref.h"
@@ -23,8 +24,8 @@
 #define BLOCKS_PER_CHUNK 32
 /* Largest candidate payload is DBX/ZBX at 16 + 17*65 bits; round up. */
 #define CAND_BUF_BYTES 256
-/* A chunk is coded in full before the raw decision (a chunk that would grow
- * is stored raw, §III-A), so the buffer holds 32 blocks of the largest
+/* A chunk is coded in full before the raw decision (a chunk that does not
+ * shrink is kept raw, §III-A), so the buffer holds 32 blocks of the largest
  * candidate plus its tag: with RAW allowed a block is at most 3 + 1024 bits,
  * but a mode without RAW (a single-codec variant) can reach
  * 3 + CAND_BUF_BYTES * 8 bits. */
@@ -261,7 +262,8 @@ static int decode_planes(bitreader *br, uint64_t *P, int K, int L, int R)
 /* The five candidates of §III-A.                                            */
 /* ------------------------------------------------------------------------ */
 
-/* ZVC: N-bit mask of non-zero symbols, then the non-zero symbols. */
+/* ZVC: an N-bit mask marking the symbols that are not zero, then those
+ * symbols in order. */
 static void encode_zvc(bitwriter *bw, const uint32_t *s, int w)
 {
     int n = 1024 / w;
@@ -301,8 +303,8 @@ static void encode_bx(bitwriter *bw, const uint32_t *s, int w)
     code_planes(bw, P, w, n, run_field_bits(w));
 }
 
-/* ZBX: N-bit zero mask, then BX over the non-zero symbols moved to the
- * front, so every plane is n bits wide. */
+/* ZBX: the same N-bit mask, then BX applied to the n non-zero symbols
+ * packed together, so every plane is n bits wide. */
 static void encode_zbx(bitwriter *bw, const uint32_t *s, int w)
 {
     int n = 1024 / w;
@@ -519,7 +521,7 @@ int64_t pzref_compress_chunk(const uint8_t *src, size_t raw_len, int w,
     }
     if (chunk.overflow) return -PZREF_ENOSPC;
 
-    /* Pad to a byte. A chunk that would grow is stored raw. */
+    /* Pad to a byte. A chunk that does not shrink is kept raw. */
     size_t coded = (size_t)((chunk.pos + 7) / 8);
     if (coded >= raw_len) {
         memcpy(payload, src, raw_len);

@@ -11,8 +11,8 @@ lengths that §III-A gives for BPC's prefix code:
 
 * 3 bits for a lone all-zero plane, 2+R bits for a run of them (R = log2 w,
   so 6 bits for w = 16 and 7 for w = 32);
-* 5 bits for an all-ones plane, or for a plane whose pre-XOR value is zero;
-* 5 bits plus a position for one 1 or two adjacent 1s;
+* 5 bits when the XORed plane is all ones or the plane before the XOR is 0;
+* 5 bits plus a position when the plane holds a single 1 or a 1-1 pair;
 * 1 bit plus the plane verbatim otherwise;
 
 with the readings of FORMAT.md (top plane kept, codes in top-down order,
@@ -105,7 +105,8 @@ def _sizes(s: np.ndarray, w: int) -> np.ndarray:
     full = np.ones((nb, N), bool)
     res[:, BX] = plane_code_bits(_bits(s, w), full, np.full(nb, N), R)
 
-    # DBX: base plus w+1 planes of the N-1 deltas in (w+1)-bit two's complement.
+    # DBX: the first symbol, then the w+1 planes of the N-1 neighbour
+    # differences written as (w+1)-bit two's complement numbers.
     d = (s[:, 1:] - s[:, :-1]) & ((1 << (w + 1)) - 1)
     res[:, DBX] = w + plane_code_bits(_bits(d, w + 1), np.ones((nb, N - 1), bool),
                                       np.full(nb, N - 1), R)

@@ -4,8 +4,8 @@ This module only makes inputs: it holds none of the codec's arithmetic, and
 both the CPU oracle's tests and the HIP path's tests and benchmark read their
 inputs from here, so that the two sides see the same bytes.
 
-The PlaneZip paper compresses activations captured from five models trained
-on real data (§IV "Tensor capture"); those captures are not available, so
+The PlaneZip paper's activations were recorded while five networks trained
+on real datasets (§IV "Tensor capture"); those captures are not available, so
 these generators stand in for them with the same shapes and the structure
 that matters to the codec: ReLU and causal-mask zeros, exponent bits shared
 between neighbours, dense near-incompressible normalised outputs, and

@@ -165,3 +165,18 @@ def test_noalloc_compress_rejects_on_host(lib):
     assert lib.pz_compress_noalloc(fake, 100, 0, 16, fake, 1000, fake + 4, None) == _lib.PZ_ERROR_INVALID_VALUE
     assert lib.pz_compress_noalloc(fake + 4, 100, 0, 16, fake, 1000, fake, None) == _lib.PZ_ERROR_INVALID_VALUE
     assert lib.pz_compress_noalloc(fake, 4097, 0, 16, fake, 4100, fake, None) == _lib.PZ_ERROR_INSUFFICIENT_BUFFER
+
+
+def test_stream_per_thread_is_refused_on_host(lib):
+    """The scratch cache is keyed by the stream handle, which hipStreamPerThread
+    does not identify: compress and decompress refuse it before touching the
+    device (hipStreamPerThread is the handle value 2)."""
+    from lossless_bit_plane_amd import _lib
+
+    fake, per_thread = 256, 2
+    assert lib.pz_compress(fake, 100, 0, 16, fake, 1000, fake, per_thread) == _lib.PZ_ERROR_INVALID_VALUE
+    assert lib.pz_decompress(fake, 1000, 0, 16, fake, 100, None, per_thread) == _lib.PZ_ERROR_INVALID_VALUE
+    srcs = (ctypes.c_void_p * 1)(fake)
+    sizes = (ctypes.c_size_t * 1)(100)
+    caps = (ctypes.c_size_t * 1)(1000)
+    assert lib.pz_compress_batch(1, srcs, sizes, 0, 16, srcs, caps, fake, per_thread) == _lib.PZ_ERROR_INVALID_VALUE

@@ -51,7 +51,7 @@ def _paper_values():
 def test_prefix_code_is_complete():
     lengths = [1, 2, 3, 5, 5, 5, 5]   # verbatim, run, lone zero, ones, pre-zero, pair, single
     assert sum(2.0 ** -n for n in lengths) == 1.0
-    # Run codes are 6 bits for w = 16 and 7 for w = 32 ("6 or 7 for a run").
+    # Run codes are 6 bits for w = 16 and 7 for w = 32 (§III-A).
     assert 2 + int(math.log2(16)) == 6 and 2 + int(math.log2(32)) == 7
 
 

@@ -37,7 +37,7 @@ def _chunked_tensor(kinds, tail_kind=None, tail_bytes=0, seed=0):
 def _closed_form_H(kind, raw_len):
     blocks = (raw_len + 127) // 128
     L = -(-9 * blocks // 8) if kind == ZERO else raw_len
-    return raw_len if L >= raw_len else L  # a chunk that would grow is stored raw
+    return raw_len if L >= raw_len else L  # a chunk that does not shrink is kept raw
 
 
 @pytest.mark.parametrize("tail_kind,tail_bytes", [(None, 0), (ZERO, 1000), (RANDOM, 1000), (ZERO, 1)])
