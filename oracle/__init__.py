@@ -18,6 +18,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libpzref.so")
+# A sanitizer build of the same source may be substituted (tests only).
+_LIB_PATH = os.environ.get("PZREF_LIB", _LIB_PATH)
 
 ZVC, DBX, BX, ZBX, RAW = 0, 1, 2, 3, 4
 CANDIDATES = ("ZVC", "DBX", "BX", "ZBX", "RAW")
