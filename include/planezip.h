@@ -75,6 +75,11 @@ typedef enum {
 #define PZ_NUM_CHUNKS(n) (((n) + 4095) / 4096)
 /* Worst case stream size: every chunk stored raw, plus its 2-byte header. */
 #define PZ_MAX_COMPRESSED_BYTES(n) (2 * PZ_NUM_CHUNKS(n) + (n))
+/* Largest raw tensor any call takes (512 GiB, above one GPU's memory): the
+ * device-wide prefix sums of chunk offsets carry 40-bit values. A larger
+ * raw_bytes (raw_bytes[i] in the batched calls) returns
+ * PZ_ERROR_INVALID_VALUE. */
+#define PZ_MAX_RAW_BYTES ((size_t)1 << 39)
 
 /* Allowed (dtype, elem_bits) pairs; elem_bits is the symbol width w:
  *   BF16 with 16 (the paper's w for BF16) or 32 (BPC's original width, the

@@ -15,6 +15,7 @@ PZ_ERROR_INSUFFICIENT_BUFFER = 2
 PZ_ERROR_CORRUPT_STREAM = 3
 PZ_ERROR_HIP = 4
 PZ_NOALLOC_MAX_BYTES = 1073545216
+PZ_MAX_RAW_BYTES = 1 << 39
 
 EXPORTS = ("pz_compressed_size", "pz_compress", "pz_decompress", "pz_block_sizes", "pz_status_string",
            "pz_compressed_size_ex", "pz_compress_ex", "pz_decompress_ex", "pz_compressed_size_sampled",

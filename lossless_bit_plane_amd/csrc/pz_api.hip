@@ -143,7 +143,7 @@ pz_status_t compress_many(int dtype, int elem_bits, uint32_t codec_mask, int tag
     return PZ_ERROR_INVALID_VALUE;
   if (count > 0 && (!srcs || !raw || !dsts || !caps || !d_out_bytes)) return PZ_ERROR_INVALID_VALUE;
   for (int i = 0; i < count; ++i) {
-    if (raw[i] && (!srcs[i] || !dsts[i])) return PZ_ERROR_INVALID_VALUE;
+    if ((raw[i] && (!srcs[i] || !dsts[i])) || raw[i] > PZ_MAX_RAW_BYTES) return PZ_ERROR_INVALID_VALUE;
     if (!aligned16(srcs[i]) || !aligned16(dsts[i])) return PZ_ERROR_INVALID_VALUE;
   }
   for (int i = 0; i < count; ++i)
@@ -196,7 +196,7 @@ pz_status_t decompress_many(int dtype, int elem_bits, uint32_t codec_mask, int t
     return PZ_ERROR_INVALID_VALUE;
   if (count > 0 && (!srcs || !comp || !dsts || !raw)) return PZ_ERROR_INVALID_VALUE;
   for (int i = 0; i < count; ++i) {
-    if ((comp[i] && !srcs[i]) || (raw[i] && !dsts[i])) return PZ_ERROR_INVALID_VALUE;
+    if ((comp[i] && !srcs[i]) || (raw[i] && !dsts[i]) || raw[i] > PZ_MAX_RAW_BYTES) return PZ_ERROR_INVALID_VALUE;
     if (!aligned16(srcs[i]) || !aligned16(dsts[i])) return PZ_ERROR_INVALID_VALUE;
   }
   for (int i = 0; i < count; ++i)
@@ -350,7 +350,8 @@ pz_status_t pz_compressed_size_ex(const void *d_src, size_t raw_bytes, int dtype
                                   uint32_t codec_mask, int tagged, uint64_t *d_out_bytes,
                                   uint16_t *d_chunk_lens, void *stream) {
   const int w = symbol_width(dtype, elem_bits);
-  if (w < 0 || !valid_mode(codec_mask, tagged) || !d_out_bytes || (raw_bytes && !d_src))
+  if (w < 0 || !valid_mode(codec_mask, tagged) || !d_out_bytes || (raw_bytes && !d_src) ||
+      raw_bytes > PZ_MAX_RAW_BYTES)
     return PZ_ERROR_INVALID_VALUE;
   if (!aligned16(d_src) || (reinterpret_cast<uintptr_t>(d_out_bytes) & 7u) ||
       (reinterpret_cast<uintptr_t>(d_chunk_lens) & 1u))
@@ -378,7 +379,8 @@ pz_status_t pz_compressed_size_sampled(const void *d_src, size_t raw_bytes, int 
                                        uint32_t chunk_stride, uint64_t *d_sample, uint16_t *d_sample_lens,
                                        void *stream) {
   const int w = symbol_width(dtype, elem_bits);
-  if (w < 0 || chunk_stride == 0 || !d_sample || (raw_bytes && !d_src)) return PZ_ERROR_INVALID_VALUE;
+  if (w < 0 || chunk_stride == 0 || !d_sample || (raw_bytes && !d_src) || raw_bytes > PZ_MAX_RAW_BYTES)
+    return PZ_ERROR_INVALID_VALUE;
   if (!aligned16(d_src) || (reinterpret_cast<uintptr_t>(d_sample) & 7u) ||
       (reinterpret_cast<uintptr_t>(d_sample_lens) & 1u))
     return PZ_ERROR_INVALID_VALUE;
@@ -403,7 +405,8 @@ pz_status_t pz_compressed_size_batch(int count, const void *const *d_srcs, const
   if (w < 0 || count < 0 || (reinterpret_cast<uintptr_t>(d_out_bytes) & 7u)) return PZ_ERROR_INVALID_VALUE;
   if (count > 0 && (!d_srcs || !raw_bytes || !d_out_bytes)) return PZ_ERROR_INVALID_VALUE;
   for (int i = 0; i < count; ++i) {
-    if ((raw_bytes[i] && !d_srcs[i]) || !aligned16(d_srcs[i])) return PZ_ERROR_INVALID_VALUE;
+    if ((raw_bytes[i] && !d_srcs[i]) || !aligned16(d_srcs[i]) || raw_bytes[i] > PZ_MAX_RAW_BYTES)
+      return PZ_ERROR_INVALID_VALUE;
     if (d_chunk_lens && (reinterpret_cast<uintptr_t>(d_chunk_lens[i]) & 1u)) return PZ_ERROR_INVALID_VALUE;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -429,7 +432,7 @@ pz_status_t pz_compressed_size_batch(int count, const void *const *d_srcs, const
 pz_status_t pz_block_sizes(const void *d_src, size_t raw_bytes, int dtype, int elem_bits,
                            uint16_t *d_sizes, uint8_t *d_tags, void *stream) {
   const int w = symbol_width(dtype, elem_bits);
-  if (w < 0 || (raw_bytes && !d_src)) return PZ_ERROR_INVALID_VALUE;
+  if (w < 0 || (raw_bytes && !d_src) || raw_bytes > PZ_MAX_RAW_BYTES) return PZ_ERROR_INVALID_VALUE;
   if (!aligned16(d_src) || (reinterpret_cast<uintptr_t>(d_sizes) & 1u)) return PZ_ERROR_INVALID_VALUE;
   return from_hip(pz::launch_block_sizes(w, static_cast<const uint8_t *>(d_src), raw_bytes, d_sizes, d_tags,
                                          static_cast<hipStream_t>(stream)));

@@ -556,7 +556,9 @@ __global__ __launch_bounds__(kGroupThreads) void decode_kernel(const DBatch batc
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const uint32_t ci = 2 * wave + (uint32_t)h;
-    const uint64_t coff = (uint64_t)__builtin_amdgcn_readlane((int)(uint32_t)my_coff, 32 * h) |
+    // Both halves zero-extended: readlane returns an int, and a sign-extended
+    // low half would corrupt every offset with bit 31 set.
+    const uint64_t coff = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)my_coff, 32 * h) |
                           ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(my_coff >> 32), 32 * h) << 32);
     const uint32_t H = (uint32_t)__builtin_amdgcn_readlane((int)my_H, 32 * h);
     const uint64_t q0 = (coff >> 2) & ~3ull;

@@ -284,3 +284,22 @@ def int64_indices(count: int) -> Tensor:
     type coded with 32-bit symbols."""
     a = np.arange(1, count + 1, dtype="<i8")
     return Tensor("int64_indices", a.view(np.uint8), OTHER, 32, (count,))
+
+
+def mixed_large(nbytes: int, seed: int = 12) -> Tensor:
+    """A BF16 tensor of any length (here: several GiB, so that its stream
+    passes 4 GiB) built from 32 KB tiles in runs of sixteen: twelve tiles of
+    uniform random bytes (chunks kept raw), one whose 128-byte blocks
+    alternate random and all-zero, one repeating a ReLU(N(0,1)) tile, one
+    all-zero and one zero in its first half. About 0.84 of the bytes stay
+    raw."""
+    rng = np.random.default_rng(seed)
+    data = rng.integers(0, 256, nbytes, dtype=np.uint8)
+    tile = 32768
+    rows = data[: (nbytes // tile) * tile].reshape(-1, tile)
+    relu = bf16_rne(np.maximum(rng.standard_normal(tile // 2, dtype=np.float32), np.float32(0)))
+    rows[12::16].reshape(-1, tile // 256, 256)[:, :, 128:] = 0
+    rows[13::16] = relu.view(np.uint8)
+    rows[14::16] = 0
+    rows[15::16, : tile // 2] = 0
+    return Tensor(f"mixed_{nbytes}B", data, BF16, 16, (nbytes,))

@@ -180,3 +180,26 @@ def test_stream_per_thread_is_refused_on_host(lib):
     sizes = (ctypes.c_size_t * 1)(100)
     caps = (ctypes.c_size_t * 1)(1000)
     assert lib.pz_compress_batch(1, srcs, sizes, 0, 16, srcs, caps, fake, per_thread) == _lib.PZ_ERROR_INVALID_VALUE
+
+
+def test_tensors_above_the_size_ceiling_are_refused_on_host(lib):
+    """Raw sizes above PZ_MAX_RAW_BYTES (the 40-bit range of the device-wide
+    offset sums, with room for the header table) are refused by every call
+    before it touches the device."""
+    from lossless_bit_plane_amd import _lib
+
+    fake = 256
+    big = _lib.PZ_MAX_RAW_BYTES + 4096
+    cap = 2 * ((big + 4095) // 4096) + big
+    inv = _lib.PZ_ERROR_INVALID_VALUE
+    assert lib.pz_compress(fake, big, 0, 16, fake, cap, fake, None) == inv
+    assert lib.pz_decompress(fake, cap, 0, 16, fake, big, None, None) == inv
+    assert lib.pz_compressed_size(fake, big, 0, 16, fake, None, None) == inv
+    assert lib.pz_compressed_size_sampled(fake, big, 0, 16, 4, fake, None, None) == inv
+    assert lib.pz_block_sizes(fake, big, 0, 16, fake, None, None) == inv
+    srcs = (ctypes.c_void_p * 2)(fake, fake)
+    sizes = (ctypes.c_size_t * 2)(100, big)
+    caps = (ctypes.c_size_t * 2)(1000, cap)
+    assert lib.pz_compress_batch(2, srcs, sizes, 0, 16, srcs, caps, fake, None) == inv
+    assert lib.pz_decompress_batch(2, srcs, caps, 0, 16, srcs, sizes, None, None) == inv
+    assert lib.pz_compressed_size_batch(2, srcs, sizes, 0, 16, fake, None, None) == inv
