@@ -20,6 +20,13 @@ dominant kernel's algorithmic HBM traffic (read raw + write compressed) per
 unit of its measured time against MI355X's 8 TB/s. The CPU baseline is the
 oracle (oracle/pzref.c) on the same tensors on this host's cores: chunk-
 parallel on the whole workload, and single-threaded on a bounded sample.
+
+Outside the timed regions the line also carries, per tensor, the encoder mix
+(blocks won by each candidate, the most frequent one, chunks stored raw: the
+'Top' column of the paper's Table III), the other four workloads' batched
+compress and decompress rates, HBM fractions and ratios (`configs`), and a
+byte-for-byte comparison of every GPU stream with the oracle's stream of the
+same tensor (`oracle_equal`, made in the CPU-baseline leg).
 """
 from __future__ import annotations
 
@@ -55,6 +62,8 @@ def parse():
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="run one plain device copy of this many MiB first (HBM counter calibration)")
     p.add_argument("--no-swap", action="store_true", help="skip the copy-path (swap) measurement")
+    p.add_argument("--headline-only", action="store_true",
+                   help="skip the rates, ratios and oracle checks of the other workloads")
     p.add_argument("--variants", action="store_true",
                    help="also time the codec variants the paper compares PlaneZip with (Fig. 3) "
                         "on the same tensors and report their ratios")
@@ -250,9 +259,6 @@ def main():
         "traffic_note": traffic_note,
     }
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(tensors, args.cpu_sample_mb)
     p10, p50, p90 = (float(x) for x in np.percentile(step_ms, [10, 50, 90]))
 
     per_tensor = {it["t"].name: {
@@ -260,7 +266,35 @@ def main():
         "ratio": round(it["t"].nbytes / it["comp"], 4),
         "compress_raw_gbps": round(it["t"].nbytes / t_comp[i] / 1e9, 1),
         "decompress_raw_gbps": round(it["t"].nbytes / t_dec[i] / 1e9, 1),
+        **block_stats(pz, it),
     } for i, it in enumerate(items)}
+    # The GPU streams, on the host, for the byte-for-byte check against the
+    # oracle's streams (outside every timed region).
+    gpu_streams = {it["t"].name: it["stream"][:it["comp"]].cpu().numpy() for it in items}
+
+    # The other workloads: batched compress and decompress rates, ratios and
+    # block statistics (their streams are checked against the oracle below).
+    configs = {}
+    other_streams = {}
+    if not args.headline_only:
+        for name in WORKLOAD_NAMES:
+            if name != args.workload:
+                configs[name], other_streams[name] = measure_config(pz, pzinputs, name, flush, cur)
+
+    cpu = None
+    oracle_equal = None
+    if not args.no_cpu_baseline:
+        cpu, oracle_equal = cpu_baseline(tensors, args.cpu_sample_mb, gpu_streams)
+        for name, (tens, streams) in other_streams.items():
+            eq = oracle_check(tens, streams)
+            configs[name]["oracle_equal"] = all(eq.values())
+            for tname, ok in eq.items():
+                configs[name]["tensors"][tname]["oracle_equal"] = ok
+        for tname, ok in oracle_equal.items():
+            per_tensor[tname]["oracle_equal"] = ok
+        if not all(oracle_equal.values()) or not all(c["oracle_equal"] for c in configs.values()):
+            log("GPU stream differs from the oracle's stream")
+    other_streams.clear()
 
     variants = measure_variants(pz, items, flush, cur) if args.variants else None
     size_only = measure_size_only(pz, items, flush, cur)
@@ -308,13 +342,125 @@ def main():
         "roofline": roofline,
         "per_call": per_call,
         "cpu_baseline": cpu,
+        "oracle_equal": None if oracle_equal is None else (
+            all(oracle_equal.values()) and all(c["oracle_equal"] for c in configs.values())),
         "tensors": per_tensor,
+        "configs": configs,
         "size_only": size_only,
         "swap": swap,
     }
     if variants is not None:
         out["variants"] = variants
     print(json.dumps(out), flush=True)
+
+
+TAG_NAMES = ("ZVC", "DBX", "BX", "ZBX", "RAW")  # tags 0..4
+
+
+def block_stats(pz, it):
+    """A tensor's encoder mix (the 'Top' column of PlaneZip's Table III):
+    the blocks each candidate wins (pz_block_sizes, the compressor's own
+    choice per block), the most frequent one, and the chunks stored raw
+    (header value equal to the chunk's length)."""
+    import torch
+
+    t = it["t"]
+    _, tags = pz.pz_block_sizes(it["src"], t.dtype, t.elem_bits)
+    hist = torch.bincount(tags.long(), minlength=5)[:5].tolist()
+    C = pz.num_chunks(t.nbytes)
+    H = it["stream"][:2 * C].view(torch.int16).to(torch.int32) & 0xFFFF
+    raw_len = torch.full((C,), 4096, dtype=torch.int32, device=H.device)
+    raw_len[-1] = t.nbytes - 4096 * (C - 1)
+    raw_chunks = int((H == raw_len).sum().item())
+    total = max(1, sum(hist))
+    return {
+        "block_tags": {n: int(c) for n, c in zip(TAG_NAMES, hist)},
+        "block_tag_share": {n: round(c / total, 4) for n, c in zip(TAG_NAMES, hist)},
+        "top": TAG_NAMES[int(np.argmax(hist))],
+        "chunks": C,
+        "raw_chunks": raw_chunks,
+    }
+
+
+def measure_config(pz, pzinputs, name, flush, cur, reps=5):
+    """One workload's batched compress and decompress (one call per
+    direction and (dtype, width) group, as in the headline step): raw GB/s
+    and fraction of HBM peak of the algorithmic bytes (read raw + write
+    stream, or the reverse), median of `reps` after a cache flush each; the
+    ratio and block statistics per tensor; round trip checked on the device.
+    Returns (result, (tensors, host copies of the GPU streams))."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    tensors = pzinputs.workload(name)
+    items = []
+    for t in tensors:
+        items.append(dict(t=t, src=torch.from_numpy(t.data).to(dev),
+                          stream=torch.empty(max(16, pz.max_compressed_bytes(t.nbytes)), dtype=torch.uint8,
+                                             device=dev),
+                          out=torch.empty(max(16, t.nbytes), dtype=torch.uint8, device=dev)))
+    groups = {}
+    for it in items:
+        groups.setdefault((it["t"].dtype, it["t"].elem_bits), []).append(it)
+    outs = {k: torch.zeros(len(g), dtype=torch.int64, device=dev) for k, g in groups.items()}
+    stats = {k: torch.zeros(len(g), dtype=torch.int32, device=dev) for k, g in groups.items()}
+    for k, g in groups.items():
+        pz.pz_compress_batch([it["src"] for it in g], k[0], k[1], [it["stream"] for it in g], outs[k])
+    torch.cuda.synchronize()
+    for k, g in groups.items():
+        for it, m in zip(g, outs[k].tolist()):
+            it["comp"] = int(m)
+
+    def compress():
+        for k, g in groups.items():
+            pz.pz_compress_batch([it["src"] for it in g], k[0], k[1], [it["stream"] for it in g], outs[k])
+
+    def decompress():
+        for k, g in groups.items():
+            pz.pz_decompress_batch([it["stream"] for it in g], [it["comp"] for it in g],
+                                   [it["t"].nbytes for it in g], k[0], k[1], [it["out"] for it in g], stats[k])
+
+    def timed(fn):
+        ts = []
+        for _ in range(reps):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            torch.cuda.synchronize()
+            flush()
+            e[0].record(cur)
+            fn()
+            e[1].record(cur)
+            torch.cuda.synchronize()
+            ts.append(e[0].elapsed_time(e[1]) / 1e3)
+        return float(np.median(ts))
+
+    t_c, t_d = timed(compress), timed(decompress)
+    for k, g in groups.items():
+        assert [int(v) for v in outs[k].tolist()] == [it["comp"] for it in g], f"{name}: unstable stream length"
+        assert not stats[k].any().item(), f"{name}: decompress reported a corrupt stream"
+        for it in g:
+            assert torch.equal(it["out"][:it["t"].nbytes], it["src"]), f"{name}: round trip on {it['t'].name}"
+    raw = sum(it["t"].nbytes for it in items)
+    comp = sum(it["comp"] for it in items)
+    res = {
+        "workload": WORKLOADS[name],
+        "raw_bytes": raw, "compressed_bytes": comp, "ratio": round(raw / comp, 4),
+        "compress_raw_gbps": round(raw / t_c / 1e9, 1),
+        "decompress_raw_gbps": round(raw / t_d / 1e9, 1),
+        "compress_hbm_frac": round((raw + comp) / t_c / 1e9 / HBM_PEAK_GBPS, 4),
+        "decompress_hbm_frac": round((raw + comp) / t_d / 1e9 / HBM_PEAK_GBPS, 4),
+        "us": {"compress": round(t_c * 1e6, 1), "decompress": round(t_d * 1e6, 1)},
+        "launches": f"{len(groups)} pz_compress_batch + {len(groups)} pz_decompress_batch call(s)",
+        "tensors": {it["t"].name: {"raw_bytes": it["t"].nbytes, "compressed_bytes": it["comp"],
+                                   "ratio": round(it["t"].nbytes / it["comp"], 4), **block_stats(pz, it)}
+                    for it in items},
+        "oracle_equal": None,
+    }
+    log(f"config {name}: ratio {raw / comp:.3f}, compress {raw / t_c / 1e9:.0f} GB/s, "
+        f"decompress {raw / t_d / 1e9:.0f} GB/s")
+    streams = {it["t"].name: it["stream"][:it["comp"]].cpu().numpy() for it in items}
+    del items
+    torch.cuda.empty_cache()
+    return res, (tensors, streams)
 
 
 # The codecs of the paper's comparison (§V-A, Fig. 3) that are defined on the
@@ -589,14 +735,37 @@ def measured_traffic(kernel, launch_names):
     return round(total), "profiles/hbm_traffic_gpt2xl_activations.json (the batched launch)"
 
 
-def cpu_baseline(tensors, sample_mb):
-    """The oracle, as it stands: chunk-parallel over the host cores on the
+def host_threads():
+    """Threads for the oracle: the job's CPU share where the host declares
+    one (OMP_NUM_THREADS), else every core of this process's affinity mask;
+    with the facts to report next to it."""
+    affinity = len(os.sched_getaffinity(0))
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    threads = min(affinity, int(share)) if share.isdigit() and int(share) > 0 else affinity
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return threads, {"nproc": affinity, "os_cpu_count": os.cpu_count(), "cpu_model": model,
+                     "omp_num_threads": share or None}
+
+
+def cpu_baseline(tensors, sample_mb, gpu_streams):
+    """The oracle, as it stands: chunk-parallel over the host threads on the
     whole workload (the reported value), and single-threaded on the same
     fraction of whole chunks from the start of every tensor (a bounded
-    sample); compress then decompress, round trip checked."""
+    sample); compress then decompress, round trip checked. The oracle's
+    streams of the whole workload are compared byte for byte with the GPU's
+    (`gpu_streams`, by tensor name). Returns (baseline, equal by tensor)."""
     import oracle
 
-    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    threads, host = host_threads()
+    equal = {}
 
     def run(frac, nthreads):
         raw = 0
@@ -610,6 +779,8 @@ def cpu_baseline(tensors, sample_mb):
             back = oracle.decompress(s, n, t.elem_bits, threads=nthreads)
             c = time.perf_counter()
             assert np.array_equal(back, part)
+            if frac >= 1.0:
+                equal[t.name] = bool(np.array_equal(s, gpu_streams[t.name]))
             raw += n
             t_c += b - a
             t_d += c - b
@@ -618,7 +789,7 @@ def cpu_baseline(tensors, sample_mb):
     total = sum(t.nbytes for t in tensors)
     raw, t_c, t_d = run(1.0, threads)
     log(f"cpu baseline: whole workload {raw / 1e6:.1f} MB, {threads} threads, "
-        f"compress {t_c:.2f}s decompress {t_d:.2f}s")
+        f"compress {t_c:.2f}s decompress {t_d:.2f}s; GPU streams equal to the oracle's: {equal}")
     frac1 = min(1.0, sample_mb * 1e6 / total)
     raw1, c1, d1 = run(frac1, 1)
     log(f"cpu baseline: {raw1 / 1e6:.1f} MB sample, 1 thread, compress {c1:.2f}s decompress {d1:.2f}s")
@@ -629,12 +800,25 @@ def cpu_baseline(tensors, sample_mb):
         "kind": "oracle",
         "sample": f"the whole workload ({raw / 1e6:.1f} MB), chunk-parallel on {threads} threads; "
                   f"compress {raw / t_c / 1e6:.1f} MB/s, decompress {raw / t_d / 1e6:.1f} MB/s",
+        "host": host,
         "single_thread": {
             "value": round(raw1 / (c1 + d1) / 1e9, 5), "unit": "GB/s", "cores": 1,
             "sample": f"first {frac1 * 100:.1f}% (whole chunks) of each tensor, {raw1 / 1e6:.1f} MB; "
                       f"compress {raw1 / c1 / 1e6:.2f} MB/s, decompress {raw1 / d1 / 1e6:.2f} MB/s",
         },
-    }
+    }, equal
+
+
+def oracle_check(tensors, gpu_streams):
+    """Byte-for-byte equality of the GPU streams with the oracle's streams of
+    the same tensors (chunk-parallel oracle, host threads), by tensor name."""
+    import oracle
+
+    threads, _ = host_threads()
+    eq = {t.name: bool(np.array_equal(oracle.compress(t.data, t.elem_bits, threads=threads), gpu_streams[t.name]))
+          for t in tensors}
+    log(f"oracle check: {eq}")
+    return eq
 
 
 if __name__ == "__main__":

@@ -45,3 +45,28 @@ def test_measured_traffic_never_raises(tmp_path, monkeypatch):
     assert bench.measured_traffic("compress_kernel<16>", names)[0] == 45
     assert bench.measured_traffic("compress_kernel<16>", [bench.batch_name(names)])[0] == 27
     assert bench.measured_traffic("compress_kernel<16>", [bench.batch_name(names[:2])])[0] is None
+
+
+def test_host_threads_follow_the_declared_share(monkeypatch):
+    n = len(os.sched_getaffinity(0))
+    monkeypatch.setenv("OMP_NUM_THREADS", "1")
+    assert bench.host_threads()[0] == 1
+    monkeypatch.delenv("OMP_NUM_THREADS")
+    threads, host = bench.host_threads()
+    assert threads == n and host["nproc"] == n and host["cpu_model"]
+
+
+def test_cpu_baseline_compares_gpu_streams_with_the_oracle():
+    import oracle
+    import pzinputs
+
+    (smoke,) = pzinputs.relu_smoke()
+    t = pzinputs.Tensor("x", smoke.data[:50000].copy(), 0, 16)
+    good = oracle.compress(t.data, 16)
+    bad = good.copy()
+    bad[-1] ^= 1
+    res, eq = bench.cpu_baseline([t], 0.01, {"x": good})
+    assert eq == {"x": True} and res["kind"] == "oracle" and res["cores"] >= 1
+    assert bench.cpu_baseline([t], 0.01, {"x": bad})[1] == {"x": False}
+    assert bench.oracle_check([t], {"x": good}) == {"x": True}
+    assert bench.oracle_check([t], {"x": bad[:-1]}) == {"x": False}
