@@ -73,13 +73,21 @@ inline DMode make_dmode(int W, uint32_t mask, int tagged) {
 constexpr int kLocateChunks = 64;  // chunks per tile (per workgroup)
 constexpr int kLocateLanes = 4;    // lanes per chunk
 constexpr int kLocateThreads = kLocateChunks * kLocateLanes;
-// Per-chunk LDS region: a 128-dword ring of the chunk's stream, one mirror
-// dword (slot 128 = slot 0, so a peek at slot 127 reads two dwords), then the
-// chunk's 32 block offsets (16-bit). 145 dwords: odd, spreads chunks over banks.
+// Per-chunk LDS region: a ring of kRingDwords dwords of the chunk's stream, one
+// mirror dword (slot kRingDwords = slot 0, so a peek at the last slot reads two
+// dwords), then the chunk's 32 block offsets (16-bit). 145 dwords: odd, spreads
+// chunks over banks. (A 64-dword ring with 16-dword refills fits twice the
+// chunks per compute unit but measured slower on every workload: the walk then
+// waits on its refills.)
 constexpr int kRingDwords = 128;
 constexpr int kRingRegion = kRingDwords + 1 + 16;
 constexpr uint32_t kBlockAhead = 38;   // dwords one block (and its look-ahead) can touch
-constexpr uint32_t kGroupDwords = 32;  // refill unit, split over the G lanes
+constexpr uint32_t kGroupDwords = kRingDwords / 4;  // refill unit, split over the G lanes
+constexpr int kStartGroups = (int)((kBlockAhead + kGroupDwords - 1) / kGroupDwords);
+// A refill made while a group is short (fill < cur + kBlockAhead) and the
+// request made after the first groups must not overwrite dwords at or above cur.
+static_assert(kBlockAhead - 1 + kGroupDwords <= (uint32_t)kRingDwords, "refill fits in the ring");
+static_assert((kStartGroups + 1) * kGroupDwords <= (uint32_t)kRingDwords, "start fits in the ring");
 
 // One of four values by the two low bits of k, as bit-tested selects (an
 // equality chain would be turned into branches).
@@ -125,7 +133,7 @@ struct ChunkRing {
   uint64_t q0;      // absolute dword index of relative dword 0 (16-byte aligned)
   uint32_t lead;    // bit offset of the chunk payload within relative dword 0
   uint32_t ql;      // lane within the group
-  uint32_t fill;    // relative dwords below fill have been stored (the last 128 are kept)
+  uint32_t fill;    // relative dwords below fill have been stored (the last kRingDwords are kept)
   bool pending;     // g holds relative dwords [fill + kPart ql, +kPart)
   uint4 g[kPart / 4];
 
@@ -150,7 +158,7 @@ struct ChunkRing {
     for (int k = 0; k < kPart / 4; ++k) g[k] = load4(fill + kPart * ql + 4 * k);
     pending = true;
   }
-  // Stores the in-flight group at fill (slots fill % 128 .. +31: never wraps).
+  // Stores the in-flight group at fill (slots fill % kRingDwords, + kGroupDwords: never wraps).
   PZ_DEV void commit() {
     uint32_t *r = ring + (fill & (kRingDwords - 1)) + kPart * ql;
 #pragma unroll
@@ -171,22 +179,25 @@ struct ChunkRing {
     ql = lane_in_group;
     q0 = (payload_off >> 2) & ~3ull;
     lead = (uint32_t)(8 * (payload_off - 4 * q0));
-    // The first two groups in one round trip, then the third requested.
-    uint4 first[kPart / 4];
+    // The groups one block needs in one round trip, then the next requested.
+    uint4 first[kStartGroups][kPart / 4];
 #pragma unroll
-    for (int k = 0; k < kPart / 4; ++k) first[k] = load4(kPart * ql + 4 * k);
-    fill = kGroupDwords;
-    issue();
-    uint32_t *w = ring + kPart * ql;
+    for (int s = 0; s < kStartGroups; ++s)
 #pragma unroll
-    for (int k = 0; k < kPart / 4; ++k) {
-      w[4 * k + 0] = first[k].x;
-      w[4 * k + 1] = first[k].y;
-      w[4 * k + 2] = first[k].z;
-      w[4 * k + 3] = first[k].w;
+      for (int k = 0; k < kPart / 4; ++k) first[s][k] = load4(s * kGroupDwords + kPart * ql + 4 * k);
+#pragma unroll
+    for (int s = 0; s < kStartGroups; ++s) {
+      uint32_t *w = ring + s * kGroupDwords + kPart * ql;
+#pragma unroll
+      for (int k = 0; k < kPart / 4; ++k) {
+        w[4 * k + 0] = first[s][k].x;
+        w[4 * k + 1] = first[s][k].y;
+        w[4 * k + 2] = first[s][k].z;
+        w[4 * k + 3] = first[s][k].w;
+      }
     }
-    if (ql == 0) ring[kRingDwords] = first[0].x;  // mirror of slot 0
-    commit();
+    if (ql == 0) ring[kRingDwords] = first[0][0].x;  // mirror of slot 0
+    fill = kStartGroups * kGroupDwords;
     issue();
   }
   // At a block start whose first bit is pos (group-uniform): makes relative
@@ -490,22 +501,24 @@ PZ_DEV void read_planes(const LdsBits &in, uint32_t &pos, uint32_t (&t)[32], int
 // decoders. Decoded blocks are gathered in LDS rows (stride 33 dwords, which
 // keeps lane-strided row access conflict free) over the dead payloads, and
 // the group's 32 KB of output leaves in coalesced 16-byte stores.
-constexpr int kDecodeChunks = kGroupThreads / kBlocksPerChunk;  // 8
+constexpr int kDecWaves = 4;  // waves per workgroup
+constexpr int kDecThreads = kWave * kDecWaves;
+constexpr int kDecodeChunks = kDecThreads / kBlocksPerChunk;  // 8
 constexpr int kDecodeBufDwords = kDecodeChunks * kChunkBufDwords;
-constexpr int kDecodeRowDwords = kGroupThreads * kLaneStride;
+constexpr int kDecodeRowDwords = kDecThreads * kLaneStride;
 constexpr int kDecodeLdsDwords =
     kDecodeBufDwords > kDecodeRowDwords ? kDecodeBufDwords : kDecodeRowDwords;
 
 template <int W>
-__global__ __launch_bounds__(kGroupThreads) void decode_kernel(const DBatch batch, const uint32_t *err_words,
+__global__ __launch_bounds__(kDecThreads) void decode_kernel(const DBatch batch, const uint32_t *err_words,
                                                                uint32_t epoch, DMode mode) {
   constexpr int N = 1024 / W;
   constexpr uint32_t WMASK = W == 16 ? 0xFFFFu : 0xFFFFFFFFu;
   __shared__ __attribute__((aligned(16))) uint32_t lds[kDecodeLdsDwords];
-  __shared__ uint32_t blk_info[kGroupThreads];    // per packed block: bit position | tag << 16 | raw << 19
-  __shared__ uint8_t slot_block[kGroupThreads];   // packed slot -> block of the group
+  __shared__ uint32_t blk_info[kDecThreads];    // per packed block: bit position | tag << 16 | raw << 19
+  __shared__ uint8_t slot_block[kDecThreads];   // packed slot -> block of the group
   __shared__ uint32_t chunk_lead[kDecodeChunks];  // bit offset of each payload in its buffer
-  __shared__ uint32_t wave_busy[kWavesPerGroup];
+  __shared__ uint32_t wave_busy[kDecWaves];
 
   const uint32_t t = threadIdx.x, lane = lane_id();
   const uint32_t wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -529,7 +542,7 @@ __global__ __launch_bounds__(kGroupThreads) void decode_kernel(const DBatch batc
   // corrupt stream with the call's epoch.
   if (gtile == 0 && t == 0 && status)
     *status = __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch ? kStatusCorrupt : 0;
-  const uint64_t gblock0 = gtile * kGroupThreads;  // first block of the group
+  const uint64_t gblock0 = gtile * kDecThreads;  // first block of the group
 
   // Every thread's metadata at once: its chunk's payload offset and header
   // and its block's bit offset, so that the staging below waits for one
@@ -631,7 +644,7 @@ __global__ __launch_bounds__(kGroupThreads) void decode_kernel(const DBatch batc
   __syncthreads();
   uint32_t nbusy = 0, first = 0;
 #pragma unroll
-  for (int k = 0; k < kWavesPerGroup; ++k) {
+  for (int k = 0; k < kDecWaves; ++k) {
     const uint32_t c = wave_busy[k];
     first += (uint32_t)k < wave ? c : 0u;
     nbusy += c;
@@ -642,7 +655,7 @@ __global__ __launch_bounds__(kGroupThreads) void decode_kernel(const DBatch batc
   // --- 3. Packed slots: raw copy, ZVC or plane decoding into d. Waves take the
   // slots in an order rotated per tile, so that the busy waves of successive
   // groups fall on different SIMDs. ---
-  const uint32_t slot = (t + kGroupThreads - 64u * (uint32_t)(gtile & 3)) & (kGroupThreads - 1);
+  const uint32_t slot = (t + kDecThreads - 64u * (uint32_t)(gtile & (kDecWaves - 1))) & (kDecThreads - 1);
   const bool active = slot < nbusy;
   const bool wave_active = __ballot(active) != 0;
   uint32_t sb = 0;
@@ -798,11 +811,11 @@ __global__ __launch_bounds__(kGroupThreads) void decode_kernel(const DBatch batc
   // --- 5. Coalesced store of the group's output span (bytes past raw_bytes
   // are not written). ---
   const uint64_t span0 = gblock0 * kBlockBytes;
-  const uint64_t span_end = min_u64(raw_bytes, span0 + (uint64_t)kGroupThreads * kBlockBytes);
+  const uint64_t span_end = min_u64(raw_bytes, span0 + (uint64_t)kDecThreads * kBlockBytes);
   const uint32_t span = (uint32_t)(span_end - span0);
 #pragma unroll
   for (int k = 0; k < kBlocksPerChunk / 4; ++k) {
-    const uint32_t u = t + (uint32_t)k * kGroupThreads;  // 16-byte unit of the span
+    const uint32_t u = t + (uint32_t)k * kDecThreads;  // 16-byte unit of the span
     const uint32_t b0 = 16 * u;
     if (b0 >= span) continue;
     const uint32_t *row = lds + (u >> 3) * kLaneStride + 4 * (u & 7);
@@ -866,10 +879,10 @@ hipError_t launch_decompress(int w, DBatch &batch, uint32_t codec_mask, int tagg
   if (e != hipSuccess) return e;
   const dim3 grid_b(batch.total_groups);
   if (w == 16)
-    hipLaunchKernelGGL(decode_kernel<16>, grid_b, dim3(kGroupThreads), 0, stream, batch, scratch.err,
+    hipLaunchKernelGGL(decode_kernel<16>, grid_b, dim3(kDecThreads), 0, stream, batch, scratch.err,
                        scratch.epoch, mode);
   else
-    hipLaunchKernelGGL(decode_kernel<32>, grid_b, dim3(kGroupThreads), 0, stream, batch, scratch.err,
+    hipLaunchKernelGGL(decode_kernel<32>, grid_b, dim3(kDecThreads), 0, stream, batch, scratch.err,
                        scratch.epoch, mode);
   return hipGetLastError();
 }
