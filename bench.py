@@ -110,6 +110,8 @@ def main():
     tensors = pzinputs.workload(args.workload)
     log(f"generated workload {args.workload} in {time.time() - t0:.1f}s: "
         + ", ".join(f"{t.name} {t.nbytes / 1e6:.1f} MB" for t in tensors))
+    inputs_ok = input_check(args.workload, tensors)
+    log(f"inputs against the SHA-256 manifest: {inputs_ok}")
 
     # Device buffers, allocated once.
     items = []
@@ -267,6 +269,7 @@ def main():
         "compress_raw_gbps": round(it["t"].nbytes / t_comp[i] / 1e9, 1),
         "decompress_raw_gbps": round(it["t"].nbytes / t_dec[i] / 1e9, 1),
         **block_stats(pz, it),
+        "input_sha256_ok": inputs_ok[it["t"].name],
     } for i, it in enumerate(items)}
     # The GPU streams, on the host, for the byte-for-byte check against the
     # oracle's streams (outside every timed region).
@@ -286,8 +289,9 @@ def main():
     if not args.no_cpu_baseline:
         cpu, oracle_equal = cpu_baseline(tensors, args.cpu_sample_mb, gpu_streams)
         for name, (tens, streams) in other_streams.items():
-            eq = oracle_check(tens, streams)
+            eq, rates = oracle_check(tens, streams)
             configs[name]["oracle_equal"] = all(eq.values())
+            configs[name]["cpu_oracle"] = rates
             for tname, ok in eq.items():
                 configs[name]["tensors"][tname]["oracle_equal"] = ok
         for tname, ok in oracle_equal.items():
@@ -355,6 +359,25 @@ def main():
 
 
 TAG_NAMES = ("ZVC", "DBX", "BX", "ZBX", "RAW")  # tags 0..4
+MANIFEST = os.path.join(ROOT, "tests", "golden", "input_sha256.txt")
+
+
+def input_check(workload, tensors):
+    """SHA-256 of each input tensor against the committed manifest
+    (tests/golden/input_sha256.txt): True / False by tensor name, None for a
+    tensor the manifest does not list."""
+    known = {}
+    if os.path.exists(MANIFEST):
+        with open(MANIFEST) as f:
+            for line in f:
+                if line.strip() and not line.startswith("#"):
+                    w, name, nbytes, digest = line.split()
+                    known[(w, name)] = (int(nbytes), digest)
+    out = {}
+    for t in tensors:
+        k = known.get((workload, t.name))
+        out[t.name] = None if k is None else (k[0] == t.nbytes and k[1] == t.sha256())
+    return out
 
 
 def block_stats(pz, it):
@@ -382,7 +405,7 @@ def block_stats(pz, it):
     }
 
 
-def measure_config(pz, pzinputs, name, flush, cur, reps=5):
+def measure_config(pz, pzinputs, name, flush, cur, reps=20, warmup=3):
     """One workload's batched compress and decompress (one call per
     direction and (dtype, width) group, as in the headline step): raw GB/s
     and fraction of HBM peak of the algorithmic bytes (read raw + write
@@ -393,6 +416,7 @@ def measure_config(pz, pzinputs, name, flush, cur, reps=5):
 
     dev = torch.device("cuda:0")
     tensors = pzinputs.workload(name)
+    inputs_ok = input_check(name, tensors)
     items = []
     for t in tensors:
         items.append(dict(t=t, src=torch.from_numpy(t.data).to(dev),
@@ -421,6 +445,8 @@ def measure_config(pz, pzinputs, name, flush, cur, reps=5):
                                    [it["t"].nbytes for it in g], k[0], k[1], [it["out"] for it in g], stats[k])
 
     def timed(fn):
+        for _ in range(warmup):
+            fn()
         ts = []
         for _ in range(reps):
             e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
@@ -431,9 +457,10 @@ def measure_config(pz, pzinputs, name, flush, cur, reps=5):
             e[1].record(cur)
             torch.cuda.synchronize()
             ts.append(e[0].elapsed_time(e[1]) / 1e3)
-        return float(np.median(ts))
+        return np.array(ts)
 
-    t_c, t_d = timed(compress), timed(decompress)
+    ts_c, ts_d = timed(compress), timed(decompress)
+    t_c, t_d = float(np.median(ts_c)), float(np.median(ts_d))
     for k, g in groups.items():
         assert [int(v) for v in outs[k].tolist()] == [it["comp"] for it in g], f"{name}: unstable stream length"
         assert not stats[k].any().item(), f"{name}: decompress reported a corrupt stream"
@@ -448,10 +475,14 @@ def measure_config(pz, pzinputs, name, flush, cur, reps=5):
         "decompress_raw_gbps": round(raw / t_d / 1e9, 1),
         "compress_hbm_frac": round((raw + comp) / t_c / 1e9 / HBM_PEAK_GBPS, 4),
         "decompress_hbm_frac": round((raw + comp) / t_d / 1e9 / HBM_PEAK_GBPS, 4),
-        "us": {"compress": round(t_c * 1e6, 1), "decompress": round(t_d * 1e6, 1)},
+        "us": {d: {"median": round(float(np.median(v)) * 1e6, 1), "p10": round(float(np.percentile(v, 10)) * 1e6, 1),
+                   "p90": round(float(np.percentile(v, 90)) * 1e6, 1)}
+               for d, v in (("compress", ts_c), ("decompress", ts_d))},
+        "timing": f"HIP events around each call, {warmup} warm-up calls, {reps} timed, a cache flush before each",
         "launches": f"{len(groups)} pz_compress_batch + {len(groups)} pz_decompress_batch call(s)",
         "tensors": {it["t"].name: {"raw_bytes": it["t"].nbytes, "compressed_bytes": it["comp"],
-                                   "ratio": round(it["t"].nbytes / it["comp"], 4), **block_stats(pz, it)}
+                                   "ratio": round(it["t"].nbytes / it["comp"], 4), **block_stats(pz, it),
+                                   "input_sha256_ok": inputs_ok[it["t"].name]}
                     for it in items},
         "oracle_equal": None,
     }
@@ -811,14 +842,29 @@ def cpu_baseline(tensors, sample_mb, gpu_streams):
 
 def oracle_check(tensors, gpu_streams):
     """Byte-for-byte equality of the GPU streams with the oracle's streams of
-    the same tensors (chunk-parallel oracle, host threads), by tensor name."""
+    the same tensors (chunk-parallel oracle on the host threads), and the
+    oracle's own compress and decompress rates on them (round trip checked).
+    Returns (equal by tensor name, rates)."""
     import oracle
 
     threads, _ = host_threads()
-    eq = {t.name: bool(np.array_equal(oracle.compress(t.data, t.elem_bits, threads=threads), gpu_streams[t.name]))
-          for t in tensors}
+    eq = {}
+    raw = 0
+    t_c = t_d = 0.0
+    for t in tensors:
+        a = time.perf_counter()
+        s = oracle.compress(t.data, t.elem_bits, threads=threads)
+        b = time.perf_counter()
+        back = oracle.decompress(s, t.nbytes, t.elem_bits, threads=threads)
+        c = time.perf_counter()
+        assert np.array_equal(back, t.data)
+        eq[t.name] = bool(np.array_equal(s, gpu_streams[t.name]))
+        raw += t.nbytes
+        t_c += b - a
+        t_d += c - b
     log(f"oracle check: {eq}")
-    return eq
+    return eq, {"threads": threads, "compress_raw_gbps": round(raw / t_c / 1e9, 4),
+                "decompress_raw_gbps": round(raw / t_d / 1e9, 4)}
 
 
 if __name__ == "__main__":

@@ -68,5 +68,22 @@ def test_cpu_baseline_compares_gpu_streams_with_the_oracle():
     res, eq = bench.cpu_baseline([t], 0.01, {"x": good})
     assert eq == {"x": True} and res["kind"] == "oracle" and res["cores"] >= 1
     assert bench.cpu_baseline([t], 0.01, {"x": bad})[1] == {"x": False}
-    assert bench.oracle_check([t], {"x": good}) == {"x": True}
-    assert bench.oracle_check([t], {"x": bad[:-1]}) == {"x": False}
+    eq, rates = bench.oracle_check([t], {"x": good})
+    assert eq == {"x": True} and rates["compress_raw_gbps"] > 0
+    assert bench.oracle_check([t], {"x": bad[:-1]})[0] == {"x": False}
+
+
+def test_input_manifest_matches_the_generators():
+    """Every workload tensor hashes to the committed manifest (the bench checks
+    its inputs against it on the GPU host), and the bench's check reports a
+    changed byte."""
+    import pzinputs
+
+    for name in pzinputs.WORKLOADS:
+        tensors = pzinputs.workload(name)
+        assert bench.input_check(name, tensors) == {t.name: True for t in tensors}, name
+        del tensors
+    (smoke,) = pzinputs.relu_smoke()
+    smoke.data[5] ^= 1
+    assert bench.input_check("relu-smoke", [smoke]) == {smoke.name: False}
+    assert bench.input_check("no-such-workload", [smoke]) == {smoke.name: None}
