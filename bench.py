@@ -303,6 +303,8 @@ def main():
     variants = measure_variants(pz, items, flush, cur) if args.variants else None
     size_only = measure_size_only(pz, items, flush, cur)
     swap = None if args.no_swap else measure_swap(pz, items, flush)
+    if swap is not None:
+        swap["eq2"] = eq2_prediction(pz, items, per_tensor, swap)
 
     ms_calls = float(step_ms_c.mean())
     per_call = {
@@ -707,6 +709,22 @@ def measure_swap(pz, items, flush, reps=3, pool_chunk_bytes=2 << 20):
     log(f"swap: plain D2H {res['plain_d2h_gbps']} GB/s, swap-out {res['swap_out_gbps']} GB/s "
         f"(x{res['swap_out_speedup']}); plain H2D {res['plain_h2d_gbps']} GB/s, swap-in "
         f"{res['swap_in_gbps']} GB/s (x{res['swap_in_speedup']})")
+    return res
+
+
+def eq2_prediction(pz, items, per_tensor, swap):
+    """The planner's cost model (§III-C, Eq. 2) fed with this run's
+    measurements: for each tensor x_t = min(m/g, max(m/(c g), m/B)), with g the
+    measured plain pinned-copy rate of each direction, B the tensor's measured
+    compress (decompress) rate and c its ratio; summed over the workload and set
+    beside the measured swap-out (swap-in) time."""
+    res = {}
+    for d, link, rate, measured in (("out", swap["plain_d2h_gbps"], "compress_raw_gbps", swap["ms"]["swap_out"]),
+                                    ("in", swap["plain_h2d_gbps"], "decompress_raw_gbps", swap["ms"]["swap_in"])):
+        x = sum(pz.transfer_time(it["t"].nbytes, it["t"].nbytes / it["comp"], link * 1e9,
+                                 per_tensor[it["t"].name][rate] * 1e9) for it in items)
+        res[f"swap_{d}_predicted_ms"] = round(x * 1e3, 3)
+        res[f"swap_{d}_measured_ms"] = measured
     return res
 
 

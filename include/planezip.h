@@ -277,6 +277,18 @@ pz_status_t pz_predictor_predict(pz_predictor_t *pred, uint64_t signature,
 size_t pz_predictor_entries(pz_predictor_t *pred);
 void pz_predictor_clear(pz_predictor_t *pred);
 
+/* Time in seconds that one swap of a tensor occupies a copy queue, the
+ * planner's cost model (§III-C, Eq. 2): x = min(m / g, max(m / (c g), m / B))
+ * with m = raw_bytes, c = ratio (raw over compressed bytes, as the predictor
+ * gives it), g = link_bytes_per_s (the copy link, per direction) and
+ * B = engine_bytes_per_s (the codec's rate in raw bytes per second, e.g. the
+ * measured pz_compress rate). A compressed transfer is bound by the slower of
+ * link and engine; the engine is bypassed (m / g) when that is not shorter.
+ * Returns -1 if ratio, link_bytes_per_s or engine_bytes_per_s is not a
+ * positive finite number. Pure host arithmetic. */
+double pz_transfer_time(uint64_t raw_bytes, double ratio, double link_bytes_per_s,
+                        double engine_bytes_per_s);
+
 /* Swap engine: the copy path of §III and Fig. 2. A swapped-out tensor is
  * compressed on the GPU into a device staging slot and its stream's exact
  * bytes are copied by DMA into equal-sized pieces of a pinned host pool (the

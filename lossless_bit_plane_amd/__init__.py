@@ -21,6 +21,6 @@ from .codec import (  # noqa: F401
 )
 from .predictor import (  # noqa: F401
     Predictor, signature, pz_predictor_create, pz_predictor_destroy, pz_predictor_update,
-    pz_predictor_predict, pz_predictor_entries, pz_predictor_clear,
+    pz_predictor_predict, pz_predictor_entries, pz_predictor_clear, transfer_time,
 )
 from .swap import Swapper, SwapHooks  # noqa: F401

@@ -23,7 +23,7 @@ EXPORTS = ("pz_compressed_size", "pz_compress", "pz_decompress", "pz_block_sizes
            "pz_predictor_entries", "pz_predictor_clear",
            "pz_swapper_create", "pz_swapper_destroy", "pz_swapper_free_chunks", "pz_swap_out", "pz_swap_wait",
            "pz_swap_in", "pz_swap_release", "pz_swap_read", "pz_compress_batch", "pz_decompress_batch",
-           "pz_compressed_size_batch", "pz_compress_noalloc")
+           "pz_compressed_size_batch", "pz_compress_noalloc", "pz_transfer_time")
 
 
 def _load():
@@ -56,6 +56,8 @@ def _load():
     lib.pz_predictor_destroy.restype = None
     lib.pz_predictor_update.argtypes = [vp, u64, u64, u64]
     lib.pz_predictor_predict.argtypes = [vp, u64, u64, ctypes.POINTER(u64), ctypes.POINTER(i)]
+    lib.pz_transfer_time.argtypes = [u64, ctypes.c_double, ctypes.c_double, ctypes.c_double]
+    lib.pz_transfer_time.restype = ctypes.c_double
     lib.pz_predictor_entries.argtypes = [vp]
     lib.pz_predictor_entries.restype = sz
     lib.pz_predictor_clear.argtypes = [vp]
@@ -76,7 +78,7 @@ def _load():
     for name in ("pz_compressed_size", "pz_compress", "pz_compress_noalloc", "pz_decompress", "pz_block_sizes",
                  "pz_compressed_size_ex", "pz_compress_ex", "pz_decompress_ex", "pz_compressed_size_sampled",
                  "pz_predictor_update", "pz_predictor_predict", "pz_compress_batch", "pz_decompress_batch",
-                 "pz_compressed_size_batch", "pz_compress_noalloc"):
+                 "pz_compressed_size_batch"):
         getattr(lib, name).restype = ctypes.c_int
     lib.pz_status_string.argtypes = [ctypes.c_int]
     lib.pz_status_string.restype = ctypes.c_char_p

@@ -58,8 +58,8 @@ inline DMode make_dmode(int W, uint32_t mask, int tagged) {
 }
 
 // ---------------------------------------------------------------------------
-// Locate. A workgroup takes a tile of 64 chunks; each chunk is walked by a
-// group of G = 4 lanes. Walking is sequential by nature (a block starts where
+// Locate. A workgroup takes a tile of 256 / G chunks (64); each chunk is
+// walked by a group of G = 4 lanes. Walking is sequential by nature (a block starts where
 // the previous one ends), and a wave's time is mostly the length of its
 // dependent instruction chain, so each step speculates: lane q of the group
 // reads the windows at pos + (4q + s)(1+L), s = 0..3, i.e. where codes 4q+s
@@ -70,9 +70,14 @@ inline DMode make_dmode(int W, uint32_t mask, int tagged) {
 // but walks four times as many steps per wave; it measured slower on every
 // tensor of the bench workload.)
 // ---------------------------------------------------------------------------
-constexpr int kLocateChunks = 64;  // chunks per tile (per workgroup)
-constexpr int kLocateLanes = 4;    // lanes per chunk
-constexpr int kLocateThreads = kLocateChunks * kLocateLanes;
+// Lanes per chunk. The kernel takes 4, 8 or 16; measured on the five
+// workloads, 8 lanes (32 speculated codes, 32 chunks per workgroup) decoded
+// the 25.7 MB FP32 CNN tensor 8% faster and the others no faster (the GPT-2
+// tensors 20% slower), 16 lanes were slower everywhere: a step's latency,
+// not its width, sets a small tensor's walk.
+constexpr int kLocateLanes = 4;
+constexpr int kLocateThreads = 256;            // four waves per workgroup
+constexpr int kLocateChunks = kLocateThreads / kLocateLanes;  // chunks per tile (per workgroup)
 // Per-chunk LDS region: a ring of kRingDwords dwords of the chunk's stream, one
 // mirror dword (slot kRingDwords = slot 0, so a peek at the last slot reads two
 // dwords), then the chunk's 32 block offsets (16-bit). 145 dwords: odd, spreads
@@ -82,7 +87,8 @@ constexpr int kLocateThreads = kLocateChunks * kLocateLanes;
 constexpr int kRingDwords = 128;
 constexpr int kRingRegion = kRingDwords + 1 + 16;
 constexpr uint32_t kBlockAhead = 38;   // dwords one block (and its look-ahead) can touch
-constexpr uint32_t kGroupDwords = kRingDwords / 4;  // refill unit, split over the G lanes
+// Refill unit: 32 dwords, split over the G lanes (at least one 16-byte load each).
+constexpr uint32_t kGroupDwords = 4 * kLocateLanes > 32 ? 4 * kLocateLanes : 32;
 constexpr int kStartGroups = (int)((kBlockAhead + kGroupDwords - 1) / kGroupDwords);
 // A refill made while a group is short (fill < cur + kBlockAhead) and the
 // request made after the first groups must not overwrite dwords at or above cur.
@@ -97,25 +103,38 @@ PZ_DEV uint32_t select4(uint32_t k, uint32_t a0, uint32_t a1, uint32_t a2, uint3
   return (k & 2u) ? hi : lo;
 }
 
-// Value of `v` in lane k (0..3) of this lane's group of four (DPP quad
-// broadcast).
+// Value of `v` in lane k of this lane's group of G (DPP quad broadcast for
+// quads, a lane permute otherwise).
 template <int G>
 PZ_DEV uint32_t group_lane(uint32_t v, uint32_t k) {
-  static_assert(G == 4, "groups are quads");
-  const uint32_t b0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x00, 0xF, 0xF, true);
-  const uint32_t b1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x55, 0xF, 0xF, true);
-  const uint32_t b2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xAA, 0xF, 0xF, true);
-  const uint32_t b3 = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xFF, 0xF, 0xF, true);
-  return select4(k, b0, b1, b2, b3);
+  if constexpr (G == 4) {
+    const uint32_t b0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x00, 0xF, 0xF, true);
+    const uint32_t b1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x55, 0xF, 0xF, true);
+    const uint32_t b2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xAA, 0xF, 0xF, true);
+    const uint32_t b3 = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xFF, 0xF, 0xF, true);
+    return select4(k, b0, b1, b2, b3);
+  } else {
+    return (uint32_t)__shfl((int)v, (int)((lane_id() & ~(uint32_t)(G - 1)) | k), 64);
+  }
 }
 
-// OR of `v` over this lane's group of four.
+// OR of `v` over this lane's group of G (4, 8 or 16 lanes of one DPP row).
 template <int G>
-PZ_DEV uint32_t group_or(uint32_t v) {
-  static_assert(G == 4, "groups are quads");
+PZ_DEV uint32_t group_or32(uint32_t v) {
+  static_assert(G == 4 || G == 8 || G == 16, "groups of 4, 8 or 16 lanes");
   v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);  // lanes 1,0,3,2
   v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);  // lanes 2,3,0,1
+  if constexpr (G >= 8) v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, true);  // half-row mirror
+  if constexpr (G >= 16) v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, true);  // row mirror
   return v;
+}
+template <int G>
+PZ_DEV uint64_t group_or(uint64_t v) {
+  if constexpr (4 * G <= 32) {
+    return group_or32<G>((uint32_t)v);
+  } else {
+    return (uint64_t)group_or32<G>((uint32_t)v) | ((uint64_t)group_or32<G>((uint32_t)(v >> 32)) << 32);
+  }
 }
 
 // A chunk's stream, read by the chunk's group through the LDS ring. The ring
@@ -287,10 +306,18 @@ PZ_DEV bool parse_chunk(ChunkRing<G> &in, bool coded, uint32_t H, uint32_t raw_l
       const uint32_t a = pos + spec;
       const uint32_t w0 = in.peek(a), w1 = in.peek(a + V), w2 = in.peek(a + 2 * V),
                      w3 = in.peek(a + 3 * V);
-      const uint32_t mine = (w0 & 1u) | ((w1 & 1u) << 1) | ((w2 & 1u) << 2) | ((w3 & 1u) << 3);
-      const uint32_t vmask = group_or<G>(mine << (4 * ql));  // bit k: code k would be verbatim
-      // Leading verbatim codes (~vmask has bit 4G set, so the count is <= 4G).
-      const uint32_t j = min((uint32_t)__builtin_ctz(~vmask), (uint32_t)left);
+      using VM = typename std::conditional<(4 * G > 32), uint64_t, uint32_t>::type;
+      const VM mine = (VM)((w0 & 1u) | ((w1 & 1u) << 1) | ((w2 & 1u) << 2) | ((w3 & 1u) << 3));
+      const VM vmask = (VM)group_or<G>((uint64_t)(mine << (4 * ql)));  // bit k: code k would be verbatim
+      // Leading verbatim codes (at most 4G: for 4G < 32 bit 4G of ~vmask is set).
+      uint32_t lead;
+      if constexpr (4 * G >= 64)
+        lead = vmask == ~0ull ? 64u : (uint32_t)__builtin_ctzll(~vmask);
+      else if constexpr (4 * G == 32)
+        lead = vmask == ~0u ? 32u : (uint32_t)__builtin_ctz(~vmask);
+      else
+        lead = (uint32_t)__builtin_ctz(~vmask);
+      const uint32_t j = min(lead, (uint32_t)left);
       pos += j * V;
       left -= (int)j;
       // The window of code j: lane j/4 of the group read it as its w[j%4].
@@ -322,11 +349,11 @@ PZ_DEV bool parse_chunk(ChunkRing<G> &in, bool coded, uint32_t H, uint32_t raw_l
 }
 
 template <int W, int G>
-__global__ __launch_bounds__(kLocateChunks * G) void locate_kernel(const DBatch batch, uint32_t *err_words,
+__global__ __launch_bounds__(kLocateThreads) void locate_kernel(const DBatch batch, uint32_t *err_words,
                                                                     uint32_t epoch, uint64_t *lb_words,
                                                                     uint32_t *tile_counter,
                                                                     uint32_t counter_base, DMode mode) {
-  constexpr int kWaves = G;  // 64 chunks x G lanes
+  constexpr int kWaves = kLocateThreads / kWave;  // 256 / G chunks x G lanes
   __shared__ uint32_t lds[kLocateChunks * kRingRegion];
   __shared__ uint64_t wave_sum[kWaves];
   __shared__ uint64_t tile_before;
@@ -389,10 +416,13 @@ __global__ __launch_bounds__(kLocateChunks * G) void locate_kernel(const DBatch 
   if (coded) {
     // The chunk's block offsets: 64 bytes, 64/G per group lane.
     const uint32_t *b32 = region + kRingDwords + 1 + (16 / G) * ql;
-    uint4 *outp = reinterpret_cast<uint4 *>(block_off + c * kBlocksPerChunk) + (4 / G) * ql;
+    if constexpr (G == 4) {
+      *(reinterpret_cast<uint4 *>(block_off + c * kBlocksPerChunk) + ql) = make_uint4(b32[0], b32[1], b32[2], b32[3]);
+    } else {
+      uint32_t *outd = reinterpret_cast<uint32_t *>(block_off + c * kBlocksPerChunk) + (16 / G) * ql;
 #pragma unroll
-    for (int k = 0; k < 4 / G; ++k)
-      outp[k] = make_uint4(b32[4 * k], b32[4 * k + 1], b32[4 * k + 2], b32[4 * k + 3]);
+      for (int k = 0; k < 16 / G; ++k) outd[k] = b32[k];
+    }
   }
   if (c < nchunks && ql == 0) {
     const bool chunk_bad = header_bad || (coded && !parsed);

@@ -14,6 +14,8 @@
 // twice the capacity, one mutex per table.
 #include "../../include/planezip.h"
 
+#include <algorithm>
+#include <cmath>
 #include <mutex>
 #include <new>
 #include <vector>
@@ -112,6 +114,16 @@ void pz_predictor_clear(pz_predictor_t *p) {
   std::lock_guard<std::mutex> lock(p->mu);
   for (pz_predictor::Slot &s : p->slots) s.used = false;
   p->count = 0;
+}
+
+double pz_transfer_time(uint64_t raw_bytes, double ratio, double link_bytes_per_s, double engine_bytes_per_s) {
+  const bool ok = std::isfinite(ratio) && std::isfinite(link_bytes_per_s) && std::isfinite(engine_bytes_per_s) &&
+                  ratio > 0 && link_bytes_per_s > 0 && engine_bytes_per_s > 0;
+  if (!ok) return -1.0;
+  const double m = (double)raw_bytes;
+  const double plain = m / link_bytes_per_s;  // the engine bypassed
+  const double coded = std::max(m / (ratio * link_bytes_per_s), m / engine_bytes_per_s);
+  return std::min(plain, coded);
 }
 
 }  // extern "C"

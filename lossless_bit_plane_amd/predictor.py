@@ -48,6 +48,15 @@ def pz_predictor_clear(handle) -> None:
     lib.pz_predictor_clear(handle)
 
 
+def transfer_time(raw_bytes: int, ratio: float, link_bytes_per_s: float, engine_bytes_per_s: float) -> float:
+    """pz_transfer_time: seconds one swap of the tensor occupies a copy queue
+    (PlaneZip §III-C, Eq. 2), min(m/g, max(m/(c g), m/B))."""
+    x = lib.pz_transfer_time(raw_bytes, ratio, link_bytes_per_s, engine_bytes_per_s)
+    if x < 0:
+        raise ValueError("pz_transfer_time: ratio and rates must be positive and finite")
+    return float(x)
+
+
 class Predictor:
     """Owns one table; the methods are the calls above."""
 

@@ -15,7 +15,7 @@ def _declared():
     for fn in os.listdir(os.path.join(ROOT, "include")):
         if fn.endswith(".h"):
             text = open(os.path.join(ROOT, "include", fn)).read()
-            names += re.findall(r"^\s*(?:pz_status_t|const char \*|pz_predictor_t \*|pz_swapper_t \*|void|size_t)\s*(pz_\w+)\s*\(",
+            names += re.findall(r"^\s*(?:pz_status_t|const char \*|pz_predictor_t \*|pz_swapper_t \*|void|size_t|double)\s*(pz_\w+)\s*\(",
                                 text, re.M)
     return sorted(set(names))
 

@@ -154,3 +154,33 @@ def test_native_predictor_from_several_threads(pzp):
     assert len(t) == len(last)
     for sig, comp in last.items():
         assert t.predict(sig, 4096) == (comp, True)
+
+
+def test_transfer_time_eq2_hand_computed(pzp):
+    """pz_transfer_time against Eq. 2 of §III-C worked by hand,
+    x = min(m/g, max(m/(c g), m/B)), with the evaluation's assumed rates
+    (PCIe 4.0 at 24 GB/s per direction, a 64 GB/s engine) on 120 MB."""
+    from lossless_bit_plane_amd import predictor
+
+    m, g, B = 120_000_000, 24e9, 64e9
+    # c = 2: link-bound compressed transfer, 120e6 / 48e9 = 2.5 ms (< 5 ms plain).
+    assert predictor.transfer_time(m, 2.0, g, B) == pytest.approx(2.5e-3, rel=1e-12)
+    # c = 4: 120e6 / 96e9 = 1.25 ms on the link, but the engine needs
+    # 120e6 / 64e9 = 1.875 ms: engine-bound.
+    assert predictor.transfer_time(m, 4.0, g, B) == pytest.approx(1.875e-3, rel=1e-12)
+    # c = 1 and c = 0.8 (a stream larger than the raw bytes): the engine is
+    # bypassed, 120e6 / 24e9 = 5 ms.
+    assert predictor.transfer_time(m, 1.0, g, B) == pytest.approx(5e-3, rel=1e-12)
+    assert predictor.transfer_time(m, 0.8, g, B) == pytest.approx(5e-3, rel=1e-12)
+    # An engine only as fast as the link never helps (§V-E): B = g, c = 3
+    # gives max(1.667 ms, 5 ms) = 5 ms = the plain copy.
+    assert predictor.transfer_time(m, 3.0, g, g) == pytest.approx(5e-3, rel=1e-12)
+    # A slow engine (10 GB/s) is bypassed: min(5 ms, max(2.5 ms, 12 ms)).
+    assert predictor.transfer_time(m, 2.0, g, 10e9) == pytest.approx(5e-3, rel=1e-12)
+    # The two lanes' 96 GB/s of §III-D at c = 4: max(1.25 ms, 1.25 ms).
+    assert predictor.transfer_time(m, 4.0, g, 96e9) == pytest.approx(1.25e-3, rel=1e-12)
+    assert predictor.transfer_time(0, 2.0, g, B) == 0.0
+    for bad in [(m, 0.0, g, B), (m, 2.0, -1.0, B), (m, 2.0, g, 0.0), (m, float("nan"), g, B),
+                (m, 2.0, float("inf"), B)]:
+        with pytest.raises(ValueError):
+            predictor.transfer_time(*bad)
