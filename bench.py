@@ -24,7 +24,7 @@ parallel on the whole workload, and single-threaded on a bounded sample.
 Outside the timed regions the line also carries, per tensor, the encoder mix
 (blocks won by each candidate, the most frequent one, chunks stored raw: the
 'Top' column of the paper's Table III), the other four workloads' batched
-compress and decompress rates, HBM fractions and ratios (`configs`), and a
+compress and decompress rates, HBM fractions and ratios (`workloads`), and a
 byte-for-byte comparison of every GPU stream with the oracle's stream of the
 same tensor (`oracle_equal`, made in the CPU-baseline leg).
 """
@@ -277,12 +277,12 @@ def main():
 
     # The other workloads: batched compress and decompress rates, ratios and
     # block statistics (their streams are checked against the oracle below).
-    configs = {}
+    workloads = {}
     other_streams = {}
     if not args.headline_only:
         for name in WORKLOAD_NAMES:
             if name != args.workload:
-                configs[name], other_streams[name] = measure_config(pz, pzinputs, name, flush, cur)
+                workloads[name], other_streams[name] = measure_workload(pz, pzinputs, name, flush, cur)
 
     cpu = None
     oracle_equal = None
@@ -290,13 +290,13 @@ def main():
         cpu, oracle_equal = cpu_baseline(tensors, args.cpu_sample_mb, gpu_streams)
         for name, (tens, streams) in other_streams.items():
             eq, rates = oracle_check(tens, streams)
-            configs[name]["oracle_equal"] = all(eq.values())
-            configs[name]["cpu_oracle"] = rates
+            workloads[name]["oracle_equal"] = all(eq.values())
+            workloads[name]["cpu_oracle"] = rates
             for tname, ok in eq.items():
-                configs[name]["tensors"][tname]["oracle_equal"] = ok
+                workloads[name]["tensors"][tname]["oracle_equal"] = ok
         for tname, ok in oracle_equal.items():
             per_tensor[tname]["oracle_equal"] = ok
-        if not all(oracle_equal.values()) or not all(c["oracle_equal"] for c in configs.values()):
+        if not all(oracle_equal.values()) or not all(c["oracle_equal"] for c in workloads.values()):
             log("GPU stream differs from the oracle's stream")
     other_streams.clear()
 
@@ -349,9 +349,9 @@ def main():
         "per_call": per_call,
         "cpu_baseline": cpu,
         "oracle_equal": None if oracle_equal is None else (
-            all(oracle_equal.values()) and all(c["oracle_equal"] for c in configs.values())),
+            all(oracle_equal.values()) and all(c["oracle_equal"] for c in workloads.values())),
         "tensors": per_tensor,
-        "configs": configs,
+        "workloads": workloads,
         "size_only": size_only,
         "swap": swap,
     }
@@ -407,7 +407,7 @@ def block_stats(pz, it):
     }
 
 
-def measure_config(pz, pzinputs, name, flush, cur, reps=20, warmup=3):
+def measure_workload(pz, pzinputs, name, flush, cur, reps=20, warmup=3):
     """One workload's batched compress and decompress (one call per
     direction and (dtype, width) group, as in the headline step): raw GB/s
     and fraction of HBM peak of the algorithmic bytes (read raw + write
@@ -488,7 +488,7 @@ def measure_config(pz, pzinputs, name, flush, cur, reps=20, warmup=3):
                     for it in items},
         "oracle_equal": None,
     }
-    log(f"config {name}: ratio {raw / comp:.3f}, compress {raw / t_c / 1e9:.0f} GB/s, "
+    log(f"workload {name}: ratio {raw / comp:.3f}, compress {raw / t_c / 1e9:.0f} GB/s, "
         f"decompress {raw / t_d / 1e9:.0f} GB/s")
     streams = {it["t"].name: it["stream"][:it["comp"]].cpu().numpy() for it in items}
     del items

@@ -685,7 +685,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DBatch batch,
   // --- 3. Packed slots: raw copy, ZVC or plane decoding into d. Waves take the
   // slots in an order rotated per tile, so that the busy waves of successive
   // groups fall on different SIMDs. ---
-  const uint32_t slot = (t + kDecThreads - 64u * (uint32_t)(gtile & (kDecWaves - 1))) & (kDecThreads - 1);
+  const uint32_t slot = (t + kDecThreads - 64u * (uint32_t)(gtile % kDecWaves)) % kDecThreads;
   const bool active = slot < nbusy;
   const bool wave_active = __ballot(active) != 0;
   uint32_t sb = 0;
