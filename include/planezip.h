@@ -204,7 +204,7 @@ pz_status_t pz_decompress_batch(int count, const void *const *d_srcs,
  * harnesses that forbid allocation. Same arguments, checks and stream as
  * pz_compress (PlaneZip with all five candidates, tagged), but its scratch
  * (a tile counter and one look-back word per 32 KB tile) lives in a fixed
- * 256 KiB device array that the library holds on each GPU it runs on until
+ * 2 MiB device array that the library holds on each GPU it runs on until
  * the process ends; the call allocates and frees nothing (no hipMalloc,
  * hipMallocAsync, hipFree or allocating library routine) and clears the
  * array with a kernel, not a memset.

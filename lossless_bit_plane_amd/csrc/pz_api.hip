@@ -175,7 +175,7 @@ pz_status_t compress_many(int dtype, int elem_bits, uint32_t codec_mask, int tag
       ++i;
     }
     if (b.n == 0) continue;
-    const pz::ScratchNeed need{b.total_tiles, 0, b.total_tiles};
+    const pz::ScratchNeed need{b.total_tiles * pz::kLookbackStride, 0, b.total_tiles};
     const hipError_t e = with_scratch(s, need, [&](const pz::Scratch &sc) {
       return pz::launch_compress(w, b, codec_mask, tagged, sc, s);
     });
@@ -249,7 +249,7 @@ pz_status_t decompress_many(int dtype, int elem_bits, uint32_t codec_mask, int t
       b.total_groups += x.ngroups;
       extra += pz::decompress_extra(raw[j]);
     }
-    const pz::ScratchNeed need{b.total_tiles, extra, b.total_tiles};
+    const pz::ScratchNeed need{b.total_tiles * pz::kLookbackStride, extra, b.total_tiles};
     const hipError_t e = with_scratch(s, need, [&](const pz::Scratch &sc) {
       return pz::launch_decompress(w, b, codec_mask, tagged, sc, s);
     });
@@ -267,7 +267,7 @@ pz_status_t decompress_many(int dtype, int elem_bits, uint32_t codec_mask, int t
 // once per device, on the first call made with that device current, and is
 // kept per device.
 // ---------------------------------------------------------------------------
-constexpr size_t kNoAllocWords = 32768;  // 256 KiB: header + look-back words
+constexpr size_t kNoAllocWords = 262144;  // 2 MiB: header + look-back words (one per 64-byte line)
 constexpr size_t kNoAllocHeaderWords = kScratchHeader / 8;
 static __device__ __align__(256) uint64_t scratch[kNoAllocWords];
 
@@ -301,7 +301,8 @@ pz_status_t pz_compress_noalloc(const void *d_src, size_t raw_bytes, int dtype, 
   if (raw_bytes && (!d_src || !d_dst)) return PZ_ERROR_INVALID_VALUE;
   if (!aligned16(d_src) || !aligned16(d_dst)) return PZ_ERROR_INVALID_VALUE;
   if (dst_capacity < PZ_MAX_COMPRESSED_BYTES(raw_bytes)) return PZ_ERROR_INSUFFICIENT_BUFFER;
-  if (raw_bytes > PZ_NOALLOC_MAX_BYTES || pz::compress_tiles(raw_bytes) > kNoAllocWords - kNoAllocHeaderWords)
+  if (raw_bytes > PZ_NOALLOC_MAX_BYTES ||
+      pz::compress_tiles(raw_bytes) * pz::kLookbackStride > kNoAllocWords - kNoAllocHeaderWords)
     return PZ_ERROR_INVALID_VALUE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (raw_bytes == 0) return from_hip(pz::fill_u64(d_out_bytes, 1, 0, s));
@@ -322,7 +323,7 @@ pz_status_t pz_compress_noalloc(const void *d_src, size_t raw_bytes, int dtype, 
   // The previous call's counter and look-back words are still there: clear
   // them (a kernel, not a memset) and count this call's tiles from 0 under
   // epoch 1.
-  e = pz::fill_u64(base, kNoAllocHeaderWords + x.ntiles, 0, s);
+  e = pz::fill_u64(base, kNoAllocHeaderWords + (uint64_t)x.ntiles * pz::kLookbackStride, 0, s);
   if (e != hipSuccess) return from_hip(e);
   pz::Scratch sc;
   sc.counter = reinterpret_cast<uint32_t *>(base);

@@ -621,7 +621,7 @@ __global__ __launch_bounds__(kCThreads, kCWavesPerSimd) void compress_kernel(con
   const uint64_t raw_bytes = batch.t[k].raw_bytes, nchunks = batch.t[k].nchunks;
   const uint32_t ntiles = batch.t[k].ntiles;
   const uint32_t tile = gtile - batch.t[k].tile_begin;
-  uint64_t *status = lb_words + batch.t[k].tile_begin;
+  uint64_t *status = lb_words + (uint64_t)batch.t[k].tile_begin * kLookbackStride;
   uint32_t d[32];
   load_tile_block(batch, gtile, t, d);
 

@@ -378,7 +378,7 @@ __global__ __launch_bounds__(kLocateThreads) void locate_kernel(const DBatch bat
   uint16_t *__restrict__ block_off = batch.t[k].block_off;
   uint32_t *err = err_words + k;
   const uint32_t tile = gtile - batch.t[k].tile_begin;
-  uint64_t *lb_status = lb_words + batch.t[k].tile_begin;
+  uint64_t *lb_status = lb_words + (uint64_t)batch.t[k].tile_begin * kLookbackStride;
 
   // Chunk offsets: a scan of the 16-bit headers over the tile, and one
   // look-back per tile for the headers before it.

@@ -44,6 +44,12 @@ constexpr uint32_t kEpochMax = (uint32_t)kEpochBits;
 
 constexpr uint64_t kBadChunk = ~0ull;
 
+// A tile's look-back word sits alone in its 64-byte line (tile t at word
+// t * kLookbackStride): each word is read at device scope by the hundreds of
+// successors whose walks pass it, and words sharing a line share those
+// reads' queue (8 words per line measured 4% slower compression).
+constexpr uint64_t kLookbackStride = 8;
+
 // Codec mode (§III-A; the single-codec columns of §V-A and Table III):
 // the candidates a block may use (bit t = tag t) and whether each block
 // carries the 3-bit tag. PlaneZip itself is {all five, tagged}; an untagged
@@ -206,7 +212,7 @@ PZ_DEV uint32_t acquire_tile(uint32_t *counter) {
 // tile's inclusive prefix and returns the exclusive prefix of `agg`.
 PZ_DEV void lookback_publish(uint64_t *status, uint32_t tile, uint64_t agg, uint32_t epoch) {
   if (lane_id() == 0)
-    atomic_store_agent(&status[tile],
+    atomic_store_agent(&status[(uint64_t)tile * kLookbackStride],
                        (tile == 0 ? kFlagPrefix : kFlagAggregate) | ((uint64_t)epoch << kEpochShift) | agg);
 }
 
@@ -218,7 +224,7 @@ PZ_DEV uint64_t lookback_resolve(uint64_t *status, uint32_t tile, uint64_t agg, 
   int64_t base = (int64_t)tile - 1;
   while (true) {
     const int64_t idx = base - (int64_t)lane;
-    const uint64_t st = idx >= 0 ? atomic_load_agent(&status[idx]) : (kFlagPrefix | stamp);
+    const uint64_t st = idx >= 0 ? atomic_load_agent(&status[(uint64_t)idx * kLookbackStride]) : (kFlagPrefix | stamp);
     const bool current = ((st >> kEpochShift) & kEpochBits) == epoch;
     const uint64_t flag = current ? st >> 62 : 0;
     const uint64_t not_ready = __ballot(flag == 0);
@@ -234,7 +240,7 @@ PZ_DEV uint64_t lookback_resolve(uint64_t *status, uint32_t tile, uint64_t agg, 
     if (prefix) break;
     base -= 64;
   }
-  if (lane == 0) atomic_store_agent(&status[tile], kFlagPrefix | stamp | (excl + agg));
+  if (lane == 0) atomic_store_agent(&status[(uint64_t)tile * kLookbackStride], kFlagPrefix | stamp | (excl + agg));
   return excl;
 }
 
