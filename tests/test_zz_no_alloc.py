@@ -1,6 +1,7 @@
 """pz_compress_noalloc (the compress call that allocates nothing) against
 pz_compress through the C ABI: two calls in a row on one GPU, the second on
-a smaller tensor, each stream and size bit-exact with pz_compress's."""
+a smaller tensor, each stream and size bit-exact with pz_compress's and
+nothing written past the stream."""
 import numpy as np
 import pytest
 import torch
@@ -36,6 +37,7 @@ def test_noalloc_matches_pz_compress_on_two_calls():
         n = int(ref_n.item())
         assert int(out.item()) == n
         assert torch.equal(dst[:n], ref[:n])
+        assert bool((dst[n:] == 0xA5).all()), "bytes past the stream were written"
         back, status = pz.pz_decompress(dst, n, data.size, pz.BF16, 16)
         torch.cuda.synchronize()
         assert int(status.item()) == 0
