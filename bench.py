@@ -744,6 +744,7 @@ KERNEL_SOURCES = {
     "compress_kernel": ["pz_device.h", "pz_compress.hip"],
     "locate_kernel": ["pz_device.h", "pz_decompress.hip"],
     "decode_kernel": ["pz_device.h", "pz_decompress.hip"],
+    "decompress_kernel": ["pz_device.h", "pz_decompress.hip"],
 }
 
 

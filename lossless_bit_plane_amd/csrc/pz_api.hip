@@ -52,11 +52,12 @@ struct ScratchEntry {
   size_t extra;       // per-call bytes held
   uint32_t epoch;     // of the last call
   uint32_t counter;   // tile counter after the last call
+  uint32_t done;      // located-tile count after the last call
   bool clear;         // the header and words must be cleared before the next call
 };
 
 constexpr size_t kScratchHeader = 48;
-static_assert(4 + 4 * pz::kMaxBatch <= kScratchHeader, "counter and error words");
+static_assert(4 + 4 * pz::kMaxBatch + 4 <= kScratchHeader, "counter, error words and located-tile count");
 
 std::mutex g_scratch_mu;
 std::vector<ScratchEntry> g_scratch;
@@ -74,7 +75,7 @@ hipError_t with_scratch(hipStream_t stream, const pz::ScratchNeed &need, F launc
   for (ScratchEntry &x : g_scratch)
     if (x.device == device && x.stream == stream) ent = &x;
   if (!ent) {
-    g_scratch.push_back(ScratchEntry{device, stream, nullptr, 0, 0, 0, 0, true});
+    g_scratch.push_back(ScratchEntry{device, stream, nullptr, 0, 0, 0, 0, 0, true});
     ent = &g_scratch.back();
   }
   if (ent->words < need.words || ent->extra < need.extra || !ent->base) {
@@ -102,20 +103,25 @@ hipError_t with_scratch(hipStream_t stream, const pz::ScratchNeed &need, F launc
     if (e != hipSuccess) return e;
     ent->epoch = 0;
     ent->counter = 0;
+    ent->done = 0;
     ent->clear = false;
   }
   pz::Scratch sc;
   sc.counter = reinterpret_cast<uint32_t *>(ent->base);
   sc.err = reinterpret_cast<uint32_t *>(ent->base) + 1;
+  sc.done = reinterpret_cast<uint32_t *>(ent->base) + 1 + pz::kMaxBatch;
   sc.words = reinterpret_cast<uint64_t *>(ent->base + kScratchHeader);
   sc.extra = ent->base + kScratchHeader + 8 * ent->words;
   sc.epoch = ++ent->epoch;
   sc.counter_base = ent->counter;
+  sc.done_base = ent->done;
   e = launch(sc);
-  if (e == hipSuccess)
+  if (e == hipSuccess) {
     ent->counter += need.counted;  // every workgroup of the call takes one tile
-  else
+    ent->done += need.done;
+  } else {
     ent->clear = true;
+  }
   return e;
 }
 
@@ -249,7 +255,7 @@ pz_status_t decompress_many(int dtype, int elem_bits, uint32_t codec_mask, int t
       b.total_groups += x.ngroups;
       extra += pz::decompress_extra(raw[j]);
     }
-    const pz::ScratchNeed need{b.total_tiles * pz::kLookbackStride, extra, b.total_tiles};
+    const pz::ScratchNeed need = pz::decompress_need(b, extra);
     const hipError_t e = with_scratch(s, need, [&](const pz::Scratch &sc) {
       return pz::launch_decompress(w, b, codec_mask, tagged, sc, s);
     });
@@ -330,8 +336,10 @@ pz_status_t pz_compress_noalloc(const void *d_src, size_t raw_bytes, int dtype, 
   sc.err = reinterpret_cast<uint32_t *>(base) + 1;
   sc.words = base + kNoAllocHeaderWords;
   sc.extra = nullptr;
+  sc.done = nullptr;
   sc.epoch = 1;
   sc.counter_base = 0;
+  sc.done_base = 0;
   return from_hip(pz::launch_compress(w, b, PZ_CODEC_ALL, 1, sc, s));
 }
 

@@ -6,7 +6,8 @@
 // decoder checks: FORMAT.md version 1, §5 and §6.
 //
 // A chunk's blocks carry no offsets, so the blocks of one chunk must be
-// parsed in order. The work is split in two kernels:
+// parsed in order. The work is split in two halves, two kernels for small
+// launches and one ticketed kernel for large ones (decompress_kernel):
 //   locate: one quad of lanes per chunk, 64 chunks per workgroup. Scans the
 //           headers (decoupled look-back across workgroups), validates them,
 //           and walks each chunk's codes without decoding them to record the
@@ -350,28 +351,36 @@ PZ_DEV bool parse_chunk(ChunkRing<G> &in, bool coded, uint32_t H, uint32_t raw_l
   return !bad;
 }
 
-template <int W, int G>
-__global__ __launch_bounds__(kLocateThreads) void locate_kernel(const DBatch batch, uint32_t *err_words,
-                                                                    uint32_t epoch, uint64_t *lb_words,
-                                                                    uint32_t *tile_counter,
-                                                                    uint32_t counter_base, DMode mode) {
-  constexpr int kWaves = kLocateThreads / kWave;  // 256 / G chunks x G lanes
-  __shared__ uint32_t lds[kLocateChunks * kRingRegion];
-  __shared__ uint64_t wave_sum[kWaves];
-  __shared__ uint64_t tile_before;
-  __shared__ uint32_t group_tile;
-  const uint32_t t = threadIdx.x, lane = lane_id(), ql = t & (G - 1);
-  const uint32_t wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  if (t == 0) group_tile = atomicAdd(tile_counter, 1u) - counter_base;
-  __syncthreads();
-  // The launch's tile -> the tensor it belongs to and the tile within it.
-  const uint32_t gtile = __builtin_amdgcn_readfirstlane(group_tile);
-  if (gtile >= batch.total_tiles) return;
+// The tensor a launch's tile belongs to (tiles are numbered across the
+// tensors, in increasing order of the tensor).
+PZ_DEV uint32_t tensor_of_tile(const DBatch &batch, uint32_t gtile) {
   uint32_t k = 0;
   if (batch.n > 1) {  // a single tensor's fields load at once
 #pragma unroll
     for (uint32_t i = 1; i < (uint32_t)kMaxBatch; ++i) k += i < batch.n && gtile >= batch.t[i].tile_begin ? 1u : 0u;
   }
+  return k;
+}
+
+struct LocateShared {
+  uint32_t lds[kLocateChunks * kRingRegion];
+  uint64_t wave_sum[kLocateThreads / kWave];
+  uint64_t tile_before;
+};
+
+// Locates tile gtile of the launch (tensor k): chunk offsets and block
+// offsets of its chunks, corruption in error word k. kShared: the offsets
+// go to decode groups of the same launch, so they are stored at device
+// scope (decompress_kernel).
+template <int W, int G, bool kShared>
+PZ_DEV void locate_tile(const DBatch &batch, uint32_t k, uint32_t gtile, uint32_t *err_words, uint32_t epoch,
+                        uint64_t *lb_words, const DMode &mode, LocateShared &sh) {
+  constexpr int kWaves = kLocateThreads / kWave;  // 256 / G chunks x G lanes
+  uint32_t *lds = sh.lds;
+  uint64_t *wave_sum = sh.wave_sum;
+  uint64_t &tile_before = sh.tile_before;
+  const uint32_t t = threadIdx.x, lane = lane_id(), ql = t & (G - 1);
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const uint8_t *__restrict__ src = batch.t[k].src;
   const uint64_t comp_bytes = batch.t[k].comp_bytes, raw_bytes = batch.t[k].raw_bytes;
   const uint64_t nchunks = batch.t[k].nchunks;
@@ -418,7 +427,13 @@ __global__ __launch_bounds__(kLocateThreads) void locate_kernel(const DBatch bat
   if (coded) {
     // The chunk's block offsets: 64 bytes, 64/G per group lane.
     const uint32_t *b32 = region + kRingDwords + 1 + (16 / G) * ql;
-    if constexpr (G == 4) {
+    if constexpr (kShared) {
+      uint64_t *o64 = reinterpret_cast<uint64_t *>(block_off + c * kBlocksPerChunk) + (8 / G) * ql;
+#pragma unroll
+      for (int k = 0; k < 8 / G; ++k)
+        __hip_atomic_store(o64 + k, (uint64_t)b32[2 * k] | ((uint64_t)b32[2 * k + 1] << 32), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    } else if constexpr (G == 4) {
       *(reinterpret_cast<uint4 *>(block_off + c * kBlocksPerChunk) + ql) = make_uint4(b32[0], b32[1], b32[2], b32[3]);
     } else {
       uint32_t *outd = reinterpret_cast<uint32_t *>(block_off + c * kBlocksPerChunk) + (16 / G) * ql;
@@ -428,9 +443,26 @@ __global__ __launch_bounds__(kLocateThreads) void locate_kernel(const DBatch bat
   }
   if (c < nchunks && ql == 0) {
     const bool chunk_bad = header_bad || (coded && !parsed);
-    chunk_off[c] = chunk_bad ? kBadChunk : off;
+    if constexpr (kShared)
+      __hip_atomic_store(chunk_off + c, chunk_bad ? kBadChunk : off, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      chunk_off[c] = chunk_bad ? kBadChunk : off;
     if (chunk_bad) atomicMax(err, epoch);
   }
+}
+
+template <int W, int G>
+__global__ __launch_bounds__(kLocateThreads) void locate_kernel(const DBatch batch, uint32_t *err_words,
+                                                                    uint32_t epoch, uint64_t *lb_words,
+                                                                    uint32_t *tile_counter,
+                                                                    uint32_t counter_base, DMode mode) {
+  __shared__ LocateShared sh;
+  __shared__ uint32_t group_tile;
+  if (threadIdx.x == 0) group_tile = atomicAdd(tile_counter, 1u) - counter_base;
+  __syncthreads();
+  const uint32_t gtile = __builtin_amdgcn_readfirstlane(group_tile);
+  if (gtile >= batch.total_tiles) return;
+  locate_tile<W, G, false>(batch, tensor_of_tile(batch, gtile), gtile, err_words, epoch, lb_words, mode, sh);
 }
 
 // Bits of a chunk payload staged in LDS; bit `pos` of the payload is bit
@@ -541,25 +573,31 @@ constexpr int kDecodeRowDwords = kDecThreads * kLaneStride;
 constexpr int kDecodeLdsDwords =
     kDecodeBufDwords > kDecodeRowDwords ? kDecodeBufDwords : kDecodeRowDwords;
 
-template <int W>
-__global__ __launch_bounds__(kDecThreads) void decode_kernel(const DBatch batch, const uint32_t *err_words,
-                                                               uint32_t epoch, DMode mode) {
+struct __attribute__((aligned(16))) DecodeShared {
+  uint32_t lds[kDecodeLdsDwords];
+  uint32_t blk_info[kDecThreads];      // per packed block: bit position | tag << 16 | raw << 19
+  uint8_t slot_block[kDecThreads];     // packed slot -> block of the group
+  uint32_t chunk_lead[kDecodeChunks];  // bit offset of each payload in its buffer
+  uint32_t wave_busy[kDecWaves];
+};
+
+// Decodes group gtile (of 8 chunks) of tensor k. With set_status, group 0
+// writes the call's status from the error word (locate must be complete).
+// kShared: the offsets come from locate tiles of the same launch and are
+// read at device scope (decompress_kernel).
+template <int W, bool kShared>
+PZ_DEV void decode_group(const DBatch &batch, uint32_t k, uint64_t gtile, const uint32_t *err_words, uint32_t epoch,
+                         const DMode &mode, bool set_status, DecodeShared &sh) {
   constexpr int N = 1024 / W;
   constexpr uint32_t WMASK = W == 16 ? 0xFFFFu : 0xFFFFFFFFu;
-  __shared__ __attribute__((aligned(16))) uint32_t lds[kDecodeLdsDwords];
-  __shared__ uint32_t blk_info[kDecThreads];    // per packed block: bit position | tag << 16 | raw << 19
-  __shared__ uint8_t slot_block[kDecThreads];   // packed slot -> block of the group
-  __shared__ uint32_t chunk_lead[kDecodeChunks];  // bit offset of each payload in its buffer
-  __shared__ uint32_t wave_busy[kDecWaves];
+  uint32_t *lds = sh.lds;
+  uint32_t *blk_info = sh.blk_info;
+  uint8_t *slot_block = sh.slot_block;
+  uint32_t *chunk_lead = sh.chunk_lead;
+  uint32_t *wave_busy = sh.wave_busy;
 
   const uint32_t t = threadIdx.x, lane = lane_id();
   const uint32_t wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  // The launch's group -> the tensor it belongs to and the group within it.
-  uint32_t k = 0;
-  if (batch.n > 1) {  // a single tensor's fields load at once
-#pragma unroll
-    for (uint32_t i = 1; i < (uint32_t)kMaxBatch; ++i) k += i < batch.n && blockIdx.x >= batch.t[i].group_begin ? 1u : 0u;
-  }
   const uint8_t *__restrict__ src = batch.t[k].src;
   uint8_t *__restrict__ dst = batch.t[k].dst;
   const uint64_t comp_bytes = batch.t[k].comp_bytes, raw_bytes = batch.t[k].raw_bytes;
@@ -568,11 +606,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DBatch batch,
   const uint16_t *__restrict__ block_off = batch.t[k].block_off;
   const uint32_t *err = err_words + k;
   int32_t *status = batch.t[k].status;
-  const uint64_t gtile = blockIdx.x - batch.t[k].group_begin;
   if (gtile * kDecodeChunks >= nchunks) return;
-  // The call's status: locate, which ran before this kernel, marked a
-  // corrupt stream with the call's epoch.
-  if (gtile == 0 && t == 0 && status)
+  // The call's status: locate, complete before this group, marked a corrupt
+  // stream with the call's epoch.
+  if (set_status && gtile == 0 && t == 0 && status)
     *status = __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch ? kStatusCorrupt : 0;
   const uint64_t gblock0 = gtile * kDecThreads;  // first block of the group
 
@@ -585,9 +622,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DBatch batch,
   uint64_t my_coff = kBadChunk;
   uint32_t my_H = 0, my_boff = 0;
   if (chunk < nchunks) {
-    my_coff = chunk_off[chunk];
+    if constexpr (kShared) {
+      my_coff = __hip_atomic_load(chunk_off + chunk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      my_boff = __hip_atomic_load(block_off + block, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      my_coff = chunk_off[chunk];
+      my_boff = block_off[block];
+    }
     my_H = hdr[chunk];
-    my_boff = block_off[block];
   }
 
   // --- 1. Stage the 8 payloads (dword-aligned copies); wave w takes 2w, 2w+1
@@ -864,6 +906,87 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DBatch batch,
   }
 }
 
+template <int W>
+__global__ __launch_bounds__(kDecThreads) void decode_kernel(const DBatch batch, const uint32_t *err_words,
+                                                               uint32_t epoch, DMode mode) {
+  __shared__ DecodeShared sh;
+  // The launch's group -> the tensor it belongs to and the group within it.
+  uint32_t k = 0;
+  if (batch.n > 1) {  // a single tensor's fields load at once
+#pragma unroll
+    for (uint32_t i = 1; i < (uint32_t)kMaxBatch; ++i) k += i < batch.n && blockIdx.x >= batch.t[i].group_begin ? 1u : 0u;
+  }
+  decode_group<W, false>(batch, k, blockIdx.x - batch.t[k].group_begin, err_words, epoch, mode, true, sh);
+}
+
+// Both halves in one launch, for launches of many tiles. Workgroups take
+// tickets in the order they start: tickets 0 .. T-1 locate tiles 0 .. T-1,
+// ticket T + g decodes group g, numbered by tile (tile u holds groups
+// 8u .. 8u+7 of its tensor; those past the tensor's last chunk exit at
+// once). A decode group waits for its tile's flag, and that tile always has
+// an earlier ticket, so every wait is on a workgroup that is running or
+// done. The decode groups of the first tiles thus run beside the last
+// walks, where two launches would leave the GPU partly idle at the end of
+// the walks and between the kernels.
+//
+// Hand-over without cache maintenance: locate stores the offsets at device
+// scope (written through to the coherence point, as relaxed atomics), and
+// each wave waits until its stores and its error-word update are performed
+// before the tile's flag is set; decode reads the flag and then the offsets
+// with device-scope loads (served from the coherence point). These are the
+// steps the gfx9 memory model takes for atomics; a release/acquire pair at
+// device scope would add an L2 write-back per locate wave and an L2
+// invalidation per decode group, which measured 60% slower.
+static_assert(kLocateChunks == 8 * kDecodeChunks, "a locate tile is eight decode groups");
+static_assert(kLocateThreads == kDecThreads, "one workgroup size for both halves");
+
+template <int W, int G>
+__global__ __launch_bounds__(kDecThreads) void decompress_kernel(const DBatch batch, uint32_t *err_words,
+                                                                   uint32_t epoch, uint64_t *lb_words,
+                                                                   uint32_t *tile_counter, uint32_t counter_base,
+                                                                   uint32_t *done, uint32_t done_base, DMode mode) {
+  __shared__ union {
+    LocateShared l;
+    DecodeShared d;
+  } sh;
+  __shared__ uint32_t ticket_s;
+  const uint32_t t = threadIdx.x;
+  if (t == 0) ticket_s = atomicAdd(tile_counter, 1u) - counter_base;
+  __syncthreads();
+  const uint32_t ticket = __builtin_amdgcn_readfirstlane(ticket_s);
+  const uint32_t T = batch.total_tiles;
+  const bool loc = ticket < T;
+  const uint32_t tile = loc ? ticket : (ticket - T) >> 3;
+  if (tile >= T) return;
+  const uint32_t k = tensor_of_tile(batch, tile);
+  uint64_t *flag = lb_words + (uint64_t)tile * kLookbackStride + 1;  // beside the tile's look-back word
+  if (loc) {
+    locate_tile<W, G, true>(batch, k, tile, err_words, epoch, lb_words, mode, sh.l);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's offset stores and error update performed
+    __syncthreads();
+    if (t == 0) {
+      __hip_atomic_store(flag, (uint64_t)epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t before = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (before - done_base == T - 1u) {
+        // The launch's last tile located: every error word is final.
+        for (uint32_t m = 0; m < batch.n; ++m)
+          if (batch.t[m].status)
+            *batch.t[m].status =
+                __hip_atomic_load(err_words + m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch ? kStatusCorrupt : 0;
+      }
+    }
+  } else {
+    const uint64_t g = (uint64_t)(tile - batch.t[k].tile_begin) * 8u + ((ticket - T) & 7u);
+    if (g * kDecodeChunks >= batch.t[k].nchunks) return;
+    if (t == 0) {
+      while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != (uint64_t)epoch)
+        __builtin_amdgcn_s_sleep(16);
+    }
+    __syncthreads();
+    decode_group<W, true>(batch, k, g, err_words, epoch, mode, false, sh.d);
+  }
+}
+
 // Sets a decompress call's status when it launches no kernel (an empty
 // tensor).
 __global__ void set_status_kernel(int32_t *status, int32_t value) { *status = value; }
@@ -892,6 +1015,18 @@ size_t decompress_extra(uint64_t raw_bytes) {
   return (size_t)(((nchunks + 1) & ~1ull) * 8 + nchunks * kBlocksPerChunk * 2);
 }
 
+// Launches of fewer tiles take two kernels: there every decode group of the
+// launch would be resident from the start, waiting beside the walks, and
+// the walks measured 4-28% slower for it (73-400 tiles); from 768 tiles on
+// the single launch was 10-12% faster.
+constexpr uint32_t kFusedMinTiles = 512;
+
+ScratchNeed decompress_need(const DBatch &b, size_t extra) {
+  if (b.total_tiles >= kFusedMinTiles)
+    return ScratchNeed{b.total_tiles * kLookbackStride, extra, 9 * b.total_tiles, b.total_tiles};
+  return ScratchNeed{b.total_tiles * kLookbackStride, extra, b.total_tiles, 0};
+}
+
 hipError_t launch_decompress(int w, DBatch &batch, uint32_t codec_mask, int tagged,
                              const Scratch &scratch, hipStream_t stream) {
   const DMode mode = make_dmode(w, codec_mask, tagged);
@@ -901,6 +1036,18 @@ hipError_t launch_decompress(int w, DBatch &batch, uint32_t codec_mask, int tagg
     x.chunk_off = reinterpret_cast<uint64_t *>(extra);
     x.block_off = reinterpret_cast<uint16_t *>(extra + ((x.nchunks + 1) & ~1ull) * 8);
     extra += decompress_extra(x.raw_bytes);
+  }
+  if (batch.total_tiles >= kFusedMinTiles) {
+    const dim3 grid(9 * batch.total_tiles);  // T locate tiles, 8T decode groups
+    if (w == 16)
+      hipLaunchKernelGGL((decompress_kernel<16, kLocateLanes>), grid, dim3(kDecThreads), 0, stream, batch, scratch.err,
+                         scratch.epoch, scratch.words, scratch.counter, scratch.counter_base, scratch.done,
+                         scratch.done_base, mode);
+    else
+      hipLaunchKernelGGL((decompress_kernel<32, kLocateLanes>), grid, dim3(kDecThreads), 0, stream, batch, scratch.err,
+                         scratch.epoch, scratch.words, scratch.counter, scratch.counter_base, scratch.done,
+                         scratch.done_base, mode);
+    return hipGetLastError();
   }
   const dim3 grid_a(batch.total_tiles);
   if (w == 16)

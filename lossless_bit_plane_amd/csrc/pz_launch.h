@@ -21,8 +21,10 @@ struct Scratch {
   uint32_t *err;          // per tensor of a launch (kMaxBatch words): the epoch of
                           // the last decompress launch that found its stream corrupt
   uint8_t *extra;         // per-call buffers (decompress: chunk and block offsets)
+  uint32_t *done;         // decompress: count of located tiles, never reset
   uint32_t epoch;         // this call's epoch, 1..kEpochMax
   uint32_t counter_base;  // tile counter at the start of this call
+  uint32_t done_base;     // located-tile count at the start of this call
 };
 
 // What a call needs of the scratch: look-back words, per-call bytes, and the
@@ -31,6 +33,7 @@ struct ScratchNeed {
   size_t words;
   size_t extra;
   uint32_t counted;
+  uint32_t done;  // advance of the located-tile count
 };
 
 // The tensors of one compress launch. The launch numbers its tiles across the
@@ -123,6 +126,8 @@ hipError_t launch_compress(int w, const CBatch &batch, uint32_t codec_mask, int 
                            const Scratch &scratch, hipStream_t stream);
 hipError_t launch_decompress(int w, DBatch &batch, uint32_t codec_mask, int tagged,
                              const Scratch &scratch, hipStream_t stream);
+// The scratch a decompress launch of the batch needs (its tiles and groups filled in).
+ScratchNeed decompress_need(const DBatch &batch, size_t extra);
 // Status of a decompress call with no chunks: corrupt unless comp_bytes is 0.
 hipError_t launch_empty_status(int32_t *status, uint64_t comp_bytes, hipStream_t stream);
 

@@ -152,3 +152,61 @@ def test_batch_corrupt_stream_flags_only_its_tensor(pz):
                                [d.size for d in datas], 0, 16, status=sentinel)
     torch.cuda.synchronize()
     assert sentinel.cpu().tolist() == [7, 7, 7]
+
+
+def _rejected_flip(stream, raw_bytes, w, chunk, rng):
+    """A copy of `stream` with one payload bit of `chunk` flipped such that
+    the oracle rejects that chunk decoded on its own (a one-chunk stream:
+    its header, then its payload); chunks decode independently of each
+    other once the headers place them."""
+    H = oracle.header_table(stream, raw_bytes).astype(np.int64)
+    assert H[chunk] < min(4096, raw_bytes - 4096 * chunk), "pick a coded chunk"
+    off = 2 * H.size + int(H[:chunk].sum())
+    raw_len = min(4096, raw_bytes - 4096 * chunk)
+    for _ in range(200):
+        pay = stream[off: off + H[chunk]].copy()
+        i = int(rng.integers(0, pay.size))
+        pay[i] ^= np.uint8(1 << int(rng.integers(0, 8)))
+        one = np.concatenate([np.array([H[chunk]], dtype="<u2").view(np.uint8), pay])
+        if oracle.decompress_status(one, raw_len, w) != oracle.OK:
+            s = stream.copy()
+            s[off + i] = pay[i]
+            return s
+    pytest.fail("no rejected flip found")
+
+
+def test_batch_single_launch_corruption_fp32(pz):
+    """Eight FP32 CNN tensors in one batch (784 locate tiles: the single
+    decompress kernel, 32-bit symbols), two of them corrupt, one in a chunk
+    of its last locate tile and one in a middle chunk, and one ragged at its
+    end: only the corrupt tensors report corruption, every other output is
+    exact; a clean batch on the same stream afterwards reports none."""
+    (t,) = pzinputs.cnn_feature_maps_fp32()
+    full = t.data
+    ragged = full[: full.size - 5 * 4096 - 20]
+    good = oracle.compress(full, 32, threads=THREADS)
+    good_r = oracle.compress(ragged, 32, threads=THREADS)
+    H = oracle.header_table(good, full.size)
+    coded = np.flatnonzero(H < 4096)
+    rng = np.random.default_rng(17)
+    bad_last = _rejected_flip(good, full.size, 32, int(coded[-1]), rng)
+    bad_mid = _rejected_flip(good, full.size, 32, int(coded[coded.size // 2]), rng)
+    assert int(coded[-1]) >= oracle.num_chunks(full.size) - 64
+    assert oracle.decompress_status(bad_last, full.size, 32) != oracle.OK
+    assert oracle.decompress_status(bad_mid, full.size, 32) != oracle.OK
+    streams = [good, bad_last, good_r, good, bad_mid, good, good, good]
+    datas = [full, full, ragged, full, full, full, full, full]
+    expect = [0, 3, 0, 0, 3, 0, 0, 0]
+    print("[batch] single-launch decompress, two corrupt FP32 tensors of eight", flush=True)
+    outs, status = pz.pz_decompress_batch([_dev(x) for x in streams], [x.size for x in streams],
+                                          [d.size for d in datas], pzinputs.FP32, 32)
+    assert status.cpu().tolist() == expect
+    for i, d in enumerate(datas):
+        if expect[i] == 0:
+            assert np.array_equal(outs[i][: d.size].cpu().numpy(), d), i
+    clean = [good if x is not good_r else good_r for x in streams]
+    outs, status = pz.pz_decompress_batch([_dev(x) for x in clean], [x.size for x in clean],
+                                          [d.size for d in datas], pzinputs.FP32, 32)
+    assert status.cpu().tolist() == [0] * 8
+    for i, d in enumerate(datas):
+        assert np.array_equal(outs[i][: d.size].cpu().numpy(), d), i
