@@ -16,8 +16,10 @@ it). Prints one JSON line.
 
 value = raw bytes of the workload / mean time of one step (each raw byte is
 both compressed and decompressed in a step). The roofline object reports the
-dominant kernel's algorithmic HBM traffic (read raw + write compressed) per
-unit of its measured time against MI355X's 8 TB/s. The CPU baseline is the
+dominant kernel's algorithmic HBM traffic (raw plus compressed bytes, one
+read and the other written) per unit of its measured time against MI355X's
+8 TB/s: the longer of the batched compress launch and, when it is a single
+kernel, the batched decompress launch. The CPU baseline is the
 oracle (oracle/pzref.c) on the same tensors on this host's cores: chunk-
 parallel on the whole workload, and single-threaded on a bounded sample.
 
@@ -245,17 +247,28 @@ def main():
     algo = raw_total + comp_total  # algorithmic HBM bytes per direction
     comp_gbps = algo / comp_s / 1e9
     dec_gbps = algo / dec_s / 1e9
-    # The dominant kernel is compress_kernel (a pz_compress_batch call is
-    # one launch of it over the group's tensors): it reads R and writes C.
-    traffic, traffic_note = measured_traffic(
-        "compress_kernel<16>", [batch_name([it["t"].name for it in g]) for g in groups.values()])
+    # The dominant kernel: a pz_compress_batch call is one launch of
+    # compress_kernel over the group's tensors (it reads R and writes C); a
+    # pz_decompress_batch call of at least SINGLE_LAUNCH_MIN_TILES locate
+    # tiles is one launch of decompress_kernel (it reads C and writes R).
+    # The roofline reports the longer of the two.
+    single = all(sum(locate_tiles(it["t"].nbytes) for it in g) >= SINGLE_LAUNCH_MIN_TILES
+                 for g in groups.values())
+    launches = [batch_name([it["t"].name for it in g]) for g in groups.values()]
+    if single and dec_s > comp_s:
+        kernel, gbps = "decompress_kernel", dec_gbps
+        desc = "decompress_kernel (one pz_decompress_batch launch over the workload's tensors: locate and decode)"
+    else:
+        kernel, gbps = "compress_kernel<16>", comp_gbps
+        desc = "compress_kernel (one pz_compress_batch launch over the workload's tensors)"
+    traffic, traffic_note = measured_traffic(kernel, launches)
     roofline = {
         "bound": "hbm",
-        "kernel": "compress_kernel (one pz_compress_batch launch over the workload's tensors)",
-        "achieved": round(comp_gbps, 1),
+        "kernel": desc,
+        "achieved": round(gbps, 1),
         "peak": HBM_PEAK_GBPS,
         "unit": "GB/s",
-        "frac": round(comp_gbps / HBM_PEAK_GBPS, 4),
+        "frac": round(gbps / HBM_PEAK_GBPS, 4),
         "traffic": traffic,
         "algorithmic_bytes": algo,
         "traffic_note": traffic_note,
@@ -736,6 +749,16 @@ def timed_once(fn, flush):
     t0 = time.perf_counter()
     fn()
     return time.perf_counter() - t0
+
+
+# Decompression of a launch of at least this many locate tiles (64 chunks
+# each) is one kernel, decompress_kernel; below it, locate_kernel and then
+# decode_kernel (the library's threshold, pz_decompress.hip).
+SINGLE_LAUNCH_MIN_TILES = 512
+
+
+def locate_tiles(raw_bytes):
+    return -(-(-(-raw_bytes // 4096)) // 64)
 
 
 # The sources each kernel is built from: counters taken for a kernel stay

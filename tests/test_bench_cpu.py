@@ -47,6 +47,25 @@ def test_measured_traffic_never_raises(tmp_path, monkeypatch):
     assert bench.measured_traffic("compress_kernel<16>", [bench.batch_name(names[:2])])[0] is None
 
 
+def test_committed_counters_match_the_kernel_sources():
+    """The counter summary under profiles/ was taken from the kernels as they
+    are: bench.py finds traffic for both candidates of its roofline object."""
+    names = ["gpt2xl_mlp_gelu", "gpt2xl_attn_probs", "gpt2xl_residual"]
+    for kernel in ("compress_kernel<16>", "decompress_kernel"):
+        total, note = bench.measured_traffic(kernel, [bench.batch_name(names)])
+        assert isinstance(total, int) and total > 0, (kernel, note)
+
+
+def test_single_launch_threshold_matches_the_library():
+    import re
+
+    src = open(os.path.join(ROOT, "lossless_bit_plane_amd", "csrc", "pz_decompress.hip")).read()
+    m = re.search(r"constexpr uint32_t kFusedMinTiles = (\d+);", src)
+    assert m and int(m.group(1)) == bench.SINGLE_LAUNCH_MIN_TILES
+    assert bench.locate_tiles(64 * 4096) == 1 and bench.locate_tiles(64 * 4096 + 1) == 2
+    assert bench.locate_tiles(419430400) == 1600
+
+
 def test_host_threads_follow_the_declared_share(monkeypatch):
     n = len(os.sched_getaffinity(0))
     monkeypatch.setenv("OMP_NUM_THREADS", "1")
