@@ -701,10 +701,14 @@ PZ_DEV void decode_group(const DBatch &batch, uint32_t k, uint64_t gtile, const 
     const bool ok = block * kBlockBytes < raw_bytes && coff != kBadChunk;
     const bool raw_chunk = ok && H == raw_len;
     const bool coded = ok && !raw_chunk;
-    uint32_t pos = 1024u * (t & 31), head = 0;
+    // Bit positions from here on count from the start of the chunk's
+    // buffer (its lead added once; at most 31 * 1024 + 1024 + 120 bits, so
+    // they fit the 16-bit field below).
+    const uint32_t lead = chunk_lead[ci];
+    uint32_t pos = lead + 1024u * (t & 31), head = 0;
     if (coded) {
-      const LdsBits in{lds + ci * kChunkBufDwords, chunk_lead[ci]};
-      pos = my_boff;
+      const LdsBits in{lds + ci * kChunkBufDwords, 0u};
+      pos = lead + my_boff;
       head = in.peek(pos);
       pos += 3u * mode.tagged;
     }
@@ -746,7 +750,7 @@ PZ_DEV void decode_group(const DBatch &batch, uint32_t k, uint64_t gtile, const 
       tag = (info >> 16) & 7u;
       raw_chunk = (info >> 19) & 1u;
     }
-    const LdsBits in{lds + (sb >> 5) * kChunkBufDwords, chunk_lead[sb >> 5]};
+    const LdsBits in{lds + (sb >> 5) * kChunkBufDwords, 0u};  // positions include the lead
 
     const bool coded = active && !raw_chunk;
     const bool want_raw = active && (raw_chunk || tag == kRAW);

@@ -100,6 +100,20 @@ def test_batch_ragged_empty_and_split(pz, w):
     assert [n[i] for i, d in enumerate(datas) if d.size == 0] == [0, 0, 0]
 
 
+def test_batch_single_launch_ragged_bf16(pz):
+    """One decompress launch of the single kernel (over 512 locate tiles):
+    the GPT-2 attention probabilities (201 MB, 768 tiles) with seven small
+    ragged tensors whose last locate tiles hold 1 to 63 chunks, so that the
+    decode groups past each tensor's end exit at once. Streams equal the
+    oracle's and outputs equal the inputs."""
+    big = pzinputs.gpt2_small_activations()[1]
+    (base,) = pzinputs.relu_smoke()
+    sizes = [1, 8 * 4096 - 1, 8 * 4096 + 1, 64 * 4096 + 2, 65 * 4096 - 2, 7 * 4096 + 100, 200000]
+    datas = [big.data] + [np.ascontiguousarray(base.data[(3001 * i) % 8192:][:n]) for i, n in enumerate(sizes)]
+    print("[batch] single-launch decompress, ragged BF16", [d.size for d in datas], flush=True)
+    _check_batch(pz, datas, pzinputs.BF16, 16)
+
+
 def test_batch_tile_edges(pz):
     """Tensors ending exactly at, one byte before and one byte after the
     tiles' edges (8 chunks per decode group, 16 per compress tile, 64 per
