@@ -1008,9 +1008,11 @@ __global__ __launch_bounds__(kCThreads, kCWavesPerSimd) void compress_kernel(con
   // a funnel shift. Unit u of the span therefore needs buffer dwords
   // 4u - dsh - 1 .. 4u - dsh + 3, which lie in the aligned quads u - 1 and u
   // (two conflict-free 16-byte LDS reads; dsh is uniform over the chunk).
-  // A lane's units are u = lane + 64 m (a chunk spans at most 257); all
-  // their LDS reads are issued before the first store. Only the first and
-  // last units (shared with the neighbouring chunks) are written piecewise. ---
+  // A lane's units are u = lane + 64 m (a chunk spans at most 257), one
+  // per iteration (issuing all of a chunk's LDS reads before its first
+  // store measured the same: the other waves hide these waits). Only the
+  // first and last units (shared with the neighbouring chunks) are written
+  // piecewise. ---
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const uint32_t c = 2 * wave + (uint32_t)h;
