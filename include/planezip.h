@@ -15,7 +15,7 @@
  *   - All data pointers are device pointers (hipMalloc'd memory or a torch
  *     CUDA/HIP tensor's data_ptr()), owned by the caller, and must be 16-byte
  *     aligned.
- *   - Device scratch (look-back words, a tile counter, per-call offsets) is
+ *   - Device scratch (look-back words, tile counters, per-call offsets) is
  *     kept by the library, one buffer per (device, stream), and reused by the
  *     calls on that stream, so a call normally allocates and clears nothing.
  *     A buffer grows, with hipFreeAsync / hipMallocAsync on its stream, when a
