@@ -123,3 +123,45 @@ def test_random_batches_bitexact(pz, seed):
         assert status.cpu().tolist() == [0] * count
         for i, d in enumerate(datas):
             assert np.array_equal(outs[i][: d.size].cpu().numpy(), d), (seed, case, i)
+
+
+def _big_tensor(rng, n):
+    """A tensor of n bytes from the same structures in pieces of 64 KB to
+    1 MB (each piece's length a random number of whole chunks, ragged at the
+    end)."""
+    parts, left = [], n
+    while left > 0:
+        k = min(left, int(rng.integers(16, 257)) * 4096)
+        parts.append(_chunk(rng, k))
+        left -= k
+    return np.concatenate(parts)[:n]
+
+
+@pytest.mark.parametrize("seed", list(range(2)))
+def test_random_batches_single_launch(pz, seed):
+    """Batches of over 512 locate tiles (one 130-200 MB tensor of mixed
+    structures with 1-5 small random ones, some empty), which decompress in
+    the single ticketed kernel: every stream bit-exact with the oracle,
+    every round trip exact."""
+    import torch
+
+    rng = np.random.default_rng(3000 + seed)
+    datas = [_big_tensor(rng, int(rng.integers(130 << 20, 200 << 20)))]
+    datas += [_tensor(rng) if rng.random() < 0.85 else np.zeros(0, np.uint8) for _ in range(int(rng.integers(1, 6)))]
+    order = rng.permutation(len(datas))
+    datas = [datas[i] for i in order]
+    dtype, bits = PAIRS[int(rng.integers(0, len(PAIRS)))]
+    print(f"[random batch, single launch] seed={seed} sizes={[d.size for d in datas]} dtype={dtype} w={bits}",
+          flush=True)
+    srcs = [torch.from_numpy(d).to("cuda") if d.size else torch.zeros(16, dtype=torch.uint8, device="cuda")[:0]
+            for d in datas]
+    dsts, nb = pz.pz_compress_batch(srcs, dtype, bits)
+    n = [int(v) for v in nb.cpu().tolist()]
+    for i, d in enumerate(datas):
+        o = oracle.compress(d, bits, threads=THREADS)
+        g = dsts[i][: n[i]].cpu().numpy()
+        assert g.size == o.size and np.array_equal(g, o), (seed, i)
+    outs, status = pz.pz_decompress_batch(dsts, n, [d.size for d in datas], dtype, bits)
+    assert status.cpu().tolist() == [0] * len(datas)
+    for i, d in enumerate(datas):
+        assert np.array_equal(outs[i][: d.size].cpu().numpy(), d), (seed, i)
