@@ -758,7 +758,8 @@ SINGLE_LAUNCH_MIN_TILES = 512
 
 
 def locate_tiles(raw_bytes):
-    return -(-(-(-raw_bytes // 4096)) // 64)
+    chunks = (raw_bytes + 4095) // 4096
+    return (chunks + 63) // 64
 
 
 # The sources each kernel is built from: counters taken for a kernel stay
