@@ -224,3 +224,24 @@ def test_batch_single_launch_corruption_fp32(pz):
     assert status.cpu().tolist() == [0] * 8
     for i, d in enumerate(datas):
         assert np.array_equal(outs[i][: d.size].cpu().numpy(), d), i
+
+
+def test_batch_single_launch_length_corruption_fp32(pz):
+    """Six FP32 CNN tensors in one batch (588 locate tiles: the single
+    decompress kernel): one stream with 16 trailing bytes and one a byte
+    short, both corrupt for the oracle (the header sum must equal the
+    stream's length), report corruption; the others decompress exactly."""
+    (t,) = pzinputs.cnn_feature_maps_fp32()
+    d = t.data
+    good = oracle.compress(d, 32, threads=THREADS)
+    long_ = np.concatenate([good, np.zeros(16, np.uint8)])
+    short = good[:-1]
+    assert oracle.decompress_status(long_, d.size, 32) != oracle.OK
+    assert oracle.decompress_status(short, d.size, 32) != oracle.OK
+    streams = [good, long_, good, short, good, good]
+    print("[batch] single-launch decompress, length-corrupt FP32 streams", flush=True)
+    outs, status = pz.pz_decompress_batch([_dev(x) for x in streams], [x.size for x in streams],
+                                          [d.size] * len(streams), pzinputs.FP32, 32)
+    assert status.cpu().tolist() == [0, 3, 0, 3, 0, 0]
+    for i in (0, 2, 4, 5):
+        assert np.array_equal(outs[i][: d.size].cpu().numpy(), d), i
