@@ -245,3 +245,35 @@ def test_batch_single_launch_length_corruption_fp32(pz):
     assert status.cpu().tolist() == [0, 3, 0, 3, 0, 0]
     for i in (0, 2, 4, 5):
         assert np.array_equal(outs[i][: d.size].cpu().numpy(), d), i
+
+
+def test_batch_single_launch_concurrent_streams(pz):
+    """Two single-kernel decompress launches (768 and 588 locate tiles) on
+    two streams with nothing ordering them, three times over: each stream's
+    scratch (tile counter, located-tile counter, look-back words and flags)
+    is its own and every wait is on a started workgroup of the same launch,
+    so both round trips stay exact."""
+    import torch
+
+    big = pzinputs.gpt2_small_activations()[1]
+    (cnn,) = pzinputs.cnn_feature_maps_fp32()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    jobs = [([big.data], pzinputs.BF16, 16), ([cnn.data] * 6, pzinputs.FP32, 32)]
+    comp = []
+    for (datas, dtype, w), s in zip(jobs, streams):
+        with torch.cuda.stream(s):
+            srcs = [_dev(d) for d in datas]
+            dsts, nb = pz.pz_compress_batch(srcs, dtype, w)
+        s.synchronize()
+        comp.append((dsts, [int(v) for v in nb.cpu().tolist()]))
+    for rep in range(3):
+        print(f"[batch] concurrent single-launch decompress on two streams, pass {rep}", flush=True)
+        results = []
+        for (datas, dtype, w), (dsts, n), s in zip(jobs, comp, streams):
+            with torch.cuda.stream(s):
+                results.append(pz.pz_decompress_batch(dsts, n, [d.size for d in datas], dtype, w))
+        torch.cuda.synchronize()
+        for (datas, _, _), (outs, status) in zip(jobs, results):
+            assert status.cpu().tolist() == [0] * len(datas)
+            for i, d in enumerate(datas):
+                assert np.array_equal(outs[i][: d.size].cpu().numpy(), d), (rep, i)
