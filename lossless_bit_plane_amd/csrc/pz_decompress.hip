@@ -526,6 +526,23 @@ PZ_DEV void read_planes(const LdsBits &in, uint32_t &pos, uint32_t (&t)[32], int
     uint32_t win;
     uint64_t after;
     in.peek_code(pos, win, after);
+    // A plane that every decoding lane codes verbatim (the low mantissa
+    // planes of dense data, in most waves): the plane is the code's payload.
+    if (!__ballot(active && live && !(fresh && (win & 1u)))) {
+      const PT p = live ? (((PT)after & ones) ^ above) : (PT)0;
+      above = live ? p : above;
+      pos += active && live ? 1u + L : 0u;
+      if (j < W) {
+        const PT ps = dbx ? (PT)(p << 1) : p;
+        if constexpr (W == 16) {
+          t[j] = (uint32_t)ps;
+          t[j + 16] = (uint32_t)((uint64_t)ps >> 32);
+        } else {
+          t[j] = (uint32_t)ps;
+        }
+      }
+      continue;
+    }
     const uint32_t tz = (uint32_t)__builtin_ctz(win | 32u);  // 5: five or more zeros
     const PT verb = (PT)after & ones;
     // Single (bit 4 set): one 1; pair: two adjacent 1s.
