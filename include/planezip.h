@@ -101,7 +101,10 @@ pz_status_t pz_compressed_size(const void *d_src, size_t raw_bytes, int dtype,
 /* Compress raw_bytes bytes of d_src into d_dst (FORMAT.md §5: the uint16
  * header table H[0..C-1], then the chunk payloads). dst_capacity must be at
  * least PZ_MAX_COMPRESSED_BYTES(raw_bytes); d_out_bytes receives the stream
- * length. The stream is a pure function of (bytes, dtype, elem_bits). */
+ * length. The stream is a pure function of (bytes, dtype, elem_bits): d_src
+ * is read in 16-byte units, so the bytes of its last unit past raw_bytes
+ * may be read (d_src is 16-byte aligned, so that unit lies in the same page
+ * as the tensor's last byte), and they do not change the stream. */
 pz_status_t pz_compress(const void *d_src, size_t raw_bytes, int dtype,
                         int elem_bits, void *d_dst, size_t dst_capacity,
                         uint64_t *d_out_bytes, void *stream);

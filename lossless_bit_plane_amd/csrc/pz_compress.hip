@@ -45,18 +45,22 @@ PZ_DEV void load_block(const uint8_t *__restrict__ src, uint64_t raw_bytes, uint
       d[4 * q + 3] = v.w;
     }
   } else {
-    // The tensor's last block: whole dwords, then the 1..3 trailing bytes.
-    const uint64_t n = off < raw_bytes ? raw_bytes - off : 0;
+    // The tensor's last block: the 16-byte units that hold some of its n
+    // bytes, with the bytes past n cleared. (A 16-byte aligned unit never
+    // crosses a page, so a unit holding a byte of the tensor can be read.)
+    const uint32_t n = off < raw_bytes ? (uint32_t)(raw_bytes - off) : 0u;
+    const uint4 *p = reinterpret_cast<const uint4 *>(src + off);
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const uint64_t b = 4 * (uint64_t)i;
-      uint32_t v = 0;
-      if (b + 4 <= n) {
-        v = *reinterpret_cast<const uint32_t *>(src + off + b);
-      } else if (b < n) {
-        for (uint64_t k = b; k < n; ++k) v |= (uint32_t)src[off + k] << (8 * (k - b));
+    for (int q = 0; q < 8; ++q) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (16u * q < n) v = p[q];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t b = 16u * q + 4u * j;  // first byte of the dword
+        const uint32_t keep = n > b ? n - b : 0u;
+        d[4 * q + j] = keep >= 4u ? w[j] : w[j] & ((1u << (8u * keep)) - 1u);
       }
-      d[i] = v;
     }
   }
 }
