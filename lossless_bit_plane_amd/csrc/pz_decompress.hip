@@ -598,12 +598,14 @@ struct __attribute__((aligned(16))) DecodeShared {
   uint32_t wave_busy[kDecWaves];
 };
 
-// Decodes group gtile (of 8 chunks) of tensor k. With set_status, group 0
-// writes the call's status from the error word (locate must be complete).
-// kShared: the offsets come from locate tiles of the same launch and are
-// read at device scope (decompress_kernel).
-template <int W, bool kShared>
-PZ_DEV void decode_group(const DBatch &batch, uint32_t k, uint64_t gtile, const uint32_t *err_words, uint32_t epoch,
+// Decodes groups gtile0 .. gtile0 + NG - 1 (of 8 chunks each) of tensor k,
+// one after another. The metadata and payload loads of all NG groups are
+// issued at the start, so that the later groups' staging is not waited for.
+// With set_status, group 0 writes the call's status from the error word
+// (locate must be complete). kShared: the offsets come from locate tiles of
+// the same launch and are read at device scope (decompress_kernel).
+template <int W, bool kShared, int NG>
+PZ_DEV void decode_group(const DBatch &batch, uint32_t k, uint64_t gtile0, const uint32_t *err_words, uint32_t epoch,
                          const DMode &mode, bool set_status, DecodeShared &sh) {
   constexpr int N = 1024 / W;
   constexpr uint32_t WMASK = W == 16 ? 0xFFFFu : 0xFFFFFFFFu;
@@ -623,77 +625,98 @@ PZ_DEV void decode_group(const DBatch &batch, uint32_t k, uint64_t gtile, const 
   const uint16_t *__restrict__ block_off = batch.t[k].block_off;
   const uint32_t *err = err_words + k;
   int32_t *status = batch.t[k].status;
-  if (gtile * kDecodeChunks >= nchunks) return;
+  if (gtile0 * kDecodeChunks >= nchunks) return;
   // The call's status: locate, complete before this group, marked a corrupt
   // stream with the call's epoch.
-  if (set_status && gtile == 0 && t == 0 && status)
+  if (set_status && gtile0 == 0 && t == 0 && status)
     *status = __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch ? kStatusCorrupt : 0;
-  const uint64_t gblock0 = gtile * kDecThreads;  // first block of the group
 
   // Every thread's metadata at once: its chunk's payload offset and header
   // and its block's bit offset, so that the staging below waits for one
   // round trip before its payload loads, and the classification none.
   const uint16_t *hdr = reinterpret_cast<const uint16_t *>(src);
-  const uint64_t block = gblock0 + t;
-  const uint64_t chunk = block >> 5;
-  uint64_t my_coff = kBadChunk;
-  uint32_t my_H = 0, my_boff = 0;
-  if (chunk < nchunks) {
-    if constexpr (kShared) {
-      my_coff = __hip_atomic_load(chunk_off + chunk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      my_boff = __hip_atomic_load(block_off + block, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-      my_coff = chunk_off[chunk];
-      my_boff = block_off[block];
+  uint64_t gm_coff[NG];
+  uint32_t gm_H[NG], gm_boff[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const uint64_t block = (gtile0 + g) * kDecThreads + t;
+    const uint64_t chunk = block >> 5;
+    gm_coff[g] = kBadChunk;
+    gm_H[g] = 0;
+    gm_boff[g] = 0;
+    if (chunk < nchunks) {
+      if constexpr (kShared) {
+        gm_coff[g] = __hip_atomic_load(chunk_off + chunk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        gm_boff[g] = __hip_atomic_load(block_off + block, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        gm_coff[g] = chunk_off[chunk];
+        gm_boff[g] = block_off[block];
+      }
+      gm_H[g] = hdr[chunk];
     }
-    my_H = hdr[chunk];
   }
 
-  // --- 1. Stage the 8 payloads (dword-aligned copies); wave w takes 2w, 2w+1
+  // --- 1. Payload loads: wave w takes chunks 2w and 2w+1 of every group
   // (whose metadata its lanes 0 and 32 hold). A payload is at most 258
-  // 16-byte units, five per lane: every load of both chunks is issued before
-  // any is stored, so that the wave waits for memory once. ---
+  // 16-byte units, five per lane: every load is issued before any is
+  // stored, so that the wave waits for memory once. ---
   constexpr int kStageUnits = (kChunkBufDwords / 4 + kWave - 1) / kWave;
-  uint4 sv[2][kStageUnits];
-  uint32_t snq[2], sfull[2];
-  uint64_t sq0[2];
+  uint4 sv[NG][2][kStageUnits];
+  uint32_t snq[NG][2], sfull[NG][2], slead[NG][2];
+  uint64_t sq0[NG][2];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const uint32_t ci = 2 * wave + (uint32_t)h;
-    // Both halves zero-extended: readlane returns an int, and a sign-extended
-    // low half would corrupt every offset with bit 31 set.
-    const uint64_t coff = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)my_coff, 32 * h) |
-                          ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(my_coff >> 32), 32 * h) << 32);
-    const uint32_t H = (uint32_t)__builtin_amdgcn_readlane((int)my_H, 32 * h);
-    const uint64_t q0 = (coff >> 2) & ~3ull;
-    if (lane == 0) chunk_lead[ci] = coff == kBadChunk ? 0u : (uint32_t)(8 * (coff - 4 * q0));
-    const uint32_t nq = coff == kBadChunk ? 0u : ((uint32_t)(coff - 4 * q0) + H + 15) / 16;
-    // Units wholly inside the stream (the others, at its very end, are read
-    // byte by byte below); the loads are unconditional, clamped to the last
-    // such unit, so that none waits for another.
-    const uint64_t inside = comp_bytes > 4 * q0 ? (comp_bytes - 4 * q0) / 16 : 0;
-    const uint32_t nfull = nq < inside ? nq : (uint32_t)inside;
-    snq[h] = nq;
-    sfull[h] = nfull;
-    sq0[h] = q0;
-    const uint4 *g = reinterpret_cast<const uint4 *>(src + 4 * q0);
-    if (nfull > 0) {  // wave-uniform
+  for (int g = 0; g < NG; ++g) {
 #pragma unroll
-      for (int k = 0; k < kStageUnits; ++k) {
-        const uint32_t u = lane + (uint32_t)kWave * k;
-        sv[h][k] = g[u < nfull ? u : nfull - 1];
+    for (int h = 0; h < 2; ++h) {
+      // Both halves zero-extended: readlane returns an int, and a sign-extended
+      // low half would corrupt every offset with bit 31 set.
+      const uint64_t coff =
+          (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)gm_coff[g], 32 * h) |
+          ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(gm_coff[g] >> 32), 32 * h) << 32);
+      const uint32_t H = (uint32_t)__builtin_amdgcn_readlane((int)gm_H[g], 32 * h);
+      const uint64_t q0 = (coff >> 2) & ~3ull;
+      slead[g][h] = coff == kBadChunk ? 0u : (uint32_t)(8 * (coff - 4 * q0));
+      const uint32_t nq = coff == kBadChunk ? 0u : ((uint32_t)(coff - 4 * q0) + H + 15) / 16;
+      // Units wholly inside the stream (the others, at its very end, are read
+      // byte by byte below); the loads are unconditional, clamped to the last
+      // such unit, so that none waits for another.
+      const uint64_t inside = comp_bytes > 4 * q0 ? (comp_bytes - 4 * q0) / 16 : 0;
+      const uint32_t nfull = nq < inside ? nq : (uint32_t)inside;
+      snq[g][h] = nq;
+      sfull[g][h] = nfull;
+      sq0[g][h] = q0;
+      const uint4 *gp = reinterpret_cast<const uint4 *>(src + 4 * q0);
+      if (nfull > 0) {  // wave-uniform
+#pragma unroll
+        for (int kk = 0; kk < kStageUnits; ++kk) {
+          const uint32_t u = lane + (uint32_t)kWave * kk;
+          sv[g][h][kk] = gp[u < nfull ? u : nfull - 1];
+        }
       }
     }
   }
+
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+  const uint64_t gtile = gtile0 + g;
+  if (gtile * kDecodeChunks >= nchunks) break;
+  if (g > 0) __syncthreads();  // the previous group's rows are stored: LDS is free
+  const uint64_t gblock0 = gtile * kDecThreads;  // first block of the group
+  const uint64_t block = gblock0 + t;
+  const uint64_t chunk = block >> 5;
+  const uint64_t my_coff = gm_coff[g];
+  const uint32_t my_H = gm_H[g], my_boff = gm_boff[g];
+  // Stage the group's 8 payloads (dword-aligned copies).
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
+    if (lane == 0) chunk_lead[2 * wave + (uint32_t)h] = slead[g][h];
     uint4 *buf4 = reinterpret_cast<uint4 *>(lds + (2 * wave + (uint32_t)h) * kChunkBufDwords);
 #pragma unroll
-    for (int k = 0; k < kStageUnits; ++k) {
-      const uint32_t u = lane + (uint32_t)kWave * k;
-      if (u >= snq[h]) continue;
-      const uint64_t b = 4 * sq0[h] + 16ull * u;
-      if (u >= sfull[h]) {
+    for (int kk = 0; kk < kStageUnits; ++kk) {
+      const uint32_t u = lane + (uint32_t)kWave * kk;
+      if (u >= snq[g][h]) continue;
+      const uint64_t b = 4 * sq0[g][h] + 16ull * u;
+      if (u >= sfull[g][h]) {
         // The stream's last bytes: byte loads below comp_bytes, zeros above.
         uint32_t tv[4] = {0, 0, 0, 0};
 #pragma unroll 1
@@ -701,9 +724,9 @@ PZ_DEV void decode_group(const DBatch &batch, uint32_t k, uint64_t gtile, const 
           const uint32_t x = (uint32_t)src[b + q] << (8 * (q & 3));
           if (q < 4) tv[0] |= x; else if (q < 8) tv[1] |= x; else if (q < 12) tv[2] |= x; else tv[3] |= x;
         }
-        sv[h][k] = make_uint4(tv[0], tv[1], tv[2], tv[3]);
+        sv[g][h][kk] = make_uint4(tv[0], tv[1], tv[2], tv[3]);
       }
-      buf4[u] = sv[h][k];
+      buf4[u] = sv[g][h][kk];
     }
   }
   __syncthreads();
@@ -925,6 +948,7 @@ PZ_DEV void decode_group(const DBatch &batch, uint32_t k, uint64_t gtile, const 
         dst[span0 + bb] = (uint8_t)(w4[(bb - b0) >> 2] >> (8 * ((bb - b0) & 3)));
     }
   }
+  }
 }
 
 template <int W>
@@ -937,15 +961,15 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DBatch batch,
 #pragma unroll
     for (uint32_t i = 1; i < (uint32_t)kMaxBatch; ++i) k += i < batch.n && blockIdx.x >= batch.t[i].group_begin ? 1u : 0u;
   }
-  decode_group<W, false>(batch, k, blockIdx.x - batch.t[k].group_begin, err_words, epoch, mode, true, sh);
+  decode_group<W, false, 1>(batch, k, blockIdx.x - batch.t[k].group_begin, err_words, epoch, mode, true, sh);
 }
 
 // Both halves in one launch, for launches of many tiles. Workgroups take
 // tickets in the order they start: tickets 0 .. T-1 locate tiles 0 .. T-1,
-// ticket T + g decodes group g, numbered by tile (tile u holds groups
-// 8u .. 8u+7 of its tensor; those past the tensor's last chunk exit at
-// once). A decode group waits for its tile's flag, and that tile always has
-// an earlier ticket, so every wait is on a workgroup that is running or
+// ticket T + j decodes groups 2j and 2j + 1, numbered by tile (tile u holds
+// groups 8u .. 8u+7 of its tensor; those past the tensor's last chunk are
+// skipped). A decode ticket waits for its tile's flag, and that tile always
+// has an earlier ticket, so every wait is on a workgroup that is running or
 // done. The decode groups of the first tiles thus run beside the last
 // walks, where two launches would leave the GPU partly idle at the end of
 // the walks and between the kernels.
@@ -959,10 +983,18 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DBatch batch,
 // device scope would add an L2 write-back per locate wave and an L2
 // invalidation per decode group, which measured 60% slower.
 static_assert(kLocateChunks == 8 * kDecodeChunks, "a locate tile is eight decode groups");
+// Decode groups per ticket of the single kernel (the second group's loads
+// are issued with the first's: measured on the GPT-2-XL batch, 2 groups per
+// ticket decompressed 3% faster than 1, and 4 or 8, with the next group
+// prefetched while one is decoded, 7% and 12% slower), and decode tickets per
+// tile.
+constexpr uint32_t kFusedGroups = 2;
+constexpr uint32_t kDecodeTickets = 8 / kFusedGroups;
+static_assert(kDecodeTickets * kFusedGroups == 8, "a tile's groups split evenly over its tickets");
 static_assert(kLocateThreads == kDecThreads, "one workgroup size for both halves");
 
 template <int W, int G>
-__global__ __launch_bounds__(kDecThreads) void decompress_kernel(const DBatch batch, uint32_t *err_words,
+__global__ __launch_bounds__(kDecThreads, 4) void decompress_kernel(const DBatch batch, uint32_t *err_words,
                                                                    uint32_t epoch, uint64_t *lb_words,
                                                                    uint32_t *tile_counter, uint32_t counter_base,
                                                                    uint32_t *done, uint32_t done_base, DMode mode) {
@@ -977,7 +1009,7 @@ __global__ __launch_bounds__(kDecThreads) void decompress_kernel(const DBatch ba
   const uint32_t ticket = __builtin_amdgcn_readfirstlane(ticket_s);
   const uint32_t T = batch.total_tiles;
   const bool loc = ticket < T;
-  const uint32_t tile = loc ? ticket : (ticket - T) >> 3;
+  const uint32_t tile = loc ? ticket : (ticket - T) / kDecodeTickets;
   if (tile >= T) return;
   const uint32_t k = tensor_of_tile(batch, tile);
   uint64_t *flag = lb_words + (uint64_t)tile * kLookbackStride + 1;  // beside the tile's look-back word
@@ -997,14 +1029,15 @@ __global__ __launch_bounds__(kDecThreads) void decompress_kernel(const DBatch ba
       }
     }
   } else {
-    const uint64_t g = (uint64_t)(tile - batch.t[k].tile_begin) * 8u + ((ticket - T) & 7u);
+    const uint64_t g =
+        (uint64_t)(tile - batch.t[k].tile_begin) * 8u + ((ticket - T) % kDecodeTickets) * kFusedGroups;
     if (g * kDecodeChunks >= batch.t[k].nchunks) return;
     if (t == 0) {
       while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != (uint64_t)epoch)
         __builtin_amdgcn_s_sleep(16);
     }
     __syncthreads();
-    decode_group<W, true>(batch, k, g, err_words, epoch, mode, false, sh.d);
+    decode_group<W, true, kFusedGroups>(batch, k, g, err_words, epoch, mode, false, sh.d);
   }
 }
 
@@ -1044,7 +1077,7 @@ constexpr uint32_t kFusedMinTiles = 512;
 
 ScratchNeed decompress_need(const DBatch &b, size_t extra) {
   if (b.total_tiles >= kFusedMinTiles)
-    return ScratchNeed{b.total_tiles * kLookbackStride, extra, 9 * b.total_tiles, b.total_tiles};
+    return ScratchNeed{b.total_tiles * kLookbackStride, extra, (1 + kDecodeTickets) * b.total_tiles, b.total_tiles};
   return ScratchNeed{b.total_tiles * kLookbackStride, extra, b.total_tiles, 0};
 }
 
@@ -1059,7 +1092,7 @@ hipError_t launch_decompress(int w, DBatch &batch, uint32_t codec_mask, int tagg
     extra += decompress_extra(x.raw_bytes);
   }
   if (batch.total_tiles >= kFusedMinTiles) {
-    const dim3 grid(9 * batch.total_tiles);  // T locate tiles, 8T decode groups
+    const dim3 grid((1 + kDecodeTickets) * batch.total_tiles);  // T locate tiles, then the decode tickets
     if (w == 16)
       hipLaunchKernelGGL((decompress_kernel<16, kLocateLanes>), grid, dim3(kDecThreads), 0, stream, batch, scratch.err,
                          scratch.epoch, scratch.words, scratch.counter, scratch.counter_base, scratch.done,
