@@ -143,6 +143,9 @@ def main():
         if flush_buf is not None:
             flush_buf.fill_(0x5A)
 
+    copy_gbps = measure_copy(torch, dev, cur)
+    log(f"plain device copy of 512 MiB: {copy_gbps:.0f} GB/s of reads plus writes")
+
     # Batched step: one call per direction for each (dtype, width) group of
     # tensors (the bench workload is one group).
     groups = {}
@@ -272,6 +275,10 @@ def main():
         "traffic": traffic,
         "algorithmic_bytes": algo,
         "traffic_note": traffic_note,
+        # A plain device-to-device copy in the same run: what the memory
+        # system gives a kernel with nothing to compute (reads plus writes).
+        "copy_gbps": round(copy_gbps, 1),
+        "frac_of_copy": round(gbps / copy_gbps, 4),
     }
 
     p10, p50, p90 = (float(x) for x in np.percentile(step_ms, [10, 50, 90]))
@@ -371,6 +378,23 @@ def main():
     if variants is not None:
         out["variants"] = variants
     print(json.dumps(out), flush=True)
+
+
+def measure_copy(torch, dev, cur, nbytes=512 << 20, reps=5):
+    """Read-plus-write GB/s of a plain device-to-device copy (torch's copy
+    kernel), best of `reps`, HIP events on the current stream."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    best = float("inf")
+    for _ in range(reps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record(cur)
+        b.copy_(a)
+        e[1].record(cur)
+        torch.cuda.synchronize()
+        best = min(best, e[0].elapsed_time(e[1]) / 1e3)
+    del a, b
+    return 2 * nbytes / best / 1e9
 
 
 TAG_NAMES = ("ZVC", "DBX", "BX", "ZBX", "RAW")  # tags 0..4
