@@ -105,9 +105,10 @@ def test_batch_single_launch_ragged_bf16(pz):
     the GPT-2 attention probabilities (201 MB, 768 tiles) with seven small
     ragged tensors whose last locate tiles hold 1 to 63 chunks, so that the
     decode groups past each tensor's end are skipped (a decode ticket takes
-    two groups: tensors of 1, 7 and 49 chunks leave a ticket's second group
-    past the end, one of 65 chunks a whole tile with one group). Streams
-    equal the oracle's and outputs equal the inputs."""
+    two groups: tensors of 1, 8, 49 and 65 chunks leave a ticket's second
+    group past the end, and the 65-chunk tensor's second tile has three
+    tickets with no group at all). Streams equal the oracle's and outputs
+    equal the inputs."""
     big = pzinputs.gpt2_small_activations()[1]
     (base,) = pzinputs.relu_smoke()
     sizes = [1, 8 * 4096 - 1, 8 * 4096 + 1, 64 * 4096 + 2, 65 * 4096 - 2, 7 * 4096 + 100, 200000]
