@@ -775,9 +775,10 @@ def timed_once(fn, flush):
     return time.perf_counter() - t0
 
 
-# Decompression of a launch of at least this many locate tiles (64 chunks
-# each) is one kernel, decompress_kernel; below it, locate_kernel and then
-# decode_kernel (the library's threshold, pz_decompress.hip).
+# Decompression of a launch of at least this many locate tiles (counted in
+# tiles of 64 chunks) is one kernel, decompress_kernel; below it,
+# locate_kernel and then decode_kernel (the library's threshold,
+# pz_decompress.hip).
 SINGLE_LAUNCH_MIN_TILES = 512
 
 

@@ -247,14 +247,12 @@ pz_status_t decompress_many(int dtype, int elem_bits, uint32_t codec_mask, int t
       x.comp_bytes = comp[j];
       x.raw_bytes = raw[j];
       x.nchunks = PZ_NUM_CHUNKS(raw[j]);
-      x.tile_begin = b.total_tiles;
-      x.ntiles = pz::locate_tiles(raw[j]);
       x.group_begin = b.total_groups;
       x.ngroups = pz::decode_groups(raw[j]);
-      b.total_tiles += x.ntiles;
       b.total_groups += x.ngroups;
       extra += pz::decompress_extra(raw[j]);
     }
+    pz::plan_decompress(w, b);
     const pz::ScratchNeed need = pz::decompress_need(b, extra);
     const hipError_t e = with_scratch(s, need, [&](const pz::Scratch &sc) {
       return pz::launch_decompress(w, b, codec_mask, tagged, sc, s);

@@ -73,14 +73,17 @@ inline DMode make_dmode(int W, uint32_t mask, int tagged) {
 // but walks four times as many steps per wave; it measured slower on every
 // tensor of the bench workload.)
 // ---------------------------------------------------------------------------
-// Lanes per chunk. The kernel takes 4, 8 or 16; measured on the five
-// workloads, 8 lanes (32 speculated codes, 32 chunks per workgroup) decoded
-// the 25.7 MB FP32 CNN tensor 8% faster and the others no faster (the GPT-2
-// tensors 20% slower), 16 lanes were slower everywhere: a step's latency,
-// not its width, sets a small tensor's walk.
+// Lanes per chunk. The kernel takes 4, 8 or 16: 4 in the single decompress
+// kernel and for 16-bit symbols, 8 for 32-bit symbols in launches of locate
+// and decode (32 speculated codes settle a block's 32 planes in fewer steps;
+// 8 lanes made the GPT-2 tensors 20% slower, 16 lanes were slower
+// everywhere: a step's latency, not its width, sets a small tensor's walk).
 constexpr int kLocateLanes = 4;
+constexpr int kLocateLanesWide = 8;
 constexpr int kLocateThreads = 256;            // four waves per workgroup
-constexpr int kLocateChunks = kLocateThreads / kLocateLanes;  // chunks per tile (per workgroup)
+template <int G>
+constexpr int locate_chunks() { return kLocateThreads / G; }  // chunks per tile (per workgroup)
+constexpr int kLocateChunks = locate_chunks<kLocateLanes>();
 // Per-chunk LDS region: a ring of kRingDwords dwords of the chunk's stream, one
 // mirror dword (slot kRingDwords = slot 0, so a peek at the last slot reads two
 // dwords), then the chunk's 32 block offsets (16-bit). 145 dwords: odd, spreads
@@ -90,13 +93,6 @@ constexpr int kLocateChunks = kLocateThreads / kLocateLanes;  // chunks per tile
 constexpr int kRingDwords = 128;
 constexpr int kRingRegion = kRingDwords + 1 + 16;
 constexpr uint32_t kBlockAhead = 38;   // dwords one block (and its look-ahead) can touch
-// Refill unit: 32 dwords, split over the G lanes (at least one 16-byte load each).
-constexpr uint32_t kGroupDwords = 4 * kLocateLanes > 32 ? 4 * kLocateLanes : 32;
-constexpr int kStartGroups = (int)((kBlockAhead + kGroupDwords - 1) / kGroupDwords);
-// A refill made while a group is short (fill < cur + kBlockAhead) and the
-// request made after the first groups must not overwrite dwords at or above cur.
-static_assert(kBlockAhead - 1 + kGroupDwords <= (uint32_t)kRingDwords, "refill fits in the ring");
-static_assert((kStartGroups + 1) * kGroupDwords <= (uint32_t)kRingDwords, "start fits in the ring");
 
 // One of four values by the two low bits of k, as bit-tested selects (an
 // equality chain would be turned into branches).
@@ -116,6 +112,12 @@ PZ_DEV uint32_t group_lane(uint32_t v, uint32_t k) {
     const uint32_t b2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xAA, 0xF, 0xF, true);
     const uint32_t b3 = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xFF, 0xF, 0xF, true);
     return select4(k, b0, b1, b2, b3);
+  } else if constexpr (G == 8) {
+    // Lane k & 3 of each quad, then the other quad's copy by a half-row mirror
+    // (lane i of the 8 reads lane 7 - i, which lies in the other quad).
+    const uint32_t b = group_lane<4>(v, k & 3u);
+    const uint32_t m = (uint32_t)__builtin_amdgcn_mov_dpp((int)b, 0x141, 0xF, 0xF, true);
+    return ((lane_id() >> 2) & 1u) == (k >> 2) ? b : m;
   } else {
     return (uint32_t)__shfl((int)v, (int)((lane_id() & ~(uint32_t)(G - 1)) | k), 64);
   }
@@ -148,6 +150,14 @@ PZ_DEV uint64_t group_or(uint64_t v) {
 // on the spot. Each of the G lanes holds and stores 32/G of the 32 dwords.
 template <int G>
 struct ChunkRing {
+  // Refill unit: 32 dwords (4G for 16 lanes), split over the G lanes (at
+  // least one 16-byte load each).
+  static constexpr uint32_t kGroupDwords = 4 * G > 32 ? 4 * G : 32;
+  static constexpr int kStartGroups = (int)((kBlockAhead + kGroupDwords - 1) / kGroupDwords);
+  // A refill made while a group is short (fill < cur + kBlockAhead) and the
+  // request made after the first groups must not overwrite dwords at or above cur.
+  static_assert(kBlockAhead - 1 + kGroupDwords <= (uint32_t)kRingDwords, "refill fits in the ring");
+  static_assert((kStartGroups + 1) * kGroupDwords <= (uint32_t)kRingDwords, "start fits in the ring");
   static constexpr int kPart = kGroupDwords / G;  // dwords per lane per refill
   uint32_t *ring;
   const uint8_t *src;
@@ -362,8 +372,9 @@ PZ_DEV uint32_t tensor_of_tile(const DBatch &batch, uint32_t gtile) {
   return k;
 }
 
+template <int G>
 struct LocateShared {
-  uint32_t lds[kLocateChunks * kRingRegion];
+  uint32_t lds[locate_chunks<G>() * kRingRegion];
   uint64_t wave_sum[kLocateThreads / kWave];
   uint64_t tile_before;
 };
@@ -374,7 +385,7 @@ struct LocateShared {
 // scope (decompress_kernel).
 template <int W, int G, bool kShared>
 PZ_DEV void locate_tile(const DBatch &batch, uint32_t k, uint32_t gtile, uint32_t *err_words, uint32_t epoch,
-                        uint64_t *lb_words, const DMode &mode, LocateShared &sh) {
+                        uint64_t *lb_words, const DMode &mode, LocateShared<G> &sh) {
   constexpr int kWaves = kLocateThreads / kWave;  // 256 / G chunks x G lanes
   uint32_t *lds = sh.lds;
   uint64_t *wave_sum = sh.wave_sum;
@@ -394,7 +405,7 @@ PZ_DEV void locate_tile(const DBatch &batch, uint32_t k, uint32_t gtile, uint32_
   // Chunk offsets: a scan of the 16-bit headers over the tile, and one
   // look-back per tile for the headers before it.
   const uint32_t ci = t / G;  // chunk within the tile
-  const uint64_t c = (uint64_t)tile * kLocateChunks + ci;
+  const uint64_t c = (uint64_t)tile * locate_chunks<G>() + ci;
   const uint32_t H = c < nchunks ? reinterpret_cast<const uint16_t *>(src)[c] : 0u;
   const uint64_t incl = wave_inclusive_scan_u64(ql == 0 ? H : 0u);  // equal over the group
   if (lane == kWave - 1) wave_sum[wave] = incl;
@@ -456,7 +467,7 @@ __global__ __launch_bounds__(kLocateThreads) void locate_kernel(const DBatch bat
                                                                     uint32_t epoch, uint64_t *lb_words,
                                                                     uint32_t *tile_counter,
                                                                     uint32_t counter_base, DMode mode) {
-  __shared__ LocateShared sh;
+  __shared__ LocateShared<G> sh;
   __shared__ uint32_t group_tile;
   if (threadIdx.x == 0) group_tile = atomicAdd(tile_counter, 1u) - counter_base;
   __syncthreads();
@@ -698,258 +709,258 @@ PZ_DEV void decode_group(const DBatch &batch, uint32_t k, uint64_t gtile0, const
 
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
-  const uint64_t gtile = gtile0 + g;
-  if (gtile * kDecodeChunks >= nchunks) break;
-  if (g > 0) __syncthreads();  // the previous group's rows are stored: LDS is free
-  const uint64_t gblock0 = gtile * kDecThreads;  // first block of the group
-  const uint64_t block = gblock0 + t;
-  const uint64_t chunk = block >> 5;
-  const uint64_t my_coff = gm_coff[g];
-  const uint32_t my_H = gm_H[g], my_boff = gm_boff[g];
-  // Stage the group's 8 payloads (dword-aligned copies).
+    const uint64_t gtile = gtile0 + g;
+    if (gtile * kDecodeChunks >= nchunks) break;
+    if (g > 0) __syncthreads();  // the previous group's rows are stored: LDS is free
+    const uint64_t gblock0 = gtile * kDecThreads;  // first block of the group
+    const uint64_t block = gblock0 + t;
+    const uint64_t chunk = block >> 5;
+    const uint64_t my_coff = gm_coff[g];
+    const uint32_t my_H = gm_H[g], my_boff = gm_boff[g];
+    // Stage the group's 8 payloads (dword-aligned copies).
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    if (lane == 0) chunk_lead[2 * wave + (uint32_t)h] = slead[g][h];
-    uint4 *buf4 = reinterpret_cast<uint4 *>(lds + (2 * wave + (uint32_t)h) * kChunkBufDwords);
+    for (int h = 0; h < 2; ++h) {
+      if (lane == 0) chunk_lead[2 * wave + (uint32_t)h] = slead[g][h];
+      uint4 *buf4 = reinterpret_cast<uint4 *>(lds + (2 * wave + (uint32_t)h) * kChunkBufDwords);
 #pragma unroll
-    for (int kk = 0; kk < kStageUnits; ++kk) {
-      const uint32_t u = lane + (uint32_t)kWave * kk;
-      if (u >= snq[g][h]) continue;
-      const uint64_t b = 4 * sq0[g][h] + 16ull * u;
-      if (u >= sfull[g][h]) {
-        // The stream's last bytes: byte loads below comp_bytes, zeros above.
-        uint32_t tv[4] = {0, 0, 0, 0};
+      for (int kk = 0; kk < kStageUnits; ++kk) {
+        const uint32_t u = lane + (uint32_t)kWave * kk;
+        if (u >= snq[g][h]) continue;
+        const uint64_t b = 4 * sq0[g][h] + 16ull * u;
+        if (u >= sfull[g][h]) {
+          // The stream's last bytes: byte loads below comp_bytes, zeros above.
+          uint32_t tv[4] = {0, 0, 0, 0};
 #pragma unroll 1
-        for (uint32_t q = 0; q < 16 && b + q < comp_bytes; ++q) {
-          const uint32_t x = (uint32_t)src[b + q] << (8 * (q & 3));
-          if (q < 4) tv[0] |= x; else if (q < 8) tv[1] |= x; else if (q < 12) tv[2] |= x; else tv[3] |= x;
+          for (uint32_t q = 0; q < 16 && b + q < comp_bytes; ++q) {
+            const uint32_t x = (uint32_t)src[b + q] << (8 * (q & 3));
+            if (q < 4) tv[0] |= x; else if (q < 8) tv[1] |= x; else if (q < 12) tv[2] |= x; else tv[3] |= x;
+          }
+          sv[g][h][kk] = make_uint4(tv[0], tv[1], tv[2], tv[3]);
         }
-        sv[g][h][kk] = make_uint4(tv[0], tv[1], tv[2], tv[3]);
+        buf4[u] = sv[g][h][kk];
       }
-      buf4[u] = sv[g][h][kk];
     }
-  }
-  __syncthreads();
+    __syncthreads();
 
-  // --- 2. Block t: all-zero blocks stay here, the rest go to the slot list. ---
-  bool busy = false;
-  {
-    const uint32_t ci = t >> 5;
-    const uint64_t coff = my_coff;
-    const uint32_t H = my_H;
-    const uint32_t raw_len = chunk < nchunks ? (uint32_t)min_u64(kChunkBytes, raw_bytes - chunk * kChunkBytes) : 0u;
-    const bool ok = block * kBlockBytes < raw_bytes && coff != kBadChunk;
-    const bool raw_chunk = ok && H == raw_len;
-    const bool coded = ok && !raw_chunk;
-    // Bit positions from here on count from the start of the chunk's
-    // buffer (its lead added once; at most 31 * 1024 + 1024 + 120 bits, so
-    // they fit the 16-bit field below).
-    const uint32_t lead = chunk_lead[ci];
-    uint32_t pos = lead + 1024u * (t & 31), head = 0;
-    if (coded) {
-      const LdsBits in{lds + ci * kChunkBufDwords, 0u};
-      pos = lead + my_boff;
-      head = in.peek(pos);
-      pos += 3u * mode.tagged;
+    // --- 2. Block t: all-zero blocks stay here, the rest go to the slot list. ---
+    bool busy = false;
+    {
+      const uint32_t ci = t >> 5;
+      const uint64_t coff = my_coff;
+      const uint32_t H = my_H;
+      const uint32_t raw_len = chunk < nchunks ? (uint32_t)min_u64(kChunkBytes, raw_bytes - chunk * kChunkBytes) : 0u;
+      const bool ok = block * kBlockBytes < raw_bytes && coff != kBadChunk;
+      const bool raw_chunk = ok && H == raw_len;
+      const bool coded = ok && !raw_chunk;
+      // Bit positions from here on count from the start of the chunk's
+      // buffer (its lead added once; at most 31 * 1024 + 1024 + 120 bits, so
+      // they fit the 16-bit field below).
+      const uint32_t lead = chunk_lead[ci];
+      uint32_t pos = lead + 1024u * (t & 31), head = 0;
+      if (coded) {
+        const LdsBits in{lds + ci * kChunkBufDwords, 0u};
+        pos = lead + my_boff;
+        head = in.peek(pos);
+        pos += 3u * mode.tagged;
+      }
+      const bool zero = coded && (head & mode.zmask) == mode.zcode;
+      const uint32_t tag = mode.tagged ? head & 7u : mode.fixed;
+      busy = raw_chunk || (coded && !zero);
+      if (busy) blk_info[t] = pos | (tag << 16) | ((uint32_t)raw_chunk << 19);
     }
-    const bool zero = coded && (head & mode.zmask) == mode.zcode;
-    const uint32_t tag = mode.tagged ? head & 7u : mode.fixed;
-    busy = raw_chunk || (coded && !zero);
-    if (busy) blk_info[t] = pos | (tag << 16) | ((uint32_t)raw_chunk << 19);
-  }
-  const uint64_t bmask = __ballot(busy);
-  if (lane == 0) wave_busy[wave] = (uint32_t)popc64(bmask);
-  __syncthreads();
-  uint32_t nbusy = 0, first = 0;
+    const uint64_t bmask = __ballot(busy);
+    if (lane == 0) wave_busy[wave] = (uint32_t)popc64(bmask);
+    __syncthreads();
+    uint32_t nbusy = 0, first = 0;
 #pragma unroll
-  for (int k = 0; k < kDecWaves; ++k) {
-    const uint32_t c = wave_busy[k];
-    first += (uint32_t)k < wave ? c : 0u;
-    nbusy += c;
-  }
-  if (busy) slot_block[first + lanes_below(bmask)] = (uint8_t)t;
-  __syncthreads();
-
-  // --- 3. Packed slots: raw copy, ZVC or plane decoding into d. Waves take the
-  // slots in an order rotated per tile, so that the busy waves of successive
-  // groups fall on different SIMDs. ---
-  const uint32_t slot = (t + kDecThreads - 64u * (uint32_t)(gtile % kDecWaves)) % kDecThreads;
-  const bool active = slot < nbusy;
-  const bool wave_active = __ballot(active) != 0;
-  uint32_t sb = 0;
-  uint64_t nzmask = 0;
-  bool want_spread = false;  // ZVC or ZBX: symbols in order of the non-zero positions
-  uint32_t d[32];
-  if (wave_active) {
-    uint32_t pos = 0, tag = kBX;
-    bool raw_chunk = false;
-    if (active) {
-      sb = slot_block[slot];
-      const uint32_t info = blk_info[sb];
-      pos = info & 0xFFFFu;
-      tag = (info >> 16) & 7u;
-      raw_chunk = (info >> 19) & 1u;
+    for (int k = 0; k < kDecWaves; ++k) {
+      const uint32_t c = wave_busy[k];
+      first += (uint32_t)k < wave ? c : 0u;
+      nbusy += c;
     }
-    const LdsBits in{lds + (sb >> 5) * kChunkBufDwords, 0u};  // positions include the lead
+    if (busy) slot_block[first + lanes_below(bmask)] = (uint8_t)t;
+    __syncthreads();
 
-    const bool coded = active && !raw_chunk;
-    const bool want_raw = active && (raw_chunk || tag == kRAW);
-    const bool want_zvc = coded && tag == kZVC;
-    const bool want_dbx = coded && tag == kDBX;
-    const bool want_planes = coded && (tag == kDBX || tag == kBX || tag == kZBX);
-    const bool want_zbx = coded && tag == kZBX;
-    // Zero mask of ZVC and ZBX (bit i = symbol i non-zero).
-    if (want_zvc || want_zbx) {
-      nzmask = W == 16 ? in.peek64(pos) : (uint64_t)in.peek(pos);
-      pos += N;
-    }
+    // --- 3. Packed slots: raw copy, ZVC or plane decoding into d. Waves take the
+    // slots in an order rotated per tile, so that the busy waves of successive
+    // groups fall on different SIMDs. ---
+    const uint32_t slot = (t + kDecThreads - 64u * (uint32_t)(gtile % kDecWaves)) % kDecThreads;
+    const bool active = slot < nbusy;
+    const bool wave_active = __ballot(active) != 0;
+    uint32_t sb = 0;
+    uint64_t nzmask = 0;
+    bool want_spread = false;  // ZVC or ZBX: symbols in order of the non-zero positions
+    uint32_t d[32];
+    if (wave_active) {
+      uint32_t pos = 0, tag = kBX;
+      bool raw_chunk = false;
+      if (active) {
+        sb = slot_block[slot];
+        const uint32_t info = blk_info[sb];
+        pos = info & 0xFFFFu;
+        tag = (info >> 16) & 7u;
+        raw_chunk = (info >> 19) & 1u;
+      }
+      const LdsBits in{lds + (sb >> 5) * kChunkBufDwords, 0u};  // positions include the lead
 
-    // Plane decoding first (it needs the most registers, and d is not yet
-    // holding anything), then the raw and ZVC blocks fill d.
-    if (__ballot(want_planes)) {
-      uint32_t base = 0;
-      if (want_dbx) {
-        base = in.peek(pos) & WMASK;
-        pos += W;
+      const bool coded = active && !raw_chunk;
+      const bool want_raw = active && (raw_chunk || tag == kRAW);
+      const bool want_zvc = coded && tag == kZVC;
+      const bool want_dbx = coded && tag == kDBX;
+      const bool want_planes = coded && (tag == kDBX || tag == kBX || tag == kZBX);
+      const bool want_zbx = coded && tag == kZBX;
+      // Zero mask of ZVC and ZBX (bit i = symbol i non-zero).
+      if (want_zvc || want_zbx) {
+        nzmask = W == 16 ? in.peek64(pos) : (uint64_t)in.peek(pos);
+        pos += N;
       }
-      int K = W;
-      uint32_t L = N;
-      if (want_dbx) {
-        K = W + 1;
-        L = N - 1;
-      } else if (want_zbx) {
-        L = (uint32_t)popc64(nzmask);
+
+      // Plane decoding first (it needs the most registers, and d is not yet
+      // holding anything), then the raw and ZVC blocks fill d.
+      if (__ballot(want_planes)) {
+        uint32_t base = 0;
+        if (want_dbx) {
+          base = in.peek(pos) & WMASK;
+          pos += W;
+        }
+        int K = W;
+        uint32_t L = N;
+        if (want_dbx) {
+          K = W + 1;
+          L = N - 1;
+        } else if (want_zbx) {
+          L = (uint32_t)popc64(nzmask);
+        }
+        uint32_t tp[32];
+        read_planes<W>(in, pos, tp, K, L, want_dbx, want_planes);
+        transpose32(tp);
+        if constexpr (W == 16) {
+          // tp[r] = symbol r | symbol r+32 << 16 -> d[i] = symbol 2i | symbol 2i+1 << 16.
+#pragma unroll
+          for (int i = 0; i < 32; ++i) {
+            if (i < 16)
+              d[i] = (tp[2 * i] & 0xFFFFu) | (tp[2 * i + 1] << 16);
+            else
+              d[i] = (tp[2 * i - 32] >> 16) | (tp[2 * i - 31] & 0xFFFF0000u);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 32; ++i) d[i] = tp[i];
+        }
+        // DBX: running sum of the deltas from the base symbol, modulo 2^w.
+        if (__ballot(want_dbx)) {
+          if constexpr (W == 16) {
+            uint32_t carry = base;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) {
+              const uint32_t v = d[i];
+              const uint32_t pair = v + (v << 16);  // (lo, lo + hi)
+              const uint32_t outv = pk_add_u16(pair, carry | (carry << 16));
+              d[i] = want_dbx ? outv : v;
+              carry = outv >> 16;
+            }
+          } else {
+            uint32_t acc = base;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) {
+              acc += d[i];
+              d[i] = want_dbx ? acc : d[i];
+            }
+          }
+        }
       }
-      uint32_t tp[32];
-      read_planes<W>(in, pos, tp, K, L, want_dbx, want_planes);
-      transpose32(tp);
-      if constexpr (W == 16) {
-        // tp[r] = symbol r | symbol r+32 << 16 -> d[i] = symbol 2i | symbol 2i+1 << 16.
+
+      // Raw chunks and RAW blocks: 1024 bits verbatim. ZVC: its payload, the
+      // non-zero symbols in order (the same layout as ZBX's compacted
+      // symbols), spread to their positions below.
+      const bool want_copy = want_raw || want_zvc;
+      if (__ballot(want_copy)) {
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
-          if (i < 16)
-            d[i] = (tp[2 * i] & 0xFFFFu) | (tp[2 * i + 1] << 16);
-          else
-            d[i] = (tp[2 * i - 32] >> 16) | (tp[2 * i - 31] & 0xFFFF0000u);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) d[i] = tp[i];
-      }
-      // DBX: running sum of the deltas from the base symbol, modulo 2^w.
-      if (__ballot(want_dbx)) {
-        if constexpr (W == 16) {
-          uint32_t carry = base;
-#pragma unroll
-          for (int i = 0; i < 32; ++i) {
-            const uint32_t v = d[i];
-            const uint32_t pair = v + (v << 16);  // (lo, lo + hi)
-            const uint32_t outv = pk_add_u16(pair, carry | (carry << 16));
-            d[i] = want_dbx ? outv : v;
-            carry = outv >> 16;
-          }
-        } else {
-          uint32_t acc = base;
-#pragma unroll
-          for (int i = 0; i < 32; ++i) {
-            acc += d[i];
-            d[i] = want_dbx ? acc : d[i];
-          }
+          const uint32_t v = in.peek(pos + 32 * i);
+          d[i] = want_copy ? v : d[i];
         }
       }
+      want_spread = want_zvc || want_zbx;
     }
+    __syncthreads();  // payloads dead: LDS becomes the output rows
 
-    // Raw chunks and RAW blocks: 1024 bits verbatim. ZVC: its payload, the
-    // non-zero symbols in order (the same layout as ZBX's compacted
-    // symbols), spread to their positions below.
-    const bool want_copy = want_raw || want_zvc;
-    if (__ballot(want_copy)) {
+    // --- 4. Output rows. All-zero (and unusable) blocks: zeros. Packed blocks:
+    // their symbols; ZVC and ZBX spread the non-zero symbols to their
+    // positions in place. ---
+    if (!busy) {
+      uint32_t *row = lds + t * kLaneStride;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const uint32_t v = in.peek(pos + 32 * i);
-        d[i] = want_copy ? v : d[i];
-      }
+      for (int i = 0; i < 32; ++i) row[i] = 0;
     }
-    want_spread = want_zvc || want_zbx;
-  }
-  __syncthreads();  // payloads dead: LDS becomes the output rows
-
-  // --- 4. Output rows. All-zero (and unusable) blocks: zeros. Packed blocks:
-  // their symbols; ZVC and ZBX spread the non-zero symbols to their
-  // positions in place. ---
-  if (!busy) {
-    uint32_t *row = lds + t * kLaneStride;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) row[i] = 0;
-  }
-  if (wave_active) {
-    uint32_t *row = lds + sb * kLaneStride;
-    if (active) {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) row[i] = d[i];
-    }
-    if (__ballot(want_spread)) {
-      wave_lds_fence();
-      if (want_spread) {
-        // Symbol i takes compacted symbol rank(i) = number of non-zero symbols
-        // before it. Every read is issued (rank <= N stays inside the padded
-        // row) and the zero positions are selected away, so the reads need no
-        // branches and no wait between them.
-        uint32_t rank = 0;
-        if constexpr (W == 16) {
-          const uint16_t *r16 = reinterpret_cast<const uint16_t *>(row);
-#pragma unroll
-          for (int i = 0; i < 32; ++i) {
-            const bool n0 = (nzmask >> (2 * i)) & 1u, n1 = (nzmask >> (2 * i + 1)) & 1u;
-            const uint32_t a = r16[rank];
-            rank += n0 ? 1u : 0u;
-            const uint32_t b = r16[rank];
-            rank += n1 ? 1u : 0u;
-            d[i] = (n0 ? a : 0u) | ((n1 ? b : 0u) << 16);
-          }
-        } else {
-#pragma unroll
-          for (int k = 0; k < 32; ++k) {
-            const bool n0 = (nzmask >> k) & 1u;
-            const uint32_t a = row[rank];
-            rank += n0 ? 1u : 0u;
-            d[k] = n0 ? a : 0u;
-          }
-        }
-      }
-      wave_lds_fence();
-      if (want_spread) {
+    if (wave_active) {
+      uint32_t *row = lds + sb * kLaneStride;
+      if (active) {
 #pragma unroll
         for (int i = 0; i < 32; ++i) row[i] = d[i];
       }
-    }
-  }
-  __syncthreads();
-
-  // --- 5. Coalesced store of the group's output span (bytes past raw_bytes
-  // are not written). (Each lane storing its own block's 128 bytes from
-  // registers, eight 16-byte stores 128 bytes apart across the lanes, made
-  // decompression 2.8 times slower.) ---
-  const uint64_t span0 = gblock0 * kBlockBytes;
-  const uint64_t span_end = min_u64(raw_bytes, span0 + (uint64_t)kDecThreads * kBlockBytes);
-  const uint32_t span = (uint32_t)(span_end - span0);
+      if (__ballot(want_spread)) {
+        wave_lds_fence();
+        if (want_spread) {
+          // Symbol i takes compacted symbol rank(i) = number of non-zero symbols
+          // before it. Every read is issued (rank <= N stays inside the padded
+          // row) and the zero positions are selected away, so the reads need no
+          // branches and no wait between them.
+          uint32_t rank = 0;
+          if constexpr (W == 16) {
+            const uint16_t *r16 = reinterpret_cast<const uint16_t *>(row);
 #pragma unroll
-  for (int k = 0; k < kBlocksPerChunk / 4; ++k) {
-    const uint32_t u = t + (uint32_t)k * kDecThreads;  // 16-byte unit of the span
-    const uint32_t b0 = 16 * u;
-    if (b0 >= span) continue;
-    const uint32_t *row = lds + (u >> 3) * kLaneStride + 4 * (u & 7);
-    const uint4 v = make_uint4(row[0], row[1], row[2], row[3]);
-    if (b0 + 16 <= span) {
-      // Non-temporal: the codec never reads its output back (1-2% faster).
-      const u32x4 q = {v.x, v.y, v.z, v.w};
-      __builtin_nontemporal_store(q, reinterpret_cast<u32x4 *>(dst + span0 + b0));
-    } else {
-      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-      for (uint32_t bb = b0; bb < span; ++bb)
-        dst[span0 + bb] = (uint8_t)(w4[(bb - b0) >> 2] >> (8 * ((bb - b0) & 3)));
+            for (int i = 0; i < 32; ++i) {
+              const bool n0 = (nzmask >> (2 * i)) & 1u, n1 = (nzmask >> (2 * i + 1)) & 1u;
+              const uint32_t a = r16[rank];
+              rank += n0 ? 1u : 0u;
+              const uint32_t b = r16[rank];
+              rank += n1 ? 1u : 0u;
+              d[i] = (n0 ? a : 0u) | ((n1 ? b : 0u) << 16);
+            }
+          } else {
+#pragma unroll
+            for (int k = 0; k < 32; ++k) {
+              const bool n0 = (nzmask >> k) & 1u;
+              const uint32_t a = row[rank];
+              rank += n0 ? 1u : 0u;
+              d[k] = n0 ? a : 0u;
+            }
+          }
+        }
+        wave_lds_fence();
+        if (want_spread) {
+#pragma unroll
+          for (int i = 0; i < 32; ++i) row[i] = d[i];
+        }
+      }
     }
-  }
+    __syncthreads();
+
+    // --- 5. Coalesced store of the group's output span (bytes past raw_bytes
+    // are not written). (Each lane storing its own block's 128 bytes from
+    // registers, eight 16-byte stores 128 bytes apart across the lanes, made
+    // decompression 2.8 times slower.) ---
+    const uint64_t span0 = gblock0 * kBlockBytes;
+    const uint64_t span_end = min_u64(raw_bytes, span0 + (uint64_t)kDecThreads * kBlockBytes);
+    const uint32_t span = (uint32_t)(span_end - span0);
+#pragma unroll
+    for (int k = 0; k < kBlocksPerChunk / 4; ++k) {
+      const uint32_t u = t + (uint32_t)k * kDecThreads;  // 16-byte unit of the span
+      const uint32_t b0 = 16 * u;
+      if (b0 >= span) continue;
+      const uint32_t *row = lds + (u >> 3) * kLaneStride + 4 * (u & 7);
+      const uint4 v = make_uint4(row[0], row[1], row[2], row[3]);
+      if (b0 + 16 <= span) {
+        // Non-temporal: the codec never reads its output back (1-2% faster).
+        const u32x4 q = {v.x, v.y, v.z, v.w};
+        __builtin_nontemporal_store(q, reinterpret_cast<u32x4 *>(dst + span0 + b0));
+      } else {
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+        for (uint32_t bb = b0; bb < span; ++bb)
+          dst[span0 + bb] = (uint8_t)(w4[(bb - b0) >> 2] >> (8 * ((bb - b0) & 3)));
+      }
+    }
   }
 }
 
@@ -1003,10 +1014,11 @@ __global__ __launch_bounds__(kDecThreads, 4) void decompress_kernel(const DBatch
                                                                    uint32_t *tile_counter, uint32_t counter_base,
                                                                    uint32_t *done, uint32_t done_base, DMode mode) {
   __shared__ union {
-    LocateShared l;
+    LocateShared<G> l;
     DecodeShared d;
   } sh;
   __shared__ uint32_t ticket_s;
+  static_assert(locate_chunks<G>() == 8 * kDecodeChunks, "a locate tile is eight decode groups");
   const uint32_t t = threadIdx.x;
   if (t == 0) ticket_s = atomicAdd(tile_counter, 1u) - counter_base;
   __syncthreads();
@@ -1056,10 +1068,6 @@ hipError_t launch_empty_status(int32_t *status, uint64_t comp_bytes, hipStream_t
   return hipGetLastError();
 }
 
-uint32_t locate_tiles(uint64_t raw_bytes) {
-  const uint64_t nchunks = (raw_bytes + kChunkBytes - 1) / kChunkBytes;
-  return (uint32_t)((nchunks + kLocateChunks - 1) / kLocateChunks);
-}
 
 uint32_t decode_groups(uint64_t raw_bytes) {
   const uint64_t nchunks = (raw_bytes + kChunkBytes - 1) / kChunkBytes;
@@ -1079,8 +1087,23 @@ size_t decompress_extra(uint64_t raw_bytes) {
 // the single launch was 10-12% faster.
 constexpr uint32_t kFusedMinTiles = 512;
 
+void plan_decompress(int w, DBatch &b) {
+  uint64_t tiles = 0;
+  for (uint32_t k = 0; k < b.n; ++k) tiles += (b.t[k].nchunks + kLocateChunks - 1) / kLocateChunks;
+  b.fused = tiles >= kFusedMinTiles ? 1u : 0u;
+  b.locate_lanes = !b.fused && w == 32 ? kLocateLanesWide : kLocateLanes;
+  const uint64_t per_tile = (uint64_t)kLocateThreads / b.locate_lanes;
+  b.total_tiles = 0;
+  for (uint32_t k = 0; k < b.n; ++k) {
+    DTensor &x = b.t[k];
+    x.tile_begin = b.total_tiles;
+    x.ntiles = (uint32_t)((x.nchunks + per_tile - 1) / per_tile);
+    b.total_tiles += x.ntiles;
+  }
+}
+
 ScratchNeed decompress_need(const DBatch &b, size_t extra) {
-  if (b.total_tiles >= kFusedMinTiles)
+  if (b.fused)
     return ScratchNeed{b.total_tiles * kLookbackStride, extra, (1 + kDecodeTickets) * b.total_tiles, b.total_tiles};
   return ScratchNeed{b.total_tiles * kLookbackStride, extra, b.total_tiles, 0};
 }
@@ -1095,7 +1118,7 @@ hipError_t launch_decompress(int w, DBatch &batch, uint32_t codec_mask, int tagg
     x.block_off = reinterpret_cast<uint16_t *>(extra + ((x.nchunks + 1) & ~1ull) * 8);
     extra += decompress_extra(x.raw_bytes);
   }
-  if (batch.total_tiles >= kFusedMinTiles) {
+  if (batch.fused) {
     const dim3 grid((1 + kDecodeTickets) * batch.total_tiles);  // T locate tiles, then the decode tickets
     if (w == 16)
       hipLaunchKernelGGL((decompress_kernel<16, kLocateLanes>), grid, dim3(kDecThreads), 0, stream, batch, scratch.err,
@@ -1108,12 +1131,14 @@ hipError_t launch_decompress(int w, DBatch &batch, uint32_t codec_mask, int tagg
     return hipGetLastError();
   }
   const dim3 grid_a(batch.total_tiles);
-  if (w == 16)
+  if (w == 16 && batch.locate_lanes == kLocateLanes)
     hipLaunchKernelGGL((locate_kernel<16, kLocateLanes>), grid_a, dim3(kLocateThreads), 0, stream, batch,
                        scratch.err, scratch.epoch, scratch.words, scratch.counter, scratch.counter_base, mode);
-  else
-    hipLaunchKernelGGL((locate_kernel<32, kLocateLanes>), grid_a, dim3(kLocateThreads), 0, stream, batch,
+  else if (w == 32 && batch.locate_lanes == kLocateLanesWide)
+    hipLaunchKernelGGL((locate_kernel<32, kLocateLanesWide>), grid_a, dim3(kLocateThreads), 0, stream, batch,
                        scratch.err, scratch.epoch, scratch.words, scratch.counter, scratch.counter_base, mode);
+  else
+    return hipErrorInvalidValue;  // a batch that plan_decompress did not number
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid_b(batch.total_groups);

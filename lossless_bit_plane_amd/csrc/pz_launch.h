@@ -76,13 +76,14 @@ struct DBatch {
   uint32_t n;
   uint32_t total_tiles;
   uint32_t total_groups;
+  uint32_t fused;         // 1: one kernel locates and decodes; 0: locate, then decode
+  uint32_t locate_lanes;  // lanes per chunk in locate (chunks per tile: 256 / locate_lanes)
   DTensor t[kMaxBatch];
 };
 
-// Compress: tiles of the tensors (CTensor::ntiles). Decompress: locate tiles
-// and decode groups of a tensor, and its per-call bytes (16-byte multiple).
+// Compress: tiles of the tensors (CTensor::ntiles). Decompress: decode groups
+// of a tensor, and its per-call bytes (16-byte multiple).
 uint32_t compress_tiles(uint64_t raw_bytes);
-uint32_t locate_tiles(uint64_t raw_bytes);
 uint32_t decode_groups(uint64_t raw_bytes);
 size_t decompress_extra(uint64_t raw_bytes);
 
@@ -126,7 +127,11 @@ hipError_t launch_compress(int w, const CBatch &batch, uint32_t codec_mask, int 
                            const Scratch &scratch, hipStream_t stream);
 hipError_t launch_decompress(int w, DBatch &batch, uint32_t codec_mask, int tagged,
                              const Scratch &scratch, hipStream_t stream);
-// The scratch a decompress launch of the batch needs (its tiles and groups filled in).
+// Chooses a decompress batch's launch form from the symbol width and its
+// chunk count (fused, locate_lanes) and numbers its locate tiles (tile_begin,
+// ntiles, total_tiles); nchunks of every tensor must be set.
+void plan_decompress(int w, DBatch &batch);
+// The scratch a decompress launch of the batch needs (plan_decompress done, groups filled in).
 ScratchNeed decompress_need(const DBatch &batch, size_t extra);
 // Status of a decompress call with no chunks: corrupt unless comp_bytes is 0.
 hipError_t launch_empty_status(int32_t *status, uint64_t comp_bytes, hipStream_t stream);

@@ -209,13 +209,19 @@ def test_oracle_streams_decode_on_gpu(pz, workload_tensors):
         assert st == 0 and np.array_equal(back, t.data)
 
 
-def test_corrupt_streams_status_matches_oracle(pz):
+@pytest.mark.parametrize("w", [16, 32])
+def test_corrupt_streams_status_matches_oracle(pz, w):
     """Random bit flips, truncations and header edits: the GPU status equals
-    the oracle's, and a good stream decodes."""
-    (base,) = pzinputs.relu_smoke()
-    data = base.data[: 24 * 4096 + 777].copy()
-    t = pzinputs.Tensor("corrupt_base", data, 0, 16)
-    stream = oracle.compress(data, 16)
+    the oracle's, and a good stream decodes. 16-bit symbols (ReLU BF16) and
+    32-bit symbols (ReLU FP32, whose walk takes 8 lanes per chunk)."""
+    if w == 16:
+        (base,) = pzinputs.relu_smoke()
+        data = base.data[: 24 * 4096 + 777].copy()
+    else:
+        x = np.random.default_rng(23).standard_normal(24 * 1024 + 200, dtype=np.float32)
+        data = np.maximum(np.float32(0.5) * x, np.float32(0)).view(np.uint8)[: 24 * 4096 + 777].copy()
+    t = pzinputs.Tensor("corrupt_base", data, 0 if w == 16 else 1, w)
+    stream = oracle.compress(data, w)
     rng = np.random.default_rng(9)
     C = oracle.num_chunks(data.size)
     cases = []
@@ -235,11 +241,11 @@ def test_corrupt_streams_status_matches_oracle(pz):
     cases.append(np.concatenate([stream, np.zeros(3, np.uint8)]))
     agree = 0
     for s in cases:
-        o = oracle.decompress_status(s, data.size, 16)
+        o = oracle.decompress_status(s, data.size, w)
         st, back = _gpu_decompress(pz, s, t)
         assert st == (0 if o == oracle.OK else 3), (o, st)
         if o == oracle.OK:
-            assert np.array_equal(back, oracle.decompress(s, data.size, 16))
+            assert np.array_equal(back, oracle.decompress(s, data.size, w))
         agree += 1
     assert agree == len(cases)
 
