@@ -1087,6 +1087,8 @@ size_t decompress_extra(uint64_t raw_bytes) {
 // the single launch was 10-12% faster.
 constexpr uint32_t kFusedMinTiles = 512;
 
+// The form is chosen on the launch's count of 64-chunk tiles; outside the
+// single kernel, 32-bit symbols walk with 8 lanes per chunk, in tiles of 32.
 void plan_decompress(int w, DBatch &b) {
   uint64_t tiles = 0;
   for (uint32_t k = 0; k < b.n; ++k) tiles += (b.t[k].nchunks + kLocateChunks - 1) / kLocateChunks;
