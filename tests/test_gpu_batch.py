@@ -250,6 +250,25 @@ def test_batch_single_launch_length_corruption_fp32(pz):
         assert np.array_equal(outs[i][: d.size].cpu().numpy(), d), i
 
 
+def test_batch_two_kernel_fp32_eight_lanes(pz):
+    """Five FP32 CNN tensors in one batch: 490 tiles of 64 chunks, just
+    under the single kernel's threshold, so locate walks with 8 lanes per
+    chunk in 980 tiles of 32 chunks. A length-corrupt stream in the middle
+    reports corruption; the others decompress exactly."""
+    (t,) = pzinputs.cnn_feature_maps_fp32()
+    d = t.data
+    good = oracle.compress(d, 32, threads=THREADS)
+    long_ = np.concatenate([good, np.zeros(16, np.uint8)])
+    assert oracle.decompress_status(long_, d.size, 32) != oracle.OK
+    streams = [good, good, long_, good, good]
+    print("[batch] two-kernel decompress, five FP32 streams (8 lanes per chunk)", flush=True)
+    outs, status = pz.pz_decompress_batch([_dev(x) for x in streams], [x.size for x in streams],
+                                          [d.size] * len(streams), pzinputs.FP32, 32)
+    assert status.cpu().tolist() == [0, 0, 3, 0, 0]
+    for i in (0, 1, 3, 4):
+        assert np.array_equal(outs[i][: d.size].cpu().numpy(), d), i
+
+
 def test_batch_single_launch_concurrent_streams(pz):
     """Two single-kernel decompress launches (768 and 588 locate tiles) on
     two streams with nothing ordering them, three times over: each stream's
